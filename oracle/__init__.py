@@ -1,0 +1,191 @@
+"""CPU oracle for the quantized-momentum Muon step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library and the product path never calls it.
+
+Parts:
+  * q8 momentum update, group sums and the scale pass: plain C in q8.c
+    (binary32 with the exact operation order, fp64 sums), wrapped here;
+  * norm plans: expansion of norm segments into one group id per block;
+  * Newton-Schulz, blocked Newton-Schulz and the block-periodic schedule:
+    fp64 numpy in ns.py / muonbp.py;
+  * the GRASP 4-bit momentum step: grasp.py.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+BLOCK = 256
+F32, BF16, F16 = 0, 1, 2
+
+_lib = None
+
+
+def lib():
+    """Load liboracle.so, compiling it first if it is not there yet."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.or_bf16_from_f32.argtypes = [ctypes.c_float]
+        L.or_bf16_from_f32.restype = ctypes.c_uint16
+        L.or_f16_from_f32.argtypes = [ctypes.c_float]
+        L.or_f16_from_f32.restype = ctypes.c_uint16
+        L.or_q8_update.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p]
+        L.or_q8_update.restype = None
+        L.or_group_sums.argtypes = [p, p, i64, ctypes.c_int32, p]
+        L.or_group_inv_norm.argtypes = [p, ctypes.c_int32, ctypes.c_float, p]
+        L.or_scale_by_group.argtypes = [p, ctypes.c_int, i64, p, p]
+        L.or_round_array.argtypes = [p, i64, ctypes.c_int, p]
+        L.or_widen_array.argtypes = [p, i64, ctypes.c_int, p]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _grad_dtype(a):
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError("pass fp32 arrays directly; 16-bit grads as (uint16 bits, dtype)")
+
+
+# ------------------------------------------------------------------ dtypes
+
+def round_to(x, dtype):
+    """fp32 array -> uint16 bit patterns of bf16 (dtype=BF16) or f16 (F16), RNE."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().or_round_array(_ptr(x), x.size, dtype, _ptr(out))
+    return out
+
+
+def widen(bits, dtype):
+    """uint16 bit patterns of bf16/f16 -> fp32 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float32)
+    lib().or_widen_array(_ptr(bits), bits.size, dtype, _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------- q8 update
+
+def q8_update(codes, absmax, grad, beta, dtype=F32):
+    """One tensor's q8 momentum update ("Quantized Muon Momentum", "Algorithm").
+
+    codes  : int8 [numel]      prior state codes
+    absmax : float32 [nblk]    prior per-256-block absmax
+    grad   : float32 [numel] (dtype F32) or uint16 bits (BF16/F16)
+    Returns (codes', absmax', m_stored, block_sumsq): the new state, m rounded
+    to the grad dtype (what lands in the grad buffer) and fp64 sum of m^2 per
+    block.  Inputs are not modified.
+    """
+    codes = np.array(codes, dtype=np.int8, copy=True).ravel()
+    absmax = np.array(absmax, dtype=np.float32, copy=True).ravel()
+    if dtype == F32:
+        g = np.array(grad, dtype=np.float32, copy=True).ravel()
+    else:
+        g = np.array(grad, dtype=np.uint16, copy=True).ravel()
+    numel = codes.size
+    nblk = (numel + BLOCK - 1) // BLOCK
+    if absmax.size != nblk or g.size != numel:
+        raise ValueError("shape mismatch between codes, absmax and grad")
+    sums = np.empty(nblk, dtype=np.float64)
+    lib().or_q8_update(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel,
+                       ctypes.c_float(beta), _ptr(sums))
+    return codes, absmax, g, sums
+
+
+# -------------------------------------------------------------- norm plans
+
+def expand_segments(numels, segments, ngroups):
+    """Norm segments -> one int32 group id per 256-block, per tensor.
+
+    segments: iterable of (tensor_index, start, length, group_id), element
+    offsets into the flattened tensor ("Quantized Muon Momentum", "Grouped QKV
+    And Sharding").  Every segment starts on a block boundary and ends on one
+    unless it ends at the tensor's end; every block of every tensor belongs to
+    exactly one segment (our reading: an uncovered block would silently skip
+    normalisation).  Raises ValueError otherwise.
+    """
+    ids = [np.full((n + BLOCK - 1) // BLOCK, -1, dtype=np.int32) for n in numels]
+    for (t, start, length, gid) in segments:
+        n = numels[t]
+        if not (0 <= gid < ngroups):
+            raise ValueError("group id out of range")
+        if length <= 0 or start < 0 or start + length > n:
+            raise ValueError("segment outside its tensor")
+        if start % BLOCK:
+            raise ValueError("segment start not block aligned")
+        end = start + length
+        if end % BLOCK and end != n:
+            raise ValueError("segment end not block aligned")
+        b0, b1 = start // BLOCK, (end + BLOCK - 1) // BLOCK
+        if np.any(ids[t][b0:b1] != -1):
+            raise ValueError("overlapping segments")
+        ids[t][b0:b1] = gid
+    for a in ids:
+        if np.any(a < 0):
+            raise ValueError("block not covered by any segment")
+    return ids
+
+
+def group_sums(block_sums, block_groups, ngroups):
+    """S_g = sum of block sums of group g, tensors in order, blocks ascending."""
+    bs = np.ascontiguousarray(np.concatenate(block_sums), dtype=np.float64)
+    bg = np.ascontiguousarray(np.concatenate(block_groups), dtype=np.int32)
+    out = np.empty(ngroups, dtype=np.float64)
+    lib().or_group_sums(_ptr(bs), _ptr(bg), bs.size, ngroups, _ptr(out))
+    return out
+
+
+def group_inv_norm(sums, eps):
+    """inv_g = 1/(sqrt(S_g) + eps) in fp64, rounded to fp32."""
+    sums = np.ascontiguousarray(sums, dtype=np.float64)
+    out = np.empty(sums.size, dtype=np.float32)
+    lib().or_group_inv_norm(_ptr(sums), sums.size, ctypes.c_float(eps), _ptr(out))
+    return out
+
+
+def scale_by_group(grad, dtype, block_group, inv):
+    """Scale pass: grad <- round(float(grad) * inv[group]) (returns a copy)."""
+    g = np.array(grad, dtype=np.float32 if dtype == F32 else np.uint16, copy=True).ravel()
+    bg = np.ascontiguousarray(block_group, dtype=np.int32)
+    inv = np.ascontiguousarray(inv, dtype=np.float32)
+    lib().or_scale_by_group(_ptr(g), dtype, g.size, _ptr(bg), _ptr(inv))
+    return g
+
+
+def update_normalize_groups(states, grads, dtypes, segments, ngroups, beta,
+                            eps, write_normalized=True):
+    """Multi-tensor q8 update + grouped Frobenius normalisation.
+
+    states : list of (codes, absmax); grads: list of fp32 arrays or uint16
+    bits; dtypes: list of F32/BF16/F16.  Returns (new_states, grads_out,
+    group_sums, inv_norm, block_groups).  grads_out holds m (rounded to the
+    grad dtype) and, with write_normalized, m scaled by its group's inverse
+    norm ("Quantized Muon Momentum", "What Exists" and "Grouped QKV And
+    Sharding").
+    """
+    numels = [np.asarray(c).size for (c, _) in states]
+    bgs = expand_segments(numels, segments, ngroups)
+    new_states, outs, bsums = [], [], []
+    for (c, a), g, dt in zip(states, grads, dtypes):
+        c2, a2, m, s = q8_update(c, a, g, beta, dt)
+        new_states.append((c2, a2))
+        outs.append(m)
+        bsums.append(s)
+    S = group_sums(bsums, bgs, ngroups)
+    inv = group_inv_norm(S, eps)
+    if write_normalized:
+        outs = [scale_by_group(m, dt, bg, inv) for m, dt, bg in zip(outs, dtypes, bgs)]
+    return new_states, outs, S, inv, bgs

@@ -1,0 +1,226 @@
+/*
+ * CPU oracle for the blockwise-int8 ("q8") Muon momentum update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code with the HIP library.
+ *
+ * Built with gcc -O2 -fopenmp -ffp-contract=off (no fast-math, no FTZ), so
+ * every float expression below is evaluated in IEEE binary32 with one
+ * rounding per operation, in exactly the order written.
+ *
+ * Source: "Quantized Muon Momentum" (cppmega docs), sections
+ *   - "What Exists": state = int8 codes (same shape as the momentum) plus
+ *     one fp32 absmax per block of 256 elements; symmetric nearest rounding
+ *     with effective range [-127, 127];
+ *   - "Algorithm": per 256-element block: load codes and absmax, dequantise
+ *     in fp32, load the grad, m = beta*old + (1-beta)*grad, store m into the
+ *     grad buffer, new block absmax, requantise, store codes and absmax,
+ *     optionally accumulate the block sum of m*m;
+ *   - "Grouped QKV And Sharding": one sum of squares per logical norm group,
+ *     then every block scaled by its group norm.
+ *
+ * Readings where the page is silent (each listed in the design notes):
+ *   - dequantisation order: old = (float)code * (absmax / 127);
+ *   - the EMA is two separately rounded products and one rounded sum (no FMA);
+ *   - "nearest" rounding is round-half-to-even (rintf in the default mode);
+ *   - an all-zero block stores codes 0 and absmax 0;
+ *   - the new absmax is taken over the fp32 m (before rounding m to the grad
+ *     dtype), and so is the block sum of squares;
+ *   - block sums of squares are accumulated in fp64 (squares of fp32 values
+ *     are exact in fp64); group sums add block sums in ascending block order;
+ *   - group inverse norm = (float)(1 / (sqrt(S_g) + eps)) computed in fp64;
+ *   - the scale pass rounds float(stored grad) * inv to the grad dtype
+ *     (round to nearest even).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define OR_BLOCK 256
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+
+/* ---------------------------------------------------------------- dtypes */
+
+static uint32_t bits_of(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float float_of(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* binary32 -> bfloat16, round to nearest, ties to even; NaN stays NaN (quiet). */
+uint16_t or_bf16_from_f32(float f)
+{
+    uint32_t u = bits_of(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep = u >> 16;
+    uint32_t rest = u & 0xffffu;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u)))
+        keep += 1u;            /* carries into the exponent correctly, incl. to inf */
+    return (uint16_t)keep;
+}
+
+float or_f32_from_bf16(uint16_t h) { return float_of((uint32_t)h << 16); }
+
+/* binary32 -> binary16, round to nearest, ties to even, with subnormals. */
+uint16_t or_f16_from_f32(float f)
+{
+    const uint32_t u = bits_of(f);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u)                 /* NaN: quiet */
+        return (uint16_t)(sign | 0x7e00u);
+    if (a >= 0x477ff000u)                /* |f| >= 65520 rounds to infinity */
+        return (uint16_t)(sign | 0x7c00u);
+    if (a >= 0x38800000u) {              /* |f| >= 2^-14: normal binary16 */
+        const uint32_t r = a - 0x38000000u;   /* exponent bias 127 -> 15 */
+        uint32_t q = r >> 13;
+        const uint32_t rem = r & 0x1fffu;
+        if (rem > 0x1000u || (rem == 0x1000u && (q & 1u)))
+            q += 1u;                     /* a carry moves into the exponent */
+        return (uint16_t)(sign | q);
+    }
+    if (a < 0x33000000u)                 /* |f| < 2^-25 rounds to zero */
+        return sign;
+    /* binary16 subnormal: |f| = sig * 2^(E-150); the unit is 2^-24 */
+    const uint32_t E = a >> 23;
+    const uint32_t sig = (a & 0x7fffffu) | 0x800000u;
+    const uint32_t s = 126u - E;         /* 14 .. 24 */
+    uint32_t q = sig >> s;
+    const uint32_t rem = sig & ((1u << s) - 1u);
+    const uint32_t half = 1u << (s - 1u);
+    if (rem > half || (rem == half && (q & 1u)))
+        q += 1u;
+    return (uint16_t)(sign | q);
+}
+
+float or_f32_from_f16(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t ex = (h >> 10) & 0x1fu;
+    uint32_t man = h & 0x3ffu;
+    if (ex == 0x1fu)
+        return float_of(sign | 0x7f800000u | (man << 13));
+    if (ex == 0) {
+        /* subnormal: man * 2^-24, exact in binary32 */
+        float v = (float)man * 5.9604644775390625e-08f;
+        return sign ? -v : v;
+    }
+    return float_of(sign | ((ex - 15 + 127) << 23) | (man << 13));
+}
+
+static float load_grad(const void *grad, int dtype, int64_t i)
+{
+    if (dtype == OR_F32) return ((const float *)grad)[i];
+    if (dtype == OR_BF16) return or_f32_from_bf16(((const uint16_t *)grad)[i]);
+    return or_f32_from_f16(((const uint16_t *)grad)[i]);
+}
+
+static void store_grad(void *grad, int dtype, int64_t i, float v)
+{
+    if (dtype == OR_F32) ((float *)grad)[i] = v;
+    else if (dtype == OR_BF16) ((uint16_t *)grad)[i] = or_bf16_from_f32(v);
+    else ((uint16_t *)grad)[i] = or_f16_from_f32(v);
+}
+
+/* ------------------------------------------------------------ q8 update */
+
+/*
+ * One tensor of `numel` elements.  codes/absmax hold the prior state and are
+ * overwritten with the new state; grad holds g and is overwritten with m
+ * rounded to its dtype.  block_sumsq (nullable) receives one fp64 sum of m*m
+ * per block.  Blocks are [256 b, min(numel, 256 b + 256)): the last block of
+ * a tensor covers the remainder.
+ */
+void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
+                  int64_t numel, float beta, double *block_sumsq)
+{
+    const int64_t nblk = (numel + OR_BLOCK - 1) / OR_BLOCK;
+    const float omb = 1.0f - beta;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; b++) {
+        const int64_t lo = b * OR_BLOCK;
+        const int64_t hi = (lo + OR_BLOCK < numel) ? lo + OR_BLOCK : numel;
+        float m[OR_BLOCK];
+        /* dequantise the old momentum, apply the EMA */
+        const float step = absmax[b] / 127.0f;
+        float amax = 0.0f;
+        for (int64_t i = lo; i < hi; i++) {
+            const float old = (float)codes[i] * step;
+            const float g = load_grad(grad, dtype, i);
+            const float t1 = beta * old;
+            const float t2 = omb * g;
+            const float mi = t1 + t2;
+            m[i - lo] = mi;
+            const float a = fabsf(mi);
+            if (a > amax) amax = a;
+        }
+        /* m goes back into the grad buffer */
+        for (int64_t i = lo; i < hi; i++)
+            store_grad(grad, dtype, i, m[i - lo]);
+        /* requantise against the new block absmax */
+        if (amax == 0.0f) {
+            for (int64_t i = lo; i < hi; i++) codes[i] = 0;
+        } else {
+            const float inv = 127.0f / amax;
+            for (int64_t i = lo; i < hi; i++) {
+                float q = rintf(m[i - lo] * inv);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+                codes[i] = (int8_t)q;
+            }
+        }
+        absmax[b] = amax;
+        if (block_sumsq) {
+            double s = 0.0;
+            for (int64_t i = lo; i < hi; i++) {
+                const double d = (double)m[i - lo];
+                s += d * d;
+            }
+            block_sumsq[b] = s;
+        }
+    }
+}
+
+/* --------------------------------------------------------- group norms */
+
+/* S_g = sum of block sums of group g, blocks visited in ascending order. */
+void or_group_sums(const double *block_sumsq, const int32_t *block_group,
+                   int64_t nblk, int32_t ngroups, double *group_sums)
+{
+    for (int32_t g = 0; g < ngroups; g++) group_sums[g] = 0.0;
+    for (int64_t b = 0; b < nblk; b++)
+        group_sums[block_group[b]] += block_sumsq[b];
+}
+
+/* inv_g = 1 / (||M_g||_F + eps), evaluated in fp64 and rounded to fp32. */
+void or_group_inv_norm(const double *group_sums, int32_t ngroups, float eps,
+                       float *inv)
+{
+    for (int32_t g = 0; g < ngroups; g++)
+        inv[g] = (float)(1.0 / (sqrt(group_sums[g]) + (double)eps));
+}
+
+/* Scale pass: grad <- round_dtype(float(grad) * inv[group of its block]). */
+void or_scale_by_group(void *grad, int dtype, int64_t numel,
+                       const int32_t *block_group, const float *inv)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < numel; i++) {
+        const float s = inv[block_group[i / OR_BLOCK]];
+        store_grad(grad, dtype, i, load_grad(grad, dtype, i) * s);
+    }
+}
+
+/* Round an fp32 array to bf16 / f16 bit patterns (used to build inputs). */
+void or_round_array(const float *src, int64_t n, int dtype, uint16_t *dst)
+{
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = dtype == OR_BF16 ? or_bf16_from_f32(src[i]) : or_f16_from_f32(src[i]);
+}
+
+void or_widen_array(const uint16_t *src, int64_t n, int dtype, float *dst)
+{
+    for (int64_t i = 0; i < n; i++)
+        dst[i] = dtype == OR_BF16 ? or_f32_from_bf16(src[i]) : or_f32_from_f16(src[i]);
+}
