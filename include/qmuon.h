@@ -1,0 +1,246 @@
+/*
+ * qmuon.h -- C ABI of libqmuon.so: one Muon optimizer step on an AMD MI355X
+ * (gfx950), as a blockwise-int8 momentum update followed by quintic
+ * Newton-Schulz orthogonalisation.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless a parameter says "host".
+ *   - The caller owns every buffer (state, grads, weights, plan copies,
+ *     workspace).  The library never allocates or frees device memory, never
+ *     synchronises the stream and never prints.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  A call returns after enqueueing.
+ *   - All arguments are validated on the host before anything is enqueued;
+ *     on any validation error nothing is launched and no buffer is written.
+ *     A launch failure returns QM_E_HIP; buffers may then be partly updated.
+ *   - qm_last_error() gives a per-thread description of the last failure.
+ *   - Calls that share buffers or workspace on one stream run in order; the
+ *     same workspace must not be used by two streams at once.
+ */
+#ifndef QMUON_H
+#define QMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QM_ABI_VERSION 1
+#define QM_BLOCK 256           /* quantisation block: elements per absmax */
+
+typedef void *qm_stream_t;     /* hipStream_t */
+
+#ifndef QM_API
+#define QM_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    QM_OK = 0,
+    QM_E_ARG = 1,          /* null pointer, bad count, bad hyperparameter   */
+    QM_E_ALIGN = 2,        /* pointer or segment alignment violated          */
+    QM_E_DTYPE = 3,        /* unknown or unsupported dtype                   */
+    QM_E_SHAPE = 4,        /* shapes inconsistent or not divisible           */
+    QM_E_WORKSPACE = 5,    /* workspace missing or too small                 */
+    QM_E_HIP = 6,          /* a HIP launch or runtime call failed            */
+    QM_E_UNSUPPORTED = 7,  /* valid request outside what is implemented      */
+    QM_E_PLAN = 8          /* plan blob malformed or of another version      */
+} qm_status;
+
+typedef enum { QM_F32 = 0, QM_BF16 = 1, QM_F16 = 2 } qm_dtype;
+
+/* Newton-Schulz arithmetic: bf16 operands with fp32 accumulation (X, A, B
+ * all held in bf16), or fp32 operands with fp32 accumulation. */
+typedef enum { QM_NS_BF16 = 0, QM_NS_F32 = 1 } qm_ns_precision;
+
+/* ------------------------------------------------------------------------
+ * q8 momentum state and norm plans
+ *
+ * State of one tensor ("Quantized Muon Momentum", section "What Exists"):
+ * `codes` int8 of the tensor's size and one fp32 absmax per 256-element block
+ * (the last block of a tensor covers the remainder).  Codes lie in
+ * [-127, 127]; element i dequantises to codes[i] * (absmax[i/256] / 127).
+ * Tensors are contiguous ("Known Limitations": contiguous only).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int8_t *codes;      /* [numel], 16-byte aligned, in/out                  */
+    float *absmax;      /* [ceil(numel/256)], 4-byte aligned, in/out         */
+    void *grad;         /* [numel] of grad_dtype, 16-byte aligned; in: g,
+                           out: m (optionally normalised)                    */
+    int64_t numel;      /* > 0                                               */
+    int32_t grad_dtype; /* qm_dtype                                          */
+    int32_t reserved;   /* must be 0                                         */
+} qm_q8_tensor;
+
+/* One slice of a tensor assigned to a norm group ("Quantized Muon Momentum",
+ * section "Grouped QKV And Sharding": fused Q, K and V use one group each).
+ * `start` and `length` are element offsets into the flattened tensor.  A
+ * segment starts on a 256-element boundary and ends on one unless it ends at
+ * the tensor's last element.  Every block of every tensor must belong to
+ * exactly one segment. */
+typedef struct {
+    int32_t tensor_index;
+    int32_t group_id;   /* 0 .. n_groups-1                                   */
+    int64_t start;
+    int64_t length;
+} qm_norm_segment;
+
+/* Build a plan blob (host only; touches no GPU).  The blob records the
+ * tensors' device pointers, one group id per block and the blocks of every
+ * group; it is built once and reused for every step.  The caller copies the
+ * bytes verbatim into device memory once (8-byte aligned) and passes both
+ * copies to the update calls.
+ *   host_blob == NULL: only *inout_blob_bytes is set to the size needed.
+ *   Otherwise *inout_blob_bytes must be >= that size; it is set to the size
+ *   written.
+ * Errors: QM_E_ARG (null/counts/group ids), QM_E_ALIGN (pointer alignment or
+ * segment boundaries), QM_E_SHAPE (overlap or an uncovered block), QM_E_DTYPE. */
+QM_API qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tensors,
+                         const qm_norm_segment *segments, int32_t n_segments,
+                         int32_t n_groups, void *host_blob,
+                         size_t *inout_blob_bytes);
+
+/* Plan facts read back from a host blob (any out pointer may be NULL). */
+QM_API qm_status qm_plan_info(const void *host_blob, int32_t *n_tensors,
+                       int32_t *n_groups, int64_t *n_blocks,
+                       int64_t *total_numel);
+
+/* Workspace bytes qmuon_update_normalize_groups needs for this plan. */
+QM_API size_t qm_update_workspace_bytes(const void *host_blob);
+
+/* In-place multi-tensor q8 update in one launch ("Quantized Muon Momentum",
+ * sections "What Exists" and "Algorithm"): for every block of every tensor,
+ * dequantise the old momentum in fp32, m = beta*old + (1-beta)*g (two
+ * separately rounded products, one rounded sum), write m to the grad buffer
+ * (round to nearest even into its dtype), absmax' = max|m| over the block,
+ * codes' = clamp(rint(m * (127/absmax')), -127, 127), or codes 0 and absmax 0
+ * for an all-zero block.  Codes and absmax are bit-identical to a CPU run of
+ * the same IEEE binary32 operations.
+ *   block_sumsq: nullable; if given, [n_blocks] fp64 receives each block's
+ *   sum of m*m (fp32 m, fp64 accumulation), indexed by global block (tensors
+ *   in plan order).
+ * Errors: QM_E_ARG, QM_E_PLAN, QM_E_HIP. */
+QM_API qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan,
+                             float beta, double *block_sumsq,
+                             qm_stream_t stream);
+
+/* The update plus grouped Frobenius normalisation ("Quantized Muon
+ * Momentum", section "Grouped QKV And Sharding"): the update kernel
+ * accumulates per-block sums of m*m; S_g sums them per group (fp64, fixed
+ * order, no atomics); inv_g = (float)(1 / (sqrt(S_g) + eps)).
+ *   write_normalized = 1: every grad element becomes
+ *     round(float(m_stored) * inv_g) (the page's in-place semantics);
+ *   write_normalized = 0: grads keep m and only inv_g is produced, for a
+ *     Newton-Schulz call to fold in.
+ *   group_inv_norm: nullable [n_groups] fp32 out.
+ *   group_sumsq:    nullable [n_groups] fp64 out (S_g).
+ *   ws: >= qm_update_workspace_bytes(host_plan) bytes, 256-byte aligned.
+ * Errors: QM_E_ARG, QM_E_PLAN, QM_E_WORKSPACE, QM_E_HIP. */
+QM_API qm_status qmuon_update_normalize_groups(const void *host_plan,
+                                        const void *dev_plan, float beta,
+                                        float eps, int32_t write_normalized,
+                                        float *group_inv_norm,
+                                        double *group_sumsq, void *ws,
+                                        size_t ws_bytes, qm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Newton-Schulz orthogonalisation
+ *
+ * Per matrix X0 (rows x cols, row stride ld elements): if rows > cols the
+ * iteration runs on X0^T so the Gram matrix is min(rows, cols) square
+ * ("MuonBP ...", key design 1, FLOP model with m <= n).  X0 is the input
+ * times inv_norm[i] when given, else the input / (||input||_F + eps).  Then
+ * T times ("NVIDIA ... Megatron", "Newton-Schulz distribuido": three products
+ * per iteration):   A = X X^T;  B = b A + c A A;  X = a X + B X.
+ * The first two products are symmetric and computed on lower-triangle tiles
+ * only ("SYRK y reducción fusionada").  The result overwrites x in its dtype.
+ * ---------------------------------------------------------------------- */
+
+/* Workspace bytes for ns_orthogonalize on `batch` matrices of this shape. */
+QM_API size_t ns_workspace_bytes(int64_t rows, int64_t cols, int32_t batch,
+                          int32_t precision);
+
+/*   x: batch matrices; matrix i starts at x + i*batch_stride elements;
+ *      dtype QM_F32 / QM_BF16 / QM_F16; ld >= cols.
+ *   inv_norm: nullable device fp32 [batch].
+ *   precision: qm_ns_precision.  steps >= 0.
+ *   ws: >= ns_workspace_bytes(rows, cols, batch, precision), 256-byte aligned.
+ * Errors: QM_E_ARG, QM_E_SHAPE, QM_E_DTYPE, QM_E_WORKSPACE, QM_E_HIP. */
+QM_API qm_status ns_orthogonalize(void *x, int32_t dtype, int64_t rows, int64_t cols,
+                           int64_t ld, int32_t batch, int64_t batch_stride,
+                           int32_t steps, float a, float b, float c, float eps,
+                           const float *inv_norm, int32_t precision, void *ws,
+                           size_t ws_bytes, qm_stream_t stream);
+
+/* Blockwise NS ("MuonBP ...", key design 1; "NVIDIA ... Megatron", blockwise
+ * mode): the rows x cols matrix is cut into (rows/block_rows) x
+ * (cols/block_cols) blocks, each orthogonalised independently with its own
+ * norm and orientation, all in one batched run.  inv_norm: nullable device
+ * fp32 [number of blocks], row-major block order.
+ * Errors: as ns_orthogonalize; QM_E_SHAPE if the blocks do not tile. */
+QM_API size_t ns_blocked_workspace_bytes(int64_t rows, int64_t cols,
+                                  int64_t block_rows, int64_t block_cols,
+                                  int32_t precision);
+QM_API qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t rows,
+                                   int64_t cols, int64_t ld,
+                                   int64_t block_rows, int64_t block_cols,
+                                   int32_t steps, float a, float b, float c,
+                                   float eps, const float *inv_norm,
+                                   int32_t precision, void *ws,
+                                   size_t ws_bytes, qm_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One full optimizer step
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    float beta;          /* momentum EMA factor                              */
+    float eps;           /* Frobenius-normalisation epsilon                  */
+    float a, b, c;       /* quintic coefficients                             */
+    float lr_full;       /* step size on full steps                          */
+    float lr_block;      /* step size on block steps                         */
+    float weight_decay;  /* lambda, decoupled                                */
+    float rms_scale;     /* update scale = rms_scale * sqrt(max(p, q))       */
+    int32_t ns_steps;    /* T                                                */
+    int32_t period;      /* P: step t is full iff t % P == 0 (P <= 1: all)   */
+    int32_t precision;   /* qm_ns_precision                                  */
+} qm_muon_hparams;
+
+typedef struct {
+    int64_t rows, cols;              /* tensor i of the plans, row-major       */
+    int64_t block_rows, block_cols;  /* partition used on block steps        */
+    float *weight;                   /* fp32 [rows*cols], nullable           */
+} qm_muon_matrix;
+
+/* Workspace for muon_step over these matrices (both step kinds). */
+QM_API size_t muon_step_workspace_bytes(const void *host_plan_full,
+                                 const void *host_plan_block,
+                                 const qm_muon_matrix *mats, int32_t n_mats,
+                                 int32_t precision);
+
+/* One Muon step with block-periodic orthogonalisation ("MuonBP ...",
+ * flowchart and key designs 2-3):
+ *   full = (period <= 1) || (step % period == 0) || no block plan;
+ *   the q8 update with plan_full (one norm group per matrix, group i =
+ *   tensor i) or plan_block (one group per block, row-major block order,
+ *   numbered consecutively across matrices);
+ *   NS of every matrix (full) or of every block (block step), input
+ *   m * inv_g, output written over the grad buffer in its dtype;
+ *   W <- W - lr (s O + weight_decay W), lr = lr_full or lr_block,
+ *   s = rms_scale * sqrt(max(p, q)) for the p x q matrix orthogonalised.
+ * step is 1-based.  Errors: as the calls above. */
+QM_API qm_status muon_step(const void *host_plan_full, const void *dev_plan_full,
+                    const void *host_plan_block, const void *dev_plan_block,
+                    const qm_muon_matrix *mats, int32_t n_mats, int64_t step,
+                    const qm_muon_hparams *hp, void *ws, size_t ws_bytes,
+                    qm_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
+QM_API const char *qm_status_string(qm_status s);
+QM_API const char *qm_last_error(void);
+QM_API int qm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMUON_H */

@@ -1,0 +1,207 @@
+"""Python binding of libqmuon.so: one quantized-momentum Muon step on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libqmuon.so.  PyTorch supplies device memory and the stream
+(torch's current stream unless one is given).  There is no CPU or PyTorch
+fallback; if the library is missing the import fails.
+
+Entry points (same names as the C ABI in include/qmuon.h):
+  Plan(...)                        qm_plan_encode + one host-to-device copy
+  qmuon_update_multi               q8 momentum update, many tensors, one launch
+  qmuon_update_normalize_groups    update + grouped Frobenius normalisation
+  ns_orthogonalize                 quintic Newton-Schulz, batched
+  ns_orthogonalize_blocked         blockwise Newton-Schulz
+  muon_step                        update + NS + weight apply, block-periodic
+"""
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_LIB = L.load()
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+PRECISION = {"bf16": L.QM_NS_BF16, "f32": L.QM_NS_F32}
+_DTYPES = {torch.float32: L.QM_F32, torch.bfloat16: L.QM_BF16, torch.float16: L.QM_F16}
+
+
+class QmuonError(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        name = L.STATUS_NAMES.get(status, str(status))
+        msg = (_LIB.qm_last_error() or b"").decode()
+        super().__init__(f"{name}: {msg}")
+
+
+def _check(st):
+    if st != L.QM_OK:
+        raise QmuonError(st)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def abi_version():
+    return _LIB.qm_abi_version()
+
+
+class Plan:
+    """A norm plan over q8 tensors, encoded once and copied to the device once.
+
+    tensors : list of (codes int8, absmax fp32, grad) contiguous device tensors
+    segments: list of (tensor_index, start, length, group_id) element ranges
+    n_groups: number of norm groups
+    """
+
+    def __init__(self, tensors, segments, n_groups, device=None):
+        n = len(tensors)
+        arr = (L.Q8Tensor * n)()
+        for i, (codes, absmax, grad) in enumerate(tensors):
+            for t in (codes, absmax, grad):
+                if not t.is_contiguous():
+                    raise ValueError("plan tensors must be contiguous")
+            arr[i] = L.Q8Tensor(codes.data_ptr(), absmax.data_ptr(), grad.data_ptr(),
+                                grad.numel(), _dtype(grad), 0)
+        segs = (L.NormSegment * len(segments))()
+        for k, (ti, start, length, gid) in enumerate(segments):
+            segs[k] = L.NormSegment(ti, gid, start, length)
+        size = ctypes.c_size_t(0)
+        _check(_LIB.qm_plan_encode(arr, n, segs, len(segments), n_groups, None,
+                                   ctypes.byref(size)))
+        self.host = torch.empty(size.value, dtype=torch.uint8)
+        _check(_LIB.qm_plan_encode(arr, n, segs, len(segments), n_groups,
+                                   ctypes.c_void_p(self.host.data_ptr()), ctypes.byref(size)))
+        dev = device if device is not None else tensors[0][0].device
+        self.dev = self.host.to(dev)
+        self._keep = [t for trip in tensors for t in trip]
+        nt, ng = ctypes.c_int32(), ctypes.c_int32()
+        nb, numel = ctypes.c_int64(), ctypes.c_int64()
+        _check(_LIB.qm_plan_info(self.hptr, ctypes.byref(nt), ctypes.byref(ng),
+                                 ctypes.byref(nb), ctypes.byref(numel)))
+        self.n_tensors, self.n_groups = nt.value, ng.value
+        self.n_blocks, self.total_numel = nb.value, numel.value
+        self.device = dev
+
+    @property
+    def hptr(self):
+        return ctypes.c_void_p(self.host.data_ptr())
+
+    @property
+    def dptr(self):
+        return ctypes.c_void_p(self.dev.data_ptr())
+
+    def workspace_bytes(self):
+        return _LIB.qm_update_workspace_bytes(self.hptr)
+
+    def workspace(self):
+        return torch.empty(max(self.workspace_bytes(), 256), dtype=torch.uint8, device=self.device)
+
+
+def qmuon_update_multi(plan, beta, block_sumsq=None, stream=None):
+    """In-place q8 update of every tensor in the plan; block_sumsq (fp64
+    [n_blocks]) optionally receives the per-block sums of m*m."""
+    _check(_LIB.qmuon_update_multi(plan.hptr, plan.dptr, beta, _ptr(block_sumsq), _stream(stream)))
+
+
+def qmuon_update_normalize_groups(plan, beta, eps, write_normalized=True, group_inv_norm=None,
+                                  group_sumsq=None, ws=None, stream=None):
+    if ws is None:
+        ws = plan.workspace()
+    _check(_LIB.qmuon_update_normalize_groups(
+        plan.hptr, plan.dptr, beta, eps, int(write_normalized), _ptr(group_inv_norm),
+        _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _matrix_args(x):
+    if x.dim() == 2:
+        rows, cols = x.shape
+        if x.stride(1) != 1:
+            raise ValueError("rows must be contiguous")
+        return 1, rows, cols, x.stride(0), 0
+    if x.dim() == 3:
+        b, rows, cols = x.shape
+        if x.stride(2) != 1:
+            raise ValueError("rows must be contiguous")
+        return b, rows, cols, x.stride(1), x.stride(0)
+    raise ValueError("expected a 2-D matrix or a 3-D batch of matrices")
+
+
+def ns_workspace_bytes(rows, cols, batch=1, precision="bf16"):
+    return _LIB.ns_workspace_bytes(rows, cols, batch, PRECISION[precision])
+
+
+def ns_orthogonalize(x, steps=5, coeffs=QUINTIC, eps=1e-7, inv_norm=None, precision="bf16",
+                     ws=None, stream=None):
+    """Overwrite x (rows x cols, or batch x rows x cols) with NS_T(x)."""
+    batch, rows, cols, ld, bstride = _matrix_args(x)
+    prec = PRECISION[precision]
+    if ws is None:
+        ws = torch.empty(_LIB.ns_workspace_bytes(rows, cols, batch, prec), dtype=torch.uint8,
+                         device=x.device)
+    a, b, c = coeffs
+    _check(_LIB.ns_orthogonalize(_ptr(x), _dtype(x), rows, cols, ld, batch, bstride, steps, a, b, c,
+                                 eps, _ptr(inv_norm), prec, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ns_orthogonalize_blocked(x, block_rows, block_cols, steps=5, coeffs=QUINTIC, eps=1e-7,
+                             inv_norm=None, precision="bf16", ws=None, stream=None):
+    """Overwrite every block_rows x block_cols block of x with its own NS."""
+    _, rows, cols, ld, _ = _matrix_args(x)
+    prec = PRECISION[precision]
+    if ws is None:
+        ws = torch.empty(_LIB.ns_blocked_workspace_bytes(rows, cols, block_rows, block_cols, prec),
+                         dtype=torch.uint8, device=x.device)
+    a, b, c = coeffs
+    _check(_LIB.ns_orthogonalize_blocked(_ptr(x), _dtype(x), rows, cols, ld, block_rows, block_cols,
+                                         steps, a, b, c, eps, _ptr(inv_norm), prec, _ptr(ws),
+                                         ws.numel(), _stream(stream)))
+
+
+def make_hparams(beta=0.95, eps=1e-7, coeffs=QUINTIC, lr_full=0.02, lr_block=0.01,
+                 weight_decay=0.0, rms_scale=0.2, ns_steps=5, period=5, precision="bf16"):
+    a, b, c = coeffs
+    return L.MuonHparams(beta, eps, a, b, c, lr_full, lr_block, weight_decay, rms_scale,
+                         ns_steps, period, PRECISION[precision])
+
+
+def _matrices(mats):
+    arr = (L.MuonMatrix * len(mats))()
+    for i, (rows, cols, br, bc, w) in enumerate(mats):
+        arr[i] = L.MuonMatrix(rows, cols, br, bc, w.data_ptr() if w is not None else None)
+    return arr
+
+
+def muon_step_workspace_bytes(plan_full, plan_block, mats, precision="bf16"):
+    arr = _matrices(mats)
+    return _LIB.muon_step_workspace_bytes(plan_full.hptr, plan_block.hptr if plan_block else None,
+                                          arr, len(mats), PRECISION[precision])
+
+
+def muon_step(plan_full, plan_block, mats, step, hparams, ws=None, stream=None):
+    """One block-periodic Muon step.  mats: list of (rows, cols, block_rows,
+    block_cols, weight fp32 tensor or None), tensor i of both plans."""
+    arr = _matrices(mats)
+    if ws is None:
+        nbytes = _LIB.muon_step_workspace_bytes(plan_full.hptr,
+                                                plan_block.hptr if plan_block else None,
+                                                arr, len(mats), hparams.precision)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=plan_full.device)
+    _check(_LIB.muon_step(plan_full.hptr, plan_full.dptr,
+                          plan_block.hptr if plan_block else None,
+                          plan_block.dptr if plan_block else None,
+                          arr, len(mats), step, ctypes.byref(hparams), _ptr(ws), ws.numel(),
+                          _stream(stream)))

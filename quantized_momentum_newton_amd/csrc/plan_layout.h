@@ -1,0 +1,57 @@
+// Byte layout of a norm-plan blob.  The host encoder writes it; the caller
+// copies it verbatim to the device; the update kernels read it there.
+//
+// A plan is what "Quantized Muon Momentum" (section "Grouped QKV And
+// Sharding") builds once and reuses: one group id per 256-element block,
+// plus, here, the tensor table (device pointers baked in, so a step needs no
+// per-call metadata copy) and the work decomposition of the kernels:
+//   task  = up to 4 consecutive blocks of one tensor, processed by one wave64;
+//   run   = up to kRunMax consecutive blocks of one group, summed by one lane
+//           in the group reduction.
+#pragma once
+#include <stdint.h>
+
+namespace qm {
+
+constexpr uint32_t kPlanMagic = 0x4e4c5051u;  // "QPLN"
+constexpr uint32_t kPlanVersion = 1;
+constexpr int kBlock = 256;
+constexpr int kBlocksPerTask = 4;
+constexpr int kTaskElems = kBlock * kBlocksPerTask;  // 1024
+constexpr int kRunMax = 64;
+
+struct PlanHeader {
+    uint32_t magic, version;
+    int32_t n_tensors, n_groups;
+    int64_t n_blocks, n_tasks, n_runs, total_numel;
+    int64_t off_tensors;       // PlanTensor[n_tensors]
+    int64_t off_task_offsets;  // int64[n_tensors + 1]
+    int64_t off_block_group;   // int32[n_blocks]
+    int64_t off_run_offsets;   // int64[n_groups + 1]
+    int64_t off_runs;          // PlanRun[n_runs]
+    int64_t total_bytes;
+};
+
+struct PlanTensor {
+    uint64_t codes, absmax, grad;  // device addresses
+    int64_t numel;
+    int64_t block_offset;          // global index of the tensor's first block
+    int64_t task_offset;           // global index of the tensor's first task
+    int32_t dtype;                 // qm_dtype
+    int32_t group_lo, group_hi;    // smallest / largest group id it touches
+    int32_t pad;
+};
+
+struct PlanRun {
+    int64_t start_block;           // global block index
+    int32_t count;                 // 1 .. kRunMax
+    int32_t pad;
+};
+
+static_assert(sizeof(PlanHeader) == 96, "plan header layout");
+static_assert(sizeof(PlanTensor) == 64, "plan tensor layout");
+static_assert(sizeof(PlanRun) == 16, "plan run layout");
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace qm

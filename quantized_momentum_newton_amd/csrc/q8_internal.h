@@ -1,0 +1,28 @@
+// Internal interface of the q8 update, used by the full optimizer step.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "plan_layout.h"
+#include "qmuon.h"
+
+namespace qm {
+
+struct UpdateWorkspace {
+    double *block_sums;  // [n_blocks]
+    double *group_sums;  // [n_groups]
+    float *inv;          // [n_groups]
+    size_t bytes;
+};
+
+UpdateWorkspace update_workspace(const PlanHeader *h, void *ws);
+
+qm_status validate_update(const void *host_plan, const void *dev_plan, float beta,
+                          const PlanHeader **out);
+
+// Update + per-group inverse norms (+ the in-place scale pass if asked).
+// inv_out / sums_out may be null: the workspace sections are used.
+qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
+                               bool write_normalized, float *inv_out, double *sums_out, void *ws,
+                               hipStream_t stream);
+
+}  // namespace qm

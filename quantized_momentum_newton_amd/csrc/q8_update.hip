@@ -1,0 +1,467 @@
+// Blockwise-int8 momentum update for gfx950 (wave64), compiled with
+// -ffp-contract=off so every binary32 expression keeps one rounding per
+// operation in the order written: codes and absmax then match a CPU run of
+// the same operations bit for bit.
+//
+// "Quantized Muon Momentum" (cppmega docs), sections "What Exists",
+// "Algorithm" and "Grouped QKV And Sharding" define what is computed:
+// dequantise the int8 state with its per-256-element absmax, the beta-EMA
+// with the grad in fp32, m back into the grad buffer, a new block absmax,
+// symmetric nearest requantisation to [-127, 127], and per-block / per-group
+// sums of m*m for the Frobenius normalisation that feeds Newton-Schulz.
+//
+// Layout on the MI355X (not the page's 64 threads x 4 elements): one wave64
+// owns a task of 4 consecutive blocks (1024 elements).  For 16-bit grads a
+// lane holds 8 elements in each of two halves of the task, so every load and
+// store instruction of the wave covers one contiguous 1 KiB (grads) or 512 B
+// (codes) span; a block is 32 lanes of one half and its absmax and sum are
+// butterfly reductions over those 32 lanes.  fp32 grads use 4 elements per
+// lane and 4 quarters, one block per quarter.  Tasks of all tensors form one
+// grid-stride index space, so one launch covers the whole tensor list.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+#include "plan_layout.h"
+#include "q8_internal.h"
+#include "qmuon.h"
+
+namespace qm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerWG = kThreads / 64;
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t f16_rne(float f) {
+    _Float16 h = (_Float16)f;  // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_val(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<QM_F32> {
+    static constexpr int kEpl = 4;  // elements per lane per part
+    static constexpr int kSize = 4;
+};
+template <> struct Elem<QM_BF16> {
+    static constexpr int kEpl = 8;
+    static constexpr int kSize = 2;
+};
+template <> struct Elem<QM_F16> {
+    static constexpr int kEpl = 8;
+    static constexpr int kSize = 2;
+};
+
+template <int DT> __device__ __forceinline__ float widen(const void *p, int64_t i) {
+    if constexpr (DT == QM_F32) return static_cast<const float *>(p)[i];
+    else if constexpr (DT == QM_BF16) return bf16_val(static_cast<const uint16_t *>(p)[i]);
+    else return f16_val(static_cast<const uint16_t *>(p)[i]);
+}
+template <int DT> __device__ __forceinline__ void narrow(void *p, int64_t i, float v) {
+    if constexpr (DT == QM_F32) static_cast<float *>(p)[i] = v;
+    else if constexpr (DT == QM_BF16) static_cast<uint16_t *>(p)[i] = bf16_rne(v);
+    else static_cast<uint16_t *>(p)[i] = f16_rne(v);
+}
+
+// Vector load/store of kEpl grad elements at element offset e (16 bytes).
+template <int DT> __device__ __forceinline__ void load_grad_vec(const void *g, int64_t e, float *out) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const char *>(g) + e * Elem<DT>::kSize);
+    if constexpr (DT == QM_F32) {
+        out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+    } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            if constexpr (DT == QM_BF16) {
+                out[2 * k] = bf16_val((uint16_t)(w[k] & 0xffffu));
+                out[2 * k + 1] = bf16_val((uint16_t)(w[k] >> 16));
+            } else {
+                out[2 * k] = f16_val((uint16_t)(w[k] & 0xffffu));
+                out[2 * k + 1] = f16_val((uint16_t)(w[k] >> 16));
+            }
+        }
+    }
+}
+template <int DT> __device__ __forceinline__ void store_grad_vec(void *g, int64_t e, const float *in) {
+    uint4 v;
+    if constexpr (DT == QM_F32) {
+        v.x = __float_as_uint(in[0]); v.y = __float_as_uint(in[1]);
+        v.z = __float_as_uint(in[2]); v.w = __float_as_uint(in[3]);
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t lo = DT == QM_BF16 ? bf16_rne(in[2 * k]) : f16_rne(in[2 * k]);
+            const uint32_t hi = DT == QM_BF16 ? bf16_rne(in[2 * k + 1]) : f16_rne(in[2 * k + 1]);
+            w[k] = lo | (hi << 16);
+        }
+        v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
+    }
+    *reinterpret_cast<uint4 *>(static_cast<char *>(g) + e * Elem<DT>::kSize) = v;
+}
+
+// kEpl int8 codes at element offset e (8 or 4 bytes, naturally aligned).
+template <int N> __device__ __forceinline__ void load_codes_vec(const int8_t *c, int64_t e, int8_t *q) {
+    if constexpr (N == 8) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; k++) { q[k] = (int8_t)(v.x >> (8 * k)); q[4 + k] = (int8_t)(v.y >> (8 * k)); }
+    } else {
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(c + e);
+#pragma unroll
+        for (int k = 0; k < 4; k++) q[k] = (int8_t)(v >> (8 * k));
+    }
+}
+template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int64_t e, const int8_t *q) {
+    if constexpr (N == 8) {
+        uint2 v = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v.x |= (uint32_t)(uint8_t)q[k] << (8 * k);
+            v.y |= (uint32_t)(uint8_t)q[4 + k] << (8 * k);
+        }
+        *reinterpret_cast<uint2 *>(c + e) = v;
+    } else {
+        uint32_t v = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) v |= (uint32_t)(uint8_t)q[k] << (8 * k);
+        *reinterpret_cast<uint32_t *>(c + e) = v;
+    }
+}
+
+// Largest i with task_offsets[i] <= task (every tensor owns >= 1 task).
+__device__ __forceinline__ int find_tensor(const int64_t *task_offsets, int n, int64_t task) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (task_offsets[mid] <= task) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ K1: update
+
+template <int DT, bool SUMS>
+__device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, float beta, float omb,
+                                            double *block_sums, int lane) {
+    constexpr int EPL = Elem<DT>::kEpl;
+    constexpr int PARTS = kTaskElems / (64 * EPL);
+    constexpr int LPB = kBlock / EPL;  // lanes per block
+    const int64_t e_task = lt * kTaskElems;
+    const int64_t rem = T.numel - e_task;
+    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
+    int8_t *codes = reinterpret_cast<int8_t *>(T.codes) + e_task;
+    float *absmax = reinterpret_cast<float *>(T.absmax) + lt * kBlocksPerTask;
+    void *grad = reinterpret_cast<char *>(T.grad) + e_task * Elem<DT>::kSize;
+
+    float m[PARTS][EPL];
+#pragma unroll
+    for (int p = 0; p < PARTS; p++) {
+        const int e0 = p * 64 * EPL + lane * EPL;
+        const int kb = e0 / kBlock;
+        float step = 0.0f;
+        if (e0 < nvalid) step = absmax[kb] / 127.0f;
+        int8_t q[EPL];
+        float g[EPL];
+        if (e0 + EPL <= nvalid) {
+            load_codes_vec<EPL>(codes, e0, q);
+            load_grad_vec<DT>(grad, e0, g);
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPL; j++) {
+                const bool ok = e0 + j < nvalid;
+                q[j] = ok ? codes[e0 + j] : (int8_t)0;
+                g[j] = ok ? widen<DT>(grad, e0 + j) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; j++) {
+            const float old = (float)q[j] * step;
+            const float t1 = beta * old;
+            const float t2 = omb * g[j];
+            m[p][j] = t1 + t2;
+        }
+    }
+
+#pragma unroll
+    for (int p = 0; p < PARTS; p++) {
+        const int e0 = p * 64 * EPL + lane * EPL;
+        const int kb = e0 / kBlock;
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < EPL; j++) amax = fmaxf(amax, fabsf(m[p][j]));
+#pragma unroll
+        for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+        int8_t q[EPL];
+#pragma unroll
+        for (int j = 0; j < EPL; j++) {
+            float r = rintf(m[p][j] * inv);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            q[j] = (int8_t)(int)r;
+        }
+        if (e0 + EPL <= nvalid) {
+            store_codes_vec<EPL>(codes, e0, q);
+            store_grad_vec<DT>(grad, e0, m[p]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPL; j++)
+                if (e0 + j < nvalid) {
+                    codes[e0 + j] = q[j];
+                    narrow<DT>(grad, e0 + j, m[p][j]);
+                }
+        }
+        double s = 0.0;
+        if constexpr (SUMS) {
+#pragma unroll
+            for (int j = 0; j < EPL; j++) {
+                const double d = (double)m[p][j];
+                s += d * d;
+            }
+#pragma unroll
+            for (int off = 1; off < LPB; off <<= 1) s += __shfl_xor(s, off);
+        }
+        if ((lane % LPB) == 0 && kb * kBlock < nvalid) {
+            absmax[kb] = amax;
+            if constexpr (SUMS) block_sums[T.block_offset + lt * kBlocksPerTask + kb] = s;
+        }
+    }
+}
+
+template <bool SUMS>
+__global__ __launch_bounds__(kThreads) void q8_update_kernel(const PlanTensor *__restrict__ tensors,
+                                                             const int64_t *__restrict__ task_offsets,
+                                                             int n_tensors, int64_t n_tasks, float beta,
+                                                             double *__restrict__ block_sums) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float omb = 1.0f - beta;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
+    for (int64_t task = (int64_t)blockIdx.x * kWavesPerWG + wave; task < n_tasks; task += stride) {
+        const int ti = find_tensor(task_offsets, n_tensors, task);
+        const PlanTensor T = tensors[ti];
+        const int64_t lt = task - T.task_offset;
+        switch (T.dtype) {
+            case QM_F32: update_task<QM_F32, SUMS>(T, lt, beta, omb, block_sums, lane); break;
+            case QM_BF16: update_task<QM_BF16, SUMS>(T, lt, beta, omb, block_sums, lane); break;
+            default: update_task<QM_F16, SUMS>(T, lt, beta, omb, block_sums, lane); break;
+        }
+    }
+}
+
+// ------------------------------------------------- K2: group sums, inverse norms
+// One workgroup per group; lane k sums runs k, k+256, ... (each a short
+// ascending range of blocks), then a fixed butterfly + fixed-order wave
+// combine: the result depends only on the plan, never on scheduling.
+
+__global__ __launch_bounds__(kThreads) void group_reduce_kernel(const int64_t *__restrict__ run_offsets,
+                                                                const PlanRun *__restrict__ runs,
+                                                                const double *__restrict__ block_sums,
+                                                                float eps, double *__restrict__ group_sums,
+                                                                float *__restrict__ inv_norm) {
+    const int g = blockIdx.x;
+    const int64_t r0 = run_offsets[g], r1 = run_offsets[g + 1];
+    double acc = 0.0;
+    for (int64_t r = r0 + threadIdx.x; r < r1; r += kThreads) {
+        const PlanRun R = runs[r];
+        for (int k = 0; k < R.count; k++) acc += block_sums[R.start_block + k];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    __shared__ double part[kWavesPerWG];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double S = part[0];
+        for (int w = 1; w < kWavesPerWG; w++) S += part[w];
+        if (group_sums) group_sums[g] = S;
+        inv_norm[g] = (float)(1.0 / (sqrt(S) + (double)eps));
+    }
+}
+
+// ------------------------------------------------------------ K3: scale pass
+
+template <int DT>
+__device__ __forceinline__ void scale_task(const PlanTensor &T, int64_t lt, const int32_t *block_group,
+                                           const float *inv, int lane) {
+    constexpr int EPL = Elem<DT>::kEpl;
+    constexpr int PARTS = kTaskElems / (64 * EPL);
+    const int64_t e_task = lt * kTaskElems;
+    const int64_t rem = T.numel - e_task;
+    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
+    void *grad = reinterpret_cast<char *>(T.grad) + e_task * Elem<DT>::kSize;
+    const int32_t *bg = block_group + T.block_offset + lt * kBlocksPerTask;
+#pragma unroll
+    for (int p = 0; p < PARTS; p++) {
+        const int e0 = p * 64 * EPL + lane * EPL;
+        if (e0 >= nvalid) continue;
+        const float s = inv[bg[e0 / kBlock]];
+        if (e0 + EPL <= nvalid) {
+            float v[EPL];
+            load_grad_vec<DT>(grad, e0, v);
+#pragma unroll
+            for (int j = 0; j < EPL; j++) v[j] = v[j] * s;
+            store_grad_vec<DT>(grad, e0, v);
+        } else {
+            for (int j = 0; j < EPL && e0 + j < nvalid; j++)
+                narrow<DT>(grad, e0 + j, widen<DT>(grad, e0 + j) * s);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void q8_scale_kernel(const PlanTensor *__restrict__ tensors,
+                                                            const int64_t *__restrict__ task_offsets,
+                                                            int n_tensors, int64_t n_tasks,
+                                                            const int32_t *__restrict__ block_group,
+                                                            const float *__restrict__ inv) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
+    for (int64_t task = (int64_t)blockIdx.x * kWavesPerWG + wave; task < n_tasks; task += stride) {
+        const int ti = find_tensor(task_offsets, n_tensors, task);
+        const PlanTensor T = tensors[ti];
+        const int64_t lt = task - T.task_offset;
+        switch (T.dtype) {
+            case QM_F32: scale_task<QM_F32>(T, lt, block_group, inv, lane); break;
+            case QM_BF16: scale_task<QM_BF16>(T, lt, block_group, inv, lane); break;
+            default: scale_task<QM_F16>(T, lt, block_group, inv, lane); break;
+        }
+    }
+}
+
+// Workgroups per streaming launch: enough waves in flight to cover HBM
+// latency on 256 CUs, few enough that the grid-stride loop amortises setup.
+int stream_grid(int64_t n_tasks) {
+    const int64_t want = (n_tasks + kWavesPerWG - 1) / kWavesPerWG;
+    const int64_t cap = 256 * 16;
+    return (int)(want < cap ? want : cap);
+}
+
+template <typename T> const T *section(const void *dev_plan, int64_t off) {
+    return reinterpret_cast<const T *>(static_cast<const char *>(dev_plan) + off);
+}
+
+qm_status check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return QM_OK;
+}
+
+}  // namespace
+
+qm_status validate_update(const void *host_plan, const void *dev_plan, float beta,
+                          const PlanHeader **out) {
+    qm_status st;
+    const PlanHeader *h = plan_header(host_plan, &st);
+    if (!h) return st;
+    if (!dev_plan) return fail(QM_E_ARG, "device plan is null");
+    if (!aligned(dev_plan, 8)) return fail(QM_E_ALIGN, "device plan must be 8-byte aligned");
+    if (!(beta >= 0.0f && beta <= 1.0f)) return fail(QM_E_ARG, "beta must lie in [0, 1]");
+    *out = h;
+    return QM_OK;
+}
+
+qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
+                        hipStream_t stream) {
+    const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
+    const int64_t *toff = section<int64_t>(dev_plan, h->off_task_offsets);
+    const int grid = stream_grid(h->n_tasks);
+    if (block_sums)
+        q8_update_kernel<true><<<grid, kThreads, 0, stream>>>(tens, toff, h->n_tensors, h->n_tasks, beta,
+                                                             block_sums);
+    else
+        q8_update_kernel<false><<<grid, kThreads, 0, stream>>>(tens, toff, h->n_tensors, h->n_tasks, beta,
+                                                              nullptr);
+    return check_launch("q8 update");
+}
+
+qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const double *block_sums,
+                              float eps, double *group_sums, float *inv, hipStream_t stream) {
+    group_reduce_kernel<<<h->n_groups, kThreads, 0, stream>>>(
+        section<int64_t>(dev_plan, h->off_run_offsets), section<PlanRun>(dev_plan, h->off_runs),
+        block_sums, eps, group_sums, inv);
+    return check_launch("group reduce");
+}
+
+qm_status launch_scale(const PlanHeader *h, const void *dev_plan, const float *inv, hipStream_t stream) {
+    q8_scale_kernel<<<stream_grid(h->n_tasks), kThreads, 0, stream>>>(
+        section<PlanTensor>(dev_plan, h->off_tensors), section<int64_t>(dev_plan, h->off_task_offsets),
+        h->n_tensors, h->n_tasks, section<int32_t>(dev_plan, h->off_block_group), inv);
+    return check_launch("group scale");
+}
+
+UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
+    UpdateWorkspace w;
+    char *p = static_cast<char *>(ws);
+    w.block_sums = reinterpret_cast<double *>(p);
+    p += align_up(h->n_blocks * 8, 256);
+    w.group_sums = reinterpret_cast<double *>(p);
+    p += align_up((int64_t)h->n_groups * 8, 256);
+    w.inv = reinterpret_cast<float *>(p);
+    p += align_up((int64_t)h->n_groups * 4, 256);
+    w.bytes = (size_t)(p - static_cast<char *>(ws));
+    return w;
+}
+
+qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
+                               bool write_normalized, float *inv_out, double *sums_out, void *ws,
+                               hipStream_t stream) {
+    const UpdateWorkspace w = update_workspace(h, ws);
+    float *inv = inv_out ? inv_out : w.inv;
+    double *sums = sums_out ? sums_out : w.group_sums;
+    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, stream);
+    if (st != QM_OK) return st;
+    st = launch_group_reduce(h, dev_plan, w.block_sums, eps, sums, inv, stream);
+    if (st != QM_OK) return st;
+    if (write_normalized) st = launch_scale(h, dev_plan, inv, stream);
+    return st;
+}
+
+}  // namespace qm
+
+using namespace qm;
+
+extern "C" qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan, float beta,
+                                        double *block_sumsq, qm_stream_t stream) {
+    clear_error();
+    const PlanHeader *h = nullptr;
+    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
+    if (st != QM_OK) return st;
+    if (block_sumsq && !aligned(block_sumsq, 8)) return fail(QM_E_ALIGN, "block_sumsq must be 8-byte aligned");
+    return launch_update(h, dev_plan, beta, block_sumsq, static_cast<hipStream_t>(stream));
+}
+
+extern "C" qm_status qmuon_update_normalize_groups(const void *host_plan, const void *dev_plan, float beta,
+                                                   float eps, int32_t write_normalized, float *group_inv_norm,
+                                                   double *group_sumsq, void *ws, size_t ws_bytes,
+                                                   qm_stream_t stream) {
+    clear_error();
+    const PlanHeader *h = nullptr;
+    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
+    if (st != QM_OK) return st;
+    if (!(eps >= 0.0f) || isinf(eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    if (write_normalized != 0 && write_normalized != 1) return fail(QM_E_ARG, "write_normalized must be 0 or 1");
+    if (group_inv_norm && !aligned(group_inv_norm, 4)) return fail(QM_E_ALIGN, "group_inv_norm alignment");
+    if (group_sumsq && !aligned(group_sumsq, 8)) return fail(QM_E_ALIGN, "group_sumsq alignment");
+    const size_t need = qm_update_workspace_bytes(host_plan);
+    if (!ws || ws_bytes < need)
+        return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
+    return run_update_normalize(h, dev_plan, beta, eps, write_normalized != 0, group_inv_norm, group_sumsq, ws,
+                                static_cast<hipStream_t>(stream));
+}

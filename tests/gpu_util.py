@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: host copies and q8 input sets."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from harness import inputs as H
+
+TORCH_TO_ORACLE = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16, torch.float16: oracle.F16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_grad(t):
+    """Device grad -> numpy (fp32 array, or uint16 bit patterns for 16-bit)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy().copy()
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def host(t):
+    return t.detach().contiguous().cpu().numpy().copy()
+
+
+class Q8Set:
+    """Device q8 tensors plus host copies of their inputs taken before any kernel."""
+
+    def __init__(self, shapes, dtypes, seed, device="cuda", outlier_frac=0.0, std=1e-3):
+        self.shapes = shapes
+        self.dtypes = dtypes
+        self.codes, self.absmax, self.grads = [], [], []
+        for i, (shape, dt) in enumerate(zip(shapes, dtypes)):
+            numel = int(np.prod(shape))
+            c, a = H.prior_state(numel, device, seed, i)
+            g = H.grad(shape, dt, device, seed, i, std=std, outlier_frac=outlier_frac).reshape(-1)
+            self.codes.append(c)
+            self.absmax.append(a)
+            self.grads.append(g)
+        torch.cuda.synchronize()
+        self.snapshot()
+
+    def snapshot(self, which=None):
+        idx = range(len(self.shapes)) if which is None else which
+        self.h_codes = {i: host(self.codes[i]) for i in idx}
+        self.h_absmax = {i: host(self.absmax[i]) for i in idx}
+        self.h_grads = {i: host_grad(self.grads[i]) for i in idx}
+
+    def triples(self):
+        return list(zip(self.codes, self.absmax, self.grads))
+
+    def odt(self, i):
+        return TORCH_TO_ORACLE[self.dtypes[i]]
+
+    def host_states(self, idx):
+        return [(self.h_codes[i], self.h_absmax[i]) for i in idx]
+
+
+def assert_bits_equal(got, exp, what):
+    got = np.asarray(got)
+    exp = np.asarray(exp)
+    assert got.shape == exp.shape, (what, got.shape, exp.shape)
+    if got.dtype.kind == "f":
+        got = got.view(np.uint32 if got.dtype == np.float32 else np.uint64)
+        exp = exp.view(got.dtype)
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}: {got[bad[:5]]} vs {exp[bad[:5]]}"

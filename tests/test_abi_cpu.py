@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and its host-side validation rejects bad requests before
+anything would be launched (no call here reaches a kernel)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import quantized_momentum_newton_amd as q
+from quantized_momentum_newton_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = q._LIB
+
+# Fake device addresses: only alignment is ever looked at on the host.
+BASE = 0x7f0000000000
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names |= set(re.findall(r"^QM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_symbols()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(LIB, n), n
+    assert names == set(L.SIGNATURES), names ^ set(L.SIGNATURES)
+    assert LIB.qm_abi_version() == 1
+    assert LIB.qm_status_string(0) == b"ok"
+
+
+def _tensors(specs):
+    """specs: list of (numel, dtype) -> array of Q8Tensor at disjoint fake addresses."""
+    arr = (L.Q8Tensor * len(specs))()
+    addr = BASE
+    for i, (n, dt) in enumerate(specs):
+        esz = 4 if dt == L.QM_F32 else 2
+        codes = addr
+        addr += (n + 4095) // 4096 * 4096
+        absmax = addr
+        addr += ((n + 255) // 256 * 4 + 4095) // 4096 * 4096
+        grad = addr
+        addr += (n * esz + 4095) // 4096 * 4096
+        arr[i] = L.Q8Tensor(codes, absmax, grad, n, dt, 0)
+    return arr
+
+
+def _segs(lst):
+    arr = (L.NormSegment * len(lst))()
+    for k, (t, s, ln, g) in enumerate(lst):
+        arr[k] = L.NormSegment(t, g, s, ln)
+    return arr
+
+
+def _encode(tens, segs, ngroups):
+    size = ctypes.c_size_t(0)
+    st = LIB.qm_plan_encode(tens, len(tens), segs, len(segs), ngroups, None, ctypes.byref(size))
+    if st != 0:
+        return st, None
+    buf = (ctypes.c_uint64 * ((size.value + 7) // 8))()
+    st = LIB.qm_plan_encode(tens, len(tens), segs, len(segs), ngroups, ctypes.cast(buf, ctypes.c_void_p),
+                            ctypes.byref(size))
+    return st, buf
+
+
+def test_plan_encode_and_info():
+    tens = _tensors([(2560 * 64, L.QM_BF16), (1000, L.QM_F32)])
+    segs = _segs([(0, 0, 2048 * 64, 0), (0, 2048 * 64, 256 * 64, 1), (0, 2304 * 64, 256 * 64, 2),
+                  (1, 0, 1000, 3)])
+    st, buf = _encode(tens, segs, 4)
+    assert st == 0
+    nt, ng, nb, numel = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    assert LIB.qm_plan_info(ctypes.cast(buf, ctypes.c_void_p), ctypes.byref(nt), ctypes.byref(ng),
+                            ctypes.byref(nb), ctypes.byref(numel)) == 0
+    assert (nt.value, ng.value, nb.value, numel.value) == (2, 4, 640 + 4, 2560 * 64 + 1000)
+    ws = LIB.qm_update_workspace_bytes(ctypes.cast(buf, ctypes.c_void_p))
+    assert ws >= 644 * 8 + 4 * 8 + 4 * 4
+
+
+@pytest.mark.parametrize("segs,ngroups,status", [
+    ([(0, 0, 300, 0), (0, 300, 724, 1)], 2, 2),       # misaligned boundary -> QM_E_ALIGN
+    ([(0, 0, 768, 0), (0, 512, 512, 1)], 2, 4),       # overlap -> QM_E_SHAPE
+    ([(0, 0, 512, 0)], 1, 4),                         # uncovered block -> QM_E_SHAPE
+    ([(0, 0, 1024, 2)], 2, 1),                        # group id out of range -> QM_E_ARG
+    ([(1, 0, 1024, 0)], 1, 1),                        # tensor index out of range
+    ([(0, 0, 2048, 0)], 1, 1),                        # outside the tensor
+    ([(0, 0, 1024, 0)], 2, 4),                        # group 1 empty -> QM_E_SHAPE
+])
+def test_plan_encode_rejects(segs, ngroups, status):
+    st, _ = _encode(_tensors([(1024, L.QM_BF16)]), _segs(segs), ngroups)
+    assert st == status, LIB.qm_last_error()
+    assert LIB.qm_last_error()
+
+
+def test_plan_encode_rejects_bad_tensors():
+    tens = _tensors([(1024, L.QM_BF16)])
+    tens[0].codes += 8                                  # codes not 16-byte aligned
+    assert _encode(tens, _segs([(0, 0, 1024, 0)]), 1)[0] == 2
+    tens = _tensors([(1024, 7)])
+    assert _encode(tens, _segs([(0, 0, 1024, 0)]), 1)[0] == 3
+    tens = _tensors([(1024, L.QM_BF16), (1024, L.QM_BF16)])
+    tens[1].grad = tens[0].grad + 1024                  # grads overlap
+    assert _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 1024, 0)]), 1)[0] == 1
+
+
+def test_final_partial_block_segment_is_allowed():
+    st, _ = _encode(_tensors([(1000, L.QM_F16)]), _segs([(0, 0, 768, 0), (0, 768, 232, 1)]), 2)
+    assert st == 0
+
+
+def test_update_calls_validate_before_launch():
+    tens = _tensors([(1024, L.QM_BF16)])
+    st, buf = _encode(tens, _segs([(0, 0, 1024, 0)]), 1)
+    hp = ctypes.cast(buf, ctypes.c_void_p)
+    fake_dev = ctypes.c_void_p(BASE)
+    assert LIB.qmuon_update_multi(None, fake_dev, 0.9, None, None) == 1
+    assert LIB.qmuon_update_multi(hp, None, 0.9, None, None) == 1
+    assert LIB.qmuon_update_multi(hp, fake_dev, 1.5, None, None) == 1
+    bad = (ctypes.c_uint64 * 16)()
+    assert LIB.qmuon_update_multi(ctypes.cast(bad, ctypes.c_void_p), fake_dev, 0.9, None, None) == 8
+    need = LIB.qm_update_workspace_bytes(hp)
+    assert LIB.qmuon_update_normalize_groups(hp, fake_dev, 0.9, 1e-7, 1, None, None,
+                                             ctypes.c_void_p(BASE), need - 1, None) == 5
+    assert LIB.qmuon_update_normalize_groups(hp, fake_dev, 0.9, -1.0, 1, None, None,
+                                             ctypes.c_void_p(BASE), need, None) == 1
+    assert LIB.qmuon_update_normalize_groups(hp, fake_dev, 0.9, 1e-7, 1, None, None,
+                                             ctypes.c_void_p(BASE + 8), need, None) == 2
