@@ -235,6 +235,19 @@ QM_API qm_status muon_step(const void *host_plan_full, const void *dev_plan_full
                     const qm_muon_hparams *hp, void *ws, size_t ws_bytes,
                     qm_stream_t stream);
 
+/* The orthogonalise-and-apply half of muon_step on its own: given the group
+ * inverse norms inv_norm (device fp32 [n_groups of the plan], e.g. from
+ * qmuon_update_normalize_groups with write_normalized = 0) and the grads
+ * holding m, run NS on every matrix (full = 1) or every block (full = 0) of
+ * the plan's tensors, write O over the grads and apply the weight update.
+ * muon_step is qmuon_update_normalize_groups followed by this call.
+ * ws: >= muon_step_workspace_bytes(...) bytes (the same workspace works).
+ * Errors: as muon_step. */
+QM_API qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mats,
+                            int32_t n_mats, int32_t full,
+                            const float *inv_norm, const qm_muon_hparams *hp,
+                            void *ws, size_t ws_bytes, qm_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 QM_API const char *qm_status_string(qm_status s);
 QM_API const char *qm_last_error(void);

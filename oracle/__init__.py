@@ -45,6 +45,8 @@ def lib():
         L.or_scale_by_group.argtypes = [p, ctypes.c_int, i64, p, p]
         L.or_round_array.argtypes = [p, i64, ctypes.c_int, p]
         L.or_widen_array.argtypes = [p, i64, ctypes.c_int, p]
+        L.or_num_threads.argtypes = []
+        L.or_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -57,6 +59,11 @@ def _grad_dtype(a):
     if a.dtype == np.float32:
         return F32
     raise TypeError("pass fp32 arrays directly; 16-bit grads as (uint16 bits, dtype)")
+
+
+def num_threads():
+    """OpenMP threads the C oracle runs with."""
+    return lib().or_num_threads()
 
 
 # ------------------------------------------------------------------ dtypes

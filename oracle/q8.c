@@ -34,6 +34,7 @@
  *     (round to nearest even).
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -224,3 +225,6 @@ void or_widen_array(const uint16_t *src, int64_t n, int dtype, float *dst)
     for (int64_t i = 0; i < n; i++)
         dst[i] = dtype == OR_BF16 ? or_f32_from_bf16(src[i]) : or_f32_from_f16(src[i]);
 }
+
+/* Threads an OpenMP region of this library uses (reported with timings). */
+int or_num_threads(void) { return omp_get_max_threads(); }

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/qmuon.h):
   ns_orthogonalize                 quintic Newton-Schulz, batched
   ns_orthogonalize_blocked         blockwise Newton-Schulz
   muon_step                        update + NS + weight apply, block-periodic
+  muon_apply                       the NS + weight-apply half of muon_step
 """
 import ctypes
 
@@ -205,3 +206,11 @@ def muon_step(plan_full, plan_block, mats, step, hparams, ws=None, stream=None):
                           plan_block.dptr if plan_block else None,
                           arr, len(mats), step, ctypes.byref(hparams), _ptr(ws), ws.numel(),
                           _stream(stream)))
+
+
+def muon_apply(plan, mats, full, inv_norm, hparams, ws, stream=None):
+    """NS + weight apply for the plan's matrices given group inverse norms
+    (device fp32 [plan.n_groups]); muon_step = update + this."""
+    arr = _matrices(mats)
+    _check(_LIB.muon_apply(plan.hptr, arr, len(mats), int(full), _ptr(inv_norm),
+                           ctypes.byref(hparams), _ptr(ws), ws.numel(), _stream(stream)))

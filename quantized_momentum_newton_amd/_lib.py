@@ -67,6 +67,8 @@ SIGNATURES = {
     "muon_step": (c_i32, [c_void_p, c_void_p, c_void_p, c_void_p, ctypes.POINTER(MuonMatrix),
                           c_i32, c_i64, ctypes.POINTER(MuonHparams), c_void_p, c_size,
                           c_void_p]),
+    "muon_apply": (c_i32, [c_void_p, ctypes.POINTER(MuonMatrix), c_i32, c_i32, c_void_p,
+                           ctypes.POINTER(MuonHparams), c_void_p, c_size, c_void_p]),
     "qm_status_string": (ctypes.c_char_p, [c_i32]),
     "qm_last_error": (ctypes.c_char_p, []),
     "qm_abi_version": (ctypes.c_int, []),

@@ -43,6 +43,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kPad = 256;       // internal dims are multiples of this
 constexpr int kMaxItems = 8;    // matrices per launch chain
@@ -92,13 +93,13 @@ __device__ __forceinline__ void store_any(void *p, int64_t i, int dtype, float v
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
-    static __device__ __forceinline__ void step(const uint4 &a, const uint4 &b, f32x16 &c) {
+    static __device__ __forceinline__ void step(const u32x4 &a, const u32x4 &b, f32x16 &c) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
 };
 template <> struct Mfma<float> {
-    static __device__ __forceinline__ void step(const uint4 &a, const uint4 &b, f32x16 &c) {
+    static __device__ __forceinline__ void step(const u32x4 &a, const u32x4 &b, f32x16 &c) {
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
@@ -183,33 +184,31 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
     const char *Qg = reinterpret_cast<const char *>(args.Q + item * args.sq + (int64_t)bj * BN * args.ldq);
     const int64_t ldpb = args.ldp * (int64_t)sizeof(T), ldqb = args.ldq * (int64_t)sizeof(T);
 
-    uint4 rp[P_LOADS], rq[Q_LOADS];
-    auto gload = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < P_LOADS; i++) {
-            const int idx = tid + i * NT, row = idx >> 3, ch = idx & 7;
-            rp[i] = *reinterpret_cast<const uint4 *>(Pg + row * ldpb + (int64_t)kt * ROWB + ch * 16);
-        }
-#pragma unroll
-        for (int i = 0; i < Q_LOADS; i++) {
-            const int idx = tid + i * NT, row = idx >> 3, ch = idx & 7;
-            rq[i] = *reinterpret_cast<const uint4 *>(Qg + row * ldqb + (int64_t)kt * ROWB + ch * 16);
-        }
-    };
-    auto swrite = [&](int buf) {
-        char *dp = sP + buf * BM * ROWB;
-        char *dq = sQ + buf * BN * ROWB;
-#pragma unroll
-        for (int i = 0; i < P_LOADS; i++) {
-            const int idx = tid + i * NT, row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4 *>(dp + row * ROWB + ((ch ^ (row & 7)) << 4)) = rp[i];
-        }
-#pragma unroll
-        for (int i = 0; i < Q_LOADS; i++) {
-            const int idx = tid + i * NT, row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4 *>(dq + row * ROWB + ((ch ^ (row & 7)) << 4)) = rq[i];
-        }
-    };
+    u32x4 rp[P_LOADS], rq[Q_LOADS];
+#define QM_GLOAD(kt)                                                                              \
+    do {                                                                                          \
+        _Pragma("unroll") for (int i_ = 0; i_ < P_LOADS; i_++) {                                  \
+            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
+            rp[i_] = *reinterpret_cast<const u32x4 *>(Pg + row * ldpb + (int64_t)(kt)*ROWB + ch * 16); \
+        }                                                                                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < Q_LOADS; i_++) {                                  \
+            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
+            rq[i_] = *reinterpret_cast<const u32x4 *>(Qg + row * ldqb + (int64_t)(kt)*ROWB + ch * 16); \
+        }                                                                                         \
+    } while (0)
+#define QM_SWRITE(buf)                                                                            \
+    do {                                                                                          \
+        char *dp_ = sP + (buf)*BM * ROWB;                                                         \
+        char *dq_ = sQ + (buf)*BN * ROWB;                                                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < P_LOADS; i_++) {                                  \
+            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
+            *reinterpret_cast<u32x4 *>(dp_ + row * ROWB + ((ch ^ (row & 7)) << 4)) = rp[i_];      \
+        }                                                                                         \
+        _Pragma("unroll") for (int i_ = 0; i_ < Q_LOADS; i_++) {                                  \
+            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
+            *reinterpret_cast<u32x4 *>(dq_ + row * ROWB + ((ch ^ (row & 7)) << 4)) = rq[i_];      \
+        }                                                                                         \
+    } while (0)
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -220,37 +219,40 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
     const int KT = args.k_tiles;
-    gload(0);
-    swrite(0);
+    QM_GLOAD(0);
+    QM_SWRITE(0);
     __syncthreads();
     const int lrow = lane & 31, lhalf = lane >> 5;
     for (int kt = 0; kt < KT; kt++) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
+        if (kt + 1 < KT) QM_GLOAD(kt + 1);
         const char *cp = sP + cur * BM * ROWB;
         const char *cq = sQ + cur * BN * ROWB;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const int ch = 2 * s + lhalf;
-            uint4 a[FM], b[FN];
+            u32x4 a[FM], b[FN];
 #pragma unroll
             for (int i = 0; i < FM; i++) {
                 const int row = wm * WM + i * 32 + lrow;
-                a[i] = *reinterpret_cast<const uint4 *>(cp + row * ROWB + ((ch ^ (row & 7)) << 4));
+                a[i] = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + ((ch ^ (row & 7)) << 4));
             }
 #pragma unroll
             for (int j = 0; j < FN; j++) {
                 const int row = wn * WN + j * 32 + lrow;
-                b[j] = *reinterpret_cast<const uint4 *>(cq + row * ROWB + ((ch ^ (row & 7)) << 4));
+                b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ (row & 7)) << 4));
             }
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++) Mfma<T>::step(a[i], b[j], acc[i][j]);
         }
-        if (kt + 1 < KT) swrite(cur ^ 1);
+        if (kt + 1 < KT) QM_SWRITE(cur ^ 1);
         __syncthreads();
     }
+
+#undef QM_GLOAD
+#undef QM_SWRITE
 
     // ---------------------------------------------------------- epilogue
     // acc[i][j][r] holds C[row][col] with row = 8(r/4) + 4 lhalf + r%4 and
@@ -469,14 +471,12 @@ template <typename T>
 qm_status run_ns_typed(const std::vector<NsRequest> &req, int steps, float a, float b, float c, float eps,
                        void *ws, hipStream_t stream) {
     const Geometry g = geometry(req[0].rows, req[0].cols, sizeof(T) == 4 ? QM_NS_F32 : QM_NS_BF16);
+    // Layout (as sized by ns_ws_bytes_for): kcap items, then the norm
+    // partials, then the computed inverse norms.
     char *base = static_cast<char *>(ws);
-    const size_t xbytes = align_up(g.x_elems * (int64_t)sizeof(T), 256);
-    const size_t abytes = align_up(g.a_elems * (int64_t)sizeof(T), 256);
-    double *partials = reinterpret_cast<double *>(base + kMaxItems * g.item_bytes);
-    float *inv_ws = reinterpret_cast<float *>(base + kMaxItems * g.item_bytes +
-                                              align_up(kMaxItems * kNormChunks * 8, 256));
-    (void)xbytes;
-    (void)abytes;
+    const int64_t kcap = std::min<int64_t>((int64_t)req.size(), kMaxItems);
+    double *partials = reinterpret_cast<double *>(base + kcap * g.item_bytes);
+    float *inv_ws = reinterpret_cast<float *>(base + kcap * g.item_bytes + align_up(kMaxItems * kNormChunks * 8, 256));
 
     for (size_t first = 0; first < req.size(); first += kMaxItems) {
         const int nit = (int)std::min<size_t>(kMaxItems, req.size() - first);
@@ -694,7 +694,8 @@ std::vector<std::vector<NsRequest>> step_requests(const PlanHeader *h, const voi
         for (int64_t bi = 0; bi < nbr; bi++)
             for (int64_t bj = 0; bj < nbc; bj++) {
                 const size_t off = (size_t)(bi * br) * (size_t)M.cols + (size_t)(bj * bc);
-                NsRequest r{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, inv + g0 + bi * nbc + bj,
+                const float *ip = inv ? inv + g0 + bi * nbc + bj : nullptr;
+                NsRequest r{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, ip,
                             M.weight ? M.weight + off : nullptr, M.cols, lr * s, lr * hp->weight_decay};
                 const std::pair<int64_t, int64_t> key{std::min(br, bc), std::max(br, bc)};
                 size_t k = 0;
@@ -763,25 +764,68 @@ extern "C" size_t muon_step_workspace_bytes(const void *host_plan_full, const vo
     return need;
 }
 
-extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_full, const void *host_plan_block,
-                               const void *dev_plan_block, const qm_muon_matrix *mats, int32_t n_mats,
-                               int64_t step, const qm_muon_hparams *hp, void *ws, size_t ws_bytes,
-                               qm_stream_t stream) {
-    clear_error();
+namespace qm {
+namespace {
+
+qm_status check_hparams(const qm_muon_hparams *hp) {
     if (!hp) return fail(QM_E_ARG, "hparams is null");
-    if (!mats || n_mats <= 0) return fail(QM_E_ARG, "no matrices");
-    if (step < 1) return fail(QM_E_ARG, "step is 1-based");
     if (hp->precision != QM_NS_BF16 && hp->precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision");
     if (hp->ns_steps < 0 || hp->ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
     if (!std::isfinite(hp->lr_full) || !std::isfinite(hp->lr_block) || !std::isfinite(hp->weight_decay) ||
         !std::isfinite(hp->rms_scale) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
         return fail(QM_E_ARG, "hyperparameters must be finite");
     if (!(hp->eps >= 0.0f) || std::isinf(hp->eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    return QM_OK;
+}
+
+// NS + weight apply of every matrix (full) or block, NS workspace at ns_ws.
+qm_status apply_phase(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
+                      bool full, const float *inv, const qm_muon_hparams *hp, void *ns_ws, hipStream_t s) {
+    const auto groups = step_requests(h, host_plan, mats, n, full, inv, hp);
+    for (const auto &g : groups) {
+        const qm_status st = run_ns(g, hp->ns_steps, hp->a, hp->b, hp->c, hp->eps, hp->precision, ns_ws, s);
+        if (st != QM_OK) return st;
+    }
+    return QM_OK;
+}
+
+}  // namespace
+}  // namespace qm
+
+extern "C" qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mats, int32_t n_mats, int32_t full,
+                                const float *inv_norm, const qm_muon_hparams *hp, void *ws, size_t ws_bytes,
+                                qm_stream_t stream) {
+    clear_error();
+    qm_status st = check_hparams(hp);
+    if (st != QM_OK) return st;
+    if (!mats || n_mats <= 0) return fail(QM_E_ARG, "no matrices");
+    if (full != 0 && full != 1) return fail(QM_E_ARG, "full must be 0 or 1");
+    if (!inv_norm || !aligned(inv_norm, 4)) return fail(QM_E_ARG, "inv_norm must be a 4-byte aligned device pointer");
+    const PlanHeader *h = nullptr;
+    st = check_step_plan(host_plan, mats, n_mats, full != 0, &h);
+    if (st != QM_OK) return st;
+    const size_t need = step_ws_bytes(h, host_plan, mats, n_mats, full != 0, hp->precision);
+    if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
+    const size_t upd = align_up(qm_update_workspace_bytes(host_plan), 256);
+    return apply_phase(h, host_plan, mats, n_mats, full != 0, inv_norm, hp, static_cast<char *>(ws) + upd,
+                       static_cast<hipStream_t>(stream));
+}
+
+extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_full, const void *host_plan_block,
+                               const void *dev_plan_block, const qm_muon_matrix *mats, int32_t n_mats,
+                               int64_t step, const qm_muon_hparams *hp, void *ws, size_t ws_bytes,
+                               qm_stream_t stream) {
+    clear_error();
+    qm_status st = check_hparams(hp);
+    if (st != QM_OK) return st;
+    if (!mats || n_mats <= 0) return fail(QM_E_ARG, "no matrices");
+    if (step < 1) return fail(QM_E_ARG, "step is 1-based");
     const bool full = hp->period <= 1 || host_plan_block == nullptr || (step % hp->period) == 0;
     const void *hplan = full ? host_plan_full : host_plan_block;
     const void *dplan = full ? dev_plan_full : dev_plan_block;
     const PlanHeader *h = nullptr;
-    qm_status st = validate_update(hplan, dplan, hp->beta, &h);
+    st = validate_update(hplan, dplan, hp->beta, &h);
     if (st != QM_OK) return st;
     st = check_step_plan(hplan, mats, n_mats, full, &h);
     if (st != QM_OK) return st;
@@ -799,10 +843,5 @@ extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_
     const UpdateWorkspace uw = update_workspace(h, ws);
     st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, s);
     if (st != QM_OK) return st;
-    const auto groups = step_requests(h, hplan, mats, n_mats, full, uw.inv, hp);
-    for (const auto &g : groups) {
-        st = run_ns(g, hp->ns_steps, hp->a, hp->b, hp->c, hp->eps, hp->precision, static_cast<char *>(ws) + upd, s);
-        if (st != QM_OK) return st;
-    }
-    return QM_OK;
+    return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, static_cast<char *>(ws) + upd, s);
 }

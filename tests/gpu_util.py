@@ -69,3 +69,29 @@ def assert_bits_equal(got, exp, what):
         exp = exp.view(got.dtype)
     bad = np.nonzero(got != exp)[0]
     assert bad.size == 0, f"{what}: {bad.size} mismatches, first at {bad[:5]}: {got[bad[:5]]} vs {exp[bad[:5]]}"
+
+
+def ns_parity(got, ref):
+    """(relative Frobenius error, minimum per-row cosine) of got vs ref; rows
+    of ref with zero norm are skipped for the cosine."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    num = np.sum(got * ref, axis=1)
+    den = np.linalg.norm(got, axis=1) * np.linalg.norm(ref, axis=1)
+    ok = np.linalg.norm(ref, axis=1) > 0
+    cos = num[ok] / np.maximum(den[ok], 1e-300)
+    return rel, (cos.min() if cos.size else 1.0)
+
+
+def as_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# Tolerances.  bf16 Newton-Schulz: the workload's stated bound.  f32: fp32
+# products with fp32 accumulation over at most a few thousand terms, five
+# iterations; the quintic amplifies input perturbations by at most
+# a^5 ~ 500 for the smallest singular values, so relative errors stay well
+# below 1e-4 on these inputs.
+NS_BF16_REL, NS_BF16_COS = 2e-2, 0.999
+NS_F32_REL, NS_F32_COS = 1e-4, 0.99999

@@ -1,0 +1,161 @@
+"""GPU parity of the full block-periodic Muon step (update + NS + weights).
+
+Int8 state bit-identical to the oracle on every step; the NS output and the
+weight change within the bf16 Newton-Schulz bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_momentum_newton_amd as q
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, as_f64, assert_bits_equal, host, host_grad,
+                      ns_parity, say)
+from harness import inputs as H
+from oracle import muonbp, ns
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+COEF = tuple(float(np.float32(c)) for c in H.NS_COEFFS)
+
+
+def _within(got, ref, what):
+    rel, cos = ns_parity(got, ref)
+    say(f"   {what}: relF {rel:.3e} min cos {cos:.6f}")
+    assert rel <= NS_BF16_REL and cos >= NS_BF16_COS, (what, rel, cos)
+
+
+def _plans(trip, mats):
+    full = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c, _, _, _) in enumerate(mats)], len(mats))
+    segs, g0 = [], 0
+    for i, (r, c, br, bc, _) in enumerate(mats):
+        s, ng = H.blocked_segments(r, c, br, bc, i, g0)
+        segs += s
+        g0 += ng
+    block = q.Plan(trip, segs, g0)
+    return full, block
+
+
+def test_reduced_muonbp_run_20_steps():
+    """Two matrices (64x2048 in 8 column blocks, 512x256 in 2 row blocks),
+    P = 5, 20 steps: state bit-exact each step, O and W checked each step."""
+    shapes = [(64, 2048, 64, 256), (512, 256, 256, 256)]
+    hp = dict(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, lr_block=0.01,
+              weight_decay=0.01, rms_scale=0.2, ns_steps=5, period=5)
+    trip, mats, W_host, states = [], [], [], []
+    for i, (r, c, br, bc) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3001, i)
+        g = torch.empty(r * c, dtype=torch.bfloat16, device=DEV)
+        w = H.weights((r, c), DEV, 3001, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, br, bc, w))
+        W_host.append(as_f64(w))
+        states.append((host(codes), host(absmax)))
+    full, block = _plans(trip, mats)
+    params = q.make_hparams(beta=hp["beta"], eps=hp["eps"], coeffs=COEF, lr_full=hp["lr_full"],
+                            lr_block=hp["lr_block"], weight_decay=hp["weight_decay"],
+                            rms_scale=hp["rms_scale"], ns_steps=5, period=5)
+    for t in range(1, 21):
+        for i, (r, c, _, _) in enumerate(shapes):
+            trip[i][2].copy_(H.grad((r, c), torch.bfloat16, DEV, 3001, i, t).reshape(-1))
+        torch.cuda.synchronize()
+        gh = [host_grad(trip[i][2]) for i in range(2)]
+        say("step", t)
+        q.muon_step(full, block, mats, t, params)
+        torch.cuda.synchronize()
+        for i, (r, c, br, bc) in enumerate(shapes):
+            W2, c2, a2, O, is_full = muonbp.muon_step(
+                W_host[i], states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c, br, bc,
+                hp["period"], hp["beta"], hp["eps"], COEF, 5, hp["lr_full"], hp["lr_block"],
+                hp["rms_scale"], hp["weight_decay"])
+            assert is_full == (t % 5 == 0)
+            assert_bits_equal(host(trip[i][0]), c2, f"t{t} codes[{i}]")
+            assert_bits_equal(host(trip[i][1]), a2, f"t{t} absmax[{i}]")
+            states[i] = (c2, a2)
+            _within(as_f64(trip[i][2]).reshape(r, c), O, f"t{t} O[{i}]")
+            dW_gpu = as_f64(mats[i][4]) - W_host[i]
+            _within(dW_gpu, W2 - W_host[i], f"t{t} dW[{i}]")
+            W_host[i] = as_f64(mats[i][4])
+
+
+def test_llama8b_layer_full_step():
+    """One full Muon step on the Llama-8B layer: state bit-exact, O and the
+    weight change on sampled rows of every matrix."""
+    tensors, segments, ng = H.config3_layout()
+    trip, mats, hin = [], [], []
+    for i, (name, r, c) in enumerate(tensors):
+        codes, absmax = H.prior_state(r * c, DEV, 1003, i)
+        g = H.grad((r, c), torch.bfloat16, DEV, 1003, i).reshape(-1)
+        w = H.weights((r, c), DEV, 1003, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, w))
+    torch.cuda.synchronize()
+    for i in range(len(tensors)):
+        hin.append((host(trip[i][0]), host(trip[i][1]), host_grad(trip[i][2])))
+    W0 = [host(m[4]) for m in mats]
+    full = q.Plan(trip, segments, ng)
+    params = q.make_hparams(lr_full=0.02, rms_scale=0.2, period=1)
+    say("llama-8B layer muon_step")
+    q.muon_step(full, None, mats, 1, params)
+    torch.cuda.synchronize()
+    states, outs, S, inv, _ = oracle.update_normalize_groups(
+        [(a, b) for a, b, _ in hin], [g for _, _, g in hin], [oracle.BF16] * 7, segments, ng,
+        H.BETA, H.NS_EPS, write_normalized=False)
+    rng = np.random.default_rng(5)
+    for i, (name, r, c) in enumerate(tensors):
+        assert_bits_equal(host(trip[i][0]), states[i][0], f"codes[{name}]")
+        assert_bits_equal(host(trip[i][1]), states[i][1], f"absmax[{name}]")
+        m = oracle.widen(outs[i], oracle.BF16).astype(np.float64).reshape(r, c)
+        rows = np.sort(rng.choice(r, 24, replace=False))
+        ref = ns.spectral_rows(m, rows, 5, COEF, H.NS_EPS, inv_norm=float(inv[i]))
+        O = as_f64(trip[i][2]).reshape(r, c)[rows]
+        _within(O, ref, f"O[{name}]")
+        s = 0.2 * math.sqrt(max(r, c))
+        dW = host(mats[i][4])[rows].astype(np.float64) - W0[i][rows]
+        _within(dW, -0.02 * s * ref, f"dW[{name}]")
+
+
+def test_muonbp_full_size_state_and_sampled_ns():
+    """4096x14336, 8 column blocks, P = 5, 20 steps: the q8 state is
+    bit-exact on all 20 steps (it does not depend on NS or W); NS is checked
+    on sampled rows at a block step (4) and a full step (5)."""
+    cfg = H.config4_shape()
+    r, c, br, bc = cfg["rows"], cfg["cols"], cfg["block_rows"], cfg["block_cols"]
+    codes, absmax = H.prior_state(r * c, DEV, 1004, 0)
+    g = torch.empty(r * c, dtype=torch.bfloat16, device=DEV)
+    w = H.weights((r, c), DEV, 1004, 0)
+    trip = [(codes, absmax, g)]
+    mats = [(r, c, br, bc, w)]
+    full, block = _plans(trip, mats)
+    params = q.make_hparams(lr_full=cfg["lr_full"], lr_block=cfg["lr_block"],
+                            rms_scale=cfg["rms_scale"], period=cfg["period"])
+    hc, ha = host(codes), host(absmax)
+    bid = muonbp.block_group_ids(r, c, br, bc)
+    fid = np.zeros(bid.size, np.int32)
+    rows = np.sort(np.random.default_rng(6).choice(r, 16, replace=False))
+    for t in range(1, cfg["steps"] + 1):
+        g.copy_(H.grad((r, c), torch.bfloat16, DEV, 1004, 0, t).reshape(-1))
+        torch.cuda.synchronize()
+        gh = host_grad(g)
+        say("muonbp step", t)
+        q.muon_step(full, block, mats, t, params)
+        torch.cuda.synchronize()
+        hc, ha, m, bs = oracle.q8_update(hc, ha, gh, H.BETA, oracle.BF16)
+        assert_bits_equal(host(codes), hc, f"t{t} codes")
+        assert_bits_equal(host(absmax), ha, f"t{t} absmax")
+        if t in (4, 5):
+            is_full = t % 5 == 0
+            gid = fid if is_full else bid
+            ngr = 1 if is_full else 8
+            inv = oracle.group_inv_norm(oracle.group_sums([bs], [gid], ngr), H.NS_EPS)
+            mf = oracle.widen(m, oracle.BF16).astype(np.float64).reshape(r, c)
+            O = as_f64(g).reshape(r, c)
+            if is_full:
+                _within(O[rows], ns.spectral_rows(mf, rows, 5, COEF, H.NS_EPS, float(inv[0])), "full O")
+            else:
+                for j in range(8):
+                    ref = ns.spectral_rows(mf[:, bc * j:bc * (j + 1)], rows, 5, COEF, H.NS_EPS,
+                                           float(inv[j]))
+                    _within(O[rows, bc * j:bc * (j + 1)], ref, f"block {j} O")

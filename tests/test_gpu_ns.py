@@ -1,0 +1,131 @@
+"""GPU parity of Newton-Schulz orthogonalisation against the fp64 oracle.
+
+bf16 mode: relative Frobenius error <= 2e-2 and every row's cosine >= 0.999
+(the workload's stated bound); f32 mode: <= 1e-4.  At full size the oracle
+runs through its spectral route on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_momentum_newton_amd as q
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, ns_parity, say)
+from harness import inputs as H
+from oracle import ns
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+COEF = tuple(float(np.float32(c)) for c in H.NS_COEFFS)
+
+
+def _check(got, ref, precision):
+    rel, cos = ns_parity(got, ref)
+    lim_rel, lim_cos = (NS_BF16_REL, NS_BF16_COS) if precision == "bf16" else (NS_F32_REL, NS_F32_COS)
+    say(f"   relF {rel:.3e}  min row cos {cos:.7f}")
+    assert rel <= lim_rel and cos >= lim_cos, (rel, cos)
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (512, 256), (100, 300), (300, 100), (128, 128),
+                                   (1, 7), (7, 1), (257, 513)])
+@pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32),
+                                             ("bf16", torch.float16)])
+def test_ns_small_shapes(shape, precision, dtype):
+    say("ns", shape, precision, dtype)
+    x = H.grad(shape, dtype, DEV, 2001, *shape)
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
+    torch.cuda.synchronize()
+    ref = ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS)
+    _check(as_f64(x), ref, precision if dtype == torch.float32 else "bf16")
+
+
+def test_config1_f32_mode():
+    """256x512 fp32, F32 arithmetic, 5 quintic steps."""
+    x = H.grad((256, 512), torch.float32, DEV, 1001, 7)
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision="f32")
+    torch.cuda.synchronize()
+    _check(as_f64(x), ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS), "f32")
+
+
+def test_given_inverse_norm_and_zero_steps():
+    x = H.grad((200, 300), torch.float32, DEV, 2002)
+    x0 = as_f64(x)
+    inv = torch.tensor([1.0 / (np.linalg.norm(x0) + 1e-7)], dtype=torch.float32, device=DEV)
+    y = x.clone()
+    q.ns_orthogonalize(y, 5, COEF, 1e-7, inv_norm=inv, precision="f32")
+    z = x.clone()
+    q.ns_orthogonalize(z, 0, COEF, 1e-7, inv_norm=inv, precision="f32")
+    torch.cuda.synchronize()
+    invf = float(inv.item())
+    _check(as_f64(y), ns.ns_orthogonalize(x0, 5, COEF, 1e-7, inv_norm=invf), "f32")
+    assert np.allclose(as_f64(z), x0 * invf, rtol=1e-6, atol=0)
+
+
+def test_batched_strided_with_canaries():
+    """Three 96x200 matrices inside a padded buffer (ld 256, gap rows):
+    each gets its own NS, the padding is untouched."""
+    b, rows, cols, ld, gap = 3, 96, 200, 256, 5
+    buf = torch.full((b * (rows + gap), ld), 7.0, dtype=torch.bfloat16, device=DEV)
+    view = torch.as_strided(buf, (b, rows, cols), ((rows + gap) * ld, ld, 1))
+    for i in range(b):
+        view[i].copy_(H.grad((rows, cols), torch.bfloat16, DEV, 2003, i))
+    ins = [as_f64(view[i]) for i in range(b)]
+    q.ns_orthogonalize(view, 5, COEF, H.NS_EPS)
+    torch.cuda.synchronize()
+    for i in range(b):
+        _check(as_f64(view[i]), ns.ns_orthogonalize(ins[i], 5, COEF, H.NS_EPS), "bf16")
+    mask = torch.ones_like(buf, dtype=torch.bool)
+    for i in range(b):
+        mask[i * (rows + gap):i * (rows + gap) + rows, :cols] = False
+    assert torch.all(buf[mask] == 7.0)
+
+
+def test_blocked_small():
+    x = H.grad((256, 1024), torch.bfloat16, DEV, 2004)
+    x0 = as_f64(x)
+    q.ns_orthogonalize_blocked(x, 256, 128, 5, COEF, H.NS_EPS)
+    torch.cuda.synchronize()
+    _check(as_f64(x), ns.ns_blocked(x0, 256, 128, 5, COEF, H.NS_EPS), "bf16")
+
+
+def _sample_rows(n, k, seed):
+    r = np.random.default_rng(seed).choice(n, size=k, replace=False)
+    return np.sort(np.concatenate([[0, n - 1], r]))
+
+
+@pytest.mark.parametrize("name,shape", [("q", (4096, 4096)), ("k", (1024, 4096)),
+                                        ("gate", (14336, 4096)), ("down", (4096, 14336))])
+def test_llama8b_shapes_full_size_sampled(name, shape):
+    say("full-size NS", name, shape)
+    x = H.grad(shape, torch.bfloat16, DEV, 1003, name == "gate", shape[0])
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS)
+    torch.cuda.synchronize()
+    rows = _sample_rows(shape[0], 64, 3)
+    ref = ns.spectral_rows(x0, rows, 5, COEF, H.NS_EPS)
+    _check(as_f64(x)[rows], ref, "bf16")
+
+
+def test_blocked_muonbp_shape_sampled():
+    """4096x14336 cut into 8 column blocks of 4096x1792, one batched NS."""
+    x = H.grad((4096, 14336), torch.bfloat16, DEV, 1004)
+    x0 = as_f64(x)
+    q.ns_orthogonalize_blocked(x, 4096, 1792, 5, COEF, H.NS_EPS)
+    torch.cuda.synchronize()
+    out = as_f64(x)
+    rows = _sample_rows(4096, 32, 4)
+    for j in range(8):
+        blk = x0[:, 1792 * j:1792 * (j + 1)]
+        ref = ns.spectral_rows(blk, rows, 5, COEF, H.NS_EPS)
+        _check(out[rows, 1792 * j:1792 * (j + 1)], ref, "bf16")
+
+
+def test_validation_errors():
+    x = torch.zeros((16, 16), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(q.QmuonError):
+        q.ns_orthogonalize(x, -1)
+    with pytest.raises(q.QmuonError):
+        q.ns_orthogonalize_blocked(x, 16, 5)
+    with pytest.raises(q.QmuonError):
+        q.ns_orthogonalize(x, 5, ws=torch.empty(16, dtype=torch.uint8, device=DEV))
