@@ -1,0 +1,441 @@
+// GRASP 4-bit momentum step for gfx950 ("4-bit-Muon-GRASP"): the momentum
+// of an m x n matrix is held as a rank-k factor P R^T (8-bit) plus a residual
+// (4-bit), both grid-quantised over 64 x 64 blocks (entry / min(row max,
+// column max) inside its block).  One step:
+//   reconstruct M_{t-1}, M_t = mu M_{t-1} + g            (grasp_momentum)
+//   Q = ColNorm(R_{t-1}) (zero columns: seeded warm start) (grasp_colnorm)
+//   P = MGS(M_t Q), R = M_t^T P                           (momentum, mgs, rt)
+//   requantise M_t - P R^T (4-bit), P and R (8-bit)       (residual_q4, factor_q8)
+//   O = NS(M_t) in f32 arithmetic, W <- W - lr (O + wd W) (the NS kernels)
+//
+// Compiled with -ffp-contract=off: fp32 products and sums stay separately
+// rounded, so the codes equal a CPU run of the same operations given the same
+// fp32 P and R.  Long reductions (M Q, M^T P, norms) accumulate in fp64 in a
+// fixed order (no atomics).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "grasp_internal.h"
+#include "internal.h"
+#include "plan_layout.h"
+#include "qmuon.h"
+
+namespace qm {
+namespace {
+
+constexpr int kGrid = 64;
+constexpr int kThreads = 256;
+
+struct Dims {
+    int64_t rows, cols;
+    int32_t rank;
+    int64_t nbr, nbc;       // 64-blocks along rows / cols
+    int64_t packed_cols;    // bytes per residual row
+};
+
+__device__ __forceinline__ float load_grad(const void *p, int64_t i, int dtype) {
+    if (dtype == QM_F32) return static_cast<const float *>(p)[i];
+    const uint16_t h = static_cast<const uint16_t *>(p)[i];
+    if (dtype == QM_BF16) return __uint_as_float((uint32_t)h << 16);
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Deterministic workgroup sum of one fp64 value per thread (fixed order).
+__device__ __forceinline__ double block_sum(double v, double *scratch) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const double s = ((scratch[0] + scratch[1]) + scratch[2]) + scratch[3];
+    __syncthreads();
+    return s;
+}
+
+// --------------------------------------------------- dequantised factors
+// P (rows x k) and R (cols x k): one 64-row block of either per k columns;
+// divisor min(row max, column max), value code * (d / 127).
+__global__ __launch_bounds__(kThreads) void deq_factors_kernel(const int8_t *pc, const float *prm, const float *pcm,
+                                                               const int8_t *rc, const float *rrm, const float *rcm,
+                                                               Dims d, float *Pd, float *Rd) {
+    const int64_t n_p = d.rows * d.rank, n_all = n_p + d.cols * d.rank;
+    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n_all; e += (int64_t)gridDim.x * kThreads) {
+        const bool isp = e < n_p;
+        const int64_t f = isp ? e : e - n_p;
+        const int64_t i = f / d.rank;
+        const int c = (int)(f % d.rank);
+        const float rmax = isp ? prm[i] : rrm[i];
+        const float cmax = isp ? pcm[(i / kGrid) * d.rank + c] : rcm[(i / kGrid) * d.rank + c];
+        const float dv = fminf(rmax, cmax);
+        const float step = dv / 127.0f;
+        const float v = (float)(isp ? pc[f] : rc[f]) * step;
+        if (isp) Pd[f] = v;
+        else Rd[f] = v;
+    }
+}
+
+// ------------------------------------------------------------ ColNorm
+__global__ __launch_bounds__(kThreads) void colnorm_kernel(const float *Rd, const float *warm, Dims d, double *Q) {
+    __shared__ double scratch[4];
+    for (int c = 0; c < d.rank; c++) {
+        double s = 0.0;
+        for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
+            const double v = (double)Rd[j * d.rank + c];
+            s += v * v;
+        }
+        const double nrm = sqrt(block_sum(s, scratch));
+        if (nrm > 0.0) {
+            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) Q[j * d.rank + c] = (double)Rd[j * d.rank + c] / nrm;
+        } else {
+            double w = 0.0;
+            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
+                const double v = (double)warm[j * d.rank + c];
+                w += v * v;
+            }
+            const double nw = sqrt(block_sum(w, scratch));
+            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) Q[j * d.rank + c] = (double)warm[j * d.rank + c] / nw;
+        }
+    }
+}
+
+// ------------------------------------------------- momentum and Y = M Q
+// Four rows per workgroup, lane t walks columns t, t+256, ...:
+//   M_prev = (float)(res + sum_c Pd[i][c] Rd[j][c])  (fp64, c in order)
+//   M = fl(fl(mu * M_prev) + g);   Y[i][c] = sum_j M[i][j] Q[j][c] (fp64)
+template <int K>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(const uint8_t *res_codes, const float *res_rmax,
+                                                            const float *res_cmax, const float *Pd, const float *Rd,
+                                                            const double *Q, const void *g, int gdt, float mu, Dims d,
+                                                            float *M, double *Y) {
+    __shared__ double part[4][4 * K];
+    const int64_t i0 = (int64_t)blockIdx.x * 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double y[4][K];
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+        for (int c = 0; c < K; c++) y[r][c] = 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int64_t i = i0 + r;
+        if (i >= d.rows) break;
+        float p[K];
+#pragma unroll
+        for (int c = 0; c < K; c++) p[c] = Pd[i * K + c];
+        for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
+            const uint8_t byte = res_codes[i * d.packed_cols + (j >> 1)];
+            const int nib = (j & 1) ? (byte >> 4) : (byte & 0xF);
+            const int code = nib >= 8 ? nib - 16 : nib;
+            const float dv = fminf(res_rmax[i * d.nbc + j / kGrid], res_cmax[(i / kGrid) * d.cols + j]);
+            const float step = dv / 7.0f;
+            const float resd = (float)code * step;
+            double acc = (double)resd;
+#pragma unroll
+            for (int c = 0; c < K; c++) acc = acc + (double)p[c] * (double)Rd[j * K + c];
+            const float mprev = (float)acc;
+            const float t1 = mu * mprev;
+            const float m = t1 + load_grad(g, i * d.cols + j, gdt);
+            M[i * d.cols + j] = m;
+#pragma unroll
+            for (int c = 0; c < K; c++) y[r][c] += (double)m * Q[j * K + c];
+        }
+    }
+    // fixed-order reduction: butterfly inside each wave, then waves 0..3
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+        for (int c = 0; c < K; c++) {
+            double v = y[r][c];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0) part[wave][r * K + c] = v;
+        }
+    __syncthreads();
+    if (threadIdx.x < 4 * K) {
+        const int r = threadIdx.x / K, c = threadIdx.x % K;
+        if (i0 + r < d.rows)
+            Y[(i0 + r) * K + c] = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                                  part[3][threadIdx.x];
+    }
+}
+
+// ------------------------------------------------------------ MGS
+// One workgroup: P = Y column by column, each earlier column projected out
+// with the current remainder (modified Gram-Schmidt), then normalised.
+__global__ __launch_bounds__(kThreads) void mgs_kernel(const double *Y, Dims d, double *P, float *P32) {
+    __shared__ double scratch[4];
+    const int K = d.rank;
+    for (int64_t e = threadIdx.x; e < d.rows * K; e += kThreads) P[e] = Y[e];
+    __syncthreads();
+    for (int c = 0; c < K; c++) {
+        for (int p = 0; p < c; p++) {
+            double s = 0.0;
+            for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) s += P[i * K + p] * P[i * K + c];
+            const double dot = block_sum(s, scratch);
+            for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) {
+                const double t = dot * P[i * K + p];
+                P[i * K + c] = P[i * K + c] - t;
+            }
+            __syncthreads();
+        }
+        double s = 0.0;
+        for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) s += P[i * K + c] * P[i * K + c];
+        const double nrm = sqrt(block_sum(s, scratch));
+        for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) P[i * K + c] = nrm > 0.0 ? P[i * K + c] / nrm : 0.0;
+        __syncthreads();
+    }
+    for (int64_t e = threadIdx.x; e < d.rows * K; e += kThreads) P32[e] = (float)P[e];
+}
+
+// ------------------------------------------------------------ R = M^T P
+// 64 columns per workgroup; lane (c, g) = (t % 64, t / 64) sums rows g, g+4,
+// ... (fp64), then the four row groups are added in order.
+template <int K>
+__global__ __launch_bounds__(kThreads) void rt_kernel(const float *M, const double *P, Dims d, float *R32) {
+    __shared__ double part[4][64 * K];
+    const int c = threadIdx.x & 63, grp = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + c;
+    double acc[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) acc[k] = 0.0;
+    if (j < d.cols)
+        for (int64_t i = grp; i < d.rows; i += 4) {
+            const double m = (double)M[i * d.cols + j];
+#pragma unroll
+            for (int k = 0; k < K; k++) acc[k] += m * P[i * K + k];
+        }
+#pragma unroll
+    for (int k = 0; k < K; k++) part[grp][c * K + k] = acc[k];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * K; e += kThreads) {
+        const int64_t jj = (int64_t)blockIdx.x * 64 + e / K;
+        if (jj < d.cols) R32[jj * K + e % K] = (float)(((part[0][e] + part[1][e]) + part[2][e]) + part[3][e]);
+    }
+}
+
+// ------------------------------------------------ residual, 4-bit codes
+// One 64x64 block (clipped) per workgroup:
+//   res = (float)(M - sum_c P32[i][c] R32[j][c])   (fp64, c in order)
+//   row / column maxima of |res| inside the block; code = d == 0 ? 0 :
+//   clamp(rint((res / d) * 7), -7, 7), two codes per byte (even column low).
+__global__ __launch_bounds__(kThreads) void residual_q4_kernel(const float *M, const float *P32, const float *R32,
+                                                               Dims d, uint8_t *codes, float *rmax_out,
+                                                               float *cmax_out) {
+    __shared__ float tile[64][65];
+    __shared__ float rm[64], cm[64];
+    const int64_t bi = blockIdx.y, bj = blockIdx.x;
+    const int64_t r0 = bi * 64, c0 = bj * 64;
+    const int br = (int)min<int64_t>(64, d.rows - r0), bc = (int)min<int64_t>(64, d.cols - c0);
+    const int K = d.rank;
+    for (int idx = threadIdx.x; idx < 4096; idx += kThreads) {
+        const int ii = idx >> 6, jj = idx & 63;
+        float v = 0.0f;
+        if (ii < br && jj < bc) {
+            const int64_t i = r0 + ii, j = c0 + jj;
+            double acc = (double)M[i * d.cols + j];
+            for (int c = 0; c < K; c++) acc = acc - (double)P32[i * K + c] * (double)R32[j * K + c];
+            v = (float)acc;
+        }
+        tile[ii][jj] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float m = 0.0f;
+        for (int jj = 0; jj < bc; jj++) m = fmaxf(m, fabsf(tile[threadIdx.x][jj]));
+        rm[threadIdx.x] = m;
+        if (threadIdx.x < br) rmax_out[(r0 + threadIdx.x) * d.nbc + bj] = m;
+    } else if (threadIdx.x < 128) {
+        const int jj = threadIdx.x - 64;
+        float m = 0.0f;
+        for (int ii = 0; ii < br; ii++) m = fmaxf(m, fabsf(tile[ii][jj]));
+        cm[jj] = m;
+        if (jj < bc) cmax_out[bi * d.cols + c0 + jj] = m;
+    }
+    __syncthreads();
+    for (int pidx = threadIdx.x; pidx < 64 * 32; pidx += kThreads) {
+        const int ii = pidx >> 5, jp = pidx & 31;
+        if (ii >= br || 2 * jp >= bc) continue;
+        int q[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int jj = 2 * jp + h;
+            if (jj >= bc) break;
+            const float dv = fminf(rm[ii], cm[jj]);
+            if (dv != 0.0f) {
+                float r = rintf((tile[ii][jj] / dv) * 7.0f);
+                r = fminf(fmaxf(r, -7.0f), 7.0f);
+                q[h] = (int)r;
+            }
+        }
+        codes[(r0 + ii) * d.packed_cols + bj * 32 + jp] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
+    }
+}
+
+// ------------------------------------------------ factors, 8-bit codes
+// P32 (rows x k) or R32 (cols x k): one 64-row block per workgroup; the k
+// columns form one clipped grid block.
+__global__ __launch_bounds__(kThreads) void factor_q8_kernel(const float *X, int64_t n, int K, int8_t *codes,
+                                                             float *rmax_out, float *cmax_out) {
+    __shared__ float rm[64], cm[64];
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int br = (int)min<int64_t>(64, n - r0);
+    if (threadIdx.x < 64) {
+        float m = 0.0f;
+        if (threadIdx.x < br)
+            for (int c = 0; c < K; c++) m = fmaxf(m, fabsf(X[(r0 + threadIdx.x) * K + c]));
+        rm[threadIdx.x] = m;
+        if (threadIdx.x < br) rmax_out[r0 + threadIdx.x] = m;
+    } else if (threadIdx.x < 64 + K) {
+        const int c = threadIdx.x - 64;
+        float m = 0.0f;
+        for (int ii = 0; ii < br; ii++) m = fmaxf(m, fabsf(X[(r0 + ii) * K + c]));
+        cm[c] = m;
+        cmax_out[blockIdx.x * K + c] = m;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < br * K; e += kThreads) {
+        const int ii = e / K, c = e % K;
+        const float dv = fminf(rm[ii], cm[c]);
+        int q = 0;
+        if (dv != 0.0f) {
+            float r = rintf((X[(r0 + ii) * K + c] / dv) * 127.0f);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            q = (int)r;
+        }
+        codes[(r0 + ii) * K + c] = (int8_t)q;
+    }
+}
+
+struct Ws {
+    float *M, *Pd, *Rd, *P32, *R32;
+    double *Q, *Y, *P;
+    void *ns;
+    size_t bytes;
+};
+
+Ws carve(const Dims &d, void *base) {
+    Ws w{};
+    char *p = static_cast<char *>(base);
+    auto take = [&](int64_t bytes) {
+        char *q = p;
+        p += align_up(bytes, 256);
+        return q;
+    };
+    const int64_t rk = d.rows * d.rank, ck = d.cols * d.rank;
+    w.M = reinterpret_cast<float *>(take(d.rows * d.cols * 4));
+    w.Pd = reinterpret_cast<float *>(take(rk * 4));
+    w.Rd = reinterpret_cast<float *>(take(ck * 4));
+    w.P32 = reinterpret_cast<float *>(take(rk * 4));
+    w.R32 = reinterpret_cast<float *>(take(ck * 4));
+    w.Q = reinterpret_cast<double *>(take(ck * 8));
+    w.Y = reinterpret_cast<double *>(take(rk * 8));
+    w.P = reinterpret_cast<double *>(take(rk * 8));
+    w.ns = p;
+    w.bytes = (size_t)(p - static_cast<char *>(base));
+    return w;
+}
+
+Dims dims(int64_t rows, int64_t cols, int32_t rank) {
+    Dims d;
+    d.rows = rows;
+    d.cols = cols;
+    d.rank = rank;
+    d.nbr = (rows + kGrid - 1) / kGrid;
+    d.nbc = (cols + kGrid - 1) / kGrid;
+    d.packed_cols = (cols + 1) / 2;
+    return d;
+}
+
+qm_status launched(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return QM_OK;
+}
+
+template <int K>
+void launch_rank_kernels(const qm_grasp_state *s, const Dims &d, const Ws &w, const void *grad, int gdt, float mu,
+                         hipStream_t st) {
+    momentum_kernel<K><<<(unsigned)((d.rows + 3) / 4), kThreads, 0, st>>>(
+        s->res_codes, s->res_rmax, s->res_cmax, w.Pd, w.Rd, w.Q, grad, gdt, mu, d, w.M, w.Y);
+}
+
+template <int K>
+void launch_rt(const Dims &d, const Ws &w, hipStream_t st) {
+    rt_kernel<K><<<(unsigned)((d.cols + 63) / 64), kThreads, 0, st>>>(w.M, w.P, d, w.R32);
+}
+
+}  // namespace
+}  // namespace qm
+
+using namespace qm;
+
+extern "C" size_t grasp_workspace_bytes(int64_t rows, int64_t cols, int32_t rank) {
+    if (rows <= 0 || cols <= 0 || rank <= 0 || rank > 16) return 0;
+    const Dims d = dims(rows, cols, rank);
+    std::vector<char> dummy;
+    const Ws w = carve(d, nullptr);
+    return w.bytes + ns_f32_workspace_bytes(rows, cols);
+}
+
+extern "C" qm_status grasp_step(const qm_grasp_state *state, int64_t rows, int64_t cols, int32_t rank,
+                                int32_t grid, void *grad, int32_t grad_dtype, const float *warm, float mu,
+                                int32_t ns_steps, float a, float b, float c, float eps, float *weight, float lr,
+                                float weight_decay, void *ws, size_t ws_bytes, qm_stream_t stream) {
+    clear_error();
+    if (!state || !grad || !warm) return fail(QM_E_ARG, "state, grad and warm are required");
+    if (!state->res_codes || !state->res_rmax || !state->res_cmax || !state->p_codes || !state->p_rmax ||
+        !state->p_cmax || !state->r_codes || !state->r_rmax || !state->r_cmax)
+        return fail(QM_E_ARG, "state buffer missing");
+    if (rows <= 0 || cols <= 0) return fail(QM_E_SHAPE, "rows and cols must be positive");
+    if (rank < 1 || rank > 16 || (rank & (rank - 1)))
+        return fail(QM_E_UNSUPPORTED, "rank must be 1, 2, 4, 8 or 16");
+    if (grid != kGrid) return fail(QM_E_UNSUPPORTED, "grid blocks must be 64x64");
+    if (grad_dtype != QM_F32 && grad_dtype != QM_BF16 && grad_dtype != QM_F16)
+        return fail(QM_E_DTYPE, "unknown grad dtype %d", grad_dtype);
+    if (!aligned(grad, grad_dtype == QM_F32 ? 4 : 2) || !aligned(warm, 4) || (weight && !aligned(weight, 4)))
+        return fail(QM_E_ALIGN, "misaligned pointer");
+    if (!std::isfinite(mu) || !std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(a) ||
+        !std::isfinite(b) || !std::isfinite(c) || !(eps >= 0.0f) || std::isinf(eps))
+        return fail(QM_E_ARG, "hyperparameters must be finite (eps >= 0)");
+    if (ns_steps < 0 || ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
+    if (std::min(rows, cols) > (1 << 16) || std::max(rows, cols) > (1 << 22))
+        return fail(QM_E_UNSUPPORTED, "matrix too large");
+    const size_t need = grasp_workspace_bytes(rows, cols, rank);
+    if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Dims d = dims(rows, cols, rank);
+    const Ws w = carve(d, ws);
+    const qm_grasp_state *s = state;
+    deq_factors_kernel<<<256, kThreads, 0, st>>>(s->p_codes, s->p_rmax, s->p_cmax, s->r_codes, s->r_rmax, s->r_cmax, d,
+                                                 w.Pd, w.Rd);
+    colnorm_kernel<<<1, kThreads, 0, st>>>(w.Rd, warm, d, w.Q);
+    switch (rank) {
+        case 1: launch_rank_kernels<1>(s, d, w, grad, grad_dtype, mu, st); break;
+        case 2: launch_rank_kernels<2>(s, d, w, grad, grad_dtype, mu, st); break;
+        case 4: launch_rank_kernels<4>(s, d, w, grad, grad_dtype, mu, st); break;
+        case 8: launch_rank_kernels<8>(s, d, w, grad, grad_dtype, mu, st); break;
+        default: launch_rank_kernels<16>(s, d, w, grad, grad_dtype, mu, st); break;
+    }
+    mgs_kernel<<<1, kThreads, 0, st>>>(w.Y, d, w.P, w.P32);
+    switch (rank) {
+        case 1: launch_rt<1>(d, w, st); break;
+        case 2: launch_rt<2>(d, w, st); break;
+        case 4: launch_rt<4>(d, w, st); break;
+        case 8: launch_rt<8>(d, w, st); break;
+        default: launch_rt<16>(d, w, st); break;
+    }
+    residual_q4_kernel<<<dim3((unsigned)d.nbc, (unsigned)d.nbr), kThreads, 0, st>>>(
+        w.M, w.P32, w.R32, d, s->res_codes, s->res_rmax, s->res_cmax);
+    factor_q8_kernel<<<(unsigned)d.nbr, kThreads, 0, st>>>(w.P32, rows, rank, s->p_codes, s->p_rmax, s->p_cmax);
+    factor_q8_kernel<<<(unsigned)d.nbc, kThreads, 0, st>>>(w.R32, cols, rank, s->r_codes, s->r_rmax, s->r_cmax);
+    qm_status stt = launched("grasp state kernels");
+    if (stt != QM_OK) return stt;
+    // O = NS(M_t) in f32 arithmetic, written over the grad; W <- W - lr (O + wd W)
+    return run_ns_f32_into(w.M, rows, cols, grad, grad_dtype, weight, lr, lr * weight_decay, ns_steps, a, b, c, eps,
+                           w.ns, st);
+}

@@ -17,12 +17,16 @@
 //     writes alongside X.  One MFMA kernel template serves all of them.
 //   * The two symmetric products run only on lower-triangle tiles and store
 //     each off-diagonal tile twice (the SYRK shortcut).
-//   * Tiles are loaded global -> registers -> LDS (double buffered, one
-//     barrier per k-tile) with a 16-byte XOR swizzle against bank conflicts;
-//     every lane feeds v_mfma_f32_32x32x16_bf16 (or 32x32x2 f32) from one
-//     16-byte LDS read per operand per step.
-//   * Workgroup ids are remapped so each XCD (own L2) gets a contiguous
-//     range of tiles.
+//   * One launch per product covers every matrix of the request (up to 8,
+//     of any shapes): tiles of all matrices form one index space, the matrix
+//     with the longest K first, so 256 CUs stay busy even when one matrix
+//     alone has few tiles.
+//   * 256x256 output tiles, four waves of 128x128 (accumulators in AGPRs),
+//     K-tiles of 128 bytes per row double-buffered in LDS and filled by
+//     direct global-to-LDS loads (no staging registers); a 16-byte XOR
+//     swizzle keeps the 16-byte fragment reads free of bank conflicts.
+//   * Workgroups are remapped so each XCD (own L2) takes runs of 8 adjacent
+//     tiles while all XCDs walk the tile list together.
 //   * Internal buffers are zero-padded to multiples of 256: zero rows and
 //     columns stay zero through the iteration, so no kernel needs bounds
 //     checks in its main loop.
@@ -31,6 +35,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <numeric>
 #include <vector>
 
 #include "internal.h"
@@ -109,10 +114,10 @@ template <> struct Mfma<float> {
 
 // ------------------------------------------------------------ GEMM kernel
 
-enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL = 3 };
+enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
 
-// Where the last product writes: the caller's matrix (original orientation,
-// its dtype) and optionally fp32 weights.
+// Where the result goes: the caller's matrix (original orientation, its
+// dtype) and optionally fp32 weights.
 struct FinalOut {
     void *out;
     float *w;
@@ -122,25 +127,34 @@ struct FinalOut {
     float lr_s, lr_wd;     // lr * s and lr * weight_decay
 };
 
-template <typename T> struct GemmArgs {
-    const T *P; int64_t ldp, sp;   // element strides: row, item
-    const T *Q; int64_t ldq, sq;
-    T *C; int64_t ldc, sc;         // primary output
-    T *CT; int64_t ldct, sct;      // transposed output (EPI_UPDATE)
-    const T *D; int64_t ldd, sd;   // epilogue input
-    int32_t tiles_m, tiles_n;      // tile grid per item (tiles_m == tiles_n for SYM)
-    int32_t tiles_per_item, n_items;
-    int32_t k_tiles;               // K / (128 / sizeof(T))
-    float alpha, beta;
-    FinalOut fo[kMaxItems];
+// One matrix of a grouped product (element strides).
+template <typename T> struct GItem {
+    const T *P;
+    const T *Q;
+    T *C;
+    T *CT;
+    const T *D;
+    int64_t ldp, ldq, ldc, ldct, ldd;
+    int32_t tiles_n;       // tile columns (non-symmetric products)
+    int32_t tile_begin;    // first logical tile of this matrix
+    int32_t k_tiles;       // K / (128 / sizeof(T))
+    int32_t pad;
 };
 
-// Logical tile for workgroup w: workgroups are issued to the 8 XCDs round
-// robin; give every XCD a contiguous range of logical tiles.
+template <typename T> struct GemmArgs {
+    GItem<T> it[kMaxItems];
+    int32_t n_items;
+    float alpha, beta;
+};
+
+// Workgroups go to the 8 XCDs round robin (w % 8).  Inside every run of 64
+// workgroups each XCD gets 8 consecutive logical tiles (which share operand
+// panels in its L2) while all XCDs advance through the tile list together.
 __device__ __forceinline__ int xcd_remap(int w, int nwg) {
-    const int per = nwg / 8, rem = nwg % 8;
-    const int x = w % 8, l = w / 8;
-    return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + l;
+    const int full = nwg / 64 * 64;
+    if (w >= full) return w;
+    const int q = w / 64, r = w % 64;
+    return q * 64 + (r % 8) * 8 + r / 8;
 }
 
 __device__ __forceinline__ void tri_coords(int t, int &bi, int &bj) {
@@ -151,64 +165,64 @@ __device__ __forceinline__ void tri_coords(int t, int &bi, int &bj) {
     bj = t - i * (i + 1) / 2;
 }
 
+__device__ __forceinline__ void lds_dma16(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
 template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int EPI, bool SYM>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs<T> args) {
-    constexpr int NT = WAVES_M * WAVES_N * 64;
+    constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int ROWB = 128;                     // LDS bytes per tile row (one k-tile)
-    constexpr int P_LOADS = BM * 8 / NT, Q_LOADS = BN * 8 / NT;
-    static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile / thread count");
+    constexpr int ROWB = 128;                       // LDS bytes per tile row (one k-tile)
+    constexpr int STAGE = (BM + BN) * ROWB;
+    constexpr int PI = BM / 8 / NW, QI = BN / 8 / NW;  // DMA instructions per wave per stage
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile / wave count");
     static_assert(FM >= 1 && FN >= 1, "wave tile");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *sP = smem;                       // [2][BM][128]
-    char *sQ = smem + 2 * BM * ROWB;       // [2][BN][128]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int item = L / args.tiles_per_item;
-    const int t = L % args.tiles_per_item;
+    int item = 0;
+    while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+    const GItem<T> &I = args.it[item];
+    const int t = L - I.tile_begin;
     int bi, bj;
     if constexpr (SYM) {
         tri_coords(t, bi, bj);
     } else {
-        bi = t / args.tiles_n;
-        bj = t % args.tiles_n;
+        bi = t / I.tiles_n;
+        bj = t % I.tiles_n;
     }
 
-    const char *Pg = reinterpret_cast<const char *>(args.P + item * args.sp + (int64_t)bi * BM * args.ldp);
-    const char *Qg = reinterpret_cast<const char *>(args.Q + item * args.sq + (int64_t)bj * BN * args.ldq);
-    const int64_t ldpb = args.ldp * (int64_t)sizeof(T), ldqb = args.ldq * (int64_t)sizeof(T);
+    const char *Pg = reinterpret_cast<const char *>(I.P + (int64_t)bi * BM * I.ldp);
+    const char *Qg = reinterpret_cast<const char *>(I.Q + (int64_t)bj * BN * I.ldq);
+    const int64_t ldpb = I.ldp * (int64_t)sizeof(T), ldqb = I.ldq * (int64_t)sizeof(T);
+    const int lr8 = lane >> 3, lch = lane & 7;
 
-    u32x4 rp[P_LOADS], rq[Q_LOADS];
-#define QM_GLOAD(kt)                                                                              \
-    do {                                                                                          \
-        _Pragma("unroll") for (int i_ = 0; i_ < P_LOADS; i_++) {                                  \
-            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
-            rp[i_] = *reinterpret_cast<const u32x4 *>(Pg + row * ldpb + (int64_t)(kt)*ROWB + ch * 16); \
-        }                                                                                         \
-        _Pragma("unroll") for (int i_ = 0; i_ < Q_LOADS; i_++) {                                  \
-            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
-            rq[i_] = *reinterpret_cast<const u32x4 *>(Qg + row * ldqb + (int64_t)(kt)*ROWB + ch * 16); \
-        }                                                                                         \
-    } while (0)
-#define QM_SWRITE(buf)                                                                            \
-    do {                                                                                          \
-        char *dp_ = sP + (buf)*BM * ROWB;                                                         \
-        char *dq_ = sQ + (buf)*BN * ROWB;                                                         \
-        _Pragma("unroll") for (int i_ = 0; i_ < P_LOADS; i_++) {                                  \
-            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
-            *reinterpret_cast<u32x4 *>(dp_ + row * ROWB + ((ch ^ (row & 7)) << 4)) = rp[i_];      \
-        }                                                                                         \
-        _Pragma("unroll") for (int i_ = 0; i_ < Q_LOADS; i_++) {                                  \
-            const int idx = tid + i_ * NT, row = idx >> 3, ch = idx & 7;                          \
-            *reinterpret_cast<u32x4 *>(dq_ + row * ROWB + ((ch ^ (row & 7)) << 4)) = rq[i_];      \
-        }                                                                                         \
-    } while (0)
+    // Direct loads: one instruction moves 8 tile rows (1 KiB) into LDS; lane
+    // l lands at LDS row r0 + l/8, position l%8, so it fetches global chunk
+    // (l%8) ^ (row%8) -- the swizzle is applied on the global side.
+    auto issue = [&](int kt, int stage) {
+        char *base = smem + stage * STAGE;
+#pragma unroll
+        for (int i = 0; i < PI; i++) {
+            const int r0 = (wave + i * NW) * 8;
+            const int row = r0 + lr8;
+            lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ (row & 7)) << 4), base + r0 * ROWB);
+        }
+#pragma unroll
+        for (int i = 0; i < QI; i++) {
+            const int r0 = (wave + i * NW) * 8;
+            const int row = r0 + lr8;
+            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ (row & 7)) << 4), base + (BM + r0) * ROWB);
+        }
+    };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -218,16 +232,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    const int KT = args.k_tiles;
-    QM_GLOAD(0);
-    QM_SWRITE(0);
-    __syncthreads();
+    const int KT = I.k_tiles;
     const int lrow = lane & 31, lhalf = lane >> 5;
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     for (int kt = 0; kt < KT; kt++) {
         const int cur = kt & 1;
-        if (kt + 1 < KT) QM_GLOAD(kt + 1);
-        const char *cp = sP + cur * BM * ROWB;
-        const char *cq = sQ + cur * BN * ROWB;
+        if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
+        const char *cp = smem + cur * STAGE;
+        const char *cq = cp + BM * ROWB;
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             const int ch = 2 * s + lhalf;
@@ -247,58 +261,59 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
 #pragma unroll
                 for (int j = 0; j < FN; j++) Mfma<T>::step(a[i], b[j], acc[i][j]);
         }
-        if (kt + 1 < KT) QM_SWRITE(cur ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
-#undef QM_GLOAD
-#undef QM_SWRITE
-
     // ---------------------------------------------------------- epilogue
     // acc[i][j][r] holds C[row][col] with row = 8(r/4) + 4 lhalf + r%4 and
-    // col = lrow inside the 32x32 MFMA tile.
+    // col = lrow inside the 32x32 MFMA tile.  In the transposed layouts
+    // (mirror tile, X^T) the four rows r%4 = 0..3 are adjacent, so each lane
+    // writes them with one vector store.  The empty asm between sub-tiles
+    // keeps the compiler from hoisting every load of the epilogue at once.
     const bool mirror = SYM && bi != bj;
-    T *C = args.C + item * args.sc;
-    T *CT = args.CT ? args.CT + item * args.sct : nullptr;
-    const T *D = args.D ? args.D + item * args.sd : nullptr;
-    const FinalOut &fo = args.fo[item < kMaxItems ? item : 0];
 #pragma unroll
     for (int i = 0; i < FM; i++)
 #pragma unroll
-        for (int j = 0; j < FN; j++)
+        for (int j = 0; j < FN; j++) {
+            const int64_t r0 = (int64_t)bi * BM + wm * WM + i * 32 + 4 * lhalf;
+            const int64_t c0 = (int64_t)bj * BN + wn * WN + j * 32 + lrow;
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int64_t gr = (int64_t)bi * BM + wm * WM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-                const int64_t gc = (int64_t)bj * BN + wn * WN + j * 32 + lrow;
-                float v = acc[i][j][r];
-                if constexpr (EPI == EPI_GRAM) {
-                    const T o = from_float<T>(v);
-                    C[gr * args.ldc + gc] = o;
-                    if (mirror) C[gc * args.ldc + gr] = o;
-                } else if constexpr (EPI == EPI_POLY) {
-                    v = args.alpha * to_float(D[gr * args.ldd + gc]) + args.beta * v;
-                    const T o = from_float<T>(v);
-                    C[gr * args.ldc + gc] = o;
-                    if (mirror) C[gc * args.ldc + gr] = o;
-                } else if constexpr (EPI == EPI_UPDATE) {
-                    v = args.alpha * to_float(D[gr * args.ldd + gc]) + v;
-                    const T o = from_float<T>(v);
-                    C[gr * args.ldc + gc] = o;
-                    CT[gc * args.ldct + gr] = o;
-                } else {
-                    v = args.alpha * to_float(D[gr * args.ldd + gc]) + v;
-                    if (gr < fo.m && gc < fo.n) {
-                        // original orientation: (gr, gc) or transposed
-                        const int64_t idx = fo.tall ? gc * fo.ld + gr : gr * fo.ld + gc;
-                        store_any(fo.out, idx, fo.dtype, v);
-                        if (fo.w) {
-                            const int64_t wi = fo.tall ? gc * fo.ldw + gr : gr * fo.ldw + gc;
-                            const float w = fo.w[wi];
-                            fo.w[wi] = w - (fo.lr_s * v + fo.lr_wd * w);
-                        }
+            for (int g = 0; g < 4; g++) {
+                const int64_t gr = r0 + 8 * g;   // rows gr .. gr+3, column c0
+                float v[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) v[q] = acc[i][j][4 * g + q];
+                if constexpr (EPI != EPI_GRAM) {
+                    const float sc = EPI == EPI_POLY ? args.beta : 1.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; q++) v[q] = args.alpha * to_float(I.D[(gr + q) * I.ldd + c0]) + sc * v[q];
+                }
+                T o[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    o[q] = from_float<T>(v[q]);
+                    I.C[(gr + q) * I.ldc + c0] = o[q];
+                }
+                T *tp = nullptr;
+                if constexpr (EPI == EPI_UPDATE) {
+                    if (I.CT) tp = I.CT + c0 * I.ldct + gr;
+                } else if (mirror) {
+                    tp = I.C + c0 * I.ldc + gr;
+                }
+                if (tp) {
+                    if constexpr (sizeof(T) == 2) {
+                        uint2 pk;
+                        pk.x = (uint32_t)o[0].bits | ((uint32_t)o[1].bits << 16);
+                        pk.y = (uint32_t)o[2].bits | ((uint32_t)o[3].bits << 16);
+                        *reinterpret_cast<uint2 *>(tp) = pk;
+                    } else {
+                        *reinterpret_cast<float4 *>(tp) = make_float4(v[0], v[1], v[2], v[3]);
                     }
                 }
             }
+            asm volatile("" ::: "memory");
+        }
 }
 
 // ------------------------------------------------------- norm + prologue
@@ -308,24 +323,32 @@ struct NsItem {
     int64_t ld;
     int32_t dtype;
     int32_t tall;
-    const float *inv;   // device scale, or null: compute from the data
+    const float *inv;      // device scale, or null: computed from the data
+    void *X, *XT;          // internal buffers (element type of the run)
+    int32_t m, n;          // valid extent in iteration orientation
+    int64_t mp, np;        // padded
+    int32_t tiles_n;       // 64-wide tiles per padded row
+    int32_t tile_begin;    // first 64x64 tile of this item
 };
 
 struct PrologueArgs {
     NsItem it[kMaxItems];
-    int32_t m, n;                  // valid extent in iteration orientation
-    int64_t mp, np;                // padded
-    int32_t tiles_n, tiles_per_item;
-    void *X; void *XT; int64_t item_stride;   // element stride between items
-    const float *inv_ws;           // per-item computed scales (when it[i].inv is null)
+    int32_t n_items;
+    const float *inv_ws;   // per-item computed scales (when it[i].inv is null)
 };
 
+__device__ __forceinline__ int find_item(const PrologueArgs &a, int L) {
+    int item = 0;
+    while (item + 1 < a.n_items && a.it[item + 1].tile_begin <= L) item++;
+    return item;
+}
+
 // Partial sums of squares: grid (kNormChunks, items); each workgroup covers
-// a fixed slice of the item's rows.
+// a fixed slice of the item's rows; fixed combine order.
 __global__ __launch_bounds__(256) void norm_partial_kernel(PrologueArgs a, double *partials) {
     const int item = blockIdx.y;
     const NsItem &it = a.it[item];
-    const int64_t rows = it.tall ? a.n : a.m, cols = it.tall ? a.m : a.n;
+    const int64_t rows = it.tall ? it.n : it.m, cols = it.tall ? it.m : it.n;
     const int64_t per = (rows + kNormChunks - 1) / kNormChunks;
     const int64_t r0 = blockIdx.x * per, r1 = min(rows, r0 + per);
     double acc = 0.0;
@@ -356,10 +379,10 @@ __global__ void norm_final_kernel(const double *partials, float eps, float *inv_
 template <typename T>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     __shared__ float tile[64][65];
-    const int item = blockIdx.x / a.tiles_per_item;
-    const int t = blockIdx.x % a.tiles_per_item;
-    const int64_t i0 = (int64_t)(t / a.tiles_n) * 64, j0 = (int64_t)(t % a.tiles_n) * 64;
+    const int item = find_item(a, blockIdx.x);
     const NsItem &it = a.it[item];
+    const int t = blockIdx.x - it.tile_begin;
+    const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
     const float s = it.inv ? it.inv[0] : a.inv_ws[item];
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
         // read along the source's contiguous dimension
@@ -367,42 +390,56 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
         const int jj = it.tall ? (idx >> 6) : (idx & 63);
         const int64_t i = i0 + ii, j = j0 + jj;
         float v = 0.0f;
-        if (i < a.m && j < a.n) {
+        if (i < it.m && j < it.n) {
             const int64_t src = it.tall ? j * it.ld + i : i * it.ld + j;
             v = load_any(it.src, src, it.dtype) * s;
         }
         tile[ii][jj] = v;
     }
     __syncthreads();
-    T *X = static_cast<T *>(a.X) + item * a.item_stride;
-    T *XT = static_cast<T *>(a.XT) + item * a.item_stride;
+    T *X = static_cast<T *>(it.X);
+    T *XT = static_cast<T *>(it.XT);
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
         const int ii = idx >> 6, jj = idx & 63;
-        X[(i0 + ii) * a.np + j0 + jj] = from_float<T>(tile[ii][jj]);
-        XT[(j0 + ii) * a.mp + i0 + jj] = from_float<T>(tile[jj][ii]);
+        X[(i0 + ii) * it.np + j0 + jj] = from_float<T>(tile[ii][jj]);
+        XT[(j0 + ii) * it.mp + i0 + jj] = from_float<T>(tile[jj][ii]);
     }
 }
 
-// steps == 0: the output is X0 itself.
+// Output of the iteration (X after the last product, or X0 when steps == 0)
+// to the caller's matrix in its orientation and dtype, with the weight
+// update W <- W - (lr s) O - (lr wd) W.  64x64 tiles through LDS so reads
+// of X and writes of O and W are all row-contiguous.
+struct WritebackArgs {
+    FinalOut fo[kMaxItems];
+};
+
 template <typename T>
-__global__ __launch_bounds__(256) void writeback_kernel(const T *X, int64_t item_stride, int64_t np,
-                                                        int32_t tiles_n, int32_t tiles_per_item,
-                                                        GemmArgs<T> g) {
-    const int item = blockIdx.x / tiles_per_item;
-    const int t = blockIdx.x % tiles_per_item;
-    const int64_t i0 = (int64_t)(t / tiles_n) * 64, j0 = (int64_t)(t % tiles_n) * 64;
-    const FinalOut &fo = g.fo[item];
-    const T *Xi = X + item * item_stride;
+__global__ __launch_bounds__(256) void writeback_kernel(PrologueArgs a, WritebackArgs wb) {
+    __shared__ float tile[64][65];
+    const int item = find_item(a, blockIdx.x);
+    const NsItem &it = a.it[item];
+    const int t = blockIdx.x - it.tile_begin;
+    const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
+    const FinalOut &fo = wb.fo[item];
+    const T *X = static_cast<const T *>(it.X);
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
-        const int64_t i = i0 + (idx >> 6), j = j0 + (idx & 63);
+        const int ii = idx >> 6, jj = idx & 63;
+        tile[ii][jj] = to_float(X[(i0 + ii) * it.np + j0 + jj]);
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 4096; idx += 256) {
+        // walk the caller's contiguous dimension
+        const int ii = fo.tall ? (idx & 63) : (idx >> 6);
+        const int jj = fo.tall ? (idx >> 6) : (idx & 63);
+        const int64_t i = i0 + ii, j = j0 + jj;
         if (i >= fo.m || j >= fo.n) continue;
-        const float v = to_float(Xi[i * np + j]);
-        const int64_t o = fo.tall ? j * fo.ld + i : i * fo.ld + j;
-        store_any(fo.out, o, fo.dtype, v);
+        const float v = tile[ii][jj];
+        store_any(fo.out, fo.tall ? j * fo.ld + i : i * fo.ld + j, fo.dtype, v);
         if (fo.w) {
-            const int64_t wi = fo.tall ? j * fo.ldw + i : i * fo.ldw + j;
-            const float w = fo.w[wi];
-            fo.w[wi] = w - (fo.lr_s * v + fo.lr_wd * w);
+            float *wp = fo.w + (fo.tall ? j * fo.ldw + i : i * fo.ldw + j);
+            const float w = *wp;
+            *wp = w - (fo.lr_s * v + fo.lr_wd * w);
         }
     }
 }
@@ -422,28 +459,57 @@ struct NsRequest {
 
 struct Geometry {
     int64_t m, n, mp, np;
-    size_t esz;
-    int64_t x_elems, a_elems;    // per item
-    size_t item_bytes;           // X + XT0 + XT1 + A + B, each 256-aligned
+    int64_t x_bytes, a_bytes;    // one X-shaped / A-shaped buffer, 256-aligned
+    int64_t item_bytes;          // X + XT0 + XT1 + A + B
 };
 
-Geometry geometry(int64_t rows, int64_t cols, int precision) {
+Geometry geometry(int64_t rows, int64_t cols, size_t esz) {
     Geometry g;
     g.m = std::min(rows, cols);
     g.n = std::max(rows, cols);
     g.mp = pad_up(g.m);
     g.np = pad_up(g.n);
-    g.esz = precision == QM_NS_F32 ? 4 : 2;
-    g.x_elems = g.mp * g.np;
-    g.a_elems = g.mp * g.mp;
-    g.item_bytes = 3 * align_up(g.x_elems * (int64_t)g.esz, 256) + 2 * align_up(g.a_elems * (int64_t)g.esz, 256);
+    g.x_bytes = align_up(g.mp * g.np * (int64_t)esz, 256);
+    g.a_bytes = align_up(g.mp * g.mp * (int64_t)esz, 256);
+    g.item_bytes = 3 * g.x_bytes + 2 * g.a_bytes;
     return g;
 }
 
-size_t ns_ws_bytes_for(int64_t rows, int64_t cols, int64_t items, int precision) {
-    const Geometry g = geometry(rows, cols, precision);
-    const int64_t k = std::min<int64_t>(items, kMaxItems);
-    return (size_t)k * g.item_bytes + align_up(kMaxItems * kNormChunks * 8, 256) + align_up(kMaxItems * 4, 256);
+size_t elem_size(int precision) { return precision == QM_NS_F32 ? 4 : 2; }
+
+// Requests are processed in chunks of up to kMaxItems, largest first; the
+// workspace holds the largest chunk plus the norm scratch.
+std::vector<std::vector<size_t>> make_chunks(const std::vector<NsRequest> &req) {
+    std::vector<size_t> order(req.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) {
+        return req[x].rows * req[x].cols > req[y].rows * req[y].cols;
+    });
+    std::vector<std::vector<size_t>> chunks;
+    for (size_t k = 0; k < order.size(); k += kMaxItems)
+        chunks.emplace_back(order.begin() + k, order.begin() + std::min(order.size(), k + kMaxItems));
+    return chunks;
+}
+
+constexpr int64_t kNormBytes = align_up_const(kMaxItems * kNormChunks * 8, 256) + align_up_const(kMaxItems * 4, 256);
+
+size_t ns_ws_bytes_req(const std::vector<NsRequest> &req, int precision) {
+    int64_t best = 0;
+    for (const auto &ch : make_chunks(req)) {
+        int64_t s = 0;
+        for (size_t i : ch) s += geometry(req[i].rows, req[i].cols, elem_size(precision)).item_bytes;
+        best = std::max(best, s);
+    }
+    return (size_t)(best + kNormBytes);
+}
+
+size_t ns_ws_bytes_uniform(int64_t rows, int64_t cols, int64_t items, int precision) {
+    std::vector<NsRequest> req((size_t)items);
+    for (auto &r : req) {
+        r.rows = rows;
+        r.cols = cols;
+    }
+    return ns_ws_bytes_req(req, precision);
 }
 
 template <typename T, int BM, int BN, int WMW, int WNW, int EPI, bool SYM>
@@ -465,119 +531,165 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
 }
 
 // Tile configuration of the NS products.
-constexpr int kBM = 128, kBN = 128, kWM = 2, kWN = 2;
+constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 2;
+
+struct ItemBufs {
+    Geometry g;
+    char *X, *XT0, *XT1, *A, *B;
+};
 
 template <typename T>
-qm_status run_ns_typed(const std::vector<NsRequest> &req, int steps, float a, float b, float c, float eps,
-                       void *ws, hipStream_t stream) {
-    const Geometry g = geometry(req[0].rows, req[0].cols, sizeof(T) == 4 ? QM_NS_F32 : QM_NS_BF16);
-    // Layout (as sized by ns_ws_bytes_for): kcap items, then the norm
-    // partials, then the computed inverse norms.
-    char *base = static_cast<char *>(ws);
-    const int64_t kcap = std::min<int64_t>((int64_t)req.size(), kMaxItems);
-    double *partials = reinterpret_cast<double *>(base + kcap * g.item_bytes);
-    float *inv_ws = reinterpret_cast<float *>(base + kcap * g.item_bytes + align_up(kMaxItems * kNormChunks * 8, 256));
-
-    for (size_t first = 0; first < req.size(); first += kMaxItems) {
-        const int nit = (int)std::min<size_t>(kMaxItems, req.size() - first);
-        // Item-major layout of the workspace: all X, then all XT0, XT1, A, B,
-        // so that every buffer kind has one uniform item stride.
-        const int64_t xs = align_up(g.x_elems * (int64_t)sizeof(T), 256) / (int64_t)sizeof(T);
-        const int64_t as = align_up(g.a_elems * (int64_t)sizeof(T), 256) / (int64_t)sizeof(T);
-        T *X = reinterpret_cast<T *>(base);
-        T *XT0 = X + nit * xs;
-        T *XT1 = XT0 + nit * xs;
-        T *A = XT1 + nit * xs;
-        T *B = A + nit * as;
-
-        PrologueArgs pa{};
-        bool need_norm = false;
-        for (int i = 0; i < nit; i++) {
-            const NsRequest &r = req[first + i];
-            pa.it[i] = NsItem{r.src, r.ld, r.dtype, r.rows > r.cols ? 1 : 0, r.inv};
-            need_norm |= r.inv == nullptr;
-        }
-        pa.m = (int32_t)g.m;
-        pa.n = (int32_t)g.n;
-        pa.mp = g.mp;
-        pa.np = g.np;
-        pa.tiles_n = (int32_t)(g.np / 64);
-        pa.tiles_per_item = (int32_t)((g.mp / 64) * (g.np / 64));
-        pa.X = X;
-        pa.XT = XT0;
-        pa.item_stride = xs;
-        pa.inv_ws = inv_ws;
-        if (need_norm) {
-            norm_partial_kernel<<<dim3(kNormChunks, nit), 256, 0, stream>>>(pa, partials);
-            norm_final_kernel<<<nit, 64, 0, stream>>>(partials, eps, inv_ws);
-        }
-        prologue_kernel<T><<<pa.tiles_per_item * nit, 256, 0, stream>>>(pa);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return fail(QM_E_HIP, "prologue: %s", hipGetErrorString(e));
-
-        GemmArgs<T> ga{};
-        for (int i = 0; i < nit; i++) {
-            const NsRequest &r = req[first + i];
-            ga.fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.dtype, r.rows > r.cols ? 1 : 0,
-                                (int32_t)g.m, (int32_t)g.n, r.lr_s, r.lr_wd};
-        }
-        if (steps == 0) {
-            writeback_kernel<T><<<pa.tiles_per_item * nit, 256, 0, stream>>>(X, xs, g.np, pa.tiles_n,
-                                                                              pa.tiles_per_item, ga);
-            e = hipGetLastError();
-            if (e != hipSuccess) return fail(QM_E_HIP, "writeback: %s", hipGetErrorString(e));
-            continue;
-        }
-        const int tm = (int)(g.mp / kBM), tn = (int)(g.np / kBN);
-        const int tri = tm * (tm + 1) / 2;
-        constexpr int kElemsPerKTile = 128 / (int)sizeof(T);
-        T *XTc = XT0, *XTn = XT1;
-        for (int s = 0; s < steps; s++) {
-            // A = X X^T
-            GemmArgs<T> g1 = ga;
-            g1.P = X; g1.ldp = g.np; g1.sp = xs;
-            g1.Q = X; g1.ldq = g.np; g1.sq = xs;
-            g1.C = A; g1.ldc = g.mp; g1.sc = as;
-            g1.tiles_m = tm; g1.tiles_n = tm; g1.tiles_per_item = tri; g1.n_items = nit;
-            g1.k_tiles = (int32_t)(g.np / kElemsPerKTile);
-            qm_status st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_GRAM, true>(g1, tri * nit, stream);
-            if (st != QM_OK) return st;
-            // B = b A + c A A
-            GemmArgs<T> g2 = ga;
-            g2.P = A; g2.ldp = g.mp; g2.sp = as;
-            g2.Q = A; g2.ldq = g.mp; g2.sq = as;
-            g2.C = B; g2.ldc = g.mp; g2.sc = as;
-            g2.D = A; g2.ldd = g.mp; g2.sd = as;
-            g2.tiles_m = tm; g2.tiles_n = tm; g2.tiles_per_item = tri; g2.n_items = nit;
-            g2.k_tiles = (int32_t)(g.mp / kElemsPerKTile);
-            g2.alpha = b; g2.beta = c;
-            st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_POLY, true>(g2, tri * nit, stream);
-            if (st != QM_OK) return st;
-            // X = a X + B X   (Q operand = X^T)
-            GemmArgs<T> g3 = ga;
-            g3.P = B; g3.ldp = g.mp; g3.sp = as;
-            g3.Q = XTc; g3.ldq = g.mp; g3.sq = xs;
-            g3.C = X; g3.ldc = g.np; g3.sc = xs;
-            g3.CT = XTn; g3.ldct = g.mp; g3.sct = xs;
-            g3.D = X; g3.ldd = g.np; g3.sd = xs;
-            g3.tiles_m = tm; g3.tiles_n = tn; g3.tiles_per_item = tm * tn; g3.n_items = nit;
-            g3.k_tiles = (int32_t)(g.mp / kElemsPerKTile);
-            g3.alpha = a;
-            if (s + 1 < steps)
-                st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_UPDATE, false>(g3, tm * tn * nit, stream);
-            else
-                st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_FINAL, false>(g3, tm * tn * nit, stream);
-            if (st != QM_OK) return st;
-            std::swap(XTc, XTn);
-        }
+qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int steps, float a,
+                    float b, float c, float eps, void *ws, hipStream_t stream) {
+    const int nit = (int)chunk.size();
+    std::vector<ItemBufs> bufs(nit);
+    char *p = static_cast<char *>(ws);
+    for (int i = 0; i < nit; i++) {
+        const NsRequest &r = req[chunk[i]];
+        ItemBufs &B = bufs[i];
+        B.g = geometry(r.rows, r.cols, sizeof(T));
+        B.X = p;   p += B.g.x_bytes;
+        B.XT0 = p; p += B.g.x_bytes;
+        B.XT1 = p; p += B.g.x_bytes;
+        B.A = p;   p += B.g.a_bytes;
+        B.B = p;   p += B.g.a_bytes;
     }
+    double *partials = reinterpret_cast<double *>(p);
+    float *inv_ws = reinterpret_cast<float *>(p + align_up(kMaxItems * kNormChunks * 8, 256));
+
+    // ---- prologue: norms (if needed), orientation, padding, X and X^T
+    PrologueArgs pa{};
+    pa.n_items = nit;
+    pa.inv_ws = inv_ws;
+    bool need_norm = false;
+    int tiles = 0;
+    for (int i = 0; i < nit; i++) {
+        const NsRequest &r = req[chunk[i]];
+        const Geometry &g = bufs[i].g;
+        NsItem &it = pa.it[i];
+        it.src = r.src;
+        it.ld = r.ld;
+        it.dtype = r.dtype;
+        it.tall = r.rows > r.cols ? 1 : 0;
+        it.inv = r.inv;
+        it.X = bufs[i].X;
+        it.XT = bufs[i].XT0;
+        it.m = (int32_t)g.m;
+        it.n = (int32_t)g.n;
+        it.mp = g.mp;
+        it.np = g.np;
+        it.tiles_n = (int32_t)(g.np / 64);
+        it.tile_begin = tiles;
+        tiles += (int32_t)((g.mp / 64) * (g.np / 64));
+        need_norm |= r.inv == nullptr;
+    }
+    if (need_norm) {
+        norm_partial_kernel<<<dim3(kNormChunks, nit), 256, 0, stream>>>(pa, partials);
+        norm_final_kernel<<<nit, 64, 0, stream>>>(partials, eps, inv_ws);
+    }
+    prologue_kernel<T><<<tiles, 256, 0, stream>>>(pa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "prologue: %s", hipGetErrorString(e));
+
+    FinalOut fo[kMaxItems];
+    for (int i = 0; i < nit; i++) {
+        const NsRequest &r = req[chunk[i]];
+        fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.dtype, r.rows > r.cols ? 1 : 0,
+                         (int32_t)bufs[i].g.m, (int32_t)bufs[i].g.n, r.lr_s, r.lr_wd};
+    }
+    WritebackArgs wb{};
+    for (int i = 0; i < nit; i++) wb.fo[i] = fo[i];
+
+    // Per-product item order: longest K first (all tiles of a matrix share K).
+    constexpr int64_t kElemsPerKTile = 128 / (int64_t)sizeof(T);
+    std::vector<int> by_n(nit), by_m(nit);
+    std::iota(by_n.begin(), by_n.end(), 0);
+    std::iota(by_m.begin(), by_m.end(), 0);
+    std::stable_sort(by_n.begin(), by_n.end(), [&](int x, int y) { return bufs[x].g.np > bufs[y].g.np; });
+    std::stable_sort(by_m.begin(), by_m.end(), [&](int x, int y) {
+        return bufs[x].g.mp * bufs[x].g.np > bufs[y].g.mp * bufs[y].g.np;
+    });
+    std::vector<int> cur(nit, 0);  // which XT buffer holds X^T for each item
+    for (int s = 0; s < steps; s++) {
+        // A = X X^T
+        GemmArgs<T> g1{};
+        g1.n_items = nit;
+        int tl = 0;
+        for (int k = 0; k < nit; k++) {
+            const ItemBufs &B = bufs[by_n[k]];
+            const int tm = (int)(B.g.mp / kBM);
+            GItem<T> &I = g1.it[k];
+            I.P = reinterpret_cast<const T *>(B.X); I.ldp = B.g.np;
+            I.Q = reinterpret_cast<const T *>(B.X); I.ldq = B.g.np;
+            I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.mp;
+            I.tiles_n = tm;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.np / kElemsPerKTile);
+            tl += tm * (tm + 1) / 2;
+        }
+        qm_status st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_GRAM, true>(g1, tl, stream);
+        if (st != QM_OK) return st;
+        // B = b A + c A A
+        GemmArgs<T> g2{};
+        g2.n_items = nit;
+        g2.alpha = b;
+        g2.beta = c;
+        tl = 0;
+        for (int k = 0; k < nit; k++) {
+            const ItemBufs &B = bufs[by_m[k]];
+            const int tm = (int)(B.g.mp / kBM);
+            GItem<T> &I = g2.it[k];
+            I.P = reinterpret_cast<const T *>(B.A); I.ldp = B.g.mp;
+            I.Q = reinterpret_cast<const T *>(B.A); I.ldq = B.g.mp;
+            I.C = reinterpret_cast<T *>(B.B); I.ldc = B.g.mp;
+            I.D = reinterpret_cast<const T *>(B.A); I.ldd = B.g.mp;
+            I.tiles_n = tm;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.mp / kElemsPerKTile);
+            tl += tm * (tm + 1) / 2;
+        }
+        st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_POLY, true>(g2, tl, stream);
+        if (st != QM_OK) return st;
+        // X = a X + B X   (Q operand = X^T)
+        GemmArgs<T> g3{};
+        g3.n_items = nit;
+        g3.alpha = a;
+        tl = 0;
+        for (int k = 0; k < nit; k++) {
+            const int i = by_m[k];
+            const ItemBufs &B = bufs[i];
+            const int tm = (int)(B.g.mp / kBM), tn = (int)(B.g.np / kBN);
+            GItem<T> &I = g3.it[k];
+            I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.mp;
+            I.Q = reinterpret_cast<const T *>(cur[i] ? B.XT1 : B.XT0); I.ldq = B.g.mp;
+            I.C = reinterpret_cast<T *>(B.X); I.ldc = B.g.np;
+            I.CT = reinterpret_cast<T *>(cur[i] ? B.XT0 : B.XT1); I.ldct = B.g.mp;
+            I.D = reinterpret_cast<const T *>(B.X); I.ldd = B.g.np;
+            I.tiles_n = tn;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.mp / kElemsPerKTile);
+            tl += tm * tn;
+            if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
+        }
+        st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_UPDATE, false>(g3, tl, stream);
+        if (st != QM_OK) return st;
+        for (int i = 0; i < nit; i++) cur[i] ^= 1;
+    }
+    writeback_kernel<T><<<tiles, 256, 0, stream>>>(pa, wb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "writeback: %s", hipGetErrorString(e));
     return QM_OK;
 }
 
 qm_status run_ns(const std::vector<NsRequest> &req, int steps, float a, float b, float c, float eps,
                  int precision, void *ws, hipStream_t stream) {
-    if (precision == QM_NS_F32) return run_ns_typed<float>(req, steps, a, b, c, eps, ws, stream);
-    return run_ns_typed<bf16_t>(req, steps, a, b, c, eps, ws, stream);
+    for (const auto &chunk : make_chunks(req)) {
+        const qm_status st = precision == QM_NS_F32
+                                 ? run_chunk<float>(req, chunk, steps, a, b, c, eps, ws, stream)
+                                 : run_chunk<bf16_t>(req, chunk, steps, a, b, c, eps, ws, stream);
+        if (st != QM_OK) return st;
+    }
+    return QM_OK;
 }
 
 qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld, int32_t steps,
@@ -587,7 +699,7 @@ qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, in
     if (precision != QM_NS_BF16 && precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision %d", precision);
     if (rows <= 0 || cols <= 0) return fail(QM_E_SHAPE, "rows and cols must be positive");
     if (ld < cols) return fail(QM_E_SHAPE, "ld must be >= cols");
-    if (std::min(rows, cols) > (1 << 20) || std::max(rows, cols) > (1 << 24))
+    if (std::min(rows, cols) > (1 << 16) || std::max(rows, cols) > (1 << 22))
         return fail(QM_E_UNSUPPORTED, "matrix too large");
     if (steps < 0 || steps > 100) return fail(QM_E_ARG, "steps must lie in [0, 100]");
     if (!std::isfinite(a) || !std::isfinite(b) || !std::isfinite(c)) return fail(QM_E_ARG, "coefficients must be finite");
@@ -604,7 +716,7 @@ using namespace qm;
 
 extern "C" size_t ns_workspace_bytes(int64_t rows, int64_t cols, int32_t batch, int32_t precision) {
     if (rows <= 0 || cols <= 0 || batch <= 0) return 0;
-    return ns_ws_bytes_for(rows, cols, batch, precision);
+    return ns_ws_bytes_uniform(rows, cols, batch, precision);
 }
 
 extern "C" qm_status ns_orthogonalize(void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -618,7 +730,7 @@ extern "C" qm_status ns_orthogonalize(void *x, int32_t dtype, int64_t rows, int6
     if (batch > 1 && batch_stride < (rows - 1) * ld + cols)
         return fail(QM_E_SHAPE, "batch_stride makes matrices overlap");
     if (inv_norm && !aligned(inv_norm, 4)) return fail(QM_E_ALIGN, "inv_norm misaligned");
-    const size_t need = ns_ws_bytes_for(rows, cols, batch, precision);
+    const size_t need = ns_ws_bytes_uniform(rows, cols, batch, precision);
     if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
     if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
     const size_t esz = dtype == QM_F32 ? 4 : 2;
@@ -635,7 +747,7 @@ extern "C" size_t ns_blocked_workspace_bytes(int64_t rows, int64_t cols, int64_t
                                              int32_t precision) {
     if (rows <= 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0) return 0;
     if (rows % block_rows || cols % block_cols) return 0;
-    return ns_ws_bytes_for(block_rows, block_cols, (rows / block_rows) * (cols / block_cols), precision);
+    return ns_ws_bytes_uniform(block_rows, block_cols, (rows / block_rows) * (cols / block_cols), precision);
 }
 
 extern "C" qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
@@ -649,7 +761,7 @@ extern "C" qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t ro
         return fail(QM_E_SHAPE, "blocks must tile the matrix");
     if (inv_norm && !aligned(inv_norm, 4)) return fail(QM_E_ALIGN, "inv_norm misaligned");
     const int64_t nbr = rows / block_rows, nbc = cols / block_cols;
-    const size_t need = ns_ws_bytes_for(block_rows, block_cols, nbr * nbc, precision);
+    const size_t need = ns_ws_bytes_uniform(block_rows, block_cols, nbr * nbc, precision);
     if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
     if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
     const size_t esz = dtype == QM_F32 ? 4 : 2;
@@ -668,19 +780,11 @@ extern "C" qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t ro
 namespace qm {
 namespace {
 
-struct StepPlan {
-    bool full;
-    const PlanHeader *h;
-    const void *dev;
-};
-
-// The NS work of one step, grouped by (m, n) so same-shaped matrices batch.
-std::vector<std::vector<NsRequest>> step_requests(const PlanHeader *h, const void *host_plan,
-                                                  const qm_muon_matrix *mats, int32_t n, bool full,
-                                                  const float *inv, const qm_muon_hparams *hp) {
+// The NS work of one step: every matrix (full step) or every block.
+std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats,
+                                     int32_t n, bool full, const float *inv, const qm_muon_hparams *hp) {
     const PlanTensor *pt = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(host_plan) + h->off_tensors);
-    std::vector<std::vector<NsRequest>> groups;
-    std::vector<std::pair<int64_t, int64_t>> keys;
+    std::vector<NsRequest> req;
     int64_t g0 = 0;
     for (int32_t i = 0; i < n; i++) {
         const qm_muon_matrix &M = mats[i];
@@ -695,20 +799,13 @@ std::vector<std::vector<NsRequest>> step_requests(const PlanHeader *h, const voi
             for (int64_t bj = 0; bj < nbc; bj++) {
                 const size_t off = (size_t)(bi * br) * (size_t)M.cols + (size_t)(bj * bc);
                 const float *ip = inv ? inv + g0 + bi * nbc + bj : nullptr;
-                NsRequest r{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, ip,
-                            M.weight ? M.weight + off : nullptr, M.cols, lr * s, lr * hp->weight_decay};
-                const std::pair<int64_t, int64_t> key{std::min(br, bc), std::max(br, bc)};
-                size_t k = 0;
-                while (k < keys.size() && keys[k] != key) k++;
-                if (k == keys.size()) {
-                    keys.push_back(key);
-                    groups.emplace_back();
-                }
-                groups[k].push_back(r);
+                req.push_back(NsRequest{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, ip,
+                                        M.weight ? M.weight + off : nullptr, M.cols, lr * s,
+                                        lr * hp->weight_decay});
             }
         g0 += nbr * nbc;
     }
-    return groups;
+    return req;
 }
 
 qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int32_t n, bool full,
@@ -726,6 +823,8 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
         const int64_t br = full ? M.rows : M.block_rows, bc = full ? M.cols : M.block_cols;
         if (br <= 0 || bc <= 0 || M.rows % br || M.cols % bc)
             return fail(QM_E_SHAPE, "matrix %d: blocks do not tile it", i);
+        if (std::min(br, bc) > (1 << 16) || std::max(br, bc) > (1 << 22))
+            return fail(QM_E_UNSUPPORTED, "matrix %d: too large", i);
         const int64_t nb = (M.rows / br) * (M.cols / bc);
         if (pt[i].group_lo != g0 || pt[i].group_hi != g0 + nb - 1)
             return fail(QM_E_PLAN, "matrix %d: plan groups %d..%d, expected %lld..%lld", i, pt[i].group_lo,
@@ -741,10 +840,26 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
 size_t step_ws_bytes(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
                      bool full, int precision) {
     qm_muon_hparams dummy{};
-    const auto groups = step_requests(h, host_plan, mats, n, full, nullptr, &dummy);
-    size_t ns = 0;
-    for (const auto &g : groups) ns = std::max(ns, ns_ws_bytes_for(g[0].rows, g[0].cols, (int64_t)g.size(), precision));
-    return align_up(qm_update_workspace_bytes(host_plan), 256) + ns;
+    const auto req = step_requests(h, host_plan, mats, n, full, nullptr, &dummy);
+    return align_up(qm_update_workspace_bytes(host_plan), 256) + ns_ws_bytes_req(req, precision);
+}
+
+qm_status check_hparams(const qm_muon_hparams *hp) {
+    if (!hp) return fail(QM_E_ARG, "hparams is null");
+    if (hp->precision != QM_NS_BF16 && hp->precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision");
+    if (hp->ns_steps < 0 || hp->ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
+    if (!std::isfinite(hp->lr_full) || !std::isfinite(hp->lr_block) || !std::isfinite(hp->weight_decay) ||
+        !std::isfinite(hp->rms_scale) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
+        return fail(QM_E_ARG, "hyperparameters must be finite");
+    if (!(hp->eps >= 0.0f) || std::isinf(hp->eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    return QM_OK;
+}
+
+// NS + weight apply of every matrix (full) or block, NS workspace at ns_ws.
+qm_status apply_phase(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
+                      bool full, const float *inv, const qm_muon_hparams *hp, void *ns_ws, hipStream_t s) {
+    const auto req = step_requests(h, host_plan, mats, n, full, inv, hp);
+    return run_ns(req, hp->ns_steps, hp->a, hp->b, hp->c, hp->eps, hp->precision, ns_ws, s);
 }
 
 }  // namespace
@@ -763,34 +878,6 @@ extern "C" size_t muon_step_workspace_bytes(const void *host_plan_full, const vo
     }
     return need;
 }
-
-namespace qm {
-namespace {
-
-qm_status check_hparams(const qm_muon_hparams *hp) {
-    if (!hp) return fail(QM_E_ARG, "hparams is null");
-    if (hp->precision != QM_NS_BF16 && hp->precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision");
-    if (hp->ns_steps < 0 || hp->ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
-    if (!std::isfinite(hp->lr_full) || !std::isfinite(hp->lr_block) || !std::isfinite(hp->weight_decay) ||
-        !std::isfinite(hp->rms_scale) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
-        return fail(QM_E_ARG, "hyperparameters must be finite");
-    if (!(hp->eps >= 0.0f) || std::isinf(hp->eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
-    return QM_OK;
-}
-
-// NS + weight apply of every matrix (full) or block, NS workspace at ns_ws.
-qm_status apply_phase(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
-                      bool full, const float *inv, const qm_muon_hparams *hp, void *ns_ws, hipStream_t s) {
-    const auto groups = step_requests(h, host_plan, mats, n, full, inv, hp);
-    for (const auto &g : groups) {
-        const qm_status st = run_ns(g, hp->ns_steps, hp->a, hp->b, hp->c, hp->eps, hp->precision, ns_ws, s);
-        if (st != QM_OK) return st;
-    }
-    return QM_OK;
-}
-
-}  // namespace
-}  // namespace qm
 
 extern "C" qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mats, int32_t n_mats, int32_t full,
                                 const float *inv_norm, const qm_muon_hparams *hp, void *ws, size_t ws_bytes,

@@ -50,10 +50,10 @@ const PlanHeader *plan_header(const void *host_blob, qm_status *st) {
 namespace {
 
 struct Layout {
-    int64_t off_tensors, off_task, off_bg, off_ro, off_runs, total;
+    int64_t off_tensors, off_task, off_bg, off_ro, off_runs, off_co, off_cg, total;
 };
 
-Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr) {
+Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr, int64_t nc) {
     Layout L;
     int64_t o = align_up(sizeof(PlanHeader), 64);
     L.off_tensors = o;  o = align_up(o + (int64_t)nt * sizeof(PlanTensor), 64);
@@ -61,6 +61,8 @@ Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr) {
     L.off_bg = o;       o = align_up(o + nb * 4, 64);
     L.off_ro = o;       o = align_up(o + (int64_t)(ng + 1) * 8, 64);
     L.off_runs = o;     o = align_up(o + nr * (int64_t)sizeof(PlanRun), 64);
+    L.off_co = o;       o = align_up(o + (int64_t)(ng + 1) * 8, 64);
+    L.off_cg = o;       o = align_up(o + nc * 4, 64);
     L.total = o;
     return L;
 }
@@ -147,12 +149,15 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
         else
             v.push_back(PlanRun{b, 1, 0});
     }
-    int64_t n_runs = 0;
-    for (auto &v : gruns) n_runs += (int64_t)v.size();
+    int64_t n_runs = 0, n_chunks = 0;
+    for (auto &v : gruns) {
+        n_runs += (int64_t)v.size();
+        n_chunks += ((int64_t)v.size() + kChunkRuns - 1) / kChunkRuns;
+    }
     for (int32_t g = 0; g < n_groups; g++)
         if (gruns[g].empty()) return fail(QM_E_SHAPE, "group %d has no blocks", g);
 
-    const Layout L = layout_for(n_tensors, n_groups, nb_total, n_runs);
+    const Layout L = layout_for(n_tensors, n_groups, nb_total, n_runs, n_chunks);
     if (!host_blob) {
         *inout_blob_bytes = (size_t)L.total;
         return QM_OK;
@@ -169,6 +174,8 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     int32_t *pbg = reinterpret_cast<int32_t *>(base + L.off_bg);
     int64_t *ro = reinterpret_cast<int64_t *>(base + L.off_ro);
     PlanRun *runs = reinterpret_cast<PlanRun *>(base + L.off_runs);
+    int64_t *co = reinterpret_cast<int64_t *>(base + L.off_co);
+    int32_t *cg = reinterpret_cast<int32_t *>(base + L.off_cg);
 
     int64_t toff = 0;
     for (int32_t i = 0; i < n_tensors; i++) {
@@ -193,12 +200,16 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     }
     task[n_tensors] = toff;
     memcpy(pbg, bg.data(), (size_t)nb_total * 4);
-    int64_t r = 0;
+    int64_t r = 0, c = 0;
     for (int32_t g = 0; g < n_groups; g++) {
         ro[g] = r;
+        co[g] = c;
         for (const PlanRun &x : gruns[g]) runs[r++] = x;
+        const int64_t nch = ((int64_t)gruns[g].size() + kChunkRuns - 1) / kChunkRuns;
+        for (int64_t k = 0; k < nch; k++) cg[c++] = g;
     }
     ro[n_groups] = r;
+    co[n_groups] = c;
 
     h->magic = kPlanMagic;
     h->version = kPlanVersion;
@@ -207,12 +218,15 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     h->n_blocks = nb_total;
     h->n_tasks = toff;
     h->n_runs = n_runs;
+    h->n_chunks = n_chunks;
     h->total_numel = total_numel;
     h->off_tensors = L.off_tensors;
     h->off_task_offsets = L.off_task;
     h->off_block_group = L.off_bg;
     h->off_run_offsets = L.off_ro;
     h->off_runs = L.off_runs;
+    h->off_chunk_offsets = L.off_co;
+    h->off_chunk_group = L.off_cg;
     h->total_bytes = L.total;
     *inout_blob_bytes = (size_t)L.total;
     return QM_OK;
@@ -231,14 +245,14 @@ extern "C" qm_status qm_plan_info(const void *host_blob, int32_t *n_tensors, int
     return QM_OK;
 }
 
-// Workspace of the grouped update: per-block fp64 sums, then fp64 group sums,
-// then fp32 inverse norms, each section 256-byte aligned.
+// Workspace of the grouped update: per-block fp64 sums, fp64 chunk partials,
+// fp64 group sums, fp32 inverse norms, each section 256-byte aligned.
 extern "C" size_t qm_update_workspace_bytes(const void *host_blob) {
     qm_status st;
     const PlanHeader *h = plan_header(host_blob, &st);
     if (!h) return 0;
-    return (size_t)(align_up(h->n_blocks * 8, 256) + align_up((int64_t)h->n_groups * 8, 256) +
-                    align_up((int64_t)h->n_groups * 4, 256));
+    return (size_t)(align_up(h->n_blocks * 8, 256) + align_up(h->n_chunks * 8, 256) +
+                    align_up((int64_t)h->n_groups * 8, 256) + align_up((int64_t)h->n_groups * 4, 256));
 }
 
 extern "C" const char *qm_status_string(qm_status s) {

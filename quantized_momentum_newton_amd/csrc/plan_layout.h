@@ -7,28 +7,34 @@
 // per-call metadata copy) and the work decomposition of the kernels:
 //   task  = up to 4 consecutive blocks of one tensor, processed by one wave64;
 //   run   = up to kRunMax consecutive blocks of one group, summed by one lane
-//           in the group reduction.
+//           in the group reduction;
+//   chunk = up to kChunkRuns runs of one group, reduced by one workgroup to
+//           one partial; a group's sum adds its chunks' partials in order.
 #pragma once
 #include <stdint.h>
 
 namespace qm {
 
 constexpr uint32_t kPlanMagic = 0x4e4c5051u;  // "QPLN"
-constexpr uint32_t kPlanVersion = 1;
+constexpr uint32_t kPlanVersion = 2;
 constexpr int kBlock = 256;
 constexpr int kBlocksPerTask = 4;
 constexpr int kTaskElems = kBlock * kBlocksPerTask;  // 1024
-constexpr int kRunMax = 64;
+constexpr int kRunMax = 16;
+constexpr int kChunkRuns = 256;
 
 struct PlanHeader {
     uint32_t magic, version;
     int32_t n_tensors, n_groups;
     int64_t n_blocks, n_tasks, n_runs, total_numel;
+    int64_t n_chunks;
     int64_t off_tensors;       // PlanTensor[n_tensors]
     int64_t off_task_offsets;  // int64[n_tensors + 1]
     int64_t off_block_group;   // int32[n_blocks]
     int64_t off_run_offsets;   // int64[n_groups + 1]
     int64_t off_runs;          // PlanRun[n_runs]
+    int64_t off_chunk_offsets; // int64[n_groups + 1]
+    int64_t off_chunk_group;   // int32[n_chunks]
     int64_t total_bytes;
 };
 
@@ -48,10 +54,11 @@ struct PlanRun {
     int32_t pad;
 };
 
-static_assert(sizeof(PlanHeader) == 96, "plan header layout");
+static_assert(sizeof(PlanHeader) == 120, "plan header layout");
 static_assert(sizeof(PlanTensor) == 64, "plan tensor layout");
 static_assert(sizeof(PlanRun) == 16, "plan run layout");
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+constexpr int64_t align_up_const(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace qm

@@ -9,6 +9,7 @@ namespace qm {
 
 struct UpdateWorkspace {
     double *block_sums;  // [n_blocks]
+    double *partials;    // [n_chunks]
     double *group_sums;  // [n_groups]
     float *inv;          // [n_groups]
     size_t bytes;

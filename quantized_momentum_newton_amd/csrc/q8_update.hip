@@ -265,19 +265,23 @@ __global__ __launch_bounds__(kThreads) void q8_update_kernel(const PlanTensor *_
 }
 
 // ------------------------------------------------- K2: group sums, inverse norms
-// One workgroup per group; lane k sums runs k, k+256, ... (each a short
-// ascending range of blocks), then a fixed butterfly + fixed-order wave
-// combine: the result depends only on the plan, never on scheduling.
+// K2a: one workgroup per chunk (<= 256 runs of one group, each <= 16 blocks):
+// lane k sums run k of the chunk in block order, then a fixed butterfly and a
+// fixed-order combine of the four waves.  K2b: per group, the chunk partials
+// are added in chunk order.  Results depend only on the plan, never on
+// scheduling, and no atomics are used.
 
-__global__ __launch_bounds__(kThreads) void group_reduce_kernel(const int64_t *__restrict__ run_offsets,
+__global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *__restrict__ run_offsets,
                                                                 const PlanRun *__restrict__ runs,
+                                                                const int64_t *__restrict__ chunk_offsets,
+                                                                const int32_t *__restrict__ chunk_group,
                                                                 const double *__restrict__ block_sums,
-                                                                float eps, double *__restrict__ group_sums,
-                                                                float *__restrict__ inv_norm) {
-    const int g = blockIdx.x;
-    const int64_t r0 = run_offsets[g], r1 = run_offsets[g + 1];
+                                                                double *__restrict__ partials) {
+    const int64_t c = blockIdx.x;
+    const int g = chunk_group[c];
+    const int64_t r = run_offsets[g] + (c - chunk_offsets[g]) * kChunkRuns + threadIdx.x;
     double acc = 0.0;
-    for (int64_t r = r0 + threadIdx.x; r < r1; r += kThreads) {
+    if (r < run_offsets[g + 1]) {
         const PlanRun R = runs[r];
         for (int k = 0; k < R.count; k++) acc += block_sums[R.start_block + k];
     }
@@ -289,9 +293,20 @@ __global__ __launch_bounds__(kThreads) void group_reduce_kernel(const int64_t *_
     if (threadIdx.x == 0) {
         double S = part[0];
         for (int w = 1; w < kWavesPerWG; w++) S += part[w];
-        if (group_sums) group_sums[g] = S;
-        inv_norm[g] = (float)(1.0 / (sqrt(S) + (double)eps));
+        partials[c] = S;
     }
+}
+
+__global__ __launch_bounds__(kThreads) void group_final_kernel(const int64_t *__restrict__ chunk_offsets,
+                                                               const double *__restrict__ partials, int n_groups,
+                                                               float eps, double *__restrict__ group_sums,
+                                                               float *__restrict__ inv_norm) {
+    const int g = blockIdx.x * kThreads + threadIdx.x;
+    if (g >= n_groups) return;
+    double S = 0.0;
+    for (int64_t c = chunk_offsets[g]; c < chunk_offsets[g + 1]; c++) S += partials[c];
+    if (group_sums) group_sums[g] = S;
+    inv_norm[g] = (float)(1.0 / (sqrt(S) + (double)eps));
 }
 
 // ------------------------------------------------------------ K3: scale pass
@@ -391,10 +406,16 @@ qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, d
 }
 
 qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const double *block_sums,
-                              float eps, double *group_sums, float *inv, hipStream_t stream) {
-    group_reduce_kernel<<<h->n_groups, kThreads, 0, stream>>>(
-        section<int64_t>(dev_plan, h->off_run_offsets), section<PlanRun>(dev_plan, h->off_runs),
-        block_sums, eps, group_sums, inv);
+                              double *partials, float eps, double *group_sums, float *inv, hipStream_t stream) {
+    const int64_t *ro = section<int64_t>(dev_plan, h->off_run_offsets);
+    const int64_t *co = section<int64_t>(dev_plan, h->off_chunk_offsets);
+    chunk_reduce_kernel<<<(unsigned)h->n_chunks, kThreads, 0, stream>>>(
+        ro, section<PlanRun>(dev_plan, h->off_runs), co, section<int32_t>(dev_plan, h->off_chunk_group),
+        block_sums, partials);
+    qm_status st = check_launch("chunk reduce");
+    if (st != QM_OK) return st;
+    group_final_kernel<<<(h->n_groups + kThreads - 1) / kThreads, kThreads, 0, stream>>>(co, partials, h->n_groups,
+                                                                                       eps, group_sums, inv);
     return check_launch("group reduce");
 }
 
@@ -410,6 +431,8 @@ UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
     char *p = static_cast<char *>(ws);
     w.block_sums = reinterpret_cast<double *>(p);
     p += align_up(h->n_blocks * 8, 256);
+    w.partials = reinterpret_cast<double *>(p);
+    p += align_up(h->n_chunks * 8, 256);
     w.group_sums = reinterpret_cast<double *>(p);
     p += align_up((int64_t)h->n_groups * 8, 256);
     w.inv = reinterpret_cast<float *>(p);
@@ -426,7 +449,7 @@ qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float 
     double *sums = sums_out ? sums_out : w.group_sums;
     qm_status st = launch_update(h, dev_plan, beta, w.block_sums, stream);
     if (st != QM_OK) return st;
-    st = launch_group_reduce(h, dev_plan, w.block_sums, eps, sums, inv, stream);
+    st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
     if (st != QM_OK) return st;
     if (write_normalized) st = launch_scale(h, dev_plan, inv, stream);
     return st;
