@@ -248,6 +248,53 @@ QM_API qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mats,
                             const float *inv_norm, const qm_muon_hparams *hp,
                             void *ws, size_t ws_bytes, qm_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * GRASP 4-bit momentum ("4-bit-Muon-GRASP")
+ *
+ * The momentum of one rows x cols matrix is a rank-k factor P R^T (P rows x
+ * k, R cols x k, 8-bit) plus a residual (4-bit), all grid-quantised over
+ * 64 x 64 blocks (clipped at the edges): an entry is divided by the smaller
+ * of its row's and its column's absolute maximum inside its block, and coded
+ * as clamp(rint((x / d) * L), -L, L), L = 7 (4-bit) or 127 (8-bit), d = 0
+ * giving code 0; it dequantises to code * (d / L).  The state starts as all
+ * zeros.  Layout (all caller-owned device buffers):
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    uint8_t *res_codes;  /* [rows][ceil(cols/2)]: two 4-bit two's-complement
+                            codes per byte, even column in the low nibble   */
+    float *res_rmax;     /* [rows][ceil(cols/64)] row maxima per block      */
+    float *res_cmax;     /* [ceil(rows/64)][cols] column maxima per block   */
+    int8_t *p_codes;     /* [rows][k]                                       */
+    float *p_rmax;       /* [rows]                                          */
+    float *p_cmax;       /* [ceil(rows/64)][k]                              */
+    int8_t *r_codes;     /* [cols][k]                                       */
+    float *r_rmax;       /* [cols]                                          */
+    float *r_cmax;       /* [ceil(cols/64)][k]                              */
+} qm_grasp_state;
+
+QM_API size_t grasp_workspace_bytes(int64_t rows, int64_t cols, int32_t rank);
+
+/* One GRASP step (the page's update equations):
+ *   M_{t-1} = deq(res) + deq(P) deq(R)^T;   M_t = mu M_{t-1} + g (no (1-mu))
+ *   Q = R_{t-1} with unit columns (a zero column is replaced by the same
+ *   column of `warm`, cols x k fp32, normalised);  P = MGS(M_t Q) (modified
+ *   Gram-Schmidt, positive diagonal);  R = M_t^T P;  residual M_t - P R^T;
+ *   requantise residual, P, R;  O = NS_T(M_t) in f32 arithmetic, written
+ *   over grad in its dtype;  W <- W - lr (O + weight_decay W) if weight.
+ * Reductions accumulate in fp64 in a fixed order; P, R are rounded to fp32
+ * before the residual.  rank in {1, 2, 4, 8, 16}; grid must be 64.
+ *   grad: in g, out O (rows x cols contiguous, dtype grad_dtype).
+ *   ws: >= grasp_workspace_bytes(rows, cols, rank), 256-byte aligned.
+ * Errors: QM_E_ARG, QM_E_SHAPE, QM_E_DTYPE, QM_E_ALIGN, QM_E_UNSUPPORTED,
+ * QM_E_WORKSPACE, QM_E_HIP. */
+QM_API qm_status grasp_step(const qm_grasp_state *state, int64_t rows,
+                            int64_t cols, int32_t rank, int32_t grid,
+                            void *grad, int32_t grad_dtype, const float *warm,
+                            float mu, int32_t ns_steps, float a, float b,
+                            float c, float eps, float *weight, float lr,
+                            float weight_decay, void *ws, size_t ws_bytes,
+                            qm_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 QM_API const char *qm_status_string(qm_status s);
 QM_API const char *qm_last_error(void);

@@ -179,9 +179,10 @@ class State:
         return _rank_k_sum(resd, Pd, Rd, +1), Rd
 
 
-def grasp_step(state, g, mu, warm, ns_steps=5, coeffs=ns.QUINTIC, eps=ns.EPS):
+def grasp_step(state, g, mu, warm, ns_steps=5, coeffs=ns.QUINTIC, eps=ns.EPS, with_ns=True):
     """One GRASP step.  Returns (new_state, M_t fp32, P fp32, R fp32, O fp64);
-    the input state is not modified."""
+    the input state is not modified.  with_ns=False skips O (returns None),
+    for callers that check NS separately."""
     s = state.s
     Mprev, Rd = state.momentum()
     t = (np.float32(mu) * Mprev).astype(np.float32)
@@ -197,8 +198,13 @@ def grasp_step(state, g, mu, warm, ns_steps=5, coeffs=ns.QUINTIC, eps=ns.EPS):
     new.res, new.res_rmax, new.res_cmax = grid_quantize(res, 4, s)
     new.p, new.p_rmax, new.p_cmax = grid_quantize(P32, 8, s)
     new.r, new.r_rmax, new.r_cmax = grid_quantize(R32, 8, s)
-    O = ns.ns_orthogonalize(M64, ns_steps, coeffs, eps)
+    O = ns.ns_orthogonalize(M64, ns_steps, coeffs, eps) if with_ns else None
     return new, M, P32, R32, O
+
+
+def residual(M, P32, R32):
+    """The fp32 residual M - P R^T the step quantises."""
+    return _rank_k_sum(M, P32, R32, -1)
 
 
 def apply_weights(W, O, lr, weight_decay=0.0):

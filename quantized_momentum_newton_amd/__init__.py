@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/qmuon.h):
   ns_orthogonalize_blocked         blockwise Newton-Schulz
   muon_step                        update + NS + weight apply, block-periodic
   muon_apply                       the NS + weight-apply half of muon_step
+  GraspState, grasp_step           the GRASP 4-bit momentum variant
 """
 import ctypes
 
@@ -214,3 +215,49 @@ def muon_apply(plan, mats, full, inv_norm, hparams, ws, stream=None):
     arr = _matrices(mats)
     _check(_LIB.muon_apply(plan.hptr, arr, len(mats), int(full), _ptr(inv_norm),
                            ctypes.byref(hparams), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+GRASP_GRID = 64
+
+
+class GraspState:
+    """Zero-initialised GRASP state buffers of one rows x cols matrix (the
+    layout of qm_grasp_state)."""
+
+    def __init__(self, rows, cols, rank, device="cuda"):
+        nbr, nbc = -(-rows // GRASP_GRID), -(-cols // GRASP_GRID)
+        z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+        self.rows, self.cols, self.rank = rows, cols, rank
+        self.res_codes = z((rows, (cols + 1) // 2), torch.uint8)
+        self.res_rmax = z((rows, nbc), torch.float32)
+        self.res_cmax = z((nbr, cols), torch.float32)
+        self.p_codes = z((rows, rank), torch.int8)
+        self.p_rmax = z((rows,), torch.float32)
+        self.p_cmax = z((nbr, rank), torch.float32)
+        self.r_codes = z((cols, rank), torch.int8)
+        self.r_rmax = z((cols,), torch.float32)
+        self.r_cmax = z((nbc, rank), torch.float32)
+
+    def c_struct(self):
+        return L.GraspStateC(*(t.data_ptr() for t in (
+            self.res_codes, self.res_rmax, self.res_cmax, self.p_codes, self.p_rmax, self.p_cmax,
+            self.r_codes, self.r_rmax, self.r_cmax)))
+
+
+def grasp_workspace_bytes(rows, cols, rank):
+    return _LIB.grasp_workspace_bytes(rows, cols, rank)
+
+
+def grasp_step(state, grad, warm, mu=0.95, ns_steps=5, coeffs=QUINTIC, eps=1e-7, weight=None,
+               lr=0.02, weight_decay=0.0, ws=None, stream=None):
+    """One GRASP step: state updated in place, grad (in: g) overwritten with
+    O = NS(M_t), weight (optional) updated."""
+    rows, cols = grad.shape
+    if ws is None:
+        ws = torch.empty(_LIB.grasp_workspace_bytes(rows, cols, state.rank), dtype=torch.uint8,
+                         device=grad.device)
+    a, b, c = coeffs
+    st = state.c_struct()
+    _check(_LIB.grasp_step(ctypes.byref(st), rows, cols, state.rank, GRASP_GRID, _ptr(grad),
+                           _dtype(grad), _ptr(warm), mu, ns_steps, a, b, c, eps, _ptr(weight), lr,
+                           weight_decay, _ptr(ws), ws.numel(), _stream(stream)))

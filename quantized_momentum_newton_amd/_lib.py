@@ -44,6 +44,12 @@ class MuonMatrix(ctypes.Structure):
                 ("block_cols", c_i64), ("weight", c_void_p)]
 
 
+class GraspStateC(ctypes.Structure):
+    _fields_ = [("res_codes", c_void_p), ("res_rmax", c_void_p), ("res_cmax", c_void_p),
+                ("p_codes", c_void_p), ("p_rmax", c_void_p), ("p_cmax", c_void_p),
+                ("r_codes", c_void_p), ("r_rmax", c_void_p), ("r_cmax", c_void_p)]
+
+
 # name -> (restype, argtypes); every symbol include/qmuon.h declares.
 SIGNATURES = {
     "qm_plan_encode": (c_i32, [ctypes.POINTER(Q8Tensor), c_i32, ctypes.POINTER(NormSegment),
@@ -69,6 +75,10 @@ SIGNATURES = {
                           c_void_p]),
     "muon_apply": (c_i32, [c_void_p, ctypes.POINTER(MuonMatrix), c_i32, c_i32, c_void_p,
                            ctypes.POINTER(MuonHparams), c_void_p, c_size, c_void_p]),
+    "grasp_workspace_bytes": (c_size, [c_i64, c_i64, c_i32]),
+    "grasp_step": (c_i32, [ctypes.POINTER(GraspStateC), c_i64, c_i64, c_i32, c_i32, c_void_p, c_i32,
+                           c_void_p, c_f32, c_i32, c_f32, c_f32, c_f32, c_f32, c_void_p, c_f32, c_f32,
+                           c_void_p, c_size, c_void_p]),
     "qm_status_string": (ctypes.c_char_p, [c_i32]),
     "qm_last_error": (ctypes.c_char_p, []),
     "qm_abi_version": (ctypes.c_int, []),

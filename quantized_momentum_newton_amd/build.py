@@ -26,6 +26,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 UNITS = [
     ("q8_update.hip", ["-ffp-contract=off"]),
     ("ns.hip", []),
+    ("grasp.hip", ["-ffp-contract=off"]),
     ("plan.cpp", []),
 ]
 

@@ -375,7 +375,6 @@ using namespace qm;
 extern "C" size_t grasp_workspace_bytes(int64_t rows, int64_t cols, int32_t rank) {
     if (rows <= 0 || cols <= 0 || rank <= 0 || rank > 16) return 0;
     const Dims d = dims(rows, cols, rank);
-    std::vector<char> dummy;
     const Ws w = carve(d, nullptr);
     return w.bytes + ns_f32_workspace_bytes(rows, cols);
 }

@@ -38,6 +38,7 @@
 #include <numeric>
 #include <vector>
 
+#include "grasp_internal.h"
 #include "internal.h"
 #include "plan_layout.h"
 #include "q8_internal.h"
@@ -450,7 +451,8 @@ struct NsRequest {
     const void *src;      // matrix start
     void *out;            // where the result goes (== src for in place)
     int64_t rows, cols, ld;
-    int32_t dtype;
+    int32_t dtype;        // of src
+    int32_t out_dtype;    // of out
     const float *inv;     // nullable device scale
     float *w;             // nullable fp32 weights (rows x cols, ldw)
     int64_t ldw;
@@ -594,7 +596,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     FinalOut fo[kMaxItems];
     for (int i = 0; i < nit; i++) {
         const NsRequest &r = req[chunk[i]];
-        fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.dtype, r.rows > r.cols ? 1 : 0,
+        fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.out_dtype, r.rows > r.cols ? 1 : 0,
                          (int32_t)bufs[i].g.m, (int32_t)bufs[i].g.n, r.lr_s, r.lr_wd};
     }
     WritebackArgs wb{};
@@ -710,6 +712,16 @@ qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, in
 }
 
 }  // namespace
+
+size_t ns_f32_workspace_bytes(int64_t rows, int64_t cols) { return ns_ws_bytes_uniform(rows, cols, 1, QM_NS_F32); }
+
+qm_status run_ns_f32_into(const float *M, int64_t rows, int64_t cols, void *out, int32_t out_dtype, float *w,
+                          float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, void *ws,
+                          hipStream_t stream) {
+    std::vector<NsRequest> req{NsRequest{M, out, rows, cols, cols, QM_F32, out_dtype, nullptr, w, cols, lr_s, lr_wd}};
+    return run_ns(req, steps, a, b, c, eps, QM_NS_F32, ws, stream);
+}
+
 }  // namespace qm
 
 using namespace qm;
@@ -737,7 +749,7 @@ extern "C" qm_status ns_orthogonalize(void *x, int32_t dtype, int64_t rows, int6
     std::vector<NsRequest> req;
     for (int32_t i = 0; i < batch; i++) {
         char *p = static_cast<char *>(x) + (size_t)i * (size_t)batch_stride * esz;
-        req.push_back(NsRequest{p, p, rows, cols, ld, dtype, inv_norm ? inv_norm + i : nullptr, nullptr, 0,
+        req.push_back(NsRequest{p, p, rows, cols, ld, dtype, dtype, inv_norm ? inv_norm + i : nullptr, nullptr, 0,
                                 0.0f, 0.0f});
     }
     return run_ns(req, steps, a, b, c, eps, precision, ws, static_cast<hipStream_t>(stream));
@@ -770,7 +782,7 @@ extern "C" qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t ro
         for (int64_t bj = 0; bj < nbc; bj++) {
             char *p = static_cast<char *>(x) + ((size_t)(bi * block_rows) * (size_t)ld + (size_t)(bj * block_cols)) * esz;
             const float *inv = inv_norm ? inv_norm + bi * nbc + bj : nullptr;
-            req.push_back(NsRequest{p, p, block_rows, block_cols, ld, dtype, inv, nullptr, 0, 0.0f, 0.0f});
+            req.push_back(NsRequest{p, p, block_rows, block_cols, ld, dtype, dtype, inv, nullptr, 0, 0.0f, 0.0f});
         }
     return run_ns(req, steps, a, b, c, eps, precision, ws, static_cast<hipStream_t>(stream));
 }
@@ -799,7 +811,7 @@ std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan,
             for (int64_t bj = 0; bj < nbc; bj++) {
                 const size_t off = (size_t)(bi * br) * (size_t)M.cols + (size_t)(bj * bc);
                 const float *ip = inv ? inv + g0 + bi * nbc + bj : nullptr;
-                req.push_back(NsRequest{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, ip,
+                req.push_back(NsRequest{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, dt, ip,
                                         M.weight ? M.weight + off : nullptr, M.cols, lr * s,
                                         lr * hp->weight_decay});
             }
