@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "layerset28", "muonbp"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ref-copy-mib", type=int, default=0,
+                    help="after the timed region, copy a buffer of this many MiB once (a kernel of "
+                         "known traffic, to calibrate HBM byte counters in a profiler run)")
     return ap.parse_args()
 
 
@@ -179,6 +182,12 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    if args.ref_copy_mib > 0:
+        src = torch.empty(args.ref_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     upd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     ns_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms_per_step = total_ms / args.steps
