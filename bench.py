@@ -9,20 +9,25 @@ group norms (qmuon_update_normalize_groups), then quintic Newton-Schulz
 product (muon_apply).  muon_step is exactly these two calls; they are issued
 separately here so HIP events on the launch stream time each phase live.
 
-Printed: one JSON line.  value = q8 update GB/s (algorithmic bytes: int8
-codes read+write, bf16 grad read+write, fp32 absmax read+write per 256
-elements = 6.03125 B/element); ns_tflops = NS TFLOP/s (algorithmic FLOPs with
-the two symmetric products at lower-triangle cost); `roofline` is for the
-dominant kernel (the NS products, MFMA bound), `roofline_update` for the HBM-
-bound update kernel; `cpu_baseline` times the CPU oracle on a bounded sample.
+Printed: one JSON line.  value = q8 update GB/s over the whole update +
+group-norm call (algorithmic bytes: int8 codes read+write, bf16 grad
+read+write, fp32 absmax read+write per 256 elements = 6.03125 B/element);
+ns_tflops = NS TFLOP/s over the whole muon_apply call (algorithmic FLOPs, the
+two symmetric products at lower-triangle cost).  `roofline` is for the
+dominant kernel (the one with the largest share of device time, measured live
+per launch with the library's event timer over the timed steps: the
+X <- aX + BX product, MFMA bound); `roofline_update` for the HBM-bound q8
+update kernel.  `traffic` is filled from the committed counter summary only
+while the kernel source still has the hash recorded there.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
 
 Other workloads (not the headline): --workload layerset28 (the 28-layer
 2048-hidden set, grouped update + normalisation only), --workload muonbp
 (4096x14336, 8 column blocks, P = 5).
 """
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -56,9 +61,61 @@ def ns_sym_flops(rows, cols, steps):
     return steps * (n * m * (m + 1) + m * m * (m + 1) + 2 * m * m * n)
 
 
+# Algorithmic work of one launch of each timed kernel class over a set of
+# matrices (rows, cols): FLOPs for the products, bytes for memory kernels.
+def launch_work(tensors, numel):
+    mn = [(min(r, c), max(r, c)) for _, r, c in tensors]
+    return {
+        "ns_gram": ("mfma", sum(m * (m + 1) * n for m, n in mn)),
+        "ns_poly": ("mfma", sum(m * m * (m + 1) for m, n in mn)),
+        "ns_xupdate": ("mfma", sum(2 * m * m * n for m, n in mn)),
+        "q8_update": ("hbm", numel * BYTES_PER_ELEM_UPDATE),
+        "ns_prologue": ("hbm", numel * 6.0),     # bf16 in, bf16 X and X^T out
+        "ns_writeback": ("hbm", numel * 12.0),   # bf16 X in, bf16 out, fp32 W read + write
+    }
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "quantized_momentum_newton_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, per kernel
+    class, kept only while the kernel's source hash matches the one recorded."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return {}
+    rec = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1])
+    if not rec:
+        return {}
+    out = {}
+    for cls, v in rec.get("per_launch_bytes", {}).items():
+        src = rec.get("sources", {}).get(cls)
+        if src and source_hash(src["file"]) == src["sha256_16"]:
+            out[cls] = v
+    return out
+
+
+def roofline(kind, work, ms_per_launch, traffic):
+    if kind == "mfma":
+        achieved = work / (ms_per_launch * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    achieved = work / (ms_per_launch * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
 def cpu_baseline(host_q, host_ns, steps):
-    """The oracle as it stands, on a bounded sample of the same workload."""
-    import numpy as np
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    q8 update of every tensor of the layer (C oracle) and fp64 NS of the
+    given matrices (numpy oracle)."""
     import oracle
     from oracle import ns
     try:
@@ -66,28 +123,27 @@ def cpu_baseline(host_q, host_ns, steps):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         blas_threads = os.cpu_count()
-    codes, absmax, grad = host_q
+    numel = 0
     t0 = time.perf_counter()
-    reps = 0
-    while True:
+    for codes, absmax, grad in host_q:
         oracle.q8_update(codes, absmax, grad, 0.95, oracle.BF16)
-        reps += 1
-        if time.perf_counter() - t0 > 5.0 or reps >= 20:
-            break
-    t_q = (time.perf_counter() - t0) / reps
-    gbs = codes.size * BYTES_PER_ELEM_UPDATE / t_q / 1e9
-    x = host_ns
-    t0 = time.perf_counter()
-    ns.ns_orthogonalize(x, steps)
-    t_ns = time.perf_counter() - t0
-    fl = ns_sym_flops(x.shape[0], x.shape[1], steps)
+        numel += codes.size
+    t_q = time.perf_counter() - t0
+    gbs = numel * BYTES_PER_ELEM_UPDATE / t_q / 1e9
+    fl, t_ns = 0, 0.0
+    for x in host_ns:
+        t0 = time.perf_counter()
+        ns.ns_orthogonalize(x, steps)
+        t_ns += time.perf_counter() - t0
+        fl += ns_sym_flops(x.shape[0], x.shape[1], steps)
+    shapes = " + ".join(f"{x.shape[0]}x{x.shape[1]}" for x in host_ns)
     return {
         "value": round(gbs, 3), "unit": "GB/s", "cores": max(oracle.num_threads(), blas_threads),
         "kind": "oracle",
-        "sample": (f"q8 update of one {codes.size}-element bf16 tensor (C oracle, {reps} reps) + "
-                   f"fp64 NS T={steps} of one {x.shape[0]}x{x.shape[1]} matrix (numpy oracle)"),
+        "sample": (f"q8 update of all {len(host_q)} tensors of the layer ({numel} bf16 elements, C oracle, once) + "
+                   f"fp64 NS T={steps} of {shapes} (numpy oracle); NS TFLOP/s counts the symmetric FLOPs"),
         "ns_tflops": round(fl / t_ns / 1e12, 5),
-        "q8_seconds": round(t_q, 4), "ns_seconds": round(t_ns, 3),
+        "q8_seconds": round(t_q, 3), "ns_seconds": round(t_ns, 3),
     }
 
 
@@ -127,14 +183,15 @@ def main():
         numel += r * c
     torch.cuda.synchronize()
     host_q = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload == "llama8b":
         import numpy as np
-        k = min(range(len(tensors)), key=lambda i: abs(tensors[i][1] * tensors[i][2] - 16 * 2 ** 20))
-        host_q = (trip[k][0].cpu().numpy(), trip[k][1].cpu().numpy(),
-                  trip[k][2].view(torch.int16).cpu().numpy().view(np.uint16))
-        kn = min(range(len(tensors)), key=lambda i: tensors[i][1] * tensors[i][2])
-        host_ns = trip[kn][2].float().cpu().numpy().astype(np.float64).reshape(
-            tensors[kn][1], tensors[kn][2])
+        host_q = [(c.cpu().numpy(), a.cpu().numpy(), g.view(torch.int16).cpu().numpy().view(np.uint16))
+                  for c, a, g in trip]
+        # NS sample: the q (4096 x 4096), k (1024 x 4096) and down (4096 x 14336)
+        # matrices, about 10 s of fp64 work on 16 host cores
+        pick = [next(i for i, t in enumerate(tensors) if t[0] == nm) for nm in ("q", "k", "down")]
+        host_ns = [trip[i][2].float().cpu().numpy().astype(np.float64).reshape(tensors[i][1], tensors[i][2])
+                   for i in pick]
 
     plan = q.Plan(trip, segments, ng)
     blk_plan = None
@@ -176,12 +233,15 @@ def main():
     evs = [mk() for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    q.timing_enable(True)
     start.record()
     for t in range(args.steps):
         step(args.warmup + 1 + t, evs[t])
     stop.record()
     torch.cuda.synchronize()
+    q.timing_enable(False)
     total_ms = start.elapsed_time(stop)
+    per_class = {k: q.timing_read(k) for k in q.KERNEL_CLASSES}
     if args.ref_copy_mib > 0:
         src = torch.empty(args.ref_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -208,18 +268,24 @@ def main():
         gbs = bytes_ / (upd_ms * 1e-3) / 1e9
         flops = sum(ns_sym_flops(r, c, H.NS_STEPS) for _, r, c in tensors)
         tfl = flops / (ns_ms * 1e-3) / 1e12
+        work = launch_work(tensors, numel)
+        traffic = recorded_traffic("llama8b_layer")
+        kernels = {k: {"ms_per_launch": round(ms / n, 4), "launches": n, "share": round(ms / total_ms, 4)}
+                   for k, (ms, n) in per_class.items() if n}
+        timed = [k for k in work if per_class[k][1]]
+        dom = max(timed, key=lambda k: per_class[k][0])
+        rl = {}
+        for k in (dom, "q8_update"):
+            ms, n = per_class[k]
+            rl[k] = roofline(work[k][0], work[k][1], ms / n, traffic.get(k))
+            rl[k]["kernel"] = k
         out.update({"value": round(gbs, 2), "unit": "GB/s", "dtype": "bf16",
                     "ns_tflops": round(tfl, 2),
                     "config": {"workload": "llama8b_layer_muon_step", "matrices": len(tensors),
                                "elements": numel, "ns_steps": H.NS_STEPS, "ns_precision": "bf16",
                                "grad_dtype": "bf16", "state": "int8", "update_ms": round(upd_ms, 4),
                                "ns_apply_ms": round(ns_ms, 4), "ns_flops_per_step": flops},
-                    "roofline": {"bound": "mfma", "achieved": round(tfl, 2), "peak": BF16_PEAK_TFLOPS,
-                                 "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
-                                 "traffic": None},
-                    "roofline_update": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                        "traffic": None}})
+                    "roofline": rl[dom], "roofline_update": rl["q8_update"], "kernels": kernels})
     else:
         out.update({"value": round(1000.0 / ms_per_step, 3), "unit": "steps/s", "dtype": "bf16",
                     "config": {"workload": "muonbp_4096x14336_P5", "blocks": 8}})

@@ -295,6 +295,39 @@ QM_API qm_status grasp_step(const qm_grasp_state *state, int64_t rows,
                             float weight_decay, void *ws, size_t ws_bytes,
                             qm_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Launch timing (measurement aid, off by default).
+ *
+ * While enabled, every launch of the classes below is bracketed by two HIP
+ * events recorded on the launch stream, so a reader gets the same per-launch
+ * device time a kernel-trace profiler reports.  Enabling clears earlier
+ * records; disabling keeps them for qm_timing_read.  Not for use inside HIP
+ * graph capture.  The recorder is process-wide and locked; launches from
+ * several threads are recorded but interleave in one list.
+ */
+typedef enum {
+    QM_K_Q8_UPDATE = 0,     /* blockwise q8 momentum update kernel */
+    QM_K_GROUP_REDUCE = 1,  /* per-group sum of squares (both stages) */
+    QM_K_Q8_SCALE = 2,      /* in-place normalisation pass */
+    QM_K_NS_NORM = 3,       /* Frobenius norm of NS inputs (both stages) */
+    QM_K_NS_PROLOGUE = 4,   /* orientation, scaling, X and X^T */
+    QM_K_NS_GRAM = 5,       /* A = X X^T (symmetric product) */
+    QM_K_NS_POLY = 6,       /* B = b A + c A A (symmetric product) */
+    QM_K_NS_XUPDATE = 7,    /* X = a X + B X */
+    QM_K_NS_WRITEBACK = 8,  /* output and fused weight update */
+    QM_K_CLASSES = 9
+} qm_kernel_class;
+
+/* on != 0: clear records and start recording; on == 0: stop.
+ * Errors: QM_E_HIP (event creation failed). */
+QM_API qm_status qm_timing_enable(int32_t on);
+
+/* Sum of the recorded launch durations of one class (milliseconds) and the
+ * number of launches.  Waits for the recorded events to complete.
+ * Errors: QM_E_ARG (class out of range, null outputs), QM_E_HIP. */
+QM_API qm_status qm_timing_read(int32_t kernel_class, double *total_ms,
+                                int64_t *launches);
+
 /* ------------------------------------------------------------------------ */
 QM_API const char *qm_status_string(qm_status s);
 QM_API const char *qm_last_error(void);

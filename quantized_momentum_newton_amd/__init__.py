@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/qmuon.h):
   muon_step                        update + NS + weight apply, block-periodic
   muon_apply                       the NS + weight-apply half of muon_step
   GraspState, grasp_step           the GRASP 4-bit momentum variant
+  timing_enable, timing_read       per-kernel-class launch timing (HIP events)
 """
 import ctypes
 
@@ -59,6 +60,23 @@ def _dtype(t):
 
 def abi_version():
     return _LIB.qm_abi_version()
+
+
+# Kernel classes of qm_timing_read (qm_kernel_class in include/qmuon.h).
+KERNEL_CLASSES = {"q8_update": 0, "group_reduce": 1, "q8_scale": 2, "ns_norm": 3, "ns_prologue": 4,
+                  "ns_gram": 5, "ns_poly": 6, "ns_xupdate": 7, "ns_writeback": 8}
+
+
+def timing_enable(on=True):
+    """Start (clearing earlier records) or stop recording launch times."""
+    _check(_LIB.qm_timing_enable(1 if on else 0))
+
+
+def timing_read(kernel_class):
+    """(total milliseconds, launches) recorded for one kernel class."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(_LIB.qm_timing_read(KERNEL_CLASSES[kernel_class], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 class Plan:

@@ -28,6 +28,7 @@ UNITS = [
     ("ns.hip", []),
     ("grasp.hip", ["-ffp-contract=off"]),
     ("plan.cpp", []),
+    ("timing.cpp", ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]),
 ]
 
 

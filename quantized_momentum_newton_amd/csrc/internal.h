@@ -16,6 +16,23 @@ void clear_error();
 struct PlanHeader;
 const PlanHeader *plan_header(const void *host_blob, qm_status *st);
 
+// Launch timing: while qm_timing_enable(1) is in effect, a Timed object
+// records a HIP event on `stream` when built and another when destroyed,
+// bracketing the launches of its scope under kernel class `cls`.
+bool timing_on();
+int timing_begin(void *stream, int cls);
+void timing_end(void *stream, int token);
+struct Timed {
+    void *stream;
+    int token;
+    Timed(void *s, int cls) : stream(s), token(timing_on() ? timing_begin(s, cls) : -1) {}
+    ~Timed() {
+        if (token >= 0) timing_end(stream, token);
+    }
+    Timed(const Timed &) = delete;
+    Timed &operator=(const Timed &) = delete;
+};
+
 inline bool aligned(const void *p, uintptr_t a) {
     return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }

@@ -24,9 +24,11 @@
 //   * 256x256 output tiles, four waves of 128x128 (accumulators in AGPRs),
 //     K-tiles of 128 bytes per row double-buffered in LDS and filled by
 //     direct global-to-LDS loads (no staging registers); a 16-byte XOR
-//     swizzle keeps the 16-byte fragment reads free of bank conflicts.
-//   * Workgroups are remapped so each XCD (own L2) takes runs of 8 adjacent
-//     tiles while all XCDs walk the tile list together.
+//     swizzle keeps the 16-byte fragment reads free of bank conflicts
+//     (64 banks: 16 lanes per cycle).
+//   * Tiles are ordered in bands of 4 tile rows walked column by column and
+//     workgroups remapped so each XCD's 32 concurrent workgroups cover a 4x8
+//     block of tiles (12 operand panels shared in that XCD's L2).
 //   * Internal buffers are zero-padded to multiples of 256: zero rows and
 //     columns stay zero through the iteration, so no kernel needs bounds
 //     checks in its main loop.
@@ -136,10 +138,10 @@ template <typename T> struct GItem {
     T *CT;
     const T *D;
     int64_t ldp, ldq, ldc, ldct, ldd;
-    int32_t tiles_n;       // tile columns (non-symmetric products)
+    int32_t tiles_m;       // tile rows
+    int32_t tiles_n;       // tile columns (== tiles_m for the symmetric products)
     int32_t tile_begin;    // first logical tile of this matrix
     int32_t k_tiles;       // K / (128 / sizeof(T))
-    int32_t pad;
 };
 
 template <typename T> struct GemmArgs {
@@ -148,22 +150,59 @@ template <typename T> struct GemmArgs {
     float alpha, beta;
 };
 
-// Workgroups go to the 8 XCDs round robin (w % 8).  Inside every run of 64
-// workgroups each XCD gets 8 consecutive logical tiles (which share operand
-// panels in its L2) while all XCDs advance through the tile list together.
-__device__ __forceinline__ int xcd_remap(int w, int nwg) {
-    const int full = nwg / 64 * 64;
+// Workgroup -> position in the tile order.  Workgroups go to the 8 XCDs
+// round robin (w % 8) and each XCD runs 32 at a time (one per CU); in every
+// round of 256, XCD x takes positions [32x, 32x + 32).  With the band order
+// below, those 32 positions are a 4 x 8 block of tiles: 4 + 8 operand
+// panels shared through that XCD's L2 instead of up to 64.
+__device__ __forceinline__ int wg_position(int w, int nwg) {
+    const int full = nwg / 256 * 256;
     if (w >= full) return w;
-    const int q = w / 64, r = w % 64;
-    return q * 64 + (r % 8) * 8 + r / 8;
+    const int x = w & 7, l = w >> 3;
+    return (l >> 5) * 256 + x * 32 + (l & 31);
 }
 
-__device__ __forceinline__ void tri_coords(int t, int &bi, int &bj) {
-    int i = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while (i * (i + 1) / 2 > t) i--;
-    while ((i + 1) * (i + 2) / 2 <= t) i++;
-    bi = i;
-    bj = t - i * (i + 1) / 2;
+constexpr int kBand = 4;   // tile rows per band
+
+// Rectangular tile grid (tm x tn), bands of kBand tile rows, each band walked
+// column by column.
+__device__ __forceinline__ void band_coords(int p, int tm, int tn, int &bi, int &bj) {
+    const int b = p / (kBand * tn);
+    const int r0 = b * kBand;
+    const int h = min(kBand, tm - r0);
+    const int q = p - r0 * tn;
+    bi = r0 + q % h;
+    bj = q / h;
+}
+
+// Lower-triangle tile grid (bi >= bj), same band order: in band b (rows
+// r0 .. r0+h-1) columns 0..r0 hold h tiles each, then column r0+k holds the
+// h-k rows r0+k .. r0+h-1.  Rows below r0 hold r0 (r0 + 1) / 2 tiles.
+__device__ __forceinline__ void band_coords_tri(int p, int tm, int &bi, int &bj) {
+    int b = 0;
+    while ((b + 1) * kBand < tm) {
+        const int r1 = (b + 1) * kBand;
+        if (r1 * (r1 + 1) / 2 > p) break;
+        b++;
+    }
+    const int r0 = b * kBand;
+    const int h = min(kBand, tm - r0);
+    int q = p - r0 * (r0 + 1) / 2;
+    if (q < (r0 + 1) * h) {
+        bi = r0 + q % h;
+        bj = q / h;
+        return;
+    }
+    q -= (r0 + 1) * h;
+    for (int k = 1; k < h; k++) {
+        if (q < h - k) {
+            bi = r0 + k + q;
+            bj = r0 + k;
+            return;
+        }
+        q -= h - k;
+    }
+    bi = bj = r0 + h - 1;  // not reached for valid p
 }
 
 __device__ __forceinline__ void lds_dma16(const void *g, void *l) {
@@ -171,16 +210,39 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *l) {
                                      (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int EPI, bool SYM>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs<T> args) {
+// Workgroup barrier for the k-loop.  __syncthreads() carries a release
+// fence whose lowering waits for every outstanding vector-memory operation,
+// LDS-DMA loads of later stages included, which would drain the prefetch
+// pipeline at each k-tile.  Here only LDS reads are completed (so no stage is
+// overwritten while a wave still reads it); the DMA of the stage about to be
+// read is waited for explicitly with wait_vmcnt_tiles before the barrier.
+__device__ __forceinline__ void kloop_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) with n a multiple of D chosen at run time (0..3 D).
+template <int D>
+__device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
+    if (tiles <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (tiles == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+    else if (tiles == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
+}
+
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int MINB, int EPI, bool SYM>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int FM = WM / 32, FN = WN / 32;
-    constexpr int ROWB = 128;                       // LDS bytes per tile row (one k-tile)
+    constexpr int CPR = ROWB / 16;                  // 16-byte chunks per tile row (one k-tile)
+    constexpr int RPI = 64 / CPR;                   // tile rows per DMA instruction
+    constexpr int SWD = 16 / CPR;                   // rows sharing one 256-byte bank row
+    constexpr int STEPS = CPR / 2;                  // MFMA k-steps per k-tile
     constexpr int STAGE = (BM + BN) * ROWB;
-    constexpr int PI = BM / 8 / NW, QI = BN / 8 / NW;  // DMA instructions per wave per stage
-    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile / wave count");
-    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    constexpr int PI = BM / RPI / NW, QI = BN / RPI / NW;  // DMA instructions per wave per operand
+    constexpr int DPT = PI + QI;                    // per wave per k-tile
+    static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wave count");
+    static_assert(FM >= 1 && FN >= 1 && NSTAGE >= 2 && NSTAGE <= 5, "config");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
@@ -188,40 +250,40 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int L = wg_position(blockIdx.x, gridDim.x);
     int item = 0;
     while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
     const GItem<T> &I = args.it[item];
     const int t = L - I.tile_begin;
     int bi, bj;
-    if constexpr (SYM) {
-        tri_coords(t, bi, bj);
-    } else {
-        bi = t / I.tiles_n;
-        bj = t % I.tiles_n;
-    }
+    if constexpr (SYM) band_coords_tri(t, I.tiles_n, bi, bj);
+    else band_coords(t, I.tiles_m, I.tiles_n, bi, bj);
 
     const char *Pg = reinterpret_cast<const char *>(I.P + (int64_t)bi * BM * I.ldp);
     const char *Qg = reinterpret_cast<const char *>(I.Q + (int64_t)bj * BN * I.ldq);
     const int64_t ldpb = I.ldp * (int64_t)sizeof(T), ldqb = I.ldq * (int64_t)sizeof(T);
-    const int lr8 = lane >> 3, lch = lane & 7;
+    const int lrw = lane / CPR, lch = lane % CPR;
 
-    // Direct loads: one instruction moves 8 tile rows (1 KiB) into LDS; lane
-    // l lands at LDS row r0 + l/8, position l%8, so it fetches global chunk
-    // (l%8) ^ (row%8) -- the swizzle is applied on the global side.
+    // Direct loads: one instruction moves RPI tile rows (1 KiB) into LDS;
+    // lane l lands at row r0 + l / CPR, position l % CPR, so it fetches global
+    // chunk (l % CPR) ^ sw(row) -- the swizzle is applied on the global side.
+    // sw(row) = (row / SWD) % CPR gives 16 consecutive rows' copies of one
+    // logical chunk 16 distinct 16-byte slots of a 256-byte bank row: the 16
+    // lanes a fragment read serves together never collide (64 banks).
     auto issue = [&](int kt, int stage) {
         char *base = smem + stage * STAGE;
 #pragma unroll
         for (int i = 0; i < PI; i++) {
-            const int r0 = (wave + i * NW) * 8;
-            const int row = r0 + lr8;
-            lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ (row & 7)) << 4), base + r0 * ROWB);
+            const int r0 = (wave + i * NW) * RPI;
+            const int row = r0 + lrw;
+            lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4), base + r0 * ROWB);
         }
 #pragma unroll
         for (int i = 0; i < QI; i++) {
-            const int r0 = (wave + i * NW) * 8;
-            const int row = r0 + lr8;
-            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ (row & 7)) << 4), base + (BM + r0) * ROWB);
+            const int r0 = (wave + i * NW) * RPI;
+            const int row = r0 + lrw;
+            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
+                      base + (BM + r0) * ROWB);
         }
     };
 
@@ -235,35 +297,70 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64) void gemm_nt_kernel(GemmArgs
 
     const int KT = I.k_tiles;
     const int lrow = lane & 31, lhalf = lane >> 5;
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int kt = 0; kt < KT; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
-        const char *cp = smem + cur * STAGE;
+    auto read_frags = [&](const char *cp, int s, u32x4 *a, u32x4 *b) {
         const char *cq = cp + BM * ROWB;
+        const int ch = 2 * s + lhalf;
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const int ch = 2 * s + lhalf;
-            u32x4 a[FM], b[FN];
+        for (int i = 0; i < FM; i++) {
+            const int row = wm * WM + i * 32 + lrow;
+            a[i] = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+        }
 #pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const int row = wm * WM + i * 32 + lrow;
-                a[i] = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + ((ch ^ (row & 7)) << 4));
+        for (int j = 0; j < FN; j++) {
+            const int row = wn * WN + j * 32 + lrow;
+            b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+        }
+    };
+    // Software pipeline.  NSTAGE LDS stages: tiles kt+1 .. kt+NSTAGE-1 are in
+    // flight while tile kt is multiplied, and each iteration waits only for
+    // tile kt+1.  The next tile's DMA is spread over the k-steps (one slice
+    // per step), and fragments for k-step s+1 are read into a second
+    // register set while the MFMAs of step s run; the next tile's first
+    // fragments are read right after the barrier, while the last MFMAs of
+    // this tile drain.
+    u32x4 fa[2][FM], fb[2][FN];
+    constexpr int DPS = (DPT + STEPS - 1) / STEPS;  // DMA instructions per k-step
+    auto issue_part = [&](int kt, int stage, int part) {
+        char *base = smem + stage * STAGE;
+#pragma unroll
+        for (int d = part * DPS; d < (part + 1) * DPS && d < DPT; d++) {
+            if (d < PI) {
+                const int r0 = (wave + d * NW) * RPI;
+                const int row = r0 + lrw;
+                lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
+                          base + r0 * ROWB);
+            } else {
+                const int r0 = (wave + (d - PI) * NW) * RPI;
+                const int row = r0 + lrw;
+                lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
+                          base + (BM + r0) * ROWB);
             }
+        }
+    };
 #pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const int row = wn * WN + j * 32 + lrow;
-                b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ (row & 7)) << 4));
-            }
+    for (int k = 0; k < NSTAGE - 1; k++)
+        if (k < KT) issue(k, k);
+    wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
+    kloop_barrier();
+    read_frags(smem, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < KT; kt++) {
+        const char *cp = smem + (kt % NSTAGE) * STAGE;
+        const int nk = kt + NSTAGE - 1;
+        const bool more = nk < KT;
+        const int nstage = nk % NSTAGE;
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            if (s + 1 < STEPS) read_frags(cp, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            if (more) issue_part(nk, nstage, s);
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
-                for (int j = 0; j < FN; j++) Mfma<T>::step(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < FN; j++) Mfma<T>::step(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // tiles still allowed in flight: those issued after kt+1
+        wait_vmcnt_tiles<DPT>(min(KT - 1, kt + NSTAGE - 1) - (kt + 1));
+        kloop_barrier();
+        if (kt + 1 < KT) read_frags(smem + ((kt + 1) % NSTAGE) * STAGE, 0, fa[STEPS & 1], fb[STEPS & 1]);
     }
 
     // ---------------------------------------------------------- epilogue
@@ -328,6 +425,7 @@ struct NsItem {
     void *X, *XT;          // internal buffers (element type of the run)
     int32_t m, n;          // valid extent in iteration orientation
     int64_t mp, np;        // padded
+    int64_t ldx, ldxt;     // leading dimensions of X (np + pad) and X^T (mp + pad)
     int32_t tiles_n;       // 64-wide tiles per padded row
     int32_t tile_begin;    // first 64x64 tile of this item
 };
@@ -402,8 +500,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     T *XT = static_cast<T *>(it.XT);
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
         const int ii = idx >> 6, jj = idx & 63;
-        X[(i0 + ii) * it.np + j0 + jj] = from_float<T>(tile[ii][jj]);
-        XT[(j0 + ii) * it.mp + i0 + jj] = from_float<T>(tile[jj][ii]);
+        X[(i0 + ii) * it.ldx + j0 + jj] = from_float<T>(tile[ii][jj]);
+        XT[(j0 + ii) * it.ldxt + i0 + jj] = from_float<T>(tile[jj][ii]);
     }
 }
 
@@ -426,7 +524,7 @@ __global__ __launch_bounds__(256) void writeback_kernel(PrologueArgs a, Writebac
     const T *X = static_cast<const T *>(it.X);
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
         const int ii = idx >> 6, jj = idx & 63;
-        tile[ii][jj] = to_float(X[(i0 + ii) * it.np + j0 + jj]);
+        tile[ii][jj] = to_float(X[(i0 + ii) * it.ldx + j0 + jj]);
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
@@ -459,9 +557,16 @@ struct NsRequest {
     float lr_s, lr_wd;
 };
 
+// Row pitch of the internal operands: the padded width plus one 128-byte
+// line, so that the rows one load instruction fetches (pitches that are
+// multiples of 4 KiB otherwise) spread over the L2 channels instead of
+// queueing on one.  The extra columns are never read.
+constexpr int64_t kRowPadBytes = 128;
+
 struct Geometry {
     int64_t m, n, mp, np;
-    int64_t x_bytes, a_bytes;    // one X-shaped / A-shaped buffer, 256-aligned
+    int64_t ldn, ldm;            // pitch (elements) of rows of length np / mp
+    int64_t x_bytes, xt_bytes, a_bytes;  // X (mp x ldn), X^T (np x ldm), A (mp x ldm)
     int64_t item_bytes;          // X + XT0 + XT1 + A + B
 };
 
@@ -471,9 +576,12 @@ Geometry geometry(int64_t rows, int64_t cols, size_t esz) {
     g.n = std::max(rows, cols);
     g.mp = pad_up(g.m);
     g.np = pad_up(g.n);
-    g.x_bytes = align_up(g.mp * g.np * (int64_t)esz, 256);
-    g.a_bytes = align_up(g.mp * g.mp * (int64_t)esz, 256);
-    g.item_bytes = 3 * g.x_bytes + 2 * g.a_bytes;
+    g.ldn = g.np + kRowPadBytes / (int64_t)esz;
+    g.ldm = g.mp + kRowPadBytes / (int64_t)esz;
+    g.x_bytes = align_up(g.mp * g.ldn * (int64_t)esz, 256);
+    g.xt_bytes = align_up(g.np * g.ldm * (int64_t)esz, 256);
+    g.a_bytes = align_up(g.mp * g.ldm * (int64_t)esz, 256);
+    g.item_bytes = g.x_bytes + 2 * g.xt_bytes + 2 * g.a_bytes;
     return g;
 }
 
@@ -514,11 +622,20 @@ size_t ns_ws_bytes_uniform(int64_t rows, int64_t cols, int64_t items, int precis
     return ns_ws_bytes_req(req, precision);
 }
 
-template <typename T, int BM, int BN, int WMW, int WNW, int EPI, bool SYM>
+// Tile configurations: <BM, BN, waves_m, waves_n, row bytes per k-tile,
+// LDS stages, workgroups per CU>.  The symmetric products need square tiles.
+struct CfgSym {
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
+};
+struct CfgRect {
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
+};
+
+template <typename T, typename C, int EPI, bool SYM>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
-    constexpr int NT = WMW * WNW * 64;
-    constexpr size_t lds = 2 * (BM + BN) * 128;
-    auto kern = gemm_nt_kernel<T, BM, BN, WMW, WNW, EPI, SYM>;
+    constexpr int NT = C::WM * C::WN * 64;
+    constexpr size_t lds = (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
+    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::MINB, EPI, SYM>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -526,14 +643,12 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
             return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", lds);
         attr_set = true;
     }
+    Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, stream, args);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "gemm launch: %s", hipGetErrorString(e));
     return QM_OK;
 }
-
-// Tile configuration of the NS products.
-constexpr int kBM = 256, kBN = 256, kWM = 2, kWN = 2;
 
 struct ItemBufs {
     Geometry g;
@@ -551,8 +666,8 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         ItemBufs &B = bufs[i];
         B.g = geometry(r.rows, r.cols, sizeof(T));
         B.X = p;   p += B.g.x_bytes;
-        B.XT0 = p; p += B.g.x_bytes;
-        B.XT1 = p; p += B.g.x_bytes;
+        B.XT0 = p; p += B.g.xt_bytes;
+        B.XT1 = p; p += B.g.xt_bytes;
         B.A = p;   p += B.g.a_bytes;
         B.B = p;   p += B.g.a_bytes;
     }
@@ -580,16 +695,22 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         it.n = (int32_t)g.n;
         it.mp = g.mp;
         it.np = g.np;
+        it.ldx = g.ldn;
+        it.ldxt = g.ldm;
         it.tiles_n = (int32_t)(g.np / 64);
         it.tile_begin = tiles;
         tiles += (int32_t)((g.mp / 64) * (g.np / 64));
         need_norm |= r.inv == nullptr;
     }
     if (need_norm) {
+        Timed tm(stream, QM_K_NS_NORM);
         norm_partial_kernel<<<dim3(kNormChunks, nit), 256, 0, stream>>>(pa, partials);
         norm_final_kernel<<<nit, 64, 0, stream>>>(partials, eps, inv_ws);
     }
-    prologue_kernel<T><<<tiles, 256, 0, stream>>>(pa);
+    {
+        Timed tm(stream, QM_K_NS_PROLOGUE);
+        prologue_kernel<T><<<tiles, 256, 0, stream>>>(pa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "prologue: %s", hipGetErrorString(e));
 
@@ -603,7 +724,8 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     for (int i = 0; i < nit; i++) wb.fo[i] = fo[i];
 
     // Per-product item order: longest K first (all tiles of a matrix share K).
-    constexpr int64_t kElemsPerKTile = 128 / (int64_t)sizeof(T);
+    constexpr int64_t kSymK = CfgSym::ROWB / (int64_t)sizeof(T);    // K elements per k-tile
+    constexpr int64_t kRectK = CfgRect::ROWB / (int64_t)sizeof(T);
     std::vector<int> by_n(nit), by_m(nit);
     std::iota(by_n.begin(), by_n.end(), 0);
     std::iota(by_m.begin(), by_m.end(), 0);
@@ -619,17 +741,18 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         int tl = 0;
         for (int k = 0; k < nit; k++) {
             const ItemBufs &B = bufs[by_n[k]];
-            const int tm = (int)(B.g.mp / kBM);
+            const int tm = (int)(B.g.mp / CfgSym::BM);
             GItem<T> &I = g1.it[k];
-            I.P = reinterpret_cast<const T *>(B.X); I.ldp = B.g.np;
-            I.Q = reinterpret_cast<const T *>(B.X); I.ldq = B.g.np;
-            I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.mp;
+            I.P = reinterpret_cast<const T *>(B.X); I.ldp = B.g.ldn;
+            I.Q = reinterpret_cast<const T *>(B.X); I.ldq = B.g.ldn;
+            I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.ldm;
+            I.tiles_m = tm;
             I.tiles_n = tm;
             I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.np / kElemsPerKTile);
+            I.k_tiles = (int32_t)(B.g.np / kSymK);
             tl += tm * (tm + 1) / 2;
         }
-        qm_status st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_GRAM, true>(g1, tl, stream);
+        qm_status st = launch_gemm<T, CfgSym, EPI_GRAM, true>(g1, tl, stream);
         if (st != QM_OK) return st;
         // B = b A + c A A
         GemmArgs<T> g2{};
@@ -639,18 +762,19 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         tl = 0;
         for (int k = 0; k < nit; k++) {
             const ItemBufs &B = bufs[by_m[k]];
-            const int tm = (int)(B.g.mp / kBM);
+            const int tm = (int)(B.g.mp / CfgSym::BM);
             GItem<T> &I = g2.it[k];
-            I.P = reinterpret_cast<const T *>(B.A); I.ldp = B.g.mp;
-            I.Q = reinterpret_cast<const T *>(B.A); I.ldq = B.g.mp;
-            I.C = reinterpret_cast<T *>(B.B); I.ldc = B.g.mp;
-            I.D = reinterpret_cast<const T *>(B.A); I.ldd = B.g.mp;
+            I.P = reinterpret_cast<const T *>(B.A); I.ldp = B.g.ldm;
+            I.Q = reinterpret_cast<const T *>(B.A); I.ldq = B.g.ldm;
+            I.C = reinterpret_cast<T *>(B.B); I.ldc = B.g.ldm;
+            I.D = reinterpret_cast<const T *>(B.A); I.ldd = B.g.ldm;
+            I.tiles_m = tm;
             I.tiles_n = tm;
             I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.mp / kElemsPerKTile);
+            I.k_tiles = (int32_t)(B.g.mp / kSymK);
             tl += tm * (tm + 1) / 2;
         }
-        st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_POLY, true>(g2, tl, stream);
+        st = launch_gemm<T, CfgSym, EPI_POLY, true>(g2, tl, stream);
         if (st != QM_OK) return st;
         // X = a X + B X   (Q operand = X^T)
         GemmArgs<T> g3{};
@@ -660,24 +784,28 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         for (int k = 0; k < nit; k++) {
             const int i = by_m[k];
             const ItemBufs &B = bufs[i];
-            const int tm = (int)(B.g.mp / kBM), tn = (int)(B.g.np / kBN);
+            const int tm = (int)(B.g.mp / CfgRect::BM), tn = (int)(B.g.np / CfgRect::BN);
             GItem<T> &I = g3.it[k];
-            I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.mp;
-            I.Q = reinterpret_cast<const T *>(cur[i] ? B.XT1 : B.XT0); I.ldq = B.g.mp;
-            I.C = reinterpret_cast<T *>(B.X); I.ldc = B.g.np;
-            I.CT = reinterpret_cast<T *>(cur[i] ? B.XT0 : B.XT1); I.ldct = B.g.mp;
-            I.D = reinterpret_cast<const T *>(B.X); I.ldd = B.g.np;
+            I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.ldm;
+            I.Q = reinterpret_cast<const T *>(cur[i] ? B.XT1 : B.XT0); I.ldq = B.g.ldm;
+            I.C = reinterpret_cast<T *>(B.X); I.ldc = B.g.ldn;
+            I.CT = reinterpret_cast<T *>(cur[i] ? B.XT0 : B.XT1); I.ldct = B.g.ldm;
+            I.D = reinterpret_cast<const T *>(B.X); I.ldd = B.g.ldn;
+            I.tiles_m = tm;
             I.tiles_n = tn;
             I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.mp / kElemsPerKTile);
+            I.k_tiles = (int32_t)(B.g.mp / kRectK);
             tl += tm * tn;
             if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
         }
-        st = launch_gemm<T, kBM, kBN, kWM, kWN, EPI_UPDATE, false>(g3, tl, stream);
+        st = launch_gemm<T, CfgRect, EPI_UPDATE, false>(g3, tl, stream);
         if (st != QM_OK) return st;
         for (int i = 0; i < nit; i++) cur[i] ^= 1;
     }
-    writeback_kernel<T><<<tiles, 256, 0, stream>>>(pa, wb);
+    {
+        Timed tm(stream, QM_K_NS_WRITEBACK);
+        writeback_kernel<T><<<tiles, 256, 0, stream>>>(pa, wb);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "writeback: %s", hipGetErrorString(e));
     return QM_OK;

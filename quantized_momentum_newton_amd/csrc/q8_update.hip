@@ -396,6 +396,7 @@ qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, d
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
     const int64_t *toff = section<int64_t>(dev_plan, h->off_task_offsets);
     const int grid = stream_grid(h->n_tasks);
+    Timed tm(stream, QM_K_Q8_UPDATE);
     if (block_sums)
         q8_update_kernel<true><<<grid, kThreads, 0, stream>>>(tens, toff, h->n_tensors, h->n_tasks, beta,
                                                              block_sums);
@@ -409,6 +410,7 @@ qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const d
                               double *partials, float eps, double *group_sums, float *inv, hipStream_t stream) {
     const int64_t *ro = section<int64_t>(dev_plan, h->off_run_offsets);
     const int64_t *co = section<int64_t>(dev_plan, h->off_chunk_offsets);
+    Timed tm(stream, QM_K_GROUP_REDUCE);
     chunk_reduce_kernel<<<(unsigned)h->n_chunks, kThreads, 0, stream>>>(
         ro, section<PlanRun>(dev_plan, h->off_runs), co, section<int32_t>(dev_plan, h->off_chunk_group),
         block_sums, partials);
@@ -420,6 +422,7 @@ qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const d
 }
 
 qm_status launch_scale(const PlanHeader *h, const void *dev_plan, const float *inv, hipStream_t stream) {
+    Timed tm(stream, QM_K_Q8_SCALE);
     q8_scale_kernel<<<stream_grid(h->n_tasks), kThreads, 0, stream>>>(
         section<PlanTensor>(dev_plan, h->off_tensors), section<int64_t>(dev_plan, h->off_task_offsets),
         h->n_tensors, h->n_tasks, section<int32_t>(dev_plan, h->off_block_group), inv);

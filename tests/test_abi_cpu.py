@@ -132,3 +132,17 @@ def test_update_calls_validate_before_launch():
                                              ctypes.c_void_p(BASE), need, None) == 1
     assert LIB.qmuon_update_normalize_groups(hp, fake_dev, 0.9, 1e-7, 1, None, None,
                                              ctypes.c_void_p(BASE + 8), need, None) == 2
+
+
+def test_timing_recorder_host_checks():
+    """The launch-timing recorder: bad class or null outputs are rejected;
+    with nothing launched every class reads zero launches."""
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+    assert LIB.qm_timing_read(99, ctypes.byref(ms), ctypes.byref(n)) == 1  # QM_E_ARG
+    assert LIB.qm_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == 1  # QM_E_ARG
+    assert LIB.qm_timing_read(0, None, ctypes.byref(n)) == 1  # QM_E_ARG
+    q.timing_enable(True)
+    q.timing_enable(False)
+    for k in q.KERNEL_CLASSES:
+        assert q.timing_read(k) == (0.0, 0)
+    assert sorted(q.KERNEL_CLASSES.values()) == list(range(9))

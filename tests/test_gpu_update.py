@@ -224,3 +224,22 @@ def test_determinism_and_canaries():
         results.append((hc, ha, hg, host(inv)))
     for x, y in zip(results[0], results[1]):
         assert np.array_equal(x, y)
+
+
+def test_launch_timing_records_each_kernel_class():
+    """The event timer sees one launch per kernel class per call, with a
+    positive duration, and nothing while it is off."""
+    qs = Q8Set([(4096, 512), (1000,)], [torch.bfloat16, torch.float32], seed=1011)
+    plan = q.Plan(qs.triples(), [(0, 0, 4096 * 512, 0), (1, 0, 1000, 1)], 2)
+    inv = torch.empty(2, dtype=torch.float32, device=DEV)
+    say("launch timing: update+normalize twice")
+    q.timing_enable(True)
+    for _ in range(2):
+        q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    q.timing_enable(False)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    torch.cuda.synchronize()
+    for k in ("q8_update", "group_reduce", "q8_scale"):
+        ms, n = q.timing_read(k)
+        assert n == 2 and ms > 0.0, (k, ms, n)
+    assert q.timing_read("ns_gram") == (0.0, 0)
