@@ -187,9 +187,9 @@ def main():
         import numpy as np
         host_q = [(c.cpu().numpy(), a.cpu().numpy(), g.view(torch.int16).cpu().numpy().view(np.uint16))
                   for c, a, g in trip]
-        # NS sample: the q (4096 x 4096), k (1024 x 4096) and down (4096 x 14336)
-        # matrices, about 10 s of fp64 work on 16 host cores
-        pick = [next(i for i, t in enumerate(tensors) if t[0] == nm) for nm in ("q", "k", "down")]
+        # NS sample: the q (4096 x 4096), k (1024 x 4096), gate (14336 x 4096)
+        # and down (4096 x 14336) matrices, about 10 s of fp64 work on 16 host cores
+        pick = [next(i for i, t in enumerate(tensors) if t[0] == nm) for nm in ("q", "k", "gate", "down")]
         host_ns = [trip[i][2].float().cpu().numpy().astype(np.float64).reshape(tensors[i][1], tensors[i][2])
                    for i in pick]
 

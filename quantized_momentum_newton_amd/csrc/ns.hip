@@ -147,7 +147,12 @@ template <typename T> struct GItem {
 template <typename T> struct GemmArgs {
     GItem<T> it[kMaxItems];
     int32_t n_items;
-    float alpha, beta;
+    float alpha, beta;     // epilogue: C = alpha D + beta acc (beta = 1 for X = aX + BX)
+    // dloop != 0: the D term is gathered inside the k-loop instead (acc +=
+    // dgain D, dgain = alpha / beta), then C = beta acc.  Valid because D's
+    // tile is a block of the Q operand (see gemm_nt_kernel).
+    int32_t dloop;
+    float dgain;
 };
 
 // Workgroup -> position in the tile order.  Workgroups go to the 8 XCDs
@@ -210,6 +215,32 @@ __device__ __forceinline__ void lds_dma16(const void *g, void *l) {
                                      (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
 
+// Eight consecutive elements <-> fp32: one 16-byte access for bf16, two
+// for fp32 (16-byte aligned addresses).
+__device__ __forceinline__ void unpack8(const u32x4 w, float *v) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const bf16_t *p, float *v) { unpack8(*reinterpret_cast<const u32x4 *>(p), v); }
+__device__ __forceinline__ void load8(const float *p, float *v) {
+    *reinterpret_cast<float4 *>(v) = *reinterpret_cast<const float4 *>(p);
+    *reinterpret_cast<float4 *>(v + 4) = *reinterpret_cast<const float4 *>(p + 4);
+}
+__device__ __forceinline__ void store8(bf16_t *p, const float *v) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+        w[k] = (uint32_t)to_bf16_bits(v[2 * k]) | ((uint32_t)to_bf16_bits(v[2 * k + 1]) << 16);
+    *reinterpret_cast<u32x4 *>(p) = w;
+}
+__device__ __forceinline__ void store8(float *p, const float *v) {
+    *reinterpret_cast<float4 *>(p) = *reinterpret_cast<const float4 *>(v);
+    *reinterpret_cast<float4 *>(p + 4) = *reinterpret_cast<const float4 *>(v + 4);
+}
+
 // Workgroup barrier for the k-loop.  __syncthreads() carries a release
 // fence whose lowering waits for every outstanding vector-memory operation,
 // LDS-DMA loads of later stages included, which would drain the prefetch
@@ -229,7 +260,8 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int MINB, int EPI, bool SYM>
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int MINB, int EPI, bool SYM,
+          bool QT>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -242,6 +274,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     constexpr int PI = BM / RPI / NW, QI = BN / RPI / NW;  // DMA instructions per wave per operand
     constexpr int DPT = PI + QI;                    // per wave per k-tile
     static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile / wave count");
+    // QT: the Q operand is stored K x N (row k holds Q[.][k] for all n, n
+    // contiguous), as X is for X = aX + BX.  Its k-tile is KK rows of BN
+    // elements in LDS; fragments are read with the transposing LDS load.
+    constexpr int KK = ROWB / (int)sizeof(T);       // k per k-tile
+    constexpr int QRB = BN * (int)sizeof(T);        // bytes of one LDS row of a QT tile
+    constexpr int QCPR = QRB / 16, QRPI = 64 / QCPR;
+    static_assert(!QT || (sizeof(T) == 2 && KK * QRB == BN * ROWB && KK % (QRPI * NW) == 0 && KK / QRPI / NW == QI),
+                  "QT layout: bf16, same stage size and DMA count as the NT layout");
     static_assert(FM >= 1 && FN >= 1 && NSTAGE >= 2 && NSTAGE <= 5, "config");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -260,9 +300,26 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     else band_coords(t, I.tiles_m, I.tiles_n, bi, bj);
 
     const char *Pg = reinterpret_cast<const char *>(I.P + (int64_t)bi * BM * I.ldp);
-    const char *Qg = reinterpret_cast<const char *>(I.Q + (int64_t)bj * BN * I.ldq);
+    const char *Qg = reinterpret_cast<const char *>(QT ? I.Q + (int64_t)bj * BN : I.Q + (int64_t)bj * BN * I.ldq);
     const int64_t ldpb = I.ldp * (int64_t)sizeof(T), ldqb = I.ldq * (int64_t)sizeof(T);
     const int lrw = lane / CPR, lch = lane % CPR;
+
+    // One DMA instruction of the Q operand's k-tile kt (i < QI) into the
+    // stage at base.  QT: QRPI rows of QRB bytes; the 16-byte chunk c of LDS
+    // row k sits at position c ^ 4 (k % 4), so the transposing fragment
+    // reads (4 rows x 64 bytes per half-wave) cover all 64 banks.
+    auto dma_q = [&](int kt, char *base, int i) {
+        if constexpr (QT) {
+            const int r0 = (wave + i * NW) * QRPI;
+            const int row = r0 + lane / QCPR, pos = lane % QCPR;
+            lds_dma16(Qg + ((int64_t)kt * KK + row) * ldqb + ((pos ^ (4 * (row & 3))) << 4), base + BM * ROWB + r0 * QRB);
+        } else {
+            const int r0 = (wave + i * NW) * RPI;
+            const int row = r0 + lrw;
+            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
+                      base + (BM + r0) * ROWB);
+        }
+    };
 
     // Direct loads: one instruction moves RPI tile rows (1 KiB) into LDS;
     // lane l lands at row r0 + l / CPR, position l % CPR, so it fetches global
@@ -279,12 +336,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
             lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4), base + r0 * ROWB);
         }
 #pragma unroll
-        for (int i = 0; i < QI; i++) {
-            const int r0 = (wave + i * NW) * RPI;
-            const int row = r0 + lrw;
-            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
-                      base + (BM + r0) * ROWB);
-        }
+        for (int i = 0; i < QI; i++) dma_q(kt, base, i);
     };
 
     f32x16 acc[FM][FN];
@@ -297,6 +349,26 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 
     const int KT = I.k_tiles;
     const int lrow = lane & 31, lhalf = lane >> 5;
+    // QT reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: if lane s
+    // of a group points at 4 consecutive elements, lane t receives element
+    // t % 4 of lanes t / 4, t / 4 + 4, t / 4 + 8, t / 4 + 12.  With lane s
+    // pointing at row k0 + s / 4, column n0 + 4 (s % 4), lane t gets column
+    // n0 + t of rows k0 .. k0 + 3.  read_qt4 gives lane l column
+    // nb + 16 ((l / 16) % 2) + l % 16 at rows k0 .. k0+3 (k0 uniform per
+    // group); read_qt8 the 8 rows k0 .. k0+7 as one MFMA fragment.
+    auto read_qt4 = [&](const char *cq, int k0, int nb) -> uint2 {
+        const int s16 = lane & 15;
+        const int row = k0 + (s16 >> 2);
+        const int cb = (nb + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
+        const char *p = cq + row * QRB + ((((cb >> 4) ^ (4 * (row & 3)))) << 4) + (cb & 15);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p));
+        return __builtin_bit_cast(uint2, v);
+    };
+    auto read_qt8 = [&](const char *cq, int k0, int nb) -> u32x4 {
+        const uint2 lo = read_qt4(cq, k0, nb), hi = read_qt4(cq, k0 + 4, nb);
+        return u32x4{lo.x, lo.y, hi.x, hi.y};
+    };
     auto read_frags = [&](const char *cp, int s, u32x4 *a, u32x4 *b) {
         const char *cq = cp + BM * ROWB;
         const int ch = 2 * s + lhalf;
@@ -307,8 +379,12 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         }
 #pragma unroll
         for (int j = 0; j < FN; j++) {
-            const int row = wn * WN + j * 32 + lrow;
-            b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+            if constexpr (QT) {
+                b[j] = read_qt8(cq, 16 * s + 8 * (lane >> 5), wn * WN + j * 32);
+            } else {
+                const int row = wn * WN + j * 32 + lrow;
+                b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+            }
         }
     };
     // Software pipeline.  NSTAGE LDS stages: tiles kt+1 .. kt+NSTAGE-1 are in
@@ -330,10 +406,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
                 lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
                           base + r0 * ROWB);
             } else {
-                const int r0 = (wave + (d - PI) * NW) * RPI;
-                const int row = r0 + lrw;
-                lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
-                          base + (BM + r0) * ROWB);
+                dma_q(kt, base, d - PI);
             }
         }
     };
@@ -343,8 +416,64 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
     kloop_barrier();
     read_frags(smem, 0, fa[0], fb[0]);
+    // D gathered from the Q operand.  For X = aX + BX (Q = X^T) and for
+    // B = bA + cA^2 (Q = A, symmetric), D's tile (bi, bj) equals the Q panel
+    // bj at k in [bi BM, bi BM + BM): element (row R, column C) of the tile
+    // is Q row bj BN + C at k = bi BM + R.  While such a k-tile is in LDS,
+    // the waves owning rows R add dgain * D to their accumulators: four
+    // consecutive rows of one column are four consecutive k, one 8-byte
+    // (bf16) or 16-byte (fp32) LDS read.  No D is read from memory.
+    static_assert(32 % KK == 0 || KK % 32 == 0, "k-tile vs sub-tile rows");
+    const bool dloop = EPI != EPI_GRAM && args.dloop;
+    auto gather_d = [&](const char *cp, int kt) {
+        const char *cq = cp + BM * ROWB;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int64_t rb = (int64_t)bi * BM + wm * WM + i * 32;  // first k of sub-tile i
+            if (rb / KK != kt) continue;
+            const int kk0 = (int)(rb % KK) + 4 * lhalf;
+            if constexpr (QT) {
+                // rows kk0 + 8 g .. +3 of column lrow: one transposing read
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int g = 0; g < 4; g++) {
+                        const uint2 w = read_qt4(cq, (int)(rb % KK) + 8 * g + 4 * lhalf, wn * WN + j * 32);
+                        const float d[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+#pragma unroll
+                        for (int q = 0; q < 4; q++) acc[i][j][4 * g + q] += args.dgain * d[q];
+                    }
+                continue;
+            }
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+                const int row = wn * WN + j * 32 + lrow;
+                const char *qr = cq + row * ROWB;
+                const int sw = (row / SWD) % CPR;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int ob = (kk0 + 8 * g) * (int)sizeof(T);
+                    const char *src = qr + (((ob >> 4) ^ sw) << 4) + (ob & 15);
+                    float d[4];
+                    if constexpr (sizeof(T) == 2) {
+                        const uint2 w = *reinterpret_cast<const uint2 *>(src);
+                        d[0] = __uint_as_float(w.x << 16);
+                        d[1] = __uint_as_float(w.x & 0xffff0000u);
+                        d[2] = __uint_as_float(w.y << 16);
+                        d[3] = __uint_as_float(w.y & 0xffff0000u);
+                    } else {
+                        *reinterpret_cast<float4 *>(d) = *reinterpret_cast<const float4 *>(src);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; q++) acc[i][j][4 * g + q] += args.dgain * d[q];
+                }
+            }
+        }
+    };
     for (int kt = 0; kt < KT; kt++) {
         const char *cp = smem + (kt % NSTAGE) * STAGE;
+        if (dloop) gather_d(cp, kt);
         const int nk = kt + NSTAGE - 1;
         const bool more = nk < KT;
         const int nstage = nk % NSTAGE;
@@ -364,54 +493,116 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     }
 
     // ---------------------------------------------------------- epilogue
-    // acc[i][j][r] holds C[row][col] with row = 8(r/4) + 4 lhalf + r%4 and
-    // col = lrow inside the 32x32 MFMA tile.  In the transposed layouts
-    // (mirror tile, X^T) the four rows r%4 = 0..3 are adjacent, so each lane
-    // writes them with one vector store.  The empty asm between sub-tiles
-    // keeps the compiler from hoisting every load of the epilogue at once.
-    const bool mirror = SYM && bi != bj;
+    // The output tile leaves through LDS, ER rows per pass, so that every
+    // global access is a 16-byte segment of a row:
+    //  1. the waves owning the pass's rows write their fp32 accumulators to
+    //     a padded LDS tile (acc[i][j][r] is row 8(r/4) + 4 lhalf + r%4,
+    //     column lrow of its 32x32 MFMA tile);
+    //  2. row phase: each thread takes 8 consecutive columns of one row,
+    //     forms the epilogue value (loading D there unless the k-loop has
+    //     gathered it), rounds it to T, stores the segment of C and writes
+    //     the rounded value back in place;
+    //  3. column phase (the fp32 runs' X^T copy, or the mirror tile of a
+    //     symmetric product): each thread takes 8 consecutive rows of one column and
+    //     stores them as a segment of the transposed target; the lanes of a
+    //     wave read consecutive columns of one LDS row per instruction.
+    // The loop's last barrier has passed, so every stage buffer is free.
+    constexpr int ER = 64;           // tile rows per pass
+    constexpr int EP = BN + 8;       // fp32 pitch; 4 EP = 32 mod 64 banks separates the two half-waves
+    constexpr int NTH = NW * 64;
+    constexpr int RIT = ER * (BN / 8) / NTH;   // row-phase items per thread
+    constexpr int CIT = BN * (ER / 8) / NTH;   // column-phase items per thread
+    static_assert(WM % ER == 0 && ER % 32 == 0 && BM % ER == 0, "epilogue pass rows");
+    static_assert((size_t)ER * EP * 4 <= (size_t)NSTAGE * STAGE, "epilogue tile must fit the stage buffers");
+    static_assert(RIT * NTH == ER * (BN / 8) && CIT * NTH == BN * (ER / 8), "epilogue work split");
+    float *et = reinterpret_cast<float *>(smem);
+    T *tgt = nullptr;                // transposed target
+    int64_t ldt = 0;
+    if constexpr (EPI == EPI_UPDATE) {
+        tgt = I.CT;
+        ldt = I.ldct;
+    } else if (SYM && bi != bj) {
+        tgt = I.C;
+        ldt = I.ldc;
+    }
+    const int64_t R0 = (int64_t)bi * BM, C0 = (int64_t)bj * BN;
+    const float sc = EPI == EPI_POLY ? args.beta : 1.0f;
+    // bf16: the D segments of every pass are loaded up front (16 bytes per
+    // item, BM / ER * RIT registers of 4 dwords), so their latency is paid
+    // once per tile instead of once per pass.
+    constexpr bool DPRE = EPI != EPI_GRAM && sizeof(T) == 2;
+    u32x4 dpre[DPRE ? BM / ER : 1][DPRE ? RIT : 1];
+    if (DPRE && !dloop) {
 #pragma unroll
-    for (int i = 0; i < FM; i++)
+        for (int p = 0; p < BM / ER; p++)
 #pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int64_t r0 = (int64_t)bi * BM + wm * WM + i * 32 + 4 * lhalf;
-            const int64_t c0 = (int64_t)bj * BN + wn * WN + j * 32 + lrow;
+            for (int it = 0; it < RIT; it++) {
+                const int idx = tid + it * NTH;
+                const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+                dpre[p][it] = *reinterpret_cast<const u32x4 *>(I.D + (R0 + p * ER + r) * I.ldd + C0 + c);
+            }
+    }
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int64_t gr = r0 + 8 * g;   // rows gr .. gr+3, column c0
-                float v[4];
+    for (int p = 0; p < BM / ER; p++) {
+        const int pw = p * ER / WM;            // owning wave row
+        const int i0 = (p * ER % WM) / 32;     // its first sub-tile in this pass
+        if (wm == pw) {
 #pragma unroll
-                for (int q = 0; q < 4; q++) v[q] = acc[i][j][4 * g + q];
-                if constexpr (EPI != EPI_GRAM) {
-                    const float sc = EPI == EPI_POLY ? args.beta : 1.0f;
+            for (int ii = 0; ii < ER / 32; ii++)
 #pragma unroll
-                    for (int q = 0; q < 4; q++) v[q] = args.alpha * to_float(I.D[(gr + q) * I.ldd + c0]) + sc * v[q];
-                }
-                T o[4];
+                for (int j = 0; j < FN; j++)
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    o[q] = from_float<T>(v[q]);
-                    I.C[(gr + q) * I.ldc + c0] = o[q];
-                }
-                T *tp = nullptr;
-                if constexpr (EPI == EPI_UPDATE) {
-                    if (I.CT) tp = I.CT + c0 * I.ldct + gr;
-                } else if (mirror) {
-                    tp = I.C + c0 * I.ldc + gr;
-                }
-                if (tp) {
-                    if constexpr (sizeof(T) == 2) {
-                        uint2 pk;
-                        pk.x = (uint32_t)o[0].bits | ((uint32_t)o[1].bits << 16);
-                        pk.y = (uint32_t)o[2].bits | ((uint32_t)o[3].bits << 16);
-                        *reinterpret_cast<uint2 *>(tp) = pk;
-                    } else {
-                        *reinterpret_cast<float4 *>(tp) = make_float4(v[0], v[1], v[2], v[3]);
+                    for (int r = 0; r < 16; r++) {
+                        const int row = ii * 32 + 8 * (r / 4) + 4 * lhalf + (r % 4);
+                        et[row * EP + wn * WN + j * 32 + lrow] = acc[i0 + ii][j][r];
                     }
+        }
+        kloop_barrier();
+        const int64_t pr = R0 + p * ER;
+#pragma unroll
+        for (int it = 0; it < RIT; it++) {
+            const int idx = tid + it * NTH;
+            const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+            float *e = et + r * EP + c;
+            float v[8];
+            *reinterpret_cast<float4 *>(v) = *reinterpret_cast<const float4 *>(e);
+            *reinterpret_cast<float4 *>(v + 4) = *reinterpret_cast<const float4 *>(e + 4);
+            if constexpr (EPI != EPI_GRAM) {
+                if (dloop) {
+#pragma unroll
+                    for (int k = 0; k < 8; k++) v[k] = sc * v[k];
+                } else {
+                    float d[8];
+                    if constexpr (DPRE)
+                        unpack8(dpre[p][it], d);
+                    else
+                        load8(I.D + (pr + r) * I.ldd + C0 + c, d);
+#pragma unroll
+                    for (int k = 0; k < 8; k++) v[k] = args.alpha * d[k] + sc * v[k];
                 }
             }
-            asm volatile("" ::: "memory");
+            store8(I.C + (pr + r) * I.ldc + C0 + c, v);
+            if (tgt) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) v[k] = to_float(from_float<T>(v[k]));
+                *reinterpret_cast<float4 *>(e) = *reinterpret_cast<const float4 *>(v);
+                *reinterpret_cast<float4 *>(e + 4) = *reinterpret_cast<const float4 *>(v + 4);
+            }
         }
+        if (tgt) {
+            kloop_barrier();
+#pragma unroll
+            for (int it = 0; it < CIT; it++) {
+                const int idx = tid + it * NTH;
+                const int c = idx % BN, r = (idx / BN) * 8;
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) v[k] = et[(r + k) * EP + c];
+                store8(tgt + (C0 + c) * ldt + pr + r, v);
+            }
+        }
+        kloop_barrier();
+    }
 }
 
 // ------------------------------------------------------- norm + prologue
@@ -501,7 +692,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     for (int idx = threadIdx.x; idx < 4096; idx += 256) {
         const int ii = idx >> 6, jj = idx & 63;
         X[(i0 + ii) * it.ldx + j0 + jj] = from_float<T>(tile[ii][jj]);
-        XT[(j0 + ii) * it.ldxt + i0 + jj] = from_float<T>(tile[jj][ii]);
+        if (XT) XT[(j0 + ii) * it.ldxt + i0 + jj] = from_float<T>(tile[jj][ii]);
     }
 }
 
@@ -581,7 +772,9 @@ Geometry geometry(int64_t rows, int64_t cols, size_t esz) {
     g.x_bytes = align_up(g.mp * g.ldn * (int64_t)esz, 256);
     g.xt_bytes = align_up(g.np * g.ldm * (int64_t)esz, 256);
     g.a_bytes = align_up(g.mp * g.ldm * (int64_t)esz, 256);
-    g.item_bytes = g.x_bytes + 2 * g.xt_bytes + 2 * g.a_bytes;
+    // bf16 runs keep two X buffers (the product X = aX + BX reads X in its
+    // K x N layout and writes the other); fp32 runs keep X and two X^T.
+    g.item_bytes = esz == 2 ? 2 * g.x_bytes + 2 * g.a_bytes : g.x_bytes + 2 * g.xt_bytes + 2 * g.a_bytes;
     return g;
 }
 
@@ -631,11 +824,11 @@ struct CfgRect {
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
 };
 
-template <typename T, typename C, int EPI, bool SYM>
+template <typename T, typename C, int EPI, bool SYM, bool QT = false>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
     constexpr size_t lds = (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
-    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::MINB, EPI, SYM>;
+    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::MINB, EPI, SYM, QT>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -650,24 +843,33 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     return QM_OK;
 }
 
+// bf16: X[0], X[1] ping-pong (X = aX + BX reads X in its K x N layout);
+// fp32: X[0] updated in place, X^T in XT[0], XT[1] ping-pong.
 struct ItemBufs {
     Geometry g;
-    char *X, *XT0, *XT1, *A, *B;
+    char *X[2] = {nullptr, nullptr};
+    char *XT[2] = {nullptr, nullptr};
+    char *A = nullptr, *B = nullptr;
 };
 
 template <typename T>
 qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int steps, float a,
                     float b, float c, float eps, void *ws, hipStream_t stream) {
     const int nit = (int)chunk.size();
+    constexpr bool kQT = sizeof(T) == 2;   // bf16: transposing reads, no X^T copy
     std::vector<ItemBufs> bufs(nit);
     char *p = static_cast<char *>(ws);
     for (int i = 0; i < nit; i++) {
         const NsRequest &r = req[chunk[i]];
         ItemBufs &B = bufs[i];
         B.g = geometry(r.rows, r.cols, sizeof(T));
-        B.X = p;   p += B.g.x_bytes;
-        B.XT0 = p; p += B.g.xt_bytes;
-        B.XT1 = p; p += B.g.xt_bytes;
+        B.X[0] = p; p += B.g.x_bytes;
+        if constexpr (kQT) {
+            B.X[1] = p; p += B.g.x_bytes;
+        } else {
+            B.XT[0] = p; p += B.g.xt_bytes;
+            B.XT[1] = p; p += B.g.xt_bytes;
+        }
         B.A = p;   p += B.g.a_bytes;
         B.B = p;   p += B.g.a_bytes;
     }
@@ -689,8 +891,8 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         it.dtype = r.dtype;
         it.tall = r.rows > r.cols ? 1 : 0;
         it.inv = r.inv;
-        it.X = bufs[i].X;
-        it.XT = bufs[i].XT0;
+        it.X = bufs[i].X[0];
+        it.XT = bufs[i].XT[0];   // null for bf16
         it.m = (int32_t)g.m;
         it.n = (int32_t)g.n;
         it.mp = g.mp;
@@ -733,7 +935,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     std::stable_sort(by_m.begin(), by_m.end(), [&](int x, int y) {
         return bufs[x].g.mp * bufs[x].g.np > bufs[y].g.mp * bufs[y].g.np;
     });
-    std::vector<int> cur(nit, 0);  // which XT buffer holds X^T for each item
+    std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
     for (int s = 0; s < steps; s++) {
         // A = X X^T
         GemmArgs<T> g1{};
@@ -743,8 +945,9 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
             const ItemBufs &B = bufs[by_n[k]];
             const int tm = (int)(B.g.mp / CfgSym::BM);
             GItem<T> &I = g1.it[k];
-            I.P = reinterpret_cast<const T *>(B.X); I.ldp = B.g.ldn;
-            I.Q = reinterpret_cast<const T *>(B.X); I.ldq = B.g.ldn;
+            const char *X = kQT ? B.X[cur[by_n[k]]] : B.X[0];
+            I.P = reinterpret_cast<const T *>(X); I.ldp = B.g.ldn;
+            I.Q = reinterpret_cast<const T *>(X); I.ldq = B.g.ldn;
             I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.ldm;
             I.tiles_m = tm;
             I.tiles_n = tm;
@@ -759,6 +962,8 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         g2.n_items = nit;
         g2.alpha = b;
         g2.beta = c;
+        g2.dloop = c != 0.0f;
+        g2.dgain = c != 0.0f ? b / c : 0.0f;
         tl = 0;
         for (int k = 0; k < nit; k++) {
             const ItemBufs &B = bufs[by_m[k]];
@@ -776,10 +981,13 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         }
         st = launch_gemm<T, CfgSym, EPI_POLY, true>(g2, tl, stream);
         if (st != QM_OK) return st;
-        // X = a X + B X   (Q operand = X^T)
+        // X = a X + B X: bf16 reads Q = X (K x N) and writes the other X
+        // buffer; fp32 reads Q = X^T and updates X in place, writing X^T.
         GemmArgs<T> g3{};
         g3.n_items = nit;
         g3.alpha = a;
+        g3.dloop = 1;
+        g3.dgain = a;
         tl = 0;
         for (int k = 0; k < nit; k++) {
             const int i = by_m[k];
@@ -787,10 +995,16 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
             const int tm = (int)(B.g.mp / CfgRect::BM), tn = (int)(B.g.np / CfgRect::BN);
             GItem<T> &I = g3.it[k];
             I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.ldm;
-            I.Q = reinterpret_cast<const T *>(cur[i] ? B.XT1 : B.XT0); I.ldq = B.g.ldm;
-            I.C = reinterpret_cast<T *>(B.X); I.ldc = B.g.ldn;
-            I.CT = reinterpret_cast<T *>(cur[i] ? B.XT0 : B.XT1); I.ldct = B.g.ldm;
-            I.D = reinterpret_cast<const T *>(B.X); I.ldd = B.g.ldn;
+            if constexpr (kQT) {
+                I.Q = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldq = B.g.ldn;
+                I.C = reinterpret_cast<T *>(B.X[cur[i] ^ 1]); I.ldc = B.g.ldn;
+                I.D = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldd = B.g.ldn;
+            } else {
+                I.Q = reinterpret_cast<const T *>(B.XT[cur[i]]); I.ldq = B.g.ldm;
+                I.C = reinterpret_cast<T *>(B.X[0]); I.ldc = B.g.ldn;
+                I.CT = reinterpret_cast<T *>(B.XT[cur[i] ^ 1]); I.ldct = B.g.ldm;
+                I.D = reinterpret_cast<const T *>(B.X[0]); I.ldd = B.g.ldn;
+            }
             I.tiles_m = tm;
             I.tiles_n = tn;
             I.tile_begin = tl;
@@ -798,10 +1012,12 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
             tl += tm * tn;
             if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
         }
-        st = launch_gemm<T, CfgRect, EPI_UPDATE, false>(g3, tl, stream);
+        st = launch_gemm<T, CfgRect, EPI_UPDATE, false, kQT>(g3, tl, stream);
         if (st != QM_OK) return st;
         for (int i = 0; i < nit; i++) cur[i] ^= 1;
     }
+    if constexpr (kQT)
+        for (int i = 0; i < nit; i++) pa.it[i].X = bufs[i].X[cur[i]];
     {
         Timed tm(stream, QM_K_NS_WRITEBACK);
         writeback_kernel<T><<<tiles, 256, 0, stream>>>(pa, wb);
