@@ -52,6 +52,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr int kPad = 256;       // internal dims are multiples of this
 constexpr int kMaxItems = 8;    // matrices per launch chain
@@ -251,6 +252,13 @@ __device__ __forceinline__ void kloop_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0) with x as an in/out operand: code using x cannot be
+// scheduled above the wait (for results of LDS reads issued as assembly).
+template <typename V>
+__device__ __forceinline__ void lds_wait(V &x) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x));
+}
+
 // s_waitcnt vmcnt(n) with n a multiple of D chosen at run time (0..3 D).
 template <int D>
 __device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
@@ -356,17 +364,26 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     // n0 + t of rows k0 .. k0 + 3.  read_qt4 gives lane l column
     // nb + 16 ((l / 16) % 2) + l % 16 at rows k0 .. k0+3 (k0 uniform per
     // group); read_qt8 the 8 rows k0 .. k0+7 as one MFMA fragment.
-    auto read_qt4 = [&](const char *cq, int k0, int nb) -> uint2 {
+    //
+    // The read is issued as inline assembly.  Through the builtin, the
+    // compiler cannot tell it from a read of the stage an LDS-DMA load is
+    // filling and puts s_waitcnt vmcnt(0) in front of it, which drains every
+    // prefetched tile.  The stage protocol of the k-loop (explicit vmcnt
+    // waits and barriers) already orders DMA and reads; the compiler does
+    // not see these reads in its lgkmcnt accounting, so their results are
+    // waited for with lds_wait below before first use.
+    auto read_qt4 = [&](const char *cq, int k0, int nb) -> u32x2 {
         const int s16 = lane & 15;
         const int row = k0 + (s16 >> 2);
         const int cb = (nb + 16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) * 2;
         const char *p = cq + row * QRB + ((((cb >> 4) ^ (4 * (row & 3)))) << 4) + (cb & 15);
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p));
-        return __builtin_bit_cast(uint2, v);
+        const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+        u32x2 r;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+        return r;
     };
     auto read_qt8 = [&](const char *cq, int k0, int nb) -> u32x4 {
-        const uint2 lo = read_qt4(cq, k0, nb), hi = read_qt4(cq, k0 + 4, nb);
+        const u32x2 lo = read_qt4(cq, k0, nb), hi = read_qt4(cq, k0 + 4, nb);
         return u32x4{lo.x, lo.y, hi.x, hi.y};
     };
     auto read_frags = [&](const char *cp, int s, u32x4 *a, u32x4 *b) {
@@ -438,7 +455,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
                 for (int j = 0; j < FN; j++)
 #pragma unroll
                     for (int g = 0; g < 4; g++) {
-                        const uint2 w = read_qt4(cq, (int)(rb % KK) + 8 * g + 4 * lhalf, wn * WN + j * 32);
+                        u32x2 w = read_qt4(cq, (int)(rb % KK) + 8 * g + 4 * lhalf, wn * WN + j * 32);
+                        lds_wait(w);
                         const float d[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                                             __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
 #pragma unroll
@@ -479,6 +497,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         const int nstage = nk % NSTAGE;
 #pragma unroll
         for (int s = 0; s < STEPS; s++) {
+            // QT: fragments of this step came from assembly reads issued a
+            // step earlier; complete them (tied to the registers, so the
+            // MFMAs below cannot move above the wait)
+            if constexpr (QT) {
+#pragma unroll
+                for (int j = 0; j < FN; j++) lds_wait(fb[s & 1][j]);
+            }
             if (s + 1 < STEPS) read_frags(cp, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
             if (more) issue_part(nk, nstage, s);
 #pragma unroll
