@@ -50,7 +50,7 @@ const PlanHeader *plan_header(const void *host_blob, qm_status *st) {
 namespace {
 
 struct Layout {
-    int64_t off_tensors, off_task, off_bg, off_ro, off_runs, off_co, off_cg, total;
+    int64_t off_tensors, off_task, off_bg, off_ro, off_runs, off_co, off_cg, off_tt, total;
 };
 
 Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr, int64_t nc) {
@@ -63,6 +63,7 @@ Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr, int64_t nc) {
     L.off_runs = o;     o = align_up(o + nr * (int64_t)sizeof(PlanRun), 64);
     L.off_co = o;       o = align_up(o + (int64_t)(ng + 1) * 8, 64);
     L.off_cg = o;       o = align_up(o + nc * 4, 64);
+    L.off_tt = o;       o = align_up(o + (int64_t)nt * 4, 64);
     L.total = o;
     return L;
 }
@@ -176,9 +177,18 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     PlanRun *runs = reinterpret_cast<PlanRun *>(base + L.off_runs);
     int64_t *co = reinterpret_cast<int64_t *>(base + L.off_co);
     int32_t *cg = reinterpret_cast<int32_t *>(base + L.off_cg);
+    int32_t *tt = reinterpret_cast<int32_t *>(base + L.off_tt);
 
+    // Task order: tensors grouped by grad dtype (stable), so that each
+    // dtype's tasks form one range; the tensor table keeps the caller's order.
+    std::vector<int32_t> order(n_tensors);
+    for (int32_t i = 0; i < n_tensors; i++) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return tensors[x].grad_dtype < tensors[y].grad_dtype; });
+    for (int d = 0; d < 3; d++) h->dt_task_lo[d] = h->dt_task_hi[d] = 0;
     int64_t toff = 0;
-    for (int32_t i = 0; i < n_tensors; i++) {
+    for (int32_t k = 0; k < n_tensors; k++) {
+        const int32_t i = order[k];
         const qm_q8_tensor &t = tensors[i];
         const int64_t nb = nblocks(t.numel);
         pt[i].codes = (uint64_t)(uintptr_t)t.codes;
@@ -195,8 +205,12 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
         }
         pt[i].group_lo = lo;
         pt[i].group_hi = hi;
-        task[i] = toff;
+        task[k] = toff;
+        tt[k] = i;
+        const int d = t.grad_dtype;
+        if (h->dt_task_hi[d] == 0) h->dt_task_lo[d] = toff;
         toff += (nb + kBlocksPerTask - 1) / kBlocksPerTask;
+        h->dt_task_hi[d] = toff;
     }
     task[n_tensors] = toff;
     memcpy(pbg, bg.data(), (size_t)nb_total * 4);
@@ -227,6 +241,7 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     h->off_runs = L.off_runs;
     h->off_chunk_offsets = L.off_co;
     h->off_chunk_group = L.off_cg;
+    h->off_task_tensor = L.off_tt;
     h->total_bytes = L.total;
     *inout_blob_bytes = (size_t)L.total;
     return QM_OK;

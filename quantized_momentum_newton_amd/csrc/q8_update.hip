@@ -143,7 +143,8 @@ template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int6
     }
 }
 
-// Largest i with task_offsets[i] <= task (every tensor owns >= 1 task).
+// Largest i with task_offsets[i] <= task (every tensor owns >= 1 task): the
+// position of the task's tensor in task order.
 __device__ __forceinline__ int find_tensor(const int64_t *task_offsets, int n, int64_t task) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
@@ -243,24 +244,26 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
     }
 }
 
-template <bool SUMS>
-__global__ __launch_bounds__(kThreads) void q8_update_kernel(const PlanTensor *__restrict__ tensors,
-                                                             const int64_t *__restrict__ task_offsets,
-                                                             int n_tensors, int64_t n_tasks, float beta,
-                                                             double *__restrict__ block_sums) {
+// One launch per grad dtype present, over that dtype's task range (the plan
+// orders the task space by dtype), so each kernel carries one element path.
+// The update is bound by how many bytes are in flight per CU: specialised,
+// the 16-bit paths fit 8 waves per SIMD in 64 VGPRs and the fp32 path 6
+// waves in 80, without spills (the kernel with all three element paths took
+// 112 VGPRs, i.e. 4 waves).
+template <int DT> constexpr int update_wgs_per_cu() { return DT == QM_F32 ? 6 : 8; }
+
+template <int DT, bool SUMS>
+__global__ __launch_bounds__(kThreads, update_wgs_per_cu<DT>()) void q8_update_kernel(
+    const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
+    const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
+    double *__restrict__ block_sums) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
-    for (int64_t task = (int64_t)blockIdx.x * kWavesPerWG + wave; task < n_tasks; task += stride) {
-        const int ti = find_tensor(task_offsets, n_tensors, task);
-        const PlanTensor T = tensors[ti];
-        const int64_t lt = task - T.task_offset;
-        switch (T.dtype) {
-            case QM_F32: update_task<QM_F32, SUMS>(T, lt, beta, omb, block_sums, lane); break;
-            case QM_BF16: update_task<QM_BF16, SUMS>(T, lt, beta, omb, block_sums, lane); break;
-            default: update_task<QM_F16, SUMS>(T, lt, beta, omb, block_sums, lane); break;
-        }
+    for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
+        const PlanTensor T = tensors[task_tensor[find_tensor(task_offsets, n_tensors, task)]];
+        update_task<DT, SUMS>(T, task - T.task_offset, beta, omb, block_sums, lane);
     }
 }
 
@@ -341,6 +344,7 @@ __device__ __forceinline__ void scale_task(const PlanTensor &T, int64_t lt, cons
 
 __global__ __launch_bounds__(kThreads) void q8_scale_kernel(const PlanTensor *__restrict__ tensors,
                                                             const int64_t *__restrict__ task_offsets,
+                                                            const int32_t *__restrict__ task_tensor,
                                                             int n_tensors, int64_t n_tasks,
                                                             const int32_t *__restrict__ block_group,
                                                             const float *__restrict__ inv) {
@@ -348,8 +352,7 @@ __global__ __launch_bounds__(kThreads) void q8_scale_kernel(const PlanTensor *__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
     for (int64_t task = (int64_t)blockIdx.x * kWavesPerWG + wave; task < n_tasks; task += stride) {
-        const int ti = find_tensor(task_offsets, n_tensors, task);
-        const PlanTensor T = tensors[ti];
+        const PlanTensor T = tensors[task_tensor[find_tensor(task_offsets, n_tensors, task)]];
         const int64_t lt = task - T.task_offset;
         switch (T.dtype) {
             case QM_F32: scale_task<QM_F32>(T, lt, block_group, inv, lane); break;
@@ -391,18 +394,28 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
     return QM_OK;
 }
 
-qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                        hipStream_t stream) {
+template <int DT>
+void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, hipStream_t stream) {
+    const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
+    if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
     const int64_t *toff = section<int64_t>(dev_plan, h->off_task_offsets);
-    const int grid = stream_grid(h->n_tasks);
-    Timed tm(stream, QM_K_Q8_UPDATE);
+    const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
+    const int grid = stream_grid(hi - lo);
     if (block_sums)
-        q8_update_kernel<true><<<grid, kThreads, 0, stream>>>(tens, toff, h->n_tensors, h->n_tasks, beta,
-                                                             block_sums);
+        q8_update_kernel<DT, true><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
+                                                                 block_sums);
     else
-        q8_update_kernel<false><<<grid, kThreads, 0, stream>>>(tens, toff, h->n_tensors, h->n_tasks, beta,
-                                                              nullptr);
+        q8_update_kernel<DT, false><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
+                                                                  nullptr);
+}
+
+qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
+                        hipStream_t stream) {
+    Timed tm(stream, QM_K_Q8_UPDATE);
+    launch_update_dt<QM_F32>(h, dev_plan, beta, block_sums, stream);
+    launch_update_dt<QM_BF16>(h, dev_plan, beta, block_sums, stream);
+    launch_update_dt<QM_F16>(h, dev_plan, beta, block_sums, stream);
     return check_launch("q8 update");
 }
 
@@ -425,7 +438,8 @@ qm_status launch_scale(const PlanHeader *h, const void *dev_plan, const float *i
     Timed tm(stream, QM_K_Q8_SCALE);
     q8_scale_kernel<<<stream_grid(h->n_tasks), kThreads, 0, stream>>>(
         section<PlanTensor>(dev_plan, h->off_tensors), section<int64_t>(dev_plan, h->off_task_offsets),
-        h->n_tensors, h->n_tasks, section<int32_t>(dev_plan, h->off_block_group), inv);
+        section<int32_t>(dev_plan, h->off_task_tensor), h->n_tensors, h->n_tasks,
+        section<int32_t>(dev_plan, h->off_block_group), inv);
     return check_launch("group scale");
 }
 
