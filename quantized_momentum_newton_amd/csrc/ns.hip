@@ -129,6 +129,7 @@ struct FinalOut {
     int32_t dtype, tall;
     int32_t m, n;          // valid extent in iteration orientation
     float lr_s, lr_wd;     // lr * s and lr * weight_decay
+    int32_t vec_out, vec_w;  // out / w rows start 16-byte aligned (8-element segments move as vectors)
 };
 
 // One matrix of a grouped product (element strides).
@@ -644,6 +645,7 @@ struct NsItem {
     int64_t ldx, ldxt;     // leading dimensions of X (np + pad) and X^T (mp + pad)
     int32_t tiles_n;       // 64-wide tiles per padded row
     int32_t tile_begin;    // first 64x64 tile of this item
+    int32_t vec;           // src rows start 16-byte aligned
 };
 
 struct PrologueArgs {
@@ -688,9 +690,62 @@ __global__ void norm_final_kernel(const double *partials, float eps, float *inv_
     inv_out[item] = (float)(1.0 / (sqrt(s) + (double)eps));
 }
 
-// X0 = orient(src) * inv, written as X (m_p x n_p) and X^T (n_p x m_p),
-// zero outside the valid extent.  One 64x64 tile per workgroup, transposed
-// through LDS so that source reads and both writes are row-contiguous.
+// Eight consecutive elements of a caller matrix at element index e, as
+// fp32: n of them valid (0..8), zero beyond.  vec: the segment starts
+// 16-byte aligned, so a full one moves with 16-byte accesses.
+__device__ __forceinline__ void load_seg(const void *p, int64_t e, int dtype, int n, bool vec, float *v) {
+    if (vec && n == 8) {
+        if (dtype == QM_F32) {
+            load8(static_cast<const float *>(p) + e, v);
+        } else {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p) + e);
+            if (dtype == QM_BF16) {
+                unpack8(w, v);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    v[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xffffu));
+                    v[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) v[k] = k < n ? load_any(p, e + k, dtype) : 0.0f;
+}
+__device__ __forceinline__ void store_seg(void *p, int64_t e, int dtype, int n, bool vec, const float *v) {
+    if (vec && n == 8) {
+        if (dtype == QM_F32) {
+            store8(static_cast<float *>(p) + e, v);
+        } else if (dtype == QM_BF16) {
+            store8(static_cast<bf16_t *>(p) + e, v);
+        } else {
+            u32x4 w;
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                w[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2 * k + 1]) << 16);
+            *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p) + e) = w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        if (k < n) store_any(p, e + k, dtype, v[k]);
+}
+
+// Valid length (0..8) of the segment at (row, col) of a rows x cols matrix.
+__device__ __forceinline__ int seg_len(int64_t row, int64_t col, int64_t rows, int64_t cols) {
+    if (row >= rows || col >= cols) return 0;
+    return cols - col < 8 ? (int)(cols - col) : 8;
+}
+
+// X0 = orient(src) * inv, written as X (m_p x n_p) and, for fp32 runs, X^T
+// (n_p x m_p), zero outside the valid extent.  One 64x64 tile per workgroup:
+// each thread moves 8-element row segments (16-byte accesses where aligned),
+// reading along the source's contiguous dimension; a tall source is
+// transposed through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     __shared__ float tile[64][65];
@@ -699,32 +754,44 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     const int t = blockIdx.x - it.tile_begin;
     const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
     const float s = it.inv ? it.inv[0] : a.inv_ws[item];
-    for (int idx = threadIdx.x; idx < 4096; idx += 256) {
-        // read along the source's contiguous dimension
-        const int ii = it.tall ? (idx & 63) : (idx >> 6);
-        const int jj = it.tall ? (idx >> 6) : (idx & 63);
-        const int64_t i = i0 + ii, j = j0 + jj;
-        float v = 0.0f;
-        if (i < it.m && j < it.n) {
-            const int64_t src = it.tall ? j * it.ld + i : i * it.ld + j;
-            v = load_any(it.src, src, it.dtype) * s;
+    const int r = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;   // 32 rows x 8 segments per pass
+    // source rows are rows of X, or of X^T when the source is tall
+    const int64_t srows = it.tall ? it.n : it.m, scols = it.tall ? it.m : it.n;
+    const int64_t sr0 = it.tall ? j0 : i0, sc0 = it.tall ? i0 : j0;
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+        const int rr = r + 32 * pass;
+        const int64_t sr = sr0 + rr, sc = sc0 + c8;
+        float v[8];
+        load_seg(it.src, sr * it.ld + sc, it.dtype, seg_len(sr, sc, srows, scols), it.vec, v);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            if (it.tall) tile[c8 + k][rr] = v[k] * s;
+            else tile[rr][c8 + k] = v[k] * s;
         }
-        tile[ii][jj] = v;
     }
     __syncthreads();
     T *X = static_cast<T *>(it.X);
     T *XT = static_cast<T *>(it.XT);
-    for (int idx = threadIdx.x; idx < 4096; idx += 256) {
-        const int ii = idx >> 6, jj = idx & 63;
-        X[(i0 + ii) * it.ldx + j0 + jj] = from_float<T>(tile[ii][jj]);
-        if (XT) XT[(j0 + ii) * it.ldxt + i0 + jj] = from_float<T>(tile[jj][ii]);
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+        const int rr = r + 32 * pass;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = tile[rr][c8 + k];
+        store8(X + (i0 + rr) * it.ldx + j0 + c8, v);
+        if (XT) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) v[k] = tile[c8 + k][rr];
+            store8(XT + (j0 + rr) * it.ldxt + i0 + c8, v);
+        }
     }
 }
 
 // Output of the iteration (X after the last product, or X0 when steps == 0)
 // to the caller's matrix in its orientation and dtype, with the weight
-// update W <- W - (lr s) O - (lr wd) W.  64x64 tiles through LDS so reads
-// of X and writes of O and W are all row-contiguous.
+// update W <- W - (lr s) O - (lr wd) W.  64x64 tiles through LDS; X is read
+// and O and W are written as 8-element row segments.
 struct WritebackArgs {
     FinalOut fo[kMaxItems];
 };
@@ -738,23 +805,35 @@ __global__ __launch_bounds__(256) void writeback_kernel(PrologueArgs a, Writebac
     const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
     const FinalOut &fo = wb.fo[item];
     const T *X = static_cast<const T *>(it.X);
-    for (int idx = threadIdx.x; idx < 4096; idx += 256) {
-        const int ii = idx >> 6, jj = idx & 63;
-        tile[ii][jj] = to_float(X[(i0 + ii) * it.ldx + j0 + jj]);
+    const int r = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+        const int rr = r + 32 * pass;
+        float v[8];
+        load8(X + (i0 + rr) * it.ldx + j0 + c8, v);
+#pragma unroll
+        for (int k = 0; k < 8; k++) tile[rr][c8 + k] = v[k];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 4096; idx += 256) {
-        // walk the caller's contiguous dimension
-        const int ii = fo.tall ? (idx & 63) : (idx >> 6);
-        const int jj = fo.tall ? (idx >> 6) : (idx & 63);
-        const int64_t i = i0 + ii, j = j0 + jj;
-        if (i >= fo.m || j >= fo.n) continue;
-        const float v = tile[ii][jj];
-        store_any(fo.out, fo.tall ? j * fo.ld + i : i * fo.ld + j, fo.dtype, v);
+    // caller rows are rows of X, or of X^T when the caller's matrix is tall
+    const int64_t orows = fo.tall ? fo.n : fo.m, ocols = fo.tall ? fo.m : fo.n;
+    const int64_t or0 = fo.tall ? j0 : i0, oc0 = fo.tall ? i0 : j0;
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+        const int rr = r + 32 * pass;
+        const int64_t orow = or0 + rr, oc = oc0 + c8;
+        const int n = seg_len(orow, oc, orows, ocols);
+        if (n == 0) continue;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = fo.tall ? tile[c8 + k][rr] : tile[rr][c8 + k];
+        store_seg(fo.out, orow * fo.ld + oc, fo.dtype, n, fo.vec_out, v);
         if (fo.w) {
-            float *wp = fo.w + (fo.tall ? j * fo.ldw + i : i * fo.ldw + j);
-            const float w = *wp;
-            *wp = w - (fo.lr_s * v + fo.lr_wd * w);
+            float w[8];
+            load_seg(fo.w, orow * fo.ldw + oc, QM_F32, n, fo.vec_w, w);
+#pragma unroll
+            for (int k = 0; k < 8; k++) w[k] = w[k] - (fo.lr_s * v[k] + fo.lr_wd * w[k]);
+            store_seg(fo.w, orow * fo.ldw + oc, QM_F32, n, fo.vec_w, w);
         }
     }
 }
@@ -914,6 +993,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         it.src = r.src;
         it.ld = r.ld;
         it.dtype = r.dtype;
+        it.vec = aligned(r.src, 16) && (r.ld * (r.dtype == QM_F32 ? 4 : 2)) % 16 == 0 ? 1 : 0;
         it.tall = r.rows > r.cols ? 1 : 0;
         it.inv = r.inv;
         it.X = bufs[i].X[0];
@@ -944,8 +1024,11 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     FinalOut fo[kMaxItems];
     for (int i = 0; i < nit; i++) {
         const NsRequest &r = req[chunk[i]];
+        const int64_t oesz = r.out_dtype == QM_F32 ? 4 : 2;
         fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.out_dtype, r.rows > r.cols ? 1 : 0,
-                         (int32_t)bufs[i].g.m, (int32_t)bufs[i].g.n, r.lr_s, r.lr_wd};
+                         (int32_t)bufs[i].g.m, (int32_t)bufs[i].g.n, r.lr_s, r.lr_wd,
+                         aligned(r.out, 16) && (r.ld * oesz) % 16 == 0 ? 1 : 0,
+                         r.w && aligned(r.w, 16) && (r.ldw * 4) % 16 == 0 ? 1 : 0};
     }
     WritebackArgs wb{};
     for (int i = 0; i < nit; i++) wb.fo[i] = fo[i];
