@@ -27,7 +27,7 @@
 extern "C" {
 #endif
 
-#define QM_ABI_VERSION 1
+#define QM_ABI_VERSION 2
 #define QM_BLOCK 256           /* quantisation block: elements per absmax */
 
 typedef void *qm_stream_t;     /* hipStream_t */
@@ -58,19 +58,32 @@ typedef enum { QM_NS_BF16 = 0, QM_NS_F32 = 1 } qm_ns_precision;
  * q8 momentum state and norm plans
  *
  * State of one tensor ("Quantized Muon Momentum", section "What Exists"):
- * `codes` int8 of the tensor's size and one fp32 absmax per 256-element block
+ * `codes` of the tensor's size and one fp32 absmax per 256-element block
  * (the last block of a tensor covers the remainder).  Codes lie in
  * [-127, 127]; element i dequantises to codes[i] * (absmax[i/256] / 127).
- * Tensors are contiguous ("Known Limitations": contiguous only).
+ * The page allows int8 or uint8 storage for the codes; a uint8 buffer holds
+ * the same two's-complement bytes (no offset), so both are passed here as
+ * `codes`.  Blocks follow the tensor's logical (row-major) element order.
+ *
+ * The codes and absmax are contiguous.  The grad may be contiguous
+ * (grad_cols = 0) or a 2-D view of numel / grad_cols rows of grad_cols
+ * elements with row pitch grad_ld elements, e.g. one slice of a fused
+ * buffer; the page lists "contiguous only" among the limitations of its
+ * kernel ("Known Limitations").
  * ---------------------------------------------------------------------- */
 typedef struct {
-    int8_t *codes;      /* [numel], 16-byte aligned, in/out                  */
+    int8_t *codes;      /* [numel] int8 (or uint8 bytes), 16-byte aligned,
+                           in/out                                            */
     float *absmax;      /* [ceil(numel/256)], 4-byte aligned, in/out         */
-    void *grad;         /* [numel] of grad_dtype, 16-byte aligned; in: g,
-                           out: m (optionally normalised)                    */
+    void *grad;         /* grad_dtype, 16-byte aligned; in: g, out: m
+                           (optionally normalised)                           */
     int64_t numel;      /* > 0                                               */
     int32_t grad_dtype; /* qm_dtype                                          */
     int32_t reserved;   /* must be 0                                         */
+    int64_t grad_cols;  /* 0: grad contiguous; else row length, a multiple
+                           of 8 dividing numel                               */
+    int64_t grad_ld;    /* grad_cols > 0: row pitch in elements, a multiple
+                           of 8, >= grad_cols; ignored otherwise             */
 } qm_q8_tensor;
 
 /* One slice of a tensor assigned to a norm group ("Quantized Muon Momentum",

@@ -82,8 +82,12 @@ def timing_read(kernel_class):
 class Plan:
     """A norm plan over q8 tensors, encoded once and copied to the device once.
 
-    tensors : list of (codes int8, absmax fp32, grad) contiguous device tensors
+    tensors : list of (codes, absmax fp32, grad) device tensors.  codes are int8,
+              or uint8 holding the same bytes; codes and absmax contiguous.  grad
+              is contiguous, or a 2-D view with unit column stride (rows of
+              grad.shape[1] elements at pitch grad.stride(0)).
     segments: list of (tensor_index, start, length, group_id) element ranges
+              (logical row-major element order)
     n_groups: number of norm groups
     """
 
@@ -91,11 +95,18 @@ class Plan:
         n = len(tensors)
         arr = (L.Q8Tensor * n)()
         for i, (codes, absmax, grad) in enumerate(tensors):
-            for t in (codes, absmax, grad):
+            for t in (codes, absmax):
                 if not t.is_contiguous():
-                    raise ValueError("plan tensors must be contiguous")
+                    raise ValueError("codes and absmax must be contiguous")
+            if codes.dtype not in (torch.int8, torch.uint8):
+                raise TypeError("codes must be int8 or uint8")
+            cols, ld = 0, 0
+            if not grad.is_contiguous():
+                if grad.dim() != 2 or grad.stride(1) != 1:
+                    raise ValueError("a non-contiguous grad must be 2-D with unit column stride")
+                cols, ld = grad.shape[1], grad.stride(0)
             arr[i] = L.Q8Tensor(codes.data_ptr(), absmax.data_ptr(), grad.data_ptr(),
-                                grad.numel(), _dtype(grad), 0)
+                                grad.numel(), _dtype(grad), 0, cols, ld)
         segs = (L.NormSegment * len(segments))()
         for k, (ti, start, length, gid) in enumerate(segments):
             segs[k] = L.NormSegment(ti, gid, start, length)

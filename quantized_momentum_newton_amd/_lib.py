@@ -24,7 +24,8 @@ c_size = ctypes.c_size_t
 
 class Q8Tensor(ctypes.Structure):
     _fields_ = [("codes", c_void_p), ("absmax", c_void_p), ("grad", c_void_p),
-                ("numel", c_i64), ("grad_dtype", c_i32), ("reserved", c_i32)]
+                ("numel", c_i64), ("grad_dtype", c_i32), ("reserved", c_i32),
+                ("grad_cols", c_i64), ("grad_ld", c_i64)]
 
 
 class NormSegment(ctypes.Structure):

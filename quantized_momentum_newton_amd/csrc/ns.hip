@@ -1259,12 +1259,14 @@ std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan,
         const int32_t dt = pt[i].dtype;
         const size_t esz = dt == QM_F32 ? 4 : 2;
         char *grad = reinterpret_cast<char *>(pt[i].grad);
+        const int64_t gld = pt[i].grad_cols ? pt[i].grad_ld : M.cols;   // row pitch of the grad
         for (int64_t bi = 0; bi < nbr; bi++)
             for (int64_t bj = 0; bj < nbc; bj++) {
-                const size_t off = (size_t)(bi * br) * (size_t)M.cols + (size_t)(bj * bc);
+                const size_t goff = (size_t)(bi * br) * (size_t)gld + (size_t)(bj * bc);
+                const size_t woff = (size_t)(bi * br) * (size_t)M.cols + (size_t)(bj * bc);
                 const float *ip = inv ? inv + g0 + bi * nbc + bj : nullptr;
-                req.push_back(NsRequest{grad + off * esz, grad + off * esz, br, bc, M.cols, dt, dt, ip,
-                                        M.weight ? M.weight + off : nullptr, M.cols, lr * s,
+                req.push_back(NsRequest{grad + goff * esz, grad + goff * esz, br, bc, gld, dt, dt, ip,
+                                        M.weight ? M.weight + woff : nullptr, M.cols, lr * s,
                                         lr * hp->weight_decay});
             }
         g0 += nbr * nbc;
@@ -1284,6 +1286,8 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
         const qm_muon_matrix &M = mats[i];
         if (M.rows <= 0 || M.cols <= 0) return fail(QM_E_SHAPE, "matrix %d: empty", i);
         if (pt[i].numel != M.rows * M.cols) return fail(QM_E_SHAPE, "matrix %d: size differs from plan tensor", i);
+        if (pt[i].grad_cols != 0 && pt[i].grad_cols != M.cols)
+            return fail(QM_E_SHAPE, "matrix %d: strided grad rows are not the matrix rows", i);
         const int64_t br = full ? M.rows : M.block_rows, bc = full ? M.cols : M.block_cols;
         if (br <= 0 || bc <= 0 || M.rows % br || M.cols % bc)
             return fail(QM_E_SHAPE, "matrix %d: blocks do not tile it", i);

@@ -70,6 +70,29 @@ Layout layout_for(int32_t nt, int32_t ng, int64_t nb, int64_t nr, int64_t nc) {
 
 int64_t nblocks(int64_t numel) { return (numel + kBlock - 1) / kBlock; }
 
+// Bytes [lo, hi) a buffer touches: all of them (pitch 0), or, for a strided
+// grad, rows of `row` bytes every `pitch` bytes starting at lo.
+struct Region {
+    uintptr_t lo, hi, pitch, row;
+};
+
+// Whether two regions whose spans intersect share a byte.  Exact for two
+// strided regions of one pitch (their rows occupy fixed column ranges modulo
+// the pitch, e.g. column slices of one fused buffer); any other pair with
+// intersecting spans counts as overlapping.
+bool regions_overlap(const Region &x, const Region &y) {
+    if (x.hi <= y.lo || y.hi <= x.lo) return false;
+    if (!x.pitch || !y.pitch || x.pitch != y.pitch) return true;
+    const uintptr_t P = x.pitch;
+    const uintptr_t a = x.lo % P, b = y.lo % P;   // row starts modulo the pitch
+    auto hits = [&](uintptr_t s0, uintptr_t l0, uintptr_t s1, uintptr_t l1) {
+        // [s0, s0 + l0) and [s1, s1 + l1) on a circle of length P (l0, l1 <= P)
+        const uintptr_t d = (s1 + P - s0) % P;
+        return d < l0 || (P - d) % P < l1;
+    };
+    return hits(a, x.row, b, y.row);
+}
+
 }  // namespace
 }  // namespace qm
 
@@ -86,7 +109,7 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
     if (!inout_blob_bytes) return fail(QM_E_ARG, "inout_blob_bytes is null");
 
     // ---- tensors
-    std::vector<std::pair<uintptr_t, uintptr_t>> spans;
+    std::vector<Region> spans;
     int64_t nb_total = 0, total_numel = 0;
     for (int32_t i = 0; i < n_tensors; i++) {
         const qm_q8_tensor &t = tensors[i];
@@ -99,17 +122,31 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
         if (!aligned(t.codes, 16) || !aligned(t.grad, 16) || !aligned(t.absmax, 4))
             return fail(QM_E_ALIGN, "tensor %d: codes/grad need 16-byte, absmax 4-byte alignment", i);
         const int64_t esz = t.grad_dtype == QM_F32 ? 4 : 2;
+        int64_t gspan = t.numel;  // elements from grad to one past its last element
+        if (t.grad_cols != 0) {
+            if (t.grad_cols < 0 || t.numel % t.grad_cols != 0)
+                return fail(QM_E_SHAPE, "tensor %d: grad_cols must be positive and divide numel", i);
+            if (t.grad_ld < t.grad_cols) return fail(QM_E_SHAPE, "tensor %d: grad_ld < grad_cols", i);
+            if (t.grad_cols % 8 != 0 || t.grad_ld % 8 != 0)
+                return fail(QM_E_ALIGN, "tensor %d: grad_cols and grad_ld must be multiples of 8", i);
+            if (t.numel >= (int64_t)1 << 32)
+                return fail(QM_E_UNSUPPORTED, "tensor %d: strided grad too large", i);
+            gspan = (t.numel / t.grad_cols - 1) * t.grad_ld + t.grad_cols;
+        }
         const uintptr_t c = (uintptr_t)t.codes, a = (uintptr_t)t.absmax, g = (uintptr_t)t.grad;
-        spans.push_back({c, c + (uintptr_t)t.numel});
-        spans.push_back({a, a + (uintptr_t)(nblocks(t.numel) * 4)});
-        spans.push_back({g, g + (uintptr_t)(t.numel * esz)});
+        spans.push_back({c, c + (uintptr_t)t.numel, 0, 0});
+        spans.push_back({a, a + (uintptr_t)(nblocks(t.numel) * 4), 0, 0});
+        if (t.grad_cols != 0)
+            spans.push_back({g, g + (uintptr_t)(gspan * esz), (uintptr_t)(t.grad_ld * esz), (uintptr_t)(t.grad_cols * esz)});
+        else
+            spans.push_back({g, g + (uintptr_t)(gspan * esz), 0, 0});
         nb_total += nblocks(t.numel);
         total_numel += t.numel;
     }
-    std::sort(spans.begin(), spans.end());
-    for (size_t k = 1; k < spans.size(); k++)
-        if (spans[k].first < spans[k - 1].second)
-            return fail(QM_E_ARG, "state/grad buffers overlap");
+    std::sort(spans.begin(), spans.end(), [](const Region &x, const Region &y) { return x.lo < y.lo; });
+    for (size_t k = 0; k < spans.size(); k++)
+        for (size_t j = k + 1; j < spans.size() && spans[j].lo < spans[k].hi; j++)
+            if (regions_overlap(spans[k], spans[j])) return fail(QM_E_ARG, "state/grad buffers overlap");
 
     // ---- segments -> one group id per block
     std::vector<int64_t> boff(n_tensors + 1, 0);
@@ -198,6 +235,8 @@ extern "C" qm_status qm_plan_encode(const qm_q8_tensor *tensors, int32_t n_tenso
         pt[i].block_offset = boff[i];
         pt[i].task_offset = toff;
         pt[i].dtype = t.grad_dtype;
+        pt[i].grad_cols = t.grad_cols;
+        pt[i].grad_ld = t.grad_cols ? t.grad_ld : 0;
         int32_t lo = n_groups, hi = -1;
         for (int64_t b = boff[i]; b < boff[i + 1]; b++) {
             lo = std::min(lo, bg[b]);

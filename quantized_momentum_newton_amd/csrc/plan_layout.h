@@ -19,7 +19,7 @@
 namespace qm {
 
 constexpr uint32_t kPlanMagic = 0x4e4c5051u;  // "QPLN"
-constexpr uint32_t kPlanVersion = 3;
+constexpr uint32_t kPlanVersion = 4;
 constexpr int kBlock = 256;
 constexpr int kBlocksPerTask = 4;
 constexpr int kTaskElems = kBlock * kBlocksPerTask;  // 1024
@@ -51,6 +51,7 @@ struct PlanTensor {
     int32_t dtype;                 // qm_dtype
     int32_t group_lo, group_hi;    // smallest / largest group id it touches
     int32_t pad;
+    int64_t grad_cols, grad_ld;    // grad rows (0: contiguous) and their pitch, elements
 };
 
 struct PlanRun {
@@ -60,7 +61,7 @@ struct PlanRun {
 };
 
 static_assert(sizeof(PlanHeader) == 176, "plan header layout");
-static_assert(sizeof(PlanTensor) == 64, "plan tensor layout");
+static_assert(sizeof(PlanTensor) == 80, "plan tensor layout");
 static_assert(sizeof(PlanRun) == 16, "plan run layout");
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }

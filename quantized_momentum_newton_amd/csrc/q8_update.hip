@@ -143,6 +143,16 @@ template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int6
     }
 }
 
+// Element offset in the grad buffer of logical element e: e itself for a
+// contiguous grad, row-major position in rows of grad_cols with pitch
+// grad_ld otherwise (numel < 2^32 there, so 32-bit division suffices).
+__device__ __forceinline__ int64_t gpos(const PlanTensor &T, int64_t e) {
+    if (T.grad_cols == 0) return e;
+    const uint32_t c = (uint32_t)T.grad_cols, ue = (uint32_t)e;
+    const uint32_t r = ue / c;
+    return (int64_t)r * T.grad_ld + (int64_t)(ue - r * c);
+}
+
 // Largest i with task_offsets[i] <= task (every tensor owns >= 1 task): the
 // position of the task's tensor in task order.
 __device__ __forceinline__ int find_tensor(const int64_t *task_offsets, int n, int64_t task) {
@@ -168,7 +178,7 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
     const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
     int8_t *codes = reinterpret_cast<int8_t *>(T.codes) + e_task;
     float *absmax = reinterpret_cast<float *>(T.absmax) + lt * kBlocksPerTask;
-    void *grad = reinterpret_cast<char *>(T.grad) + e_task * Elem<DT>::kSize;
+    void *grad = reinterpret_cast<void *>(T.grad);   // addressed through gpos
 
     float m[PARTS][EPL];
 #pragma unroll
@@ -181,13 +191,13 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         float g[EPL];
         if (e0 + EPL <= nvalid) {
             load_codes_vec<EPL>(codes, e0, q);
-            load_grad_vec<DT>(grad, e0, g);
+            load_grad_vec<DT>(grad, gpos(T, e_task + e0), g);
         } else {
 #pragma unroll
             for (int j = 0; j < EPL; j++) {
                 const bool ok = e0 + j < nvalid;
                 q[j] = ok ? codes[e0 + j] : (int8_t)0;
-                g[j] = ok ? widen<DT>(grad, e0 + j) : 0.0f;
+                g[j] = ok ? widen<DT>(grad, gpos(T, e_task + e0 + j)) : 0.0f;
             }
         }
 #pragma unroll
@@ -218,13 +228,13 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         }
         if (e0 + EPL <= nvalid) {
             store_codes_vec<EPL>(codes, e0, q);
-            store_grad_vec<DT>(grad, e0, m[p]);
+            store_grad_vec<DT>(grad, gpos(T, e_task + e0), m[p]);
         } else {
 #pragma unroll
             for (int j = 0; j < EPL; j++)
                 if (e0 + j < nvalid) {
                     codes[e0 + j] = q[j];
-                    narrow<DT>(grad, e0 + j, m[p][j]);
+                    narrow<DT>(grad, gpos(T, e_task + e0 + j), m[p][j]);
                 }
         }
         double s = 0.0;
@@ -322,22 +332,34 @@ __device__ __forceinline__ void scale_task(const PlanTensor &T, int64_t lt, cons
     const int64_t e_task = lt * kTaskElems;
     const int64_t rem = T.numel - e_task;
     const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
-    void *grad = reinterpret_cast<char *>(T.grad) + e_task * Elem<DT>::kSize;
+    void *grad = reinterpret_cast<void *>(T.grad);   // addressed through gpos
     const int32_t *bg = block_group + T.block_offset + lt * kBlocksPerTask;
 #pragma unroll
     for (int p = 0; p < PARTS; p++) {
         const int e0 = p * 64 * EPL + lane * EPL;
         if (e0 >= nvalid) continue;
         const float s = inv[bg[e0 / kBlock]];
+        // The product is pinned to an fp32 register (empty asm) before it is
+        // narrowed: otherwise the f16 path becomes one v_fma_mixlo_f16 (h * s
+        // + 0 rounded once to f16), which turns -0 into +0 and skips the fp32
+        // rounding of the product that the definition has.
         if (e0 + EPL <= nvalid) {
+            const int64_t ge = gpos(T, e_task + e0);
             float v[EPL];
-            load_grad_vec<DT>(grad, e0, v);
+            load_grad_vec<DT>(grad, ge, v);
 #pragma unroll
-            for (int j = 0; j < EPL; j++) v[j] = v[j] * s;
-            store_grad_vec<DT>(grad, e0, v);
+            for (int j = 0; j < EPL; j++) {
+                v[j] = v[j] * s;
+                asm volatile("" : "+v"(v[j]));
+            }
+            store_grad_vec<DT>(grad, ge, v);
         } else {
-            for (int j = 0; j < EPL && e0 + j < nvalid; j++)
-                narrow<DT>(grad, e0 + j, widen<DT>(grad, e0 + j) * s);
+            for (int j = 0; j < EPL && e0 + j < nvalid; j++) {
+                const int64_t ge = gpos(T, e_task + e0 + j);
+                float v = widen<DT>(grad, ge) * s;
+                asm volatile("" : "+v"(v));
+                narrow<DT>(grad, ge, v);
+            }
         }
     }
 }

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(LIB, n), n
     assert names == set(L.SIGNATURES), names ^ set(L.SIGNATURES)
-    assert LIB.qm_abi_version() == 1
+    assert LIB.qm_abi_version() == 2
     assert LIB.qm_status_string(0) == b"ok"
 
 
@@ -110,6 +110,35 @@ def test_plan_encode_rejects_bad_tensors():
     assert _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 1024, 0)]), 1)[0] == 1
 
 
+@pytest.mark.parametrize("cols,ld,status", [
+    (64, 64, 0),        # strided view with pitch == row length
+    (64, 96, 0),        # rows of 64 at pitch 96
+    (48, 48, 4),        # 48 does not divide 1024 -> QM_E_SHAPE
+    (64, 32, 4),        # pitch below the row length -> QM_E_SHAPE
+    (4, 8, 2),          # row length not a multiple of 8 -> QM_E_ALIGN
+    (64, 100, 2),       # pitch not a multiple of 8 -> QM_E_ALIGN
+    (-8, 8, 4),         # negative row length
+])
+def test_plan_strided_grad_rules(cols, ld, status):
+    tens = _tensors([(1024, L.QM_BF16)])
+    tens[0].grad_cols, tens[0].grad_ld = cols, ld
+    st, _ = _encode(tens, _segs([(0, 0, 1024, 0)]), 1)
+    assert st == status, LIB.qm_last_error()
+
+
+def test_plan_strided_grad_span_counts_in_overlap_check():
+    # 1024 elements as 16 rows of 64 at pitch 4096 span 61 KiB of bf16: a second
+    # tensor's grad placed 32 KiB after the first must be reported as an overlap
+    tens = _tensors([(1024, L.QM_BF16), (1024, L.QM_BF16)])
+    tens[0].grad_cols, tens[0].grad_ld = 64, 4096
+    tens[1].grad = tens[0].grad + 32768
+    assert _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 1024, 0)]), 1)[0] == 1
+    tens[1].grad = tens[0].grad + 16 * 4096 * 2
+    tens[1].codes = tens[1].codes + 16 * 4096 * 2      # keep codes clear of the moved grad
+    tens[1].absmax = tens[1].absmax + 16 * 4096 * 2
+    assert _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 1024, 0)]), 1)[0] == 0, LIB.qm_last_error()
+
+
 def test_final_partial_block_segment_is_allowed():
     st, _ = _encode(_tensors([(1000, L.QM_F16)]), _segs([(0, 0, 768, 0), (0, 768, 232, 1)]), 2)
     assert st == 0
@@ -146,3 +175,19 @@ def test_timing_recorder_host_checks():
     for k in q.KERNEL_CLASSES:
         assert q.timing_read(k) == (0.0, 0)
     assert sorted(q.KERNEL_CLASSES.values()) == list(range(9))
+
+
+@pytest.mark.parametrize("c1,ld1,off1,c2,ld2,off2,status", [
+    (64, 256, 0, 128, 256, 64, 0),      # disjoint column slices of one fused buffer
+    (64, 256, 0, 128, 256, 32, 1),      # second slice starts inside the first -> overlap
+    (128, 256, 128, 128, 256, 0, 0),    # slices in the other order
+    (64, 256, 0, 64, 264, 64, 1),       # different pitches with intersecting spans: reported
+    (64, 256, 192, 64, 256, 0, 0),      # first slice ends at the row end, second starts at 0
+])
+def test_plan_strided_views_of_one_buffer(c1, ld1, off1, c2, ld2, off2, status):
+    tens = _tensors([(64 * c1, L.QM_BF16), (64 * c2, L.QM_BF16)])
+    base = BASE + (1 << 30)              # fused buffer far from the state arrays
+    for t, (c, ld, off) in zip(tens, ((c1, ld1, off1), (c2, ld2, off2))):
+        t.grad, t.grad_cols, t.grad_ld = base + off * 2, c, ld
+    segs = _segs([(0, 0, 64 * c1, 0), (1, 0, 64 * c2, 1)])
+    assert _encode(tens, segs, 2)[0] == status, LIB.qm_last_error()

@@ -159,3 +159,50 @@ def test_muonbp_full_size_state_and_sampled_ns():
                     ref = ns.spectral_rows(mf[:, bc * j:bc * (j + 1)], rows, 5, COEF, H.NS_EPS,
                                            float(inv[j]))
                     _within(O[rows, bc * j:bc * (j + 1)], ref, f"block {j} O")
+
+
+def test_muon_step_on_strided_grad_views():
+    """Grads as column slices of one fused buffer (row pitch > row length), P = 2
+    over 4 steps (block and full steps): state bit-exact and O, W within the
+    bf16 bound against the oracle on contiguous copies; the fused buffer's
+    remaining columns are untouched."""
+    rows, widths, pad = 512, [256, 512], 64     # block rows must start on 256-element blocks
+    blocks = [(256, 256), (512, 256)]
+    W = sum(widths) + pad
+    buf = torch.zeros((rows, W), dtype=torch.bfloat16, device=DEV)
+    views = [buf[:, 0:256], buf[:, 256:768]]
+    buf[:, 768:] = 7.0
+    trip, mats, W_host, states = [], [], [], []
+    for i, (v, (br, bc)) in enumerate(zip(views, blocks)):
+        r, c = v.shape
+        codes, absmax = H.prior_state(r * c, DEV, 3003, i)
+        w = H.weights((r, c), DEV, 3003, i)
+        trip.append((codes, absmax, v))
+        mats.append((r, c, br, bc, w))
+        W_host.append(as_f64(w))
+        states.append((host(codes), host(absmax)))
+    full, block = _plans(trip, mats)
+    params = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, lr_block=0.01,
+                            weight_decay=0.0, rms_scale=0.2, ns_steps=5, period=2)
+    for t in range(1, 5):
+        for i, v in enumerate(views):
+            v.copy_(H.grad(tuple(v.shape), torch.bfloat16, DEV, 3003, i, t))
+        torch.cuda.synchronize()
+        gh = [host_grad(v) for v in views]
+        say("strided step", t)
+        q.muon_step(full, block, mats, t, params)
+        torch.cuda.synchronize()
+        for i, v in enumerate(views):
+            r, c = v.shape
+            br, bc = blocks[i]
+            W2, c2, a2, O, is_full = muonbp.muon_step(
+                W_host[i], states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c, br, bc,
+                2, 0.95, 1e-7, COEF, 5, 0.02, 0.01, 0.2, 0.0)
+            assert is_full == (t % 2 == 0)
+            assert_bits_equal(host(trip[i][0]), c2, f"t{t} codes[{i}]")
+            assert_bits_equal(host(trip[i][1]), a2, f"t{t} absmax[{i}]")
+            states[i] = (c2, a2)
+            _within(as_f64(v), O, f"t{t} O[{i}]")
+            _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"t{t} dW[{i}]")
+            W_host[i] = as_f64(mats[i][4])
+        assert bool((buf[:, 768:] == 7.0).all())

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import quantized_momentum_newton_amd as q
-from gpu_util import Q8Set, assert_bits_equal, host, host_grad, say
+from gpu_util import TORCH_TO_ORACLE, Q8Set, assert_bits_equal, host, host_grad, say
 from harness import inputs as H
 
 pytestmark = pytest.mark.gpu
@@ -243,3 +243,96 @@ def test_launch_timing_records_each_kernel_class():
         ms, n = q.timing_read(k)
         assert n == 2 and ms > 0.0, (k, ms, n)
     assert q.timing_read("ns_gram") == (0.0, 0)
+
+
+def _fused_views(rows, widths, pad, dtype, seed):
+    """A fused (rows x sum(widths)+pad) grad buffer and 2-D views of its column
+    slices (unit column stride, row pitch the full width); the last `pad`
+    columns are canaries no view covers."""
+    W = sum(widths) + pad
+    buf = H.grad((rows, W), dtype, DEV, seed, 0)
+    views, c0 = [], 0
+    for w in widths:
+        views.append(buf[:, c0:c0 + w])
+        c0 += w
+    return buf, views
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float16])
+def test_strided_grad_views_of_a_fused_buffer(dtype):
+    """Grads given as column slices of one fused buffer (row pitch > row length):
+    blocks of 256 follow each view's row-major order and cross rows; codes,
+    absmax, the views' m and the normalised values match the oracle on the
+    contiguous copies bit for bit; the buffer's other columns are untouched."""
+    rows, widths, pad = 300, [512, 320, 184], 40
+    buf, views = _fused_views(rows, widths, pad, dtype, 1021)
+    states = [H.prior_state(v.numel(), DEV, 1021, i + 1) for i, v in enumerate(views)]
+    torch.cuda.synchronize()
+    h_states = [(host(c), host(a)) for c, a in states]
+    h_grads = [host_grad(v).reshape(-1) for v in views]
+    h_canary = host_grad(buf[:, sum(widths):]).reshape(-1)
+    segs = [(i, 0, v.numel(), i) for i, v in enumerate(views)]
+    plan = q.Plan([(c, a, v) for (c, a), v in zip(states, views)], segs, len(views))
+    inv = torch.empty(len(views), dtype=torch.float32, device=DEV)
+    say("strided views", dtype, widths)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    torch.cuda.synchronize()
+    odt = TORCH_TO_ORACLE[dtype]
+    o_states, outs, S, inv_o, _ = oracle.update_normalize_groups(
+        h_states, h_grads, [odt] * len(views), segs, len(views), H.BETA, H.NS_EPS, True)
+    for i, v in enumerate(views):
+        assert_bits_equal(host(states[i][0]), o_states[i][0], f"codes[{i}]")
+        assert_bits_equal(host(states[i][1]), o_states[i][1], f"absmax[{i}]")
+        assert_bits_equal(host_grad(v).reshape(-1), outs[i], f"grad view[{i}]")
+    assert np.array_equal(host(inv), np.asarray(inv_o, dtype=np.float32))
+    assert_bits_equal(host_grad(buf[:, sum(widths):]).reshape(-1), h_canary, "canary columns")
+
+
+def test_uint8_codes_same_bytes_as_int8():
+    """uint8 storage of the codes: the kernel reads and writes the same bytes as
+    for int8, so codes, absmax and m agree bit for bit with the int8 run."""
+    shapes = [(4096, 128), (999,)]
+    a = Q8Set(shapes, [torch.bfloat16, torch.float32], seed=1023)
+    b = Q8Set(shapes, [torch.bfloat16, torch.float32], seed=1023)
+    segs = [(0, 0, 4096 * 128, 0), (1, 0, 999, 1)]
+    pa = q.Plan(a.triples(), segs, 2)
+    pb = q.Plan([(c.view(torch.uint8), am, g) for c, am, g in b.triples()], segs, 2)
+    say("uint8 codes")
+    for _ in range(2):
+        q.qmuon_update_multi(pa, H.BETA)
+        q.qmuon_update_multi(pb, H.BETA)
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(a.codes[i], b.codes[i])
+        assert torch.equal(a.absmax[i], b.absmax[i])
+        assert torch.equal(a.grads[i].view(torch.int16) if a.grads[i].dtype != torch.float32 else a.grads[i],
+                           b.grads[i].view(torch.int16) if b.grads[i].dtype != torch.float32 else b.grads[i])
+
+
+def test_f16_negative_zero_survives_normalisation():
+    """Momentum that rounds to f16 -0 stays -0 through the normalisation pass.
+    With absmax 127 * 2^-16 (exact), code 1 and grads 0x8cc0..0x8cc2, the fp32
+    EMA gives a value in (-2^-25, 0), stored as 0x8000; float(-0) * inv is -0.
+    (A fused mixed-precision multiply-add with a +0 addend would give +0.)"""
+    n = 2048
+    rng = np.random.default_rng(1031)
+    codes = rng.integers(-127, 128, n).astype(np.int8)
+    codes[1::2] = 1
+    absmax = np.full(n // 256, 127.0 * 2.0 ** -16, dtype=np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float16).view(np.uint16)
+    g[1::2] = np.array([0x8cc0, 0x8cc1, 0x8cc2], dtype=np.uint16)[np.arange(n // 2) % 3]
+    c_d = torch.from_numpy(codes.copy()).to(DEV)
+    a_d = torch.from_numpy(absmax.copy()).to(DEV)
+    g_d = torch.from_numpy(g.view(np.int16).copy()).to(DEV).view(torch.float16)
+    plan = q.Plan([(c_d, a_d, g_d)], [(0, 0, n, 0)], 1)
+    inv = torch.empty(1, dtype=torch.float32, device=DEV)
+    say("f16 negative zero")
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    torch.cuda.synchronize()
+    st, outs, _, _, _ = oracle.update_normalize_groups([(codes, absmax)], [g], [oracle.F16], [(0, 0, n, 0)], 1,
+                                                        H.BETA, H.NS_EPS, True)
+    exp = np.asarray(outs[0])
+    assert (exp[1::2] == 0x8000).all()          # the case is exercised
+    assert_bits_equal(host(c_d), st[0][0], "codes")
+    assert_bits_equal(host(a_d), st[0][1], "absmax")
+    assert_bits_equal(host_grad(g_d), exp, "normalised grad")
