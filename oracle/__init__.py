@@ -39,6 +39,9 @@ def lib():
         L.or_f16_from_f32.argtypes = [ctypes.c_float]
         L.or_f16_from_f32.restype = ctypes.c_uint16
         L.or_q8_update.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p]
+        L.or_q8_update_ex.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p, ctypes.c_int,
+                                      ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
+        L.or_philox4x32_10.argtypes = [p, p, p]
         L.or_q8_update.restype = None
         L.or_group_sums.argtypes = [p, p, i64, ctypes.c_int32, p]
         L.or_group_inv_norm.argtypes = [p, ctypes.c_int32, ctypes.c_float, p]
@@ -86,12 +89,26 @@ def widen(bits, dtype):
 
 # --------------------------------------------------------------- q8 update
 
-def q8_update(codes, absmax, grad, beta, dtype=F32):
+ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter and 2-word key (C implementation)."""
+    c = np.asarray(ctr, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    lib().or_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def q8_update(codes, absmax, grad, beta, dtype=F32, rounding=ROUND_NEAREST, seed=0, offset=0, tensor=0):
     """One tensor's q8 momentum update ("Quantized Muon Momentum", "Algorithm").
 
     codes  : int8 [numel]      prior state codes
     absmax : float32 [nblk]    prior per-256-block absmax
     grad   : float32 [numel] (dtype F32) or uint16 bits (BF16/F16)
+    rounding: ROUND_NEAREST, or ROUND_STOCHASTIC with the random stream chosen
+    by (seed, offset, tensor) (q8.c header).
     Returns (codes', absmax', m_stored, block_sumsq): the new state, m rounded
     to the grad dtype (what lands in the grad buffer) and fp64 sum of m^2 per
     block.  Inputs are not modified.
@@ -107,8 +124,8 @@ def q8_update(codes, absmax, grad, beta, dtype=F32):
     if absmax.size != nblk or g.size != numel:
         raise ValueError("shape mismatch between codes, absmax and grad")
     sums = np.empty(nblk, dtype=np.float64)
-    lib().or_q8_update(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel,
-                       ctypes.c_float(beta), _ptr(sums))
+    lib().or_q8_update_ex(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel, ctypes.c_float(beta), _ptr(sums),
+                          rounding, seed, offset, tensor)
     return codes, absmax, g, sums
 
 
@@ -173,7 +190,7 @@ def scale_by_group(grad, dtype, block_group, inv):
 
 
 def update_normalize_groups(states, grads, dtypes, segments, ngroups, beta,
-                            eps, write_normalized=True):
+                            eps, write_normalized=True, rounding=ROUND_NEAREST, seed=0, offset=0):
     """Multi-tensor q8 update + grouped Frobenius normalisation.
 
     states : list of (codes, absmax); grads: list of fp32 arrays or uint16
@@ -186,8 +203,8 @@ def update_normalize_groups(states, grads, dtypes, segments, ngroups, beta,
     numels = [np.asarray(c).size for (c, _) in states]
     bgs = expand_segments(numels, segments, ngroups)
     new_states, outs, bsums = [], [], []
-    for (c, a), g, dt in zip(states, grads, dtypes):
-        c2, a2, m, s = q8_update(c, a, g, beta, dt)
+    for ti, ((c, a), g, dt) in enumerate(zip(states, grads, dtypes)):
+        c2, a2, m, s = q8_update(c, a, g, beta, dt, rounding, seed, offset, ti)
         new_states.append((c2, a2))
         outs.append(m)
         bsums.append(s)

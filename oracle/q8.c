@@ -32,6 +32,17 @@
  *   - group inverse norm = (float)(1 / (sqrt(S_g) + eps)) computed in fp64;
  *   - the scale pass rounds float(stored grad) * inv to the grad dtype
  *     (round to nearest even).
+ *
+ * Stochastic rounding ("Known Limitations" names it as not implemented on
+ * the page; this is the reading taken for it):
+ *   - x = m * (127 / amax) exactly as for nearest rounding; q = floor(x) + 1
+ *     with probability frac(x) = x - floor(x), else floor(x); clamped to
+ *     [-127, 127].  floor(x) and x - floor(x) are exact in binary32;
+ *   - the uniform u in [0, 1) is (r >> 8) * 2^-24 for a 32-bit word r of
+ *     Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+ *     as easy as 1, 2, 3", SC 2011): counter (e / 4 low word, e / 4 high
+ *     word, offset, tensor index), key (seed low word, seed high word), r is
+ *     output word e mod 4; round up iff u < frac(x).
  */
 #include <math.h>
 #include <omp.h>
@@ -124,17 +135,60 @@ static void store_grad(void *grad, int dtype, int64_t i, float v)
     else ((uint16_t *)grad)[i] = or_f16_from_f32(v);
 }
 
+/* ---------------------------------------------------------- Philox4x32 */
+
+/* Philox4x32 with 10 rounds, from the SC 2011 paper: each round multiplies
+ * counter words 0 and 2 by two fixed 32-bit constants, forms the new counter
+ * from the high halves xor-ed with the other words and the key and the low
+ * halves, and the key is advanced by the two Weyl constants between rounds. */
+void or_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c[4] = {ctr_in[0], ctr_in[1], ctr_in[2], ctr_in[3]};
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t p0 = (uint64_t)M0 * c[0];
+        const uint64_t p1 = (uint64_t)M1 * c[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+    }
+    for (int i = 0; i < 4; i++) out[i] = c[i];
+}
+
+/* The uniform of element e for stochastic rounding (see the header). */
+static float sr_uniform(int64_t e, uint64_t seed, uint32_t offset, uint32_t tensor)
+{
+    const uint64_t q = (uint64_t)e >> 2;
+    const uint32_t ctr[4] = {(uint32_t)q, (uint32_t)(q >> 32), offset, tensor};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t r[4];
+    or_philox4x32_10(ctr, key, r);
+    return (float)(r[e & 3] >> 8) * 0x1p-24f;
+}
+
 /* ------------------------------------------------------------ q8 update */
+
+enum { OR_ROUND_NEAREST = 0, OR_ROUND_STOCHASTIC = 1 };
 
 /*
  * One tensor of `numel` elements.  codes/absmax hold the prior state and are
  * overwritten with the new state; grad holds g and is overwritten with m
  * rounded to its dtype.  block_sumsq (nullable) receives one fp64 sum of m*m
  * per block.  Blocks are [256 b, min(numel, 256 b + 256)): the last block of
- * a tensor covers the remainder.
+ * a tensor covers the remainder.  rounding: nearest, or stochastic with
+ * (seed, offset, tensor) selecting the random stream (header).
  */
-void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
-                  int64_t numel, float beta, double *block_sumsq)
+void or_q8_update_ex(int8_t *codes, float *absmax, void *grad, int dtype,
+                     int64_t numel, float beta, double *block_sumsq,
+                     int rounding, uint64_t seed, uint32_t offset, uint32_t tensor)
 {
     const int64_t nblk = (numel + OR_BLOCK - 1) / OR_BLOCK;
     const float omb = 1.0f - beta;
@@ -165,7 +219,14 @@ void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
         } else {
             const float inv = 127.0f / amax;
             for (int64_t i = lo; i < hi; i++) {
-                float q = rintf(m[i - lo] * inv);
+                const float x = m[i - lo] * inv;
+                float q;
+                if (rounding == OR_ROUND_STOCHASTIC) {
+                    const float fl = floorf(x);
+                    q = sr_uniform(i, seed, offset, tensor) < x - fl ? fl + 1.0f : fl;
+                } else {
+                    q = rintf(x);
+                }
                 if (q > 127.0f) q = 127.0f;
                 if (q < -127.0f) q = -127.0f;
                 codes[i] = (int8_t)q;
@@ -181,6 +242,12 @@ void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
             block_sumsq[b] = s;
         }
     }
+}
+
+void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
+                  int64_t numel, float beta, double *block_sumsq)
+{
+    or_q8_update_ex(codes, absmax, grad, dtype, numel, beta, block_sumsq, OR_ROUND_NEAREST, 0, 0, 0);
 }
 
 /* --------------------------------------------------------- group norms */
