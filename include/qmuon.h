@@ -122,6 +122,24 @@ QM_API qm_status qm_plan_info(const void *host_blob, int32_t *n_tensors,
 /* Workspace bytes qmuon_update_normalize_groups needs for this plan. */
 QM_API size_t qm_update_workspace_bytes(const void *host_blob);
 
+/* Requantisation rounding.  Nearest: round half to even.  Stochastic (the
+ * page lists it under "Known Limitations" as not yet implemented; this is
+ * the reading taken): x = m * (127 / absmax') as for nearest; the code is
+ * floor(x) + 1 if u < x - floor(x), else floor(x), clamped to [-127, 127],
+ * both operations in binary32; u = (r >> 8) * 2^-24 where r is word (e mod 4)
+ * of Philox4x32-10 ("Parallel random numbers: as easy as 1, 2, 3", Salmon,
+ * Moraes, Dror and Shaw, SC 2011) with counter (e / 4 low word, e / 4 high
+ * word, offset, the tensor's index in the plan) and key (seed low word, seed
+ * high word), e the element's index in its tensor.  The codes remain
+ * bit-identical to a CPU run of the same definition. */
+typedef enum { QM_ROUND_NEAREST = 0, QM_ROUND_STOCHASTIC = 1 } qm_rounding;
+
+typedef struct {
+    int32_t rounding;   /* qm_rounding                                        */
+    uint32_t offset;    /* counter word 2 (e.g. the step number)              */
+    uint64_t seed;      /* Philox key                                         */
+} qm_round_opts;
+
 /* In-place multi-tensor q8 update in one launch ("Quantized Muon Momentum",
  * sections "What Exists" and "Algorithm"): for every block of every tensor,
  * dequantise the old momentum in fp32, m = beta*old + (1-beta)*g (two
@@ -137,6 +155,13 @@ QM_API size_t qm_update_workspace_bytes(const void *host_blob);
 QM_API qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan,
                              float beta, double *block_sumsq,
                              qm_stream_t stream);
+
+/* qmuon_update_multi with the requantisation rounding chosen by `opts`
+ * (nullable: nearest).  Errors: as qmuon_update_multi; QM_E_ARG for an
+ * unknown rounding mode. */
+QM_API qm_status qmuon_update_multi_ex(const void *host_plan, const void *dev_plan,
+                                float beta, const qm_round_opts *opts,
+                                double *block_sumsq, qm_stream_t stream);
 
 /* The update plus grouped Frobenius normalisation ("Quantized Muon
  * Momentum", section "Grouped QKV And Sharding"): the update kernel
@@ -156,6 +181,17 @@ QM_API qm_status qmuon_update_normalize_groups(const void *host_plan,
                                         float *group_inv_norm,
                                         double *group_sumsq, void *ws,
                                         size_t ws_bytes, qm_stream_t stream);
+
+/* qmuon_update_normalize_groups with the requantisation rounding chosen by
+ * `opts` (nullable: nearest).  Errors: as qmuon_update_normalize_groups;
+ * QM_E_ARG for an unknown rounding mode. */
+QM_API qm_status qmuon_update_normalize_groups_ex(const void *host_plan,
+                                           const void *dev_plan, float beta,
+                                           float eps, int32_t write_normalized,
+                                           const qm_round_opts *opts,
+                                           float *group_inv_norm,
+                                           double *group_sumsq, void *ws,
+                                           size_t ws_bytes, qm_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Newton-Schulz orthogonalisation
@@ -217,6 +253,9 @@ typedef struct {
     int32_t ns_steps;    /* T                                                */
     int32_t period;      /* P: step t is full iff t % P == 0 (P <= 1: all)   */
     int32_t precision;   /* qm_ns_precision                                  */
+    int32_t rounding;    /* qm_rounding of the requantisation; stochastic uses
+                            the step number as the counter offset            */
+    uint64_t seed;       /* Philox key for stochastic rounding               */
 } qm_muon_hparams;
 
 typedef struct {

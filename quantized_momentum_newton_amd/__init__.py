@@ -142,19 +142,39 @@ class Plan:
         return torch.empty(max(self.workspace_bytes(), 256), dtype=torch.uint8, device=self.device)
 
 
-def qmuon_update_multi(plan, beta, block_sumsq=None, stream=None):
+ROUNDING = {"nearest": L.QM_ROUND_NEAREST, "stochastic": L.QM_ROUND_STOCHASTIC}
+
+
+def _round_opts(rounding, seed, offset):
+    if rounding == "nearest":
+        return None
+    return ctypes.byref(L.RoundOpts(ROUNDING[rounding], offset, seed))
+
+
+def qmuon_update_multi(plan, beta, block_sumsq=None, stream=None, rounding="nearest", seed=0, offset=0):
     """In-place q8 update of every tensor in the plan; block_sumsq (fp64
-    [n_blocks]) optionally receives the per-block sums of m*m."""
-    _check(_LIB.qmuon_update_multi(plan.hptr, plan.dptr, beta, _ptr(block_sumsq), _stream(stream)))
+    [n_blocks]) optionally receives the per-block sums of m*m.  rounding:
+    "nearest" or "stochastic" (random stream chosen by seed and offset)."""
+    if rounding == "nearest":
+        _check(_LIB.qmuon_update_multi(plan.hptr, plan.dptr, beta, _ptr(block_sumsq), _stream(stream)))
+    else:
+        _check(_LIB.qmuon_update_multi_ex(plan.hptr, plan.dptr, beta, _round_opts(rounding, seed, offset),
+                                          _ptr(block_sumsq), _stream(stream)))
 
 
 def qmuon_update_normalize_groups(plan, beta, eps, write_normalized=True, group_inv_norm=None,
-                                  group_sumsq=None, ws=None, stream=None):
+                                  group_sumsq=None, ws=None, stream=None, rounding="nearest", seed=0,
+                                  offset=0):
     if ws is None:
         ws = plan.workspace()
-    _check(_LIB.qmuon_update_normalize_groups(
-        plan.hptr, plan.dptr, beta, eps, int(write_normalized), _ptr(group_inv_norm),
-        _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
+    if rounding == "nearest":
+        _check(_LIB.qmuon_update_normalize_groups(
+            plan.hptr, plan.dptr, beta, eps, int(write_normalized), _ptr(group_inv_norm),
+            _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
+    else:
+        _check(_LIB.qmuon_update_normalize_groups_ex(
+            plan.hptr, plan.dptr, beta, eps, int(write_normalized), _round_opts(rounding, seed, offset),
+            _ptr(group_inv_norm), _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def _matrix_args(x):
@@ -203,10 +223,11 @@ def ns_orthogonalize_blocked(x, block_rows, block_cols, steps=5, coeffs=QUINTIC,
 
 
 def make_hparams(beta=0.95, eps=1e-7, coeffs=QUINTIC, lr_full=0.02, lr_block=0.01,
-                 weight_decay=0.0, rms_scale=0.2, ns_steps=5, period=5, precision="bf16"):
+                 weight_decay=0.0, rms_scale=0.2, ns_steps=5, period=5, precision="bf16",
+                 rounding="nearest", seed=0):
     a, b, c = coeffs
     return L.MuonHparams(beta, eps, a, b, c, lr_full, lr_block, weight_decay, rms_scale,
-                         ns_steps, period, PRECISION[precision])
+                         ns_steps, period, PRECISION[precision], ROUNDING[rounding], seed)
 
 
 def _matrices(mats):

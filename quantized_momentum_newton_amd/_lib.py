@@ -9,6 +9,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqmuon.so")
 
 QM_OK = 0
+QM_ROUND_NEAREST, QM_ROUND_STOCHASTIC = 0, 1
 STATUS_NAMES = {0: "QM_OK", 1: "QM_E_ARG", 2: "QM_E_ALIGN", 3: "QM_E_DTYPE",
                 4: "QM_E_SHAPE", 5: "QM_E_WORKSPACE", 6: "QM_E_HIP",
                 7: "QM_E_UNSUPPORTED", 8: "QM_E_PLAN"}
@@ -37,7 +38,11 @@ class MuonHparams(ctypes.Structure):
     _fields_ = [("beta", c_f32), ("eps", c_f32), ("a", c_f32), ("b", c_f32), ("c", c_f32),
                 ("lr_full", c_f32), ("lr_block", c_f32), ("weight_decay", c_f32),
                 ("rms_scale", c_f32), ("ns_steps", c_i32), ("period", c_i32),
-                ("precision", c_i32)]
+                ("precision", c_i32), ("rounding", c_i32), ("seed", ctypes.c_uint64)]
+
+
+class RoundOpts(ctypes.Structure):
+    _fields_ = [("rounding", c_i32), ("offset", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
 
 
 class MuonMatrix(ctypes.Structure):
@@ -61,6 +66,11 @@ SIGNATURES = {
     "qmuon_update_multi": (c_i32, [c_void_p, c_void_p, c_f32, c_void_p, c_void_p]),
     "qmuon_update_normalize_groups": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_i32,
                                               c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
+    "qmuon_update_multi_ex": (c_i32, [c_void_p, c_void_p, c_f32, ctypes.POINTER(RoundOpts), c_void_p,
+                                      c_void_p]),
+    "qmuon_update_normalize_groups_ex": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_i32,
+                                                 ctypes.POINTER(RoundOpts), c_void_p, c_void_p,
+                                                 c_void_p, c_size, c_void_p]),
     "ns_workspace_bytes": (c_size, [c_i64, c_i64, c_i32, c_i32]),
     "ns_orthogonalize": (c_i32, [c_void_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i64, c_i32,
                                  c_f32, c_f32, c_f32, c_f32, c_void_p, c_i32, c_void_p,

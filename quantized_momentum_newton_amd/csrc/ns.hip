@@ -1320,6 +1320,8 @@ qm_status check_hparams(const qm_muon_hparams *hp) {
         !std::isfinite(hp->rms_scale) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))
         return fail(QM_E_ARG, "hyperparameters must be finite");
     if (!(hp->eps >= 0.0f) || std::isinf(hp->eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    if (hp->rounding != QM_ROUND_NEAREST && hp->rounding != QM_ROUND_STOCHASTIC)
+        return fail(QM_E_ARG, "unknown rounding mode %d", hp->rounding);
     return QM_OK;
 }
 
@@ -1396,7 +1398,8 @@ extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t upd = align_up(qm_update_workspace_bytes(hplan), 256);
     const UpdateWorkspace uw = update_workspace(h, ws);
-    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, s);
+    const qm_round_opts ro{hp->rounding, (uint32_t)step, hp->seed};
+    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s);
     if (st != QM_OK) return st;
     return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, static_cast<char *>(ws) + upd, s);
 }

@@ -21,9 +21,10 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
                           const PlanHeader **out);
 
 // Update + per-group inverse norms (+ the in-place scale pass if asked).
-// inv_out / sums_out may be null: the workspace sections are used.
+// inv_out / sums_out may be null: the workspace sections are used.  ro:
+// requantisation rounding (null: nearest).
 qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
                                bool write_normalized, float *inv_out, double *sums_out, void *ws,
-                               hipStream_t stream);
+                               const qm_round_opts *ro, hipStream_t stream);
 
 }  // namespace qm

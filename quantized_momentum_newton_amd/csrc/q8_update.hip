@@ -167,9 +167,50 @@ __device__ __forceinline__ int find_tensor(const int64_t *task_offsets, int n, i
 
 // ------------------------------------------------------------ K1: update
 
-template <int DT, bool SUMS>
+// Stochastic rounding: Philox4x32-10 ("Parallel random numbers: as easy as
+// 1, 2, 3", Salmon, Moraes, Dror and Shaw, SC 2011): ten rounds, each
+// multiplying counter words 0 and 2 by two fixed constants and mixing the
+// high halves with the other words and the key, the key advanced by the two
+// Weyl constants between rounds.  Counter (e / 4 as 64 bits, offset, tensor),
+// key (seed); word e % 4 serves element e.
+struct SrParams {
+    uint64_t seed;
+    uint32_t offset;
+};
+
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t *out) {
+    constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; r++) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
+        const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+// Random words of elements e .. e+3 (e a multiple of 4) of tensor `tensor`.
+__device__ __forceinline__ void sr_words(int64_t e, const SrParams &sr, uint32_t tensor, uint32_t *out) {
+    const uint64_t q = (uint64_t)e >> 2;
+    philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), sr.offset, tensor, (uint32_t)sr.seed,
+                  (uint32_t)(sr.seed >> 32), out);
+}
+
+template <int DT, bool SUMS, bool SR>
 __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, float beta, float omb,
-                                            double *block_sums, int lane) {
+                                            double *block_sums, int lane, const SrParams &sr, uint32_t tensor) {
     constexpr int EPL = Elem<DT>::kEpl;
     constexpr int PARTS = kTaskElems / (64 * EPL);
     constexpr int LPB = kBlock / EPL;  // lanes per block
@@ -220,11 +261,27 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
         int8_t q[EPL];
+        if constexpr (SR) {
+            // floor(x) + 1 with probability frac(x); u = top 24 bits * 2^-24
+            uint32_t w[EPL];
 #pragma unroll
-        for (int j = 0; j < EPL; j++) {
-            float r = rintf(m[p][j] * inv);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            q[j] = (int8_t)(int)r;
+            for (int k = 0; k < EPL; k += 4) sr_words(e_task + e0 + k, sr, tensor, w + k);
+#pragma unroll
+            for (int j = 0; j < EPL; j++) {
+                const float x = m[p][j] * inv;
+                const float fl = floorf(x);
+                const float u = (float)(w[j] >> 8) * 0x1p-24f;
+                float r = u < x - fl ? fl + 1.0f : fl;
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                q[j] = (int8_t)(int)r;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPL; j++) {
+                float r = rintf(m[p][j] * inv);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                q[j] = (int8_t)(int)r;
+            }
         }
         if (e0 + EPL <= nvalid) {
             store_codes_vec<EPL>(codes, e0, q);
@@ -260,20 +317,22 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
 // the 16-bit paths fit 8 waves per SIMD in 64 VGPRs and the fp32 path 6
 // waves in 80, without spills (the kernel with all three element paths took
 // 112 VGPRs, i.e. 4 waves).
-template <int DT> constexpr int update_wgs_per_cu() { return DT == QM_F32 ? 6 : 8; }
+// With stochastic rounding the Philox state costs registers: 6 waves.
+template <int DT, bool SR> constexpr int update_wgs_per_cu() { return DT == QM_F32 || SR ? 6 : 8; }
 
-template <int DT, bool SUMS>
-__global__ __launch_bounds__(kThreads, update_wgs_per_cu<DT>()) void q8_update_kernel(
+template <int DT, bool SUMS, bool SR>
+__global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_update_kernel(
     const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
     const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
-    double *__restrict__ block_sums) {
+    double *__restrict__ block_sums, SrParams sr) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
     for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
-        const PlanTensor T = tensors[task_tensor[find_tensor(task_offsets, n_tensors, task)]];
-        update_task<DT, SUMS>(T, task - T.task_offset, beta, omb, block_sums, lane);
+        const int ti = task_tensor[find_tensor(task_offsets, n_tensors, task)];
+        const PlanTensor T = tensors[ti];
+        update_task<DT, SUMS, SR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti);
     }
 }
 
@@ -416,8 +475,9 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
     return QM_OK;
 }
 
-template <int DT>
-void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, hipStream_t stream) {
+template <int DT, bool SR>
+void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, const SrParams &sr,
+                      hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
@@ -425,19 +485,28 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
     const int grid = stream_grid(hi - lo);
     if (block_sums)
-        q8_update_kernel<DT, true><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
-                                                                 block_sums);
+        q8_update_kernel<DT, true, SR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
+                                                                     block_sums, sr);
     else
-        q8_update_kernel<DT, false><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
-                                                                  nullptr);
+        q8_update_kernel<DT, false, SR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
+                                                                      nullptr, sr);
+}
+
+template <bool SR>
+void launch_update_all(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
+                       const SrParams &sr, hipStream_t stream) {
+    launch_update_dt<QM_F32, SR>(h, dev_plan, beta, block_sums, sr, stream);
+    launch_update_dt<QM_BF16, SR>(h, dev_plan, beta, block_sums, sr, stream);
+    launch_update_dt<QM_F16, SR>(h, dev_plan, beta, block_sums, sr, stream);
 }
 
 qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                        hipStream_t stream) {
+                        const qm_round_opts *ro, hipStream_t stream) {
     Timed tm(stream, QM_K_Q8_UPDATE);
-    launch_update_dt<QM_F32>(h, dev_plan, beta, block_sums, stream);
-    launch_update_dt<QM_BF16>(h, dev_plan, beta, block_sums, stream);
-    launch_update_dt<QM_F16>(h, dev_plan, beta, block_sums, stream);
+    if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
+        launch_update_all<true>(h, dev_plan, beta, block_sums, SrParams{ro->seed, ro->offset}, stream);
+    else
+        launch_update_all<false>(h, dev_plan, beta, block_sums, SrParams{0, 0}, stream);
     return check_launch("q8 update");
 }
 
@@ -482,11 +551,11 @@ UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
 
 qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
                                bool write_normalized, float *inv_out, double *sums_out, void *ws,
-                               hipStream_t stream) {
+                               const qm_round_opts *ro, hipStream_t stream) {
     const UpdateWorkspace w = update_workspace(h, ws);
     float *inv = inv_out ? inv_out : w.inv;
     double *sums = sums_out ? sums_out : w.group_sums;
-    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, stream);
+    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, stream);
     if (st != QM_OK) return st;
     st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
     if (st != QM_OK) return st;
@@ -498,24 +567,33 @@ qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float 
 
 using namespace qm;
 
-extern "C" qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan, float beta,
-                                        double *block_sumsq, qm_stream_t stream) {
-    clear_error();
-    const PlanHeader *h = nullptr;
-    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
-    if (st != QM_OK) return st;
-    if (block_sumsq && !aligned(block_sumsq, 8)) return fail(QM_E_ALIGN, "block_sumsq must be 8-byte aligned");
-    return launch_update(h, dev_plan, beta, block_sumsq, static_cast<hipStream_t>(stream));
+namespace {
+
+qm_status check_round(const qm_round_opts *ro) {
+    if (ro && ro->rounding != QM_ROUND_NEAREST && ro->rounding != QM_ROUND_STOCHASTIC)
+        return fail(QM_E_ARG, "unknown rounding mode %d", ro->rounding);
+    return QM_OK;
 }
 
-extern "C" qm_status qmuon_update_normalize_groups(const void *host_plan, const void *dev_plan, float beta,
-                                                   float eps, int32_t write_normalized, float *group_inv_norm,
-                                                   double *group_sumsq, void *ws, size_t ws_bytes,
-                                                   qm_stream_t stream) {
+qm_status update_multi(const void *host_plan, const void *dev_plan, float beta, const qm_round_opts *ro,
+                       double *block_sumsq, qm_stream_t stream) {
     clear_error();
     const PlanHeader *h = nullptr;
     qm_status st = validate_update(host_plan, dev_plan, beta, &h);
     if (st != QM_OK) return st;
+    if ((st = check_round(ro)) != QM_OK) return st;
+    if (block_sumsq && !aligned(block_sumsq, 8)) return fail(QM_E_ALIGN, "block_sumsq must be 8-byte aligned");
+    return launch_update(h, dev_plan, beta, block_sumsq, ro, static_cast<hipStream_t>(stream));
+}
+
+qm_status update_normalize(const void *host_plan, const void *dev_plan, float beta, float eps,
+                           int32_t write_normalized, const qm_round_opts *ro, float *group_inv_norm,
+                           double *group_sumsq, void *ws, size_t ws_bytes, qm_stream_t stream) {
+    clear_error();
+    const PlanHeader *h = nullptr;
+    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
+    if (st != QM_OK) return st;
+    if ((st = check_round(ro)) != QM_OK) return st;
     if (!(eps >= 0.0f) || isinf(eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
     if (write_normalized != 0 && write_normalized != 1) return fail(QM_E_ARG, "write_normalized must be 0 or 1");
     if (group_inv_norm && !aligned(group_inv_norm, 4)) return fail(QM_E_ALIGN, "group_inv_norm alignment");
@@ -525,5 +603,33 @@ extern "C" qm_status qmuon_update_normalize_groups(const void *host_plan, const 
         return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
     if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
     return run_update_normalize(h, dev_plan, beta, eps, write_normalized != 0, group_inv_norm, group_sumsq, ws,
-                                static_cast<hipStream_t>(stream));
+                                ro, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan, float beta,
+                                        double *block_sumsq, qm_stream_t stream) {
+    return update_multi(host_plan, dev_plan, beta, nullptr, block_sumsq, stream);
+}
+
+extern "C" qm_status qmuon_update_multi_ex(const void *host_plan, const void *dev_plan, float beta,
+                                           const qm_round_opts *opts, double *block_sumsq, qm_stream_t stream) {
+    return update_multi(host_plan, dev_plan, beta, opts, block_sumsq, stream);
+}
+
+extern "C" qm_status qmuon_update_normalize_groups(const void *host_plan, const void *dev_plan, float beta,
+                                                   float eps, int32_t write_normalized, float *group_inv_norm,
+                                                   double *group_sumsq, void *ws, size_t ws_bytes,
+                                                   qm_stream_t stream) {
+    return update_normalize(host_plan, dev_plan, beta, eps, write_normalized, nullptr, group_inv_norm, group_sumsq,
+                            ws, ws_bytes, stream);
+}
+
+extern "C" qm_status qmuon_update_normalize_groups_ex(const void *host_plan, const void *dev_plan, float beta,
+                                                      float eps, int32_t write_normalized, const qm_round_opts *opts,
+                                                      float *group_inv_norm, double *group_sumsq, void *ws,
+                                                      size_t ws_bytes, qm_stream_t stream) {
+    return update_normalize(host_plan, dev_plan, beta, eps, write_normalized, opts, group_inv_norm, group_sumsq, ws,
+                            ws_bytes, stream);
 }

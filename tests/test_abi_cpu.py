@@ -191,3 +191,17 @@ def test_plan_strided_views_of_one_buffer(c1, ld1, off1, c2, ld2, off2, status):
         t.grad, t.grad_cols, t.grad_ld = base + off * 2, c, ld
     segs = _segs([(0, 0, 64 * c1, 0), (1, 0, 64 * c2, 1)])
     assert _encode(tens, segs, 2)[0] == status, LIB.qm_last_error()
+
+
+def test_rounding_options_are_validated():
+    tens = _tensors([(1024, L.QM_BF16)])
+    st, buf = _encode(tens, _segs([(0, 0, 1024, 0)]), 1)
+    hp = ctypes.cast(buf, ctypes.c_void_p)
+    fake_dev = ctypes.c_void_p(BASE)
+    bad = L.RoundOpts(7, 0, 0)
+    assert LIB.qmuon_update_multi_ex(hp, fake_dev, 0.9, ctypes.byref(bad), None, None) == 1
+    need = LIB.qm_update_workspace_bytes(hp)
+    assert LIB.qmuon_update_normalize_groups_ex(hp, fake_dev, 0.9, 1e-7, 1, ctypes.byref(bad), None, None,
+                                                ctypes.c_void_p(BASE), need, None) == 1
+    assert "rounding" in LIB.qm_last_error().decode()
+    assert ctypes.sizeof(L.MuonHparams) == 64 and ctypes.sizeof(L.RoundOpts) == 16

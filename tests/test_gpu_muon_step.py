@@ -206,3 +206,35 @@ def test_muon_step_on_strided_grad_views():
             _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"t{t} dW[{i}]")
             W_host[i] = as_f64(mats[i][4])
         assert bool((buf[:, 768:] == 7.0).all())
+
+
+def test_muon_step_stochastic_rounding_state():
+    """muon_step with stochastic requantisation: the state after steps 1..3 is
+    bit-identical to the oracle's update with the step number as the counter
+    offset (the NS half is the one checked by the other tests)."""
+    shapes = [(256, 512), (128, 256)]
+    seed = 99
+    trip, mats, states = [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3005, i)
+        g = torch.empty(r * c, dtype=torch.bfloat16, device=DEV)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, None))
+        states.append((host(codes), host(absmax)))
+    full, _ = _plans(trip, mats)
+    params = q.make_hparams(period=1, rounding="stochastic", seed=seed)
+    for t in range(1, 4):
+        for i, (r, c) in enumerate(shapes):
+            trip[i][2].copy_(H.grad((r, c), torch.bfloat16, DEV, 3005, i, t).reshape(-1))
+        torch.cuda.synchronize()
+        gh = [host_grad(trip[i][2]) for i in range(2)]
+        say("stochastic muon step", t)
+        q.muon_step(full, None, mats, t, params)
+        torch.cuda.synchronize()
+        segs = [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)]
+        st, _, _, _, _ = oracle.update_normalize_groups(states, gh, [oracle.BF16] * 2, segs, 2, 0.95, 1e-7, False,
+                                                        oracle.ROUND_STOCHASTIC, seed, t)
+        for i in range(2):
+            assert_bits_equal(host(trip[i][0]), st[i][0], f"t{t} codes[{i}]")
+            assert_bits_equal(host(trip[i][1]), st[i][1], f"t{t} absmax[{i}]")
+        states = [(c, a) for c, a in st]

@@ -336,3 +336,41 @@ def test_f16_negative_zero_survives_normalisation():
     assert_bits_equal(host(c_d), st[0][0], "codes")
     assert_bits_equal(host(a_d), st[0][1], "absmax")
     assert_bits_equal(host_grad(g_d), exp, "normalised grad")
+
+
+def test_stochastic_rounding_matches_oracle():
+    """Stochastic requantisation: codes, absmax, m and the normalised grads bit
+    for bit against the oracle's definition (Philox4x32-10 stream per element,
+    tensor index and offset) over mixed dtypes and ragged tails; another offset
+    gives other codes; the same offset the same ones."""
+    shapes = [(2048, 96), (1000,), (257, 33)]
+    dts = [torch.bfloat16, torch.float32, torch.float16]
+    segs = [(0, 0, 2048 * 96, 0), (1, 0, 1000, 1), (2, 0, 257 * 33, 2)]
+    seed, offset = 0x1234_5678_9abc_def0, 17
+    qs = Q8Set(shapes, dts, seed=1041)
+    plan = q.Plan(qs.triples(), segs, 3)
+    inv = torch.empty(3, dtype=torch.float32, device=DEV)
+    say("stochastic rounding: seed", hex(seed), "offset", offset)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv, rounding="stochastic",
+                                    seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    idx = [0, 1, 2]
+    st, outs, S, inv_o, _ = oracle.update_normalize_groups(
+        qs.host_states(idx), [qs.h_grads[i] for i in idx], [qs.odt(i) for i in idx], segs, 3, H.BETA, H.NS_EPS,
+        True, oracle.ROUND_STOCHASTIC, seed, offset)
+    for i in idx:
+        assert_bits_equal(host(qs.codes[i]), st[i][0], f"codes[{i}]")
+        assert_bits_equal(host(qs.absmax[i]), st[i][1], f"absmax[{i}]")
+        assert_bits_equal(host_grad(qs.grads[i]), outs[i], f"grad[{i}]")
+    near = oracle.update_normalize_groups(qs.host_states(idx), [qs.h_grads[i] for i in idx],
+                                          [qs.odt(i) for i in idx], segs, 3, H.BETA, H.NS_EPS, True)[0]
+    assert not np.array_equal(st[0][0], near[0][0])           # the stochastic path is exercised
+    # same stream twice, another offset
+    runs = []
+    for off in (5, 5, 6):
+        q2 = Q8Set(shapes, dts, seed=1041)
+        p2 = q.Plan(q2.triples(), segs, 3)
+        q.qmuon_update_multi(p2, H.BETA, rounding="stochastic", seed=seed, offset=off)
+        torch.cuda.synchronize()
+        runs.append(host(q2.codes[0]))
+    assert np.array_equal(runs[0], runs[1]) and not np.array_equal(runs[0], runs[2])
