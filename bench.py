@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "layerset28", "muonbp"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
+                    help="requantisation rounding of the update (the headline uses nearest)")
     ap.add_argument("--ref-copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once (a kernel of "
                          "known traffic, to calibrate HBM byte counters in a profiler run)")
@@ -211,12 +213,14 @@ def main():
     def step(t, ev):
         if args.workload == "layerset28":
             ev[0].record()
-            q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv, ws=ws_u)
+            q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv, ws=ws_u,
+                                            rounding=args.rounding, seed=1234, offset=t)
             ev[1].record()
             ev[2].record()
         elif args.workload == "llama8b":
             ev[0].record()
-            q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, False, group_inv_norm=inv, ws=ws_u)
+            q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, False, group_inv_norm=inv, ws=ws_u,
+                                            rounding=args.rounding, seed=1234, offset=t)
             ev[1].record()
             q.muon_apply(plan, mats, True, inv, hp, ws_ns)
             ev[2].record()
@@ -283,7 +287,8 @@ def main():
                     "ns_tflops": round(tfl, 2),
                     "config": {"workload": "llama8b_layer_muon_step", "matrices": len(tensors),
                                "elements": numel, "ns_steps": H.NS_STEPS, "ns_precision": "bf16",
-                               "grad_dtype": "bf16", "state": "int8", "update_ms": round(upd_ms, 4),
+                               "grad_dtype": "bf16", "state": "int8", "rounding": args.rounding,
+                               "update_ms": round(upd_ms, 4),
                                "ns_apply_ms": round(ns_ms, 4), "ns_flops_per_step": flops},
                     "roofline": rl[dom], "roofline_update": rl["q8_update"], "kernels": kernels})
     else:

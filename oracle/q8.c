@@ -37,7 +37,8 @@
  * the page; this is the reading taken for it):
  *   - x = m * (127 / amax) exactly as for nearest rounding; q = floor(x) + 1
  *     with probability frac(x) = x - floor(x), else floor(x); clamped to
- *     [-127, 127].  floor(x) and x - floor(x) are exact in binary32;
+ *     [-127, 127].  floor(x) is exact; x - floor(x) is one binary32
+ *     subtraction (exact for x >= 0, rounded once for some negative x);
  *   - the uniform u in [0, 1) is (r >> 8) * 2^-24 for a 32-bit word r of
  *     Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
  *     as easy as 1, 2, 3", SC 2011): counter (e / 4 low word, e / 4 high
