@@ -42,6 +42,13 @@ def lib():
         L.or_q8_update_ex.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p, ctypes.c_int,
                                       ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
         L.or_philox4x32_10.argtypes = [p, p, p]
+        L.or_e4m3_from_f32.argtypes = [ctypes.c_float]
+        L.or_e4m3_from_f32.restype = ctypes.c_uint8
+        L.or_f32_from_e4m3.argtypes = [ctypes.c_uint8]
+        L.or_f32_from_e4m3.restype = ctypes.c_float
+        L.or_mx_scale_byte.argtypes = [ctypes.c_float]
+        L.or_mx_scale_byte.restype = ctypes.c_uint8
+        L.or_q8_update_carrier.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p, p, p]
         L.or_q8_update.restype = None
         L.or_group_sums.argtypes = [p, p, i64, ctypes.c_int32, p]
         L.or_group_inv_norm.argtypes = [p, ctypes.c_int32, ctypes.c_float, p]
@@ -127,6 +134,53 @@ def q8_update(codes, absmax, grad, beta, dtype=F32, rounding=ROUND_NEAREST, seed
     lib().or_q8_update_ex(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel, ctypes.c_float(beta), _ptr(sums),
                           rounding, seed, offset, tensor)
     return codes, absmax, g, sums
+
+
+# ----------------------------------------------------------- MXFP8 carrier
+
+def e4m3_from_f32(v):
+    """fp32 -> E4M3 byte: round to nearest even, saturating at +-448 (q8.c)."""
+    return int(lib().or_e4m3_from_f32(float(np.float32(v))))
+
+
+def f32_from_e4m3(c):
+    return float(lib().or_f32_from_e4m3(int(c)))
+
+
+def mx_scale_byte(amax):
+    """E8M0 scale byte of a 32-element block with absolute maximum amax."""
+    return int(lib().or_mx_scale_byte(float(np.float32(amax))))
+
+
+def decode_carrier(payload, scales):
+    """Payload bytes [n] and scale bytes [n / 32] -> fp64 values (m as carried)."""
+    payload = np.asarray(payload, np.uint8).ravel()
+    scales = np.asarray(scales, np.uint8).ravel()
+    table = np.array([f32_from_e4m3(c) for c in range(256)], dtype=np.float64)
+    x = table[payload].reshape(-1, 32)
+    return (x * np.ldexp(1.0, scales.astype(np.int64) - 127)[:, None]).ravel()
+
+
+def q8_update_carrier(codes, absmax, grad, beta, dtype=F32):
+    """The q8 update emitting the MXFP8 carrier instead of writing m (q8.c,
+    "Wave18B MXFP8 Carrier Probe").  numel a multiple of 32.  Returns (codes',
+    absmax', payload uint8 [numel], scales uint8 [numel / 32], block_sumsq).
+    codes and absmax are copied; the grad goes to the C routine as it is, which
+    only reads it."""
+    codes = np.array(codes, dtype=np.int8, copy=True).ravel()
+    absmax = np.array(absmax, dtype=np.float32, copy=True).ravel()
+    g = np.ascontiguousarray(grad, dtype=np.float32 if dtype == F32 else np.uint16).reshape(-1)  # read in place
+    numel = codes.size
+    if numel % 32:
+        raise ValueError("numel must be a multiple of 32")
+    if absmax.size != (numel + BLOCK - 1) // BLOCK or g.size != numel:
+        raise ValueError("shape mismatch between codes, absmax and grad")
+    payload = np.zeros(numel, np.uint8)
+    scales = np.zeros(numel // 32, np.uint8)
+    sums = np.empty((numel + BLOCK - 1) // BLOCK, dtype=np.float64)
+    lib().or_q8_update_carrier(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel, ctypes.c_float(beta),
+                               _ptr(payload), _ptr(scales), _ptr(sums))
+    return codes, absmax, payload, scales, sums
 
 
 # -------------------------------------------------------------- norm plans

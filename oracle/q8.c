@@ -251,6 +251,127 @@ void or_q8_update(int8_t *codes, float *absmax, void *grad, int dtype,
     or_q8_update_ex(codes, absmax, grad, dtype, numel, beta, block_sumsq, OR_ROUND_NEAREST, 0, 0, 0);
 }
 
+/* -------------------------------------------------------- MXFP8 carrier */
+
+/*
+ * "Quantized Muon Momentum", section "Wave18B MXFP8 Carrier Probe": the
+ * update emits, instead of writing m into the grad buffer, a row-wise MXFP8
+ * carrier (E4M3 payload bytes, one E8M0 scale byte per 32 elements of a row)
+ * plus one fp32 inverse Frobenius norm.  Readings (design notes): the payload
+ * encodes the fp32 m of the update (one pass; inv_norm beside it carries the
+ * normalisation); the scale of a 32-element block is 2^(floor(log2 amax) - 8)
+ * (the OCP Microscaling rule for E4M3, whose largest exponent is 8), E8M0
+ * byte = that exponent + 127, clamped to [0, 254]; an all-zero block has
+ * scale byte 0 and zero payload; elements are m / scale rounded to E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities) to nearest even, saturating at +-448.
+ */
+uint8_t or_e4m3_from_f32(float v)
+{
+    const uint32_t u = bits_of(v);
+    const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+    const float a = fabsf(v);
+    if (a != a) return (uint8_t)(sign | 0x7Fu);            /* NaN */
+    if (a >= 0x1p-6f) {                                     /* normal range */
+        uint32_t w = bits_of(a);
+        w += 0x7FFFFu + ((w >> 20) & 1u);                   /* round to 3 mantissa bits, ties to even */
+        w &= 0xFFF00000u;
+        const float r = float_of(w);
+        if (r > 448.0f) return (uint8_t)(sign | 0x7Eu);     /* saturate */
+        const uint32_t e = ((w >> 23) & 0xFFu) - 127u + 7u;  /* 1 .. 15 */
+        const uint32_t m = (w >> 20) & 7u;
+        return (uint8_t)(sign | (e << 3) | m);
+    }
+    /* subnormal: multiples of 2^-9 (a rounds to 8 = the smallest normal) */
+    const float n = rintf(a * 512.0f);
+    return (uint8_t)(sign | (uint8_t)n);
+}
+
+float or_f32_from_e4m3(uint8_t c)
+{
+    const float s = (c & 0x80u) ? -1.0f : 1.0f;
+    const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    if (e == 0xFu && m == 7u) return s * NAN;
+    if (e == 0) return s * (float)m * 0x1p-9f;
+    return s * ldexpf(1.0f + (float)m / 8.0f, (int)e - 7);
+}
+
+/* E8M0 scale byte of a block with absolute maximum amax (finite, >= 0). */
+uint8_t or_mx_scale_byte(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int e2;
+    frexpf(amax, &e2);                 /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+    int e = (e2 - 1) - 8;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (uint8_t)(e + 127);
+}
+
+/*
+ * The q8 update with the carrier in place of writing m: codes/absmax as
+ * or_q8_update (nearest rounding), grad only read, payload [numel] and
+ * scales [numel / 32] written; numel and cols multiples of 32.
+ */
+void or_q8_update_carrier(int8_t *codes, float *absmax, const void *grad, int dtype,
+                          int64_t numel, float beta, uint8_t *payload, uint8_t *scales,
+                          double *block_sumsq)
+{
+    const int64_t nblk = (numel + OR_BLOCK - 1) / OR_BLOCK;
+    const float omb = 1.0f - beta;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; b++) {
+        const int64_t lo = b * OR_BLOCK;
+        const int64_t hi = (lo + OR_BLOCK < numel) ? lo + OR_BLOCK : numel;
+        float m[OR_BLOCK];
+        const float step = absmax[b] / 127.0f;
+        float amax = 0.0f;
+        for (int64_t i = lo; i < hi; i++) {
+            const float old = (float)codes[i] * step;
+            const float g = load_grad(grad, dtype, i);
+            const float t1 = beta * old;
+            const float t2 = omb * g;
+            const float mi = t1 + t2;
+            m[i - lo] = mi;
+            const float a = fabsf(mi);
+            if (a > amax) amax = a;
+        }
+        /* carrier: 32-element MX blocks inside this 256-block */
+        for (int64_t k = lo; k < hi; k += 32) {
+            float bm = 0.0f;
+            for (int64_t i = k; i < k + 32; i++) {
+                const float a = fabsf(m[i - lo]);
+                if (a > bm) bm = a;
+            }
+            const uint8_t sb = or_mx_scale_byte(bm);
+            scales[k / 32] = sb;
+            const float inv_scale = ldexpf(1.0f, -((int)sb - 127));   /* 1 / 2^(sb - 127), exact */
+            for (int64_t i = k; i < k + 32; i++)
+                payload[i] = bm == 0.0f ? 0 : or_e4m3_from_f32(m[i - lo] * inv_scale);
+        }
+        if (amax == 0.0f) {
+            for (int64_t i = lo; i < hi; i++) codes[i] = 0;
+        } else {
+            const float inv = 127.0f / amax;
+            for (int64_t i = lo; i < hi; i++) {
+                float q = rintf(m[i - lo] * inv);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+                codes[i] = (int8_t)q;
+            }
+        }
+        absmax[b] = amax;
+        if (block_sumsq) {
+            double s = 0.0;
+            for (int64_t i = lo; i < hi; i++) {
+                const double d = (double)m[i - lo];
+                s += d * d;
+            }
+            block_sumsq[b] = s;
+        }
+    }
+}
+
 /* --------------------------------------------------------- group norms */
 
 /* S_g = sum of block sums of group g, blocks visited in ascending order. */
