@@ -159,3 +159,16 @@ def config5_shape():
     """GRASP-shaped 4096x4096, rank 8, 64x64 grid blocks, mu=0.95, 20 steps."""
     return dict(rows=4096, cols=4096, rank=8, grid=64, mu=0.95, steps=20,
                 lr=0.02, weight_decay=0.0)
+
+
+def carrier_bytes(rows, cols, device, *keys, scale_lo=110, scale_hi=126):
+    """Random MXFP8 carrier arrays of a rows x cols matrix: payload bytes
+    uniform over every code except the two NaN patterns (0x7F, 0xFF, which
+    become 0x7E, 0xFE), one scale byte per 32 elements of a row, uniform in
+    [scale_lo, scale_hi]."""
+    g = gen(device, 5, *keys)
+    data = torch.randint(0, 256, (rows, cols), generator=g, device=device, dtype=torch.int32)
+    data = torch.where((data & 0x7F) == 0x7F, data - 1, data).to(torch.uint8)
+    scale = torch.randint(scale_lo, scale_hi + 1, (rows, cols // 32), generator=g, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+    return data, scale

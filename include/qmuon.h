@@ -27,7 +27,7 @@
 extern "C" {
 #endif
 
-#define QM_ABI_VERSION 2
+#define QM_ABI_VERSION 3
 #define QM_BLOCK 256           /* quantisation block: elements per absmax */
 
 typedef void *qm_stream_t;     /* hipStream_t */
@@ -193,6 +193,40 @@ QM_API qm_status qmuon_update_normalize_groups_ex(const void *host_plan,
                                            double *group_sumsq, void *ws,
                                            size_t ws_bytes, qm_stream_t stream);
 
+/* The update emitting a row-wise MXFP8 carrier of m instead of writing m
+ * to the grads ("Quantized Muon Momentum", section "Wave18B MXFP8 Carrier
+ * Probe": uint8 E4M3 data, uint8 E8M0 inverse scales per 32 elements of a
+ * row, one fp32 inverse Frobenius norm).  State: as qmuon_update_multi
+ * with nearest rounding; the grads are only read.  Per 32 consecutive
+ * elements of a tensor: amax = max|m|, scale byte
+ * sb = clamp(floor(log2 amax) - 8, -127, 127) + 127 (0 when amax == 0),
+ * data bytes = E4M3 of m * 2^(127 - sb) rounded to nearest even and
+ * saturated at +-448 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, no infinities); m ~ E4M3 * 2^(sb - 127).  inv_norm: as
+ * group_inv_norm of qmuon_update_normalize_groups, the input scale of
+ * Newton-Schulz being inv_norm[g] times the decoded carrier.
+ *   Layout: both arrays cover every tensor of the plan; tensor t occupies
+ *   data bytes [256 B_t, 256 B_t + numel_t) and scale bytes
+ *   [8 B_t, 8 B_t + numel_t / 32), B_t = sum of ceil(numel_s / 256) over the
+ *   tensors s before t.  A row-major rows x cols tensor with cols % 32 == 0
+ *   therefore has data shaped (rows, cols) and scales (rows, cols / 32).
+ *   rowwise_data:      [n_blocks * 256] bytes, 8-byte aligned.
+ *   rowwise_scale_inv: [n_blocks * 8] bytes.
+ *   inv_norm:          [n_groups] fp32 out, required.
+ *   group_sumsq:       nullable [n_groups] fp64 out.
+ *   ws: >= qm_update_workspace_bytes(host_plan) bytes, 256-byte aligned.
+ * Every tensor's numel must be a multiple of 32 (else QM_E_SHAPE); the
+ * carrier arrays must not overlap each other (QM_E_ARG) or the plan's
+ * buffers.  Errors: QM_E_ARG, QM_E_ALIGN, QM_E_SHAPE, QM_E_PLAN,
+ * QM_E_WORKSPACE, QM_E_HIP. */
+QM_API qm_status qmuon_update_mxfp8_carrier(const void *host_plan,
+                                            const void *dev_plan, float beta,
+                                            float eps, uint8_t *rowwise_data,
+                                            uint8_t *rowwise_scale_inv,
+                                            float *inv_norm,
+                                            double *group_sumsq, void *ws,
+                                            size_t ws_bytes, qm_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Newton-Schulz orthogonalisation
  *
@@ -239,6 +273,26 @@ QM_API qm_status ns_orthogonalize_blocked(void *x, int32_t dtype, int64_t rows,
                                    int32_t precision, void *ws,
                                    size_t ws_bytes, qm_stream_t stream);
 
+/* Newton-Schulz of one rows x cols matrix handed over as an MXFP8 carrier
+ * ("Quantized Muon Momentum", section "Wave18B MXFP8 Carrier Probe"; the
+ * carrier of qmuon_update_mxfp8_carrier): X0 = inv_norm[0] * decode(data,
+ * scale), decode(r, c) = E4M3(rowwise_data[r * cols + c]) *
+ * 2^(rowwise_scale_inv[r * (cols / 32) + c / 32] - 127), then the iteration
+ * of ns_orthogonalize; O is written to out (rows x cols, row pitch out_ld
+ * elements, out_dtype).
+ *   rowwise_data: [rows * cols] bytes, 8-byte aligned; cols % 32 == 0.
+ *   rowwise_scale_inv: [rows * cols / 32] bytes.  inv_norm: device fp32
+ *   [1], required.  ws: >= ns_workspace_bytes(rows, cols, 1, precision).
+ * Errors: as ns_orthogonalize. */
+QM_API qm_status ns_orthogonalize_mxfp8(const uint8_t *rowwise_data,
+                                        const uint8_t *rowwise_scale_inv,
+                                        const float *inv_norm, int64_t rows,
+                                        int64_t cols, void *out,
+                                        int32_t out_dtype, int64_t out_ld,
+                                        int32_t steps, float a, float b,
+                                        float c, int32_t precision, void *ws,
+                                        size_t ws_bytes, qm_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * One full optimizer step
  * ---------------------------------------------------------------------- */
@@ -255,6 +309,11 @@ typedef struct {
     int32_t precision;   /* qm_ns_precision                                  */
     int32_t rounding;    /* qm_rounding of the requantisation; stochastic uses
                             the step number as the counter offset            */
+    int32_t carrier;     /* 1: the update hands m to Newton-Schulz as the
+                            MXFP8 carrier of qmuon_update_mxfp8_carrier (in
+                            the workspace; grads only read until O is
+                            written; nearest rounding; cols and block_cols
+                            multiples of 32); 0: m is written to the grads */
     uint64_t seed;       /* Philox key for stochastic rounding               */
 } qm_muon_hparams;
 
@@ -264,11 +323,20 @@ typedef struct {
     float *weight;                   /* fp32 [rows*cols], nullable           */
 } qm_muon_matrix;
 
-/* Workspace for muon_step over these matrices (both step kinds). */
+/* Workspace for muon_step over these matrices (both step kinds), with
+ * carrier = 0. */
 QM_API size_t muon_step_workspace_bytes(const void *host_plan_full,
                                  const void *host_plan_block,
                                  const qm_muon_matrix *mats, int32_t n_mats,
                                  int32_t precision);
+
+/* Workspace for muon_step with these hyperparameters: as above, plus
+ * 264 bytes per 256-element block for the carrier when hp->carrier = 1.
+ * 0 if the plans, matrices or hp are unusable. */
+QM_API size_t muon_step_workspace_bytes_ex(const void *host_plan_full,
+                                    const void *host_plan_block,
+                                    const qm_muon_matrix *mats, int32_t n_mats,
+                                    const qm_muon_hparams *hp);
 
 /* One Muon step with block-periodic orthogonalisation ("MuonBP ...",
  * flowchart and key designs 2-3):

@@ -55,16 +55,25 @@ def block_group_ids(rows, cols, block_rows, block_cols):
 
 def muon_step(W, codes, absmax, grad, dtype, t, rows, cols, block_rows,
               block_cols, period, beta, eps, coeffs, ns_steps, lr_full,
-              lr_block, rms_scale, weight_decay=0.0):
-    """One step for one matrix.  Returns (W', codes', absmax', O, full)."""
+              lr_block, rms_scale, weight_decay=0.0, carrier=False):
+    """One step for one matrix.  Returns (W', codes', absmax', O, full).
+
+    carrier: m reaches Newton-Schulz as the MXFP8 carrier ("Quantized Muon
+    Momentum", section "Wave18B MXFP8 Carrier Probe"): the NS input is the
+    decoded carrier times the group inverse norm, which still comes from the
+    fp32 m of the update; otherwise it is m as stored in the grad dtype."""
     full = is_full_step(t, period)
     br, bc = (rows, cols) if full else (block_rows, block_cols)
     gid = block_group_ids(rows, cols, br, bc)
     ngroups = (rows // br) * (cols // bc)
-    c2, a2, m, bsum = oracle.q8_update(codes, absmax, grad, beta, dtype)
+    if carrier:
+        c2, a2, payload, scales, bsum = oracle.q8_update_carrier(codes, absmax, grad, beta, dtype)
+        mf = oracle.decode_carrier(payload, scales)
+    else:
+        c2, a2, m, bsum = oracle.q8_update(codes, absmax, grad, beta, dtype)
+        mf = (m if dtype == oracle.F32 else oracle.widen(m, dtype)).astype(np.float64)
     S = oracle.group_sums([bsum], [gid], ngroups)
     inv = oracle.group_inv_norm(S, eps)
-    mf = (m if dtype == oracle.F32 else oracle.widen(m, dtype)).astype(np.float64)
     mf = mf.reshape(rows, cols)
     O = ns.ns_blocked(mf, br, bc, ns_steps, coeffs, eps, inv_norms=inv)
     lr = lr_full if full else lr_block

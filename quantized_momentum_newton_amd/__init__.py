@@ -9,6 +9,9 @@ Entry points (same names as the C ABI in include/qmuon.h):
   Plan(...)                        qm_plan_encode + one host-to-device copy
   qmuon_update_multi               q8 momentum update, many tensors, one launch
   qmuon_update_normalize_groups    update + grouped Frobenius normalisation
+  MXCarrier, qmuon_update_mxfp8_carrier
+                                   update emitting the MXFP8 carrier of m
+  ns_orthogonalize_mxfp8           Newton-Schulz of a carrier-held matrix
   ns_orthogonalize                 quintic Newton-Schulz, batched
   ns_orthogonalize_blocked         blockwise Newton-Schulz
   muon_step                        update + NS + weight apply, block-periodic
@@ -25,6 +28,7 @@ from . import _lib as L
 _LIB = L.load()
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
+BLOCK = 256      # elements per absmax block
 PRECISION = {"bf16": L.QM_NS_BF16, "f32": L.QM_NS_F32}
 _DTYPES = {torch.float32: L.QM_F32, torch.bfloat16: L.QM_BF16, torch.float16: L.QM_F16}
 
@@ -126,6 +130,11 @@ class Plan:
         self.n_tensors, self.n_groups = nt.value, ng.value
         self.n_blocks, self.total_numel = nb.value, numel.value
         self.device = dev
+        # global index of each tensor's first 256-element block (plan order)
+        self.numels = [int(t[2].numel()) for t in tensors]
+        self.block_offsets = [0]
+        for n_ in self.numels[:-1]:
+            self.block_offsets.append(self.block_offsets[-1] + -(-n_ // BLOCK))
 
     @property
     def hptr(self):
@@ -177,6 +186,67 @@ def qmuon_update_normalize_groups(plan, beta, eps, write_normalized=True, group_
             _ptr(group_inv_norm), _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+class MXCarrier:
+    """Row-wise MXFP8 carrier arrays covering every tensor of a plan (the
+    layout qmuon_update_mxfp8_carrier writes): E4M3 bytes [n_blocks * 256],
+    E8M0 scale bytes [n_blocks * 8], fp32 inverse norms [n_groups]."""
+
+    def __init__(self, plan):
+        self.plan = plan
+        dev = plan.device
+        self.rowwise_data = torch.empty(plan.n_blocks * BLOCK, dtype=torch.uint8, device=dev)
+        self.rowwise_scale_inv = torch.empty(plan.n_blocks * (BLOCK // 32), dtype=torch.uint8, device=dev)
+        self.inv_norm = torch.empty(plan.n_groups, dtype=torch.float32, device=dev)
+
+    def data(self, i, shape=None):
+        """Tensor i's E4M3 bytes (numel, or shaped (rows, cols))."""
+        e0, n = self.plan.block_offsets[i] * BLOCK, self.plan.numels[i]
+        v = self.rowwise_data[e0:e0 + n]
+        return v.view(shape) if shape is not None else v
+
+    def scale_inv(self, i, shape=None):
+        """Tensor i's E8M0 bytes (numel / 32, or shaped (rows, cols / 32))."""
+        e0, n = self.plan.block_offsets[i] * (BLOCK // 32), self.plan.numels[i] // 32
+        v = self.rowwise_scale_inv[e0:e0 + n]
+        return v.view(shape[0], shape[1] // 32) if shape is not None else v
+
+
+def qmuon_update_mxfp8_carrier(plan, beta, eps, carrier=None, group_sumsq=None, ws=None, stream=None):
+    """q8 update of every tensor in the plan emitting the MXFP8 carrier of m
+    (and the group inverse norms into carrier.inv_norm); grads are only read.
+    Returns the carrier."""
+    if carrier is None:
+        carrier = MXCarrier(plan)
+    if ws is None:
+        ws = plan.workspace()
+    _check(_LIB.qmuon_update_mxfp8_carrier(plan.hptr, plan.dptr, beta, eps, _ptr(carrier.rowwise_data),
+                                           _ptr(carrier.rowwise_scale_inv), _ptr(carrier.inv_norm),
+                                           _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
+    return carrier
+
+
+def ns_orthogonalize_mxfp8(data, scale_inv, inv_norm, out, steps=5, coeffs=QUINTIC, precision="bf16",
+                           ws=None, stream=None):
+    """NS of the rows x cols matrix carried as (data uint8 (rows, cols),
+    scale_inv uint8 (rows, cols / 32), inv_norm fp32 [1]); O written to out
+    (rows x cols, unit column stride, fp32/bf16/f16)."""
+    rows, cols = out.shape
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    for t in (data, scale_inv):
+        if not t.is_contiguous():
+            raise ValueError("carrier arrays must be contiguous")
+    if data.numel() != rows * cols or scale_inv.numel() * 32 != rows * cols:
+        raise ValueError("carrier arrays do not match out's shape")
+    prec = PRECISION[precision]
+    if ws is None:
+        ws = torch.empty(_LIB.ns_workspace_bytes(rows, cols, 1, prec), dtype=torch.uint8, device=out.device)
+    a, b, c = coeffs
+    _check(_LIB.ns_orthogonalize_mxfp8(_ptr(data), _ptr(scale_inv), _ptr(inv_norm), rows, cols, _ptr(out),
+                                       _dtype(out), out.stride(0), steps, a, b, c, prec, _ptr(ws), ws.numel(),
+                                       _stream(stream)))
+
+
 def _matrix_args(x):
     if x.dim() == 2:
         rows, cols = x.shape
@@ -224,10 +294,10 @@ def ns_orthogonalize_blocked(x, block_rows, block_cols, steps=5, coeffs=QUINTIC,
 
 def make_hparams(beta=0.95, eps=1e-7, coeffs=QUINTIC, lr_full=0.02, lr_block=0.01,
                  weight_decay=0.0, rms_scale=0.2, ns_steps=5, period=5, precision="bf16",
-                 rounding="nearest", seed=0):
+                 rounding="nearest", seed=0, carrier=False):
     a, b, c = coeffs
     return L.MuonHparams(beta, eps, a, b, c, lr_full, lr_block, weight_decay, rms_scale,
-                         ns_steps, period, PRECISION[precision], ROUNDING[rounding], seed)
+                         ns_steps, period, PRECISION[precision], ROUNDING[rounding], int(carrier), seed)
 
 
 def _matrices(mats):
@@ -237,8 +307,11 @@ def _matrices(mats):
     return arr
 
 
-def muon_step_workspace_bytes(plan_full, plan_block, mats, precision="bf16"):
+def muon_step_workspace_bytes(plan_full, plan_block, mats, precision="bf16", hparams=None):
     arr = _matrices(mats)
+    if hparams is not None:
+        return _LIB.muon_step_workspace_bytes_ex(plan_full.hptr, plan_block.hptr if plan_block else None,
+                                                 arr, len(mats), ctypes.byref(hparams))
     return _LIB.muon_step_workspace_bytes(plan_full.hptr, plan_block.hptr if plan_block else None,
                                           arr, len(mats), PRECISION[precision])
 
@@ -248,9 +321,9 @@ def muon_step(plan_full, plan_block, mats, step, hparams, ws=None, stream=None):
     block_cols, weight fp32 tensor or None), tensor i of both plans."""
     arr = _matrices(mats)
     if ws is None:
-        nbytes = _LIB.muon_step_workspace_bytes(plan_full.hptr,
-                                                plan_block.hptr if plan_block else None,
-                                                arr, len(mats), hparams.precision)
+        nbytes = _LIB.muon_step_workspace_bytes_ex(plan_full.hptr,
+                                                   plan_block.hptr if plan_block else None,
+                                                   arr, len(mats), ctypes.byref(hparams))
         ws = torch.empty(nbytes, dtype=torch.uint8, device=plan_full.device)
     _check(_LIB.muon_step(plan_full.hptr, plan_full.dptr,
                           plan_block.hptr if plan_block else None,

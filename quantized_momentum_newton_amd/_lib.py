@@ -38,7 +38,8 @@ class MuonHparams(ctypes.Structure):
     _fields_ = [("beta", c_f32), ("eps", c_f32), ("a", c_f32), ("b", c_f32), ("c", c_f32),
                 ("lr_full", c_f32), ("lr_block", c_f32), ("weight_decay", c_f32),
                 ("rms_scale", c_f32), ("ns_steps", c_i32), ("period", c_i32),
-                ("precision", c_i32), ("rounding", c_i32), ("seed", ctypes.c_uint64)]
+                ("precision", c_i32), ("rounding", c_i32), ("carrier", c_i32),
+                ("seed", ctypes.c_uint64)]
 
 
 class RoundOpts(ctypes.Structure):
@@ -71,6 +72,12 @@ SIGNATURES = {
     "qmuon_update_normalize_groups_ex": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_i32,
                                                  ctypes.POINTER(RoundOpts), c_void_p, c_void_p,
                                                  c_void_p, c_size, c_void_p]),
+    "qmuon_update_mxfp8_carrier": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_size, c_void_p]),
+    "ns_orthogonalize_mxfp8": (c_i32, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i32, c_i64,
+                                       c_i32, c_f32, c_f32, c_f32, c_i32, c_void_p, c_size, c_void_p]),
+    "muon_step_workspace_bytes_ex": (c_size, [c_void_p, c_void_p, ctypes.POINTER(MuonMatrix), c_i32,
+                                              ctypes.POINTER(MuonHparams)]),
     "ns_workspace_bytes": (c_size, [c_i64, c_i64, c_i32, c_i32]),
     "ns_orthogonalize": (c_i32, [c_void_p, c_i32, c_i64, c_i64, c_i64, c_i32, c_i64, c_i32,
                                  c_f32, c_f32, c_f32, c_f32, c_void_p, c_i32, c_void_p,

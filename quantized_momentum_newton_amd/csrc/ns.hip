@@ -633,9 +633,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 
 // ------------------------------------------------------- norm + prologue
 
+// Source format code of an MXFP8 carrier (payload bytes + per-32 E8M0
+// scales); the public qm_dtype codes are 0..2.
+constexpr int32_t kSrcMx8 = 16;
+
 struct NsItem {
     const void *src;
     int64_t ld;
+    const uint8_t *sc;     // carrier scales (kSrcMx8): byte (r, c / 32) at sc[r * sld + c / 32]
+    int64_t sld;
     int32_t dtype;
     int32_t tall;
     const float *inv;      // device scale, or null: computed from the data
@@ -665,6 +671,7 @@ __device__ __forceinline__ int find_item(const PrologueArgs &a, int L) {
 __global__ __launch_bounds__(256) void norm_partial_kernel(PrologueArgs a, double *partials) {
     const int item = blockIdx.y;
     const NsItem &it = a.it[item];
+    if (it.inv) return;   // scale given (always so for a carrier source): nothing to sum
     const int64_t rows = it.tall ? it.n : it.m, cols = it.tall ? it.m : it.n;
     const int64_t per = (rows + kNormChunks - 1) / kNormChunks;
     const int64_t r0 = blockIdx.x * per, r1 = min(rows, r0 + per);
@@ -741,6 +748,32 @@ __device__ __forceinline__ int seg_len(int64_t row, int64_t col, int64_t rows, i
     return cols - col < 8 ? (int)(cols - col) : 8;
 }
 
+// Eight carrier elements (r, c .. c+7) of one 32-element block, as fp32:
+// E4M3 byte (sign, 4 exponent bits biased by 7, 3 mantissa bits,
+// subnormals k 2^-9, S.1111.111 NaN) times 2^(scale byte - 127).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t mag = c & 0x7fu;
+    float v = mag >= 8u ? __uint_as_float((mag + (120u << 3)) << 20)   // rebias the exponent 7 -> 127
+                        : (float)mag * 0x1p-9f;
+    if (mag == 0x7fu) v = __builtin_nanf("");
+    return (c & 0x80u) ? -v : v;
+}
+__device__ __forceinline__ void load_mx8(const uint8_t *data, const uint8_t *sc, int64_t r, int64_t c, int64_t ld,
+                                         int64_t sld, int n, float *v) {
+    if (n == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) v[k] = 0.0f;
+        return;
+    }
+    const uint2 w = *reinterpret_cast<const uint2 *>(data + r * ld + c);
+    const int e = (int)sc[r * sld + c / 32] - 127;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        v[k] = ldexpf(e4m3_value((w.x >> (8 * k)) & 0xffu), e);
+        v[4 + k] = ldexpf(e4m3_value((w.y >> (8 * k)) & 0xffu), e);
+    }
+}
+
 // X0 = orient(src) * inv, written as X (m_p x n_p) and, for fp32 runs, X^T
 // (n_p x m_p), zero outside the valid extent.  One 64x64 tile per workgroup:
 // each thread moves 8-element row segments (16-byte accesses where aligned),
@@ -763,7 +796,11 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
         const int rr = r + 32 * pass;
         const int64_t sr = sr0 + rr, sc = sc0 + c8;
         float v[8];
-        load_seg(it.src, sr * it.ld + sc, it.dtype, seg_len(sr, sc, srows, scols), it.vec, v);
+        const int n = seg_len(sr, sc, srows, scols);
+        if (it.dtype == kSrcMx8)   // row length a multiple of 32: n is 0 or 8
+            load_mx8(static_cast<const uint8_t *>(it.src), it.sc, sr, sc, it.ld, it.sld, n, v);
+        else
+            load_seg(it.src, sr * it.ld + sc, it.dtype, n, it.vec, v);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             if (it.tall) tile[c8 + k][rr] = v[k] * s;
@@ -844,12 +881,15 @@ struct NsRequest {
     const void *src;      // matrix start
     void *out;            // where the result goes (== src for in place)
     int64_t rows, cols, ld;
-    int32_t dtype;        // of src
+    int32_t dtype;        // of src (kSrcMx8: an MXFP8 carrier, inv required)
     int32_t out_dtype;    // of out
     const float *inv;     // nullable device scale
     float *w;             // nullable fp32 weights (rows x cols, ldw)
     int64_t ldw;
     float lr_s, lr_wd;
+    const uint8_t *sc = nullptr;   // carrier scales and their row pitch
+    int64_t sld = 0;
+    int64_t out_ld = 0;            // row pitch of out; 0: ld
 };
 
 // Row pitch of the internal operands: the padded width plus one 128-byte
@@ -992,8 +1032,10 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         NsItem &it = pa.it[i];
         it.src = r.src;
         it.ld = r.ld;
+        it.sc = r.sc;
+        it.sld = r.sld;
         it.dtype = r.dtype;
-        it.vec = aligned(r.src, 16) && (r.ld * (r.dtype == QM_F32 ? 4 : 2)) % 16 == 0 ? 1 : 0;
+        it.vec = r.dtype != kSrcMx8 && aligned(r.src, 16) && (r.ld * (r.dtype == QM_F32 ? 4 : 2)) % 16 == 0 ? 1 : 0;
         it.tall = r.rows > r.cols ? 1 : 0;
         it.inv = r.inv;
         it.X = bufs[i].X[0];
@@ -1025,9 +1067,10 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     for (int i = 0; i < nit; i++) {
         const NsRequest &r = req[chunk[i]];
         const int64_t oesz = r.out_dtype == QM_F32 ? 4 : 2;
-        fo[i] = FinalOut{r.out, r.w, r.ld, r.ldw, r.out_dtype, r.rows > r.cols ? 1 : 0,
+        const int64_t old_ = r.out_ld ? r.out_ld : r.ld;
+        fo[i] = FinalOut{r.out, r.w, old_, r.ldw, r.out_dtype, r.rows > r.cols ? 1 : 0,
                          (int32_t)bufs[i].g.m, (int32_t)bufs[i].g.n, r.lr_s, r.lr_wd,
-                         aligned(r.out, 16) && (r.ld * oesz) % 16 == 0 ? 1 : 0,
+                         aligned(r.out, 16) && (old_ * oesz) % 16 == 0 ? 1 : 0,
                          r.w && aligned(r.w, 16) && (r.ldw * 4) % 16 == 0 ? 1 : 0};
     }
     WritebackArgs wb{};
@@ -1207,6 +1250,28 @@ extern "C" qm_status ns_orthogonalize(void *x, int32_t dtype, int64_t rows, int6
     return run_ns(req, steps, a, b, c, eps, precision, ws, static_cast<hipStream_t>(stream));
 }
 
+extern "C" qm_status ns_orthogonalize_mxfp8(const uint8_t *rowwise_data, const uint8_t *rowwise_scale_inv,
+                                            const float *inv_norm, int64_t rows, int64_t cols, void *out,
+                                            int32_t out_dtype, int64_t out_ld, int32_t steps, float a, float b,
+                                            float c, int32_t precision, void *ws, size_t ws_bytes,
+                                            qm_stream_t stream) {
+    clear_error();
+    qm_status st = check_ns_common(out, out_dtype, rows, cols, out_ld, steps, a, b, c, 0.0f, precision);
+    if (st != QM_OK) return st;
+    if (!rowwise_data || !rowwise_scale_inv) return fail(QM_E_ARG, "carrier arrays must not be null");
+    if (!aligned(rowwise_data, 8)) return fail(QM_E_ALIGN, "carrier data must be 8-byte aligned");
+    if (cols % 32) return fail(QM_E_SHAPE, "cols must be a multiple of the 32-element carrier block");
+    if (!inv_norm || !aligned(inv_norm, 4)) return fail(QM_E_ARG, "inv_norm must be a 4-byte aligned device pointer");
+    const size_t need = ns_ws_bytes_uniform(rows, cols, 1, precision);
+    if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
+    NsRequest r{rowwise_data, out, rows, cols, cols, kSrcMx8, out_dtype, inv_norm, nullptr, 0, 0.0f, 0.0f};
+    r.sc = rowwise_scale_inv;
+    r.sld = cols / 32;
+    r.out_ld = out_ld;
+    return run_ns(std::vector<NsRequest>{r}, steps, a, b, c, 0.0f, precision, ws, static_cast<hipStream_t>(stream));
+}
+
 extern "C" size_t ns_blocked_workspace_bytes(int64_t rows, int64_t cols, int64_t block_rows, int64_t block_cols,
                                              int32_t precision) {
     if (rows <= 0 || cols <= 0 || block_rows <= 0 || block_cols <= 0) return 0;
@@ -1245,8 +1310,15 @@ namespace qm {
 namespace {
 
 // The NS work of one step: every matrix (full step) or every block.
+// carrier: the MXFP8 carrier arrays of the plan (data, scales) the NS
+// inputs are read from; null: the grads hold m.
+struct CarrierIn {
+    const uint8_t *data, *scale;
+};
+
 std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats,
-                                     int32_t n, bool full, const float *inv, const qm_muon_hparams *hp) {
+                                     int32_t n, bool full, const float *inv, const qm_muon_hparams *hp,
+                                     const CarrierIn *carrier = nullptr) {
     const PlanTensor *pt = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(host_plan) + h->off_tensors);
     std::vector<NsRequest> req;
     int64_t g0 = 0;
@@ -1268,6 +1340,16 @@ std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan,
                 req.push_back(NsRequest{grad + goff * esz, grad + goff * esz, br, bc, gld, dt, dt, ip,
                                         M.weight ? M.weight + woff : nullptr, M.cols, lr * s,
                                         lr * hp->weight_decay});
+                if (carrier) {   // dense (rows, cols) bytes and (rows, cols / 32) scales of tensor i
+                    NsRequest &r = req.back();
+                    const int64_t e0 = pt[i].block_offset * kBlock, e = (bi * br) * M.cols + bj * bc;
+                    r.src = carrier->data + e0 + e;
+                    r.ld = M.cols;
+                    r.dtype = kSrcMx8;
+                    r.sc = carrier->scale + (e0 + e) / 32;
+                    r.sld = M.cols / 32;
+                    r.out_ld = gld;
+                }
             }
         g0 += nbr * nbc;
     }
@@ -1275,7 +1357,7 @@ std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan,
 }
 
 qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int32_t n, bool full,
-                          const PlanHeader **out) {
+                          const PlanHeader **out, bool carrier = false) {
     qm_status st;
     const PlanHeader *h = plan_header(host_plan, &st);
     if (!h) return st;
@@ -1298,6 +1380,8 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
             return fail(QM_E_PLAN, "matrix %d: plan groups %d..%d, expected %lld..%lld", i, pt[i].group_lo,
                         pt[i].group_hi, (long long)g0, (long long)(g0 + nb - 1));
         if (M.weight && !aligned(M.weight, 4)) return fail(QM_E_ALIGN, "matrix %d: weight misaligned", i);
+        if (carrier && (M.cols % 32 || bc % 32))
+            return fail(QM_E_SHAPE, "matrix %d: the MXFP8 carrier needs cols and block_cols multiples of 32", i);
         g0 += nb;
     }
     if (h->n_groups != g0) return fail(QM_E_PLAN, "plan has %d groups, expected %lld", h->n_groups, (long long)g0);
@@ -1305,11 +1389,30 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
     return QM_OK;
 }
 
+// Workspace: [update sums, norms][carrier data, scales (carrier mode)][NS].
+int64_t carrier_ws_bytes(const PlanHeader *h) {
+    return align_up(h->n_blocks * kBlock, 256) + align_up(h->n_blocks * (kBlock / 32), 256);
+}
+
 size_t step_ws_bytes(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
-                     bool full, int precision) {
+                     bool full, int precision, bool carrier = false) {
     qm_muon_hparams dummy{};
     const auto req = step_requests(h, host_plan, mats, n, full, nullptr, &dummy);
-    return align_up(qm_update_workspace_bytes(host_plan), 256) + ns_ws_bytes_req(req, precision);
+    return align_up(qm_update_workspace_bytes(host_plan), 256) + (carrier ? carrier_ws_bytes(h) : 0) +
+           ns_ws_bytes_req(req, precision);
+}
+
+size_t step_ws_total(const void *host_plan_full, const void *host_plan_block, const qm_muon_matrix *mats,
+                     int32_t n_mats, int32_t precision, bool carrier) {
+    if (!mats || n_mats <= 0) return 0;
+    const PlanHeader *h = nullptr;
+    if (check_step_plan(host_plan_full, mats, n_mats, true, &h, carrier) != QM_OK) return 0;
+    size_t need = step_ws_bytes(h, host_plan_full, mats, n_mats, true, precision, carrier);
+    if (host_plan_block) {
+        if (check_step_plan(host_plan_block, mats, n_mats, false, &h, carrier) != QM_OK) return 0;
+        need = std::max(need, step_ws_bytes(h, host_plan_block, mats, n_mats, false, precision, carrier));
+    }
+    return need;
 }
 
 qm_status check_hparams(const qm_muon_hparams *hp) {
@@ -1322,13 +1425,17 @@ qm_status check_hparams(const qm_muon_hparams *hp) {
     if (!(hp->eps >= 0.0f) || std::isinf(hp->eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
     if (hp->rounding != QM_ROUND_NEAREST && hp->rounding != QM_ROUND_STOCHASTIC)
         return fail(QM_E_ARG, "unknown rounding mode %d", hp->rounding);
+    if (hp->carrier != 0 && hp->carrier != 1) return fail(QM_E_ARG, "carrier must be 0 or 1");
+    if (hp->carrier && hp->rounding != QM_ROUND_NEAREST)
+        return fail(QM_E_UNSUPPORTED, "the MXFP8 carrier update rounds to nearest only");
     return QM_OK;
 }
 
 // NS + weight apply of every matrix (full) or block, NS workspace at ns_ws.
 qm_status apply_phase(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats, int32_t n,
-                      bool full, const float *inv, const qm_muon_hparams *hp, void *ns_ws, hipStream_t s) {
-    const auto req = step_requests(h, host_plan, mats, n, full, inv, hp);
+                      bool full, const float *inv, const qm_muon_hparams *hp, void *ns_ws, hipStream_t s,
+                      const CarrierIn *carrier = nullptr) {
+    const auto req = step_requests(h, host_plan, mats, n, full, inv, hp, carrier);
     return run_ns(req, hp->ns_steps, hp->a, hp->b, hp->c, hp->eps, hp->precision, ns_ws, s);
 }
 
@@ -1337,16 +1444,14 @@ qm_status apply_phase(const PlanHeader *h, const void *host_plan, const qm_muon_
 
 extern "C" size_t muon_step_workspace_bytes(const void *host_plan_full, const void *host_plan_block,
                                             const qm_muon_matrix *mats, int32_t n_mats, int32_t precision) {
-    if (!mats || n_mats <= 0) return 0;
-    const PlanHeader *h = nullptr;
-    size_t need = 0;
-    if (check_step_plan(host_plan_full, mats, n_mats, true, &h) != QM_OK) return 0;
-    need = step_ws_bytes(h, host_plan_full, mats, n_mats, true, precision);
-    if (host_plan_block) {
-        if (check_step_plan(host_plan_block, mats, n_mats, false, &h) != QM_OK) return 0;
-        need = std::max(need, step_ws_bytes(h, host_plan_block, mats, n_mats, false, precision));
-    }
-    return need;
+    return step_ws_total(host_plan_full, host_plan_block, mats, n_mats, precision, false);
+}
+
+extern "C" size_t muon_step_workspace_bytes_ex(const void *host_plan_full, const void *host_plan_block,
+                                               const qm_muon_matrix *mats, int32_t n_mats,
+                                               const qm_muon_hparams *hp) {
+    if (!hp) return 0;
+    return step_ws_total(host_plan_full, host_plan_block, mats, n_mats, hp->precision, hp->carrier == 1);
 }
 
 extern "C" qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mats, int32_t n_mats, int32_t full,
@@ -1358,6 +1463,7 @@ extern "C" qm_status muon_apply(const void *host_plan, const qm_muon_matrix *mat
     if (!mats || n_mats <= 0) return fail(QM_E_ARG, "no matrices");
     if (full != 0 && full != 1) return fail(QM_E_ARG, "full must be 0 or 1");
     if (!inv_norm || !aligned(inv_norm, 4)) return fail(QM_E_ARG, "inv_norm must be a 4-byte aligned device pointer");
+    if (hp->carrier) return fail(QM_E_UNSUPPORTED, "muon_apply reads m from the grads: carrier must be 0");
     const PlanHeader *h = nullptr;
     st = check_step_plan(host_plan, mats, n_mats, full != 0, &h);
     if (st != QM_OK) return st;
@@ -1379,27 +1485,38 @@ extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_
     if (!mats || n_mats <= 0) return fail(QM_E_ARG, "no matrices");
     if (step < 1) return fail(QM_E_ARG, "step is 1-based");
     const bool full = hp->period <= 1 || host_plan_block == nullptr || (step % hp->period) == 0;
+    const bool car = hp->carrier == 1;
     const void *hplan = full ? host_plan_full : host_plan_block;
     const void *dplan = full ? dev_plan_full : dev_plan_block;
     const PlanHeader *h = nullptr;
     st = validate_update(hplan, dplan, hp->beta, &h);
     if (st != QM_OK) return st;
-    st = check_step_plan(hplan, mats, n_mats, full, &h);
+    st = check_step_plan(hplan, mats, n_mats, full, &h, car);
     if (st != QM_OK) return st;
     if (full && host_plan_block) {
         const PlanHeader *hb = nullptr;
-        st = check_step_plan(host_plan_block, mats, n_mats, false, &hb);
+        st = check_step_plan(host_plan_block, mats, n_mats, false, &hb, car);
         if (st != QM_OK) return st;
     }
-    const size_t need = muon_step_workspace_bytes(host_plan_full, host_plan_block, mats, n_mats, hp->precision);
+    const size_t need = step_ws_total(host_plan_full, host_plan_block, mats, n_mats, hp->precision, car);
     if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
     if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    char *p = static_cast<char *>(ws);
     const size_t upd = align_up(qm_update_workspace_bytes(hplan), 256);
     const UpdateWorkspace uw = update_workspace(h, ws);
     const qm_round_opts ro{hp->rounding, (uint32_t)step, hp->seed};
-    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s);
+    if (!car) {
+        st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s);
+        if (st != QM_OK) return st;
+        return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, p + upd, s);
+    }
+    uint8_t *cdata = reinterpret_cast<uint8_t *>(p + upd);
+    uint8_t *cscale = cdata + align_up(h->n_blocks * kBlock, 256);
+    if ((st = check_carrier(h, hplan, cdata, cscale)) != QM_OK) return st;
+    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s, cdata, cscale);
     if (st != QM_OK) return st;
-    return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, static_cast<char *>(ws) + upd, s);
+    const CarrierIn cin{cdata, cscale};
+    return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, p + upd + carrier_ws_bytes(h), s, &cin);
 }

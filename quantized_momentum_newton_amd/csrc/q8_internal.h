@@ -22,9 +22,17 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
 
 // Update + per-group inverse norms (+ the in-place scale pass if asked).
 // inv_out / sums_out may be null: the workspace sections are used.  ro:
-// requantisation rounding (null: nearest).
+// requantisation rounding (null: nearest).  carrier_data / carrier_scale
+// non-null: m goes to the MXFP8 carrier (bytes [n_blocks * 256], scales
+// [n_blocks * 8]) instead of the grad buffers; nearest rounding; every
+// tensor's numel a multiple of 32 (checked by the caller).
 qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
                                bool write_normalized, float *inv_out, double *sums_out, void *ws,
-                               const qm_round_opts *ro, hipStream_t stream);
+                               const qm_round_opts *ro, hipStream_t stream, uint8_t *carrier_data = nullptr,
+                               uint8_t *carrier_scale = nullptr);
+
+// QM_OK if every tensor of the plan can carry an MXFP8 carrier (numel a
+// multiple of 32) and the two arrays are usable; else the error, recorded.
+qm_status check_carrier(const PlanHeader *h, const void *host_plan, const void *data, const void *scale);
 
 }  // namespace qm

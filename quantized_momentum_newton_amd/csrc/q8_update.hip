@@ -51,6 +51,27 @@ __device__ __forceinline__ float f16_val(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// E4M3 byte of x (1 sign bit, 4 exponent bits biased by 7, 3 mantissa
+// bits, subnormals below 2^-6, largest finite 448, no infinities): round to
+// nearest even, magnitudes past 448 saturate to 448.  Here |x| < 512.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t mag = u & 0x7fffffffu;
+    if (mag > 0x7f800000u) return sign | 0x7fu;          // NaN
+    uint32_t code;
+    if (mag >= 0x3c800000u) {                            // >= 2^-6: normal
+        // drop 20 mantissa bits with round-half-even; a carry moves the
+        // exponent up by one, which is the right result
+        const uint32_t r = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;   // (exp << 3) | m3
+        code = r - (120u << 3);                          // rebias 127 -> 7
+        if (code > 0x7eu) code = 0x7eu;
+    } else {
+        code = (uint32_t)rintf(__uint_as_float(mag) * 512.0f);   // k * 2^-9, k in 0..8
+    }
+    return sign | code;
+}
+
 template <int DT> struct Elem;
 template <> struct Elem<QM_F32> {
     static constexpr int kEpl = 4;  // elements per lane per part
@@ -208,12 +229,25 @@ __device__ __forceinline__ void sr_words(int64_t e, const SrParams &sr, uint32_t
                   (uint32_t)(sr.seed >> 32), out);
 }
 
-template <int DT, bool SUMS, bool SR>
+// MXFP8 carrier output ("Quantized Muon Momentum", section "Wave18B MXFP8
+// Carrier Probe"): instead of m in the grad buffer, E4M3 bytes of m / s and
+// one E8M0 byte per 32 elements, s = 2^(floor(log2 max|m|) - 8) with the
+// exponent clamped at -127 (the OCP Microscaling rule for E4M3).  The arrays
+// hold every tensor of the plan: tensor t's bytes start at element
+// 256 * (its first block).
+struct CarrierOut {
+    uint8_t *data;
+    uint8_t *scale;
+};
+
+template <int DT, bool SUMS, bool SR, bool CAR>
 __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, float beta, float omb,
-                                            double *block_sums, int lane, const SrParams &sr, uint32_t tensor) {
+                                            double *block_sums, int lane, const SrParams &sr, uint32_t tensor,
+                                            const CarrierOut &co) {
     constexpr int EPL = Elem<DT>::kEpl;
     constexpr int PARTS = kTaskElems / (64 * EPL);
     constexpr int LPB = kBlock / EPL;  // lanes per block
+    constexpr int LPX = 32 / EPL;      // lanes per 32-element carrier block
     const int64_t e_task = lt * kTaskElems;
     const int64_t rem = T.numel - e_task;
     const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
@@ -257,8 +291,13 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         float amax = 0.0f;
 #pragma unroll
         for (int j = 0; j < EPL; j++) amax = fmaxf(amax, fabsf(m[p][j]));
+        // the first butterfly stages reduce over the lanes of one 32-element
+        // carrier block, the rest over the 256-element block
 #pragma unroll
-        for (int off = 1; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        for (int off = 1; off < LPX; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float xmax = amax;
+#pragma unroll
+        for (int off = LPX; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
         int8_t q[EPL];
         if constexpr (SR) {
@@ -283,7 +322,30 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                 q[j] = (int8_t)(int)r;
             }
         }
-        if (e0 + EPL <= nvalid) {
+        if constexpr (CAR) {
+            // numel is a multiple of 32, so a carrier block is all valid or all past the end
+            if (e0 < nvalid) {
+                store_codes_vec<EPL>(codes, e0, q);
+                // E8M0 byte: biased exponent of xmax minus 8, 0 for zero / tiny blocks
+                const uint32_t xe = __float_as_uint(xmax) >> 23;
+                const uint32_t sb = xe > 8u ? xe - 8u : 0u;
+                const float inv_s = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), exact
+                uint32_t w[EPL / 4];
+#pragma unroll
+                for (int k = 0; k < EPL / 4; k++) {
+                    w[k] = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        w[k] |= e4m3_rne_sat(m[p][4 * k + j] * inv_s) << (8 * j);
+                }
+                const int64_t ce = T.block_offset * kBlock + e_task + e0;
+                if constexpr (EPL == 8)
+                    *reinterpret_cast<uint2 *>(co.data + ce) = make_uint2(w[0], w[1]);
+                else
+                    *reinterpret_cast<uint32_t *>(co.data + ce) = w[0];
+                if ((lane % LPX) == 0) co.scale[ce / 32] = (uint8_t)sb;
+            }
+        } else if (e0 + EPL <= nvalid) {
             store_codes_vec<EPL>(codes, e0, q);
             store_grad_vec<DT>(grad, gpos(T, e_task + e0), m[p]);
         } else {
@@ -320,11 +382,11 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
 // With stochastic rounding the Philox state costs registers: 6 waves.
 template <int DT, bool SR> constexpr int update_wgs_per_cu() { return DT == QM_F32 || SR ? 6 : 8; }
 
-template <int DT, bool SUMS, bool SR>
+template <int DT, bool SUMS, bool SR, bool CAR>
 __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_update_kernel(
     const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
     const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
-    double *__restrict__ block_sums, SrParams sr) {
+    double *__restrict__ block_sums, SrParams sr, CarrierOut co) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
@@ -332,7 +394,7 @@ __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_up
     for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
         const int ti = task_tensor[find_tensor(task_offsets, n_tensors, task)];
         const PlanTensor T = tensors[ti];
-        update_task<DT, SUMS, SR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti);
+        update_task<DT, SUMS, SR, CAR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti, co);
     }
 }
 
@@ -475,9 +537,9 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
     return QM_OK;
 }
 
-template <int DT, bool SR>
+template <int DT, bool SR, bool CAR>
 void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, const SrParams &sr,
-                      hipStream_t stream) {
+                      const CarrierOut &co, hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
@@ -485,28 +547,33 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
     const int grid = stream_grid(hi - lo);
     if (block_sums)
-        q8_update_kernel<DT, true, SR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
-                                                                     block_sums, sr);
+        q8_update_kernel<DT, true, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+                                                                          beta, block_sums, sr, co);
     else
-        q8_update_kernel<DT, false, SR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi, beta,
-                                                                      nullptr, sr);
+        q8_update_kernel<DT, false, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+                                                                           beta, nullptr, sr, co);
 }
 
-template <bool SR>
+template <bool SR, bool CAR>
 void launch_update_all(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                       const SrParams &sr, hipStream_t stream) {
-    launch_update_dt<QM_F32, SR>(h, dev_plan, beta, block_sums, sr, stream);
-    launch_update_dt<QM_BF16, SR>(h, dev_plan, beta, block_sums, sr, stream);
-    launch_update_dt<QM_F16, SR>(h, dev_plan, beta, block_sums, sr, stream);
+                       const SrParams &sr, const CarrierOut &co, hipStream_t stream) {
+    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
 }
 
+// co non-null: the carrier replaces the grad write (nearest rounding only).
 qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                        const qm_round_opts *ro, hipStream_t stream) {
+                        const qm_round_opts *ro, const CarrierOut *co, hipStream_t stream) {
     Timed tm(stream, QM_K_Q8_UPDATE);
-    if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
-        launch_update_all<true>(h, dev_plan, beta, block_sums, SrParams{ro->seed, ro->offset}, stream);
+    if (co)
+        launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, *co, stream);
+    else if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
+        launch_update_all<true, false>(h, dev_plan, beta, block_sums, SrParams{ro->seed, ro->offset},
+                                       CarrierOut{nullptr, nullptr}, stream);
     else
-        launch_update_all<false>(h, dev_plan, beta, block_sums, SrParams{0, 0}, stream);
+        launch_update_all<false, false>(h, dev_plan, beta, block_sums, SrParams{0, 0}, CarrierOut{nullptr, nullptr},
+                                        stream);
     return check_launch("q8 update");
 }
 
@@ -551,16 +618,32 @@ UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
 
 qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
                                bool write_normalized, float *inv_out, double *sums_out, void *ws,
-                               const qm_round_opts *ro, hipStream_t stream) {
+                               const qm_round_opts *ro, hipStream_t stream, uint8_t *carrier_data,
+                               uint8_t *carrier_scale) {
     const UpdateWorkspace w = update_workspace(h, ws);
     float *inv = inv_out ? inv_out : w.inv;
     double *sums = sums_out ? sums_out : w.group_sums;
-    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, stream);
+    const CarrierOut co{carrier_data, carrier_scale};
+    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, carrier_data ? &co : nullptr, stream);
     if (st != QM_OK) return st;
     st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
     if (st != QM_OK) return st;
     if (write_normalized) st = launch_scale(h, dev_plan, inv, stream);
     return st;
+}
+
+qm_status check_carrier(const PlanHeader *h, const void *host_plan, const void *data, const void *scale) {
+    if (!data || !scale) return fail(QM_E_ARG, "carrier arrays must not be null");
+    if (!aligned(data, 8)) return fail(QM_E_ALIGN, "carrier data must be 8-byte aligned");
+    const PlanTensor *pt = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(host_plan) + h->off_tensors);
+    for (int32_t i = 0; i < h->n_tensors; i++)
+        if (pt[i].numel % 32)
+            return fail(QM_E_SHAPE, "tensor %d: %lld elements, not a multiple of the 32-element carrier block", i,
+                        (long long)pt[i].numel);
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(data), s0 = reinterpret_cast<uintptr_t>(scale);
+    const uintptr_t dn = (uintptr_t)h->n_blocks * kBlock, sn = (uintptr_t)h->n_blocks * (kBlock / 32);
+    if (d0 < s0 + sn && s0 < d0 + dn) return fail(QM_E_ARG, "carrier data and scales overlap");
+    return QM_OK;
 }
 
 }  // namespace qm
@@ -583,7 +666,7 @@ qm_status update_multi(const void *host_plan, const void *dev_plan, float beta, 
     if (st != QM_OK) return st;
     if ((st = check_round(ro)) != QM_OK) return st;
     if (block_sumsq && !aligned(block_sumsq, 8)) return fail(QM_E_ALIGN, "block_sumsq must be 8-byte aligned");
-    return launch_update(h, dev_plan, beta, block_sumsq, ro, static_cast<hipStream_t>(stream));
+    return launch_update(h, dev_plan, beta, block_sumsq, ro, nullptr, static_cast<hipStream_t>(stream));
 }
 
 qm_status update_normalize(const void *host_plan, const void *dev_plan, float beta, float eps,
@@ -606,7 +689,32 @@ qm_status update_normalize(const void *host_plan, const void *dev_plan, float be
                                 ro, static_cast<hipStream_t>(stream));
 }
 
+qm_status update_carrier(const void *host_plan, const void *dev_plan, float beta, float eps, uint8_t *data,
+                         uint8_t *scale, float *inv_norm, double *group_sumsq, void *ws, size_t ws_bytes,
+                         qm_stream_t stream) {
+    clear_error();
+    const PlanHeader *h = nullptr;
+    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
+    if (st != QM_OK) return st;
+    if ((st = check_carrier(h, host_plan, data, scale)) != QM_OK) return st;
+    if (!(eps >= 0.0f) || isinf(eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    if (!inv_norm || !aligned(inv_norm, 4)) return fail(QM_E_ARG, "inv_norm must be a 4-byte aligned device pointer");
+    if (group_sumsq && !aligned(group_sumsq, 8)) return fail(QM_E_ALIGN, "group_sumsq alignment");
+    const size_t need = qm_update_workspace_bytes(host_plan);
+    if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);
+    if (!aligned(ws, 256)) return fail(QM_E_ALIGN, "workspace must be 256-byte aligned");
+    return run_update_normalize(h, dev_plan, beta, eps, false, inv_norm, group_sumsq, ws, nullptr,
+                                static_cast<hipStream_t>(stream), data, scale);
+}
+
 }  // namespace
+
+extern "C" qm_status qmuon_update_mxfp8_carrier(const void *host_plan, const void *dev_plan, float beta, float eps,
+                                                uint8_t *rowwise_data, uint8_t *rowwise_scale_inv, float *inv_norm,
+                                                double *group_sumsq, void *ws, size_t ws_bytes, qm_stream_t stream) {
+    return update_carrier(host_plan, dev_plan, beta, eps, rowwise_data, rowwise_scale_inv, inv_norm, group_sumsq, ws,
+                          ws_bytes, stream);
+}
 
 extern "C" qm_status qmuon_update_multi(const void *host_plan, const void *dev_plan, float beta,
                                         double *block_sumsq, qm_stream_t stream) {

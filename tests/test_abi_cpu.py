@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(LIB, n), n
     assert names == set(L.SIGNATURES), names ^ set(L.SIGNATURES)
-    assert LIB.qm_abi_version() == 2
+    assert LIB.qm_abi_version() == 3
     assert LIB.qm_status_string(0) == b"ok"
 
 
@@ -205,3 +205,72 @@ def test_rounding_options_are_validated():
                                                 ctypes.c_void_p(BASE), need, None) == 1
     assert "rounding" in LIB.qm_last_error().decode()
     assert ctypes.sizeof(L.MuonHparams) == 64 and ctypes.sizeof(L.RoundOpts) == 16
+
+
+def _carrier_call(hp, ws_need, data=BASE + (1 << 32), scale=BASE + (1 << 33), inv=BASE + (1 << 34), eps=1e-7,
+                  ws=BASE + (1 << 35), ws_bytes=None):
+    v = lambda a: ctypes.c_void_p(a) if a is not None else None
+    return LIB.qmuon_update_mxfp8_carrier(hp, ctypes.c_void_p(BASE), 0.9, eps, v(data), v(scale), v(inv), None,
+                                          v(ws), ws_need if ws_bytes is None else ws_bytes, None)
+
+
+def test_carrier_update_validates_before_launch():
+    tens = _tensors([(1024, L.QM_BF16), (1000, L.QM_F32)])
+    st, buf = _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 1000, 1)]), 2)
+    hp = ctypes.cast(buf, ctypes.c_void_p)
+    need = LIB.qm_update_workspace_bytes(hp)
+    assert _carrier_call(hp, need) == 4                        # 1000 elements: off the 32 grid
+    assert "32" in LIB.qm_last_error().decode()
+    tens = _tensors([(1024, L.QM_BF16), (992, L.QM_F32)])
+    st, buf = _encode(tens, _segs([(0, 0, 1024, 0), (1, 0, 992, 1)]), 2)
+    hp = ctypes.cast(buf, ctypes.c_void_p)
+    need = LIB.qm_update_workspace_bytes(hp)
+    assert _carrier_call(hp, need, data=None) == 1
+    assert _carrier_call(hp, need, data=BASE + (1 << 32) + 4) == 2     # data 8-byte alignment
+    assert _carrier_call(hp, need, scale=BASE + (1 << 32) + 512) == 1  # scales inside the data array
+    assert _carrier_call(hp, need, inv=None) == 1
+    assert _carrier_call(hp, need, eps=-1.0) == 1
+    assert _carrier_call(hp, need, ws_bytes=need - 1) == 5
+
+
+def test_ns_mxfp8_validates_before_launch():
+    def call(data=BASE, scale=BASE + (1 << 30), inv=BASE + (1 << 31), rows=64, cols=256, out=BASE + (1 << 32),
+             ws_bytes=1 << 30):
+        v = lambda a: ctypes.c_void_p(a) if a is not None else None
+        return LIB.ns_orthogonalize_mxfp8(v(data), v(scale), v(inv), rows, cols, v(out), L.QM_BF16, cols, 5, 3.4445,
+                                          -4.775, 2.0315, 0, ctypes.c_void_p(BASE + (1 << 33)), ws_bytes, None)
+    assert call(cols=48) == 4                                  # cols off the 32 grid
+    assert call(inv=None) == 1
+    assert call(data=BASE + 4) == 2
+    assert call(data=None) == 1
+    assert call(out=None) == 1
+    assert call(ws_bytes=16) == 5
+    need = LIB.ns_workspace_bytes(64, 256, 1, 0)
+    assert call(ws_bytes=need - 1) == 5
+
+
+def test_carrier_hparams_and_workspace():
+    tens = _tensors([(64 * 256, L.QM_BF16)])
+    st, buf = _encode(tens, _segs([(0, 0, 64 * 256, 0)]), 1)
+    hp = ctypes.cast(buf, ctypes.c_void_p)
+    mats = (L.MuonMatrix * 1)()
+    mats[0] = L.MuonMatrix(64, 256, 64, 256, None)
+    h = q.make_hparams(period=1)
+    plain = LIB.muon_step_workspace_bytes(hp, None, mats, 1, 0)
+    assert LIB.muon_step_workspace_bytes_ex(hp, None, mats, 1, ctypes.byref(h)) == plain
+    h.carrier = 1
+    nb = 64
+    assert LIB.muon_step_workspace_bytes_ex(hp, None, mats, 1, ctypes.byref(h)) == plain + nb * 256 + 512
+    fake = ctypes.c_void_p(BASE)
+    ws = ctypes.c_void_p(BASE + (1 << 34))
+    h.carrier = 2
+    assert LIB.muon_step(hp, fake, None, None, mats, 1, 1, ctypes.byref(h), ws, 1 << 40, None) == 1
+    h.carrier, h.rounding = 1, L.QM_ROUND_STOCHASTIC
+    assert LIB.muon_step(hp, fake, None, None, mats, 1, 1, ctypes.byref(h), ws, 1 << 40, None) == 7
+    h.rounding = L.QM_ROUND_NEAREST
+    assert LIB.muon_apply(hp, mats, 1, 1, fake, ctypes.byref(h), ws, 1 << 40, None) == 7
+    # cols off the 32 grid: no carrier-mode workspace
+    tens = _tensors([(64 * 48, L.QM_BF16)])
+    st, buf = _encode(tens, _segs([(0, 0, 64 * 48, 0)]), 1)
+    mats[0] = L.MuonMatrix(64, 48, 64, 48, None)
+    assert LIB.muon_step_workspace_bytes_ex(ctypes.cast(buf, ctypes.c_void_p), None, mats, 1, ctypes.byref(h)) == 0
