@@ -21,6 +21,11 @@ update kernel.  `traffic` is filled from the committed counter summary only
 while the kernel source still has the hash recorded there.  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
 
+--carrier: the same step with m handed to Newton-Schulz as the MXFP8 carrier
+(muon_step with hparams.carrier = 1: the update writes E4M3 bytes + per-32
+E8M0 scales, 5.0625 B/element, and the NS prologue decodes them); the update
+/ NS split then comes from the per-kernel timer.
+
 Other workloads (not the headline): --workload layerset28 (the 28-layer
 2048-hidden set, grouped update + normalisation only), --workload muonbp
 (4096x14336, 8 column blocks, P = 5).
@@ -41,6 +46,7 @@ BF16_PEAK_TFLOPS = 2500.0
 F32_PEAK_TFLOPS = 157.3
 BYTES_PER_ELEM_UPDATE = 6.03125      # 1+1 code, 2+2 bf16 grad, 8/256 absmax
 BYTES_PER_ELEM_SCALE = 4.0           # bf16 grad read + write (normalise pass)
+BYTES_PER_ELEM_CARRIER = 5.0625      # 1+1 code, 2 bf16 grad read, 1 + 1/32 carrier write, 8/256 absmax
 
 
 def parse():
@@ -52,6 +58,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="requantisation rounding of the update (the headline uses nearest)")
+    ap.add_argument("--carrier", action="store_true",
+                    help="hand m to Newton-Schulz as the MXFP8 carrier (muon_step with hparams.carrier = 1) "
+                         "instead of bf16 in the grads (llama8b and muonbp workloads)")
     ap.add_argument("--ref-copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once (a kernel of "
                          "known traffic, to calibrate HBM byte counters in a profiler run)")
@@ -65,14 +74,15 @@ def ns_sym_flops(rows, cols, steps):
 
 # Algorithmic work of one launch of each timed kernel class over a set of
 # matrices (rows, cols): FLOPs for the products, bytes for memory kernels.
-def launch_work(tensors, numel):
+def launch_work(tensors, numel, carrier=False):
     mn = [(min(r, c), max(r, c)) for _, r, c in tensors]
     return {
         "ns_gram": ("mfma", sum(m * (m + 1) * n for m, n in mn)),
         "ns_poly": ("mfma", sum(m * m * (m + 1) for m, n in mn)),
         "ns_xupdate": ("mfma", sum(2 * m * m * n for m, n in mn)),
-        "q8_update": ("hbm", numel * BYTES_PER_ELEM_UPDATE),
-        "ns_prologue": ("hbm", numel * 6.0),     # bf16 in, bf16 X and X^T out
+        "q8_update": ("hbm", numel * (BYTES_PER_ELEM_CARRIER if carrier else BYTES_PER_ELEM_UPDATE)),
+        # bf16 m in (or the carrier: 1 + 1/32), bf16 X out
+        "ns_prologue": ("hbm", numel * ((1 + 1 / 32) if carrier else 2.0) + numel * 2.0),
         "ns_writeback": ("hbm", numel * 12.0),   # bf16 X in, bf16 out, fp32 W read + write
     }
 
@@ -202,12 +212,15 @@ def main():
         blk_plan = q.Plan(trip, segs, ngb)
     ws_u = plan.workspace()
     inv = torch.empty(ng, dtype=torch.float32, device=dev)
+    if args.carrier and (args.workload == "layerset28" or args.rounding != "nearest"):
+        print("--carrier needs the llama8b or muonbp workload and nearest rounding", file=sys.stderr)
+        sys.exit(2)
     hp = q.make_hparams(beta=H.BETA, eps=H.NS_EPS, coeffs=H.NS_COEFFS, lr_full=0.02, lr_block=0.01,
                         rms_scale=0.2, ns_steps=H.NS_STEPS,
-                        period=cfg["period"] if args.workload == "muonbp" else 1)
+                        period=cfg["period"] if args.workload == "muonbp" else 1, carrier=args.carrier)
     ws_ns = None
     if mats:
-        nbytes = q.muon_step_workspace_bytes(plan, blk_plan, mats)
+        nbytes = q.muon_step_workspace_bytes(plan, blk_plan, mats, hparams=hp)
         ws_ns = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
     def step(t, ev):
@@ -215,6 +228,12 @@ def main():
             ev[0].record()
             q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv, ws=ws_u,
                                             rounding=args.rounding, seed=1234, offset=t)
+            ev[1].record()
+            ev[2].record()
+        elif args.workload == "llama8b" and args.carrier:
+            # one call; the update / NS split comes from the per-kernel timer
+            ev[0].record()
+            q.muon_step(plan, None, mats, t, hp, ws=ws_ns)
             ev[1].record()
             ev[2].record()
         elif args.workload == "llama8b":
@@ -254,6 +273,10 @@ def main():
         del src, dst
     upd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     ns_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    if args.carrier and args.workload == "llama8b":
+        call_ms = upd_ms
+        upd_ms = (per_class["q8_update"][0] + per_class["group_reduce"][0]) / args.steps
+        ns_ms = call_ms - upd_ms
     ms_per_step = total_ms / args.steps
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -268,12 +291,12 @@ def main():
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}})
     elif args.workload == "llama8b":
-        bytes_ = numel * BYTES_PER_ELEM_UPDATE
+        bytes_ = numel * (BYTES_PER_ELEM_CARRIER if args.carrier else BYTES_PER_ELEM_UPDATE)
         gbs = bytes_ / (upd_ms * 1e-3) / 1e9
         flops = sum(ns_sym_flops(r, c, H.NS_STEPS) for _, r, c in tensors)
         tfl = flops / (ns_ms * 1e-3) / 1e12
-        work = launch_work(tensors, numel)
-        traffic = recorded_traffic("llama8b_layer")
+        work = launch_work(tensors, numel, args.carrier)
+        traffic = recorded_traffic("llama8b_layer_carrier" if args.carrier else "llama8b_layer")
         kernels = {k: {"ms_per_launch": round(ms / n, 4), "launches": n, "share": round(ms / total_ms, 4)}
                    for k, (ms, n) in per_class.items() if n}
         timed = [k for k in work if per_class[k][1]]
@@ -288,12 +311,14 @@ def main():
                     "config": {"workload": "llama8b_layer_muon_step", "matrices": len(tensors),
                                "elements": numel, "ns_steps": H.NS_STEPS, "ns_precision": "bf16",
                                "grad_dtype": "bf16", "state": "int8", "rounding": args.rounding,
+                               "handoff": "mxfp8_carrier" if args.carrier else "bf16_grad",
                                "update_ms": round(upd_ms, 4),
                                "ns_apply_ms": round(ns_ms, 4), "ns_flops_per_step": flops},
                     "roofline": rl[dom], "roofline_update": rl["q8_update"], "kernels": kernels})
     else:
         out.update({"value": round(1000.0 / ms_per_step, 3), "unit": "steps/s", "dtype": "bf16",
-                    "config": {"workload": "muonbp_4096x14336_P5", "blocks": 8}})
+                    "config": {"workload": "muonbp_4096x14336_P5", "blocks": 8,
+                               "handoff": "mxfp8_carrier" if args.carrier else "bf16_grad"}})
     if host_q is not None:
         out["cpu_baseline"] = cpu_baseline(host_q, host_ns, H.NS_STEPS)
     print(json.dumps(out), flush=True)

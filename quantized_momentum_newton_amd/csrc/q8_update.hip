@@ -51,25 +51,18 @@ __device__ __forceinline__ float f16_val(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// E4M3 byte of x (1 sign bit, 4 exponent bits biased by 7, 3 mantissa
-// bits, subnormals below 2^-6, largest finite 448, no infinities): round to
-// nearest even, magnitudes past 448 saturate to 448.  Here |x| < 512.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t mag = u & 0x7fffffffu;
-    if (mag > 0x7f800000u) return sign | 0x7fu;          // NaN
-    uint32_t code;
-    if (mag >= 0x3c800000u) {                            // >= 2^-6: normal
-        // drop 20 mantissa bits with round-half-even; a carry moves the
-        // exponent up by one, which is the right result
-        const uint32_t r = (mag + 0x7ffffu + ((mag >> 20) & 1u)) >> 20;   // (exp << 3) | m3
-        code = r - (120u << 3);                          // rebias 127 -> 7
-        if (code > 0x7eu) code = 0x7eu;
-    } else {
-        code = (uint32_t)rintf(__uint_as_float(mag) * 512.0f);   // k * 2^-9, k in 0..8
-    }
-    return sign | code;
+// Four E4M3 bytes (1 sign bit, 4 exponent bits biased by 7, 3 mantissa
+// bits, subnormals below 2^-6, largest finite 448, no infinities) of x[0..3],
+// byte j from x[j]: round to nearest even, magnitudes past 448 saturate to
+// 448.  gfx950's v_cvt_pk_fp8_f32 converts to this format with round to
+// nearest even; the clamp in front gives the saturation (a NaN passes through
+// and comes out as a NaN byte).
+__device__ __forceinline__ uint32_t e4m3x4_rne_sat(const float *x) {
+    float c[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) c[j] = x[j] != x[j] ? x[j] : fminf(fmaxf(x[j], -448.0f), 448.0f);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
 }
 
 template <int DT> struct Elem;
@@ -333,10 +326,10 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                 uint32_t w[EPL / 4];
 #pragma unroll
                 for (int k = 0; k < EPL / 4; k++) {
-                    w[k] = 0;
+                    float x[4];
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        w[k] |= e4m3_rne_sat(m[p][4 * k + j] * inv_s) << (8 * j);
+                    for (int j = 0; j < 4; j++) x[j] = m[p][4 * k + j] * inv_s;   // exact: a power of two
+                    w[k] = e4m3x4_rne_sat(x);
                 }
                 const int64_t ce = T.block_offset * kBlock + e_task + e0;
                 if constexpr (EPL == 8)

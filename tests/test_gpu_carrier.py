@@ -142,6 +142,37 @@ def test_carrier_update_llama8b_layer_full():
     check_carrier(qs, segments, ng, H.BETA, H.NS_EPS)
 
 
+def test_carrier_e4m3_encoding_sweep():
+    """Every fp32 pattern of magnitude 2^-12 .. 512 on a 2^12-ulp grid (all
+    E4M3 codes, every tie, the values just around ties, saturation), both
+    signs.  beta = 0 and a zero state make m the fp32 grad exactly; each
+    32-element block leads with 256, so its scale is 2^0 and the payload is
+    the E4M3 byte of the value itself."""
+    pats = np.arange(0x39800000, 0x44000000, 1 << 12, dtype=np.uint32)
+    vals = np.concatenate([pats.view(np.float32), -pats.view(np.float32)])
+    nblk32 = -(-vals.size // 31)
+    body = np.zeros(nblk32 * 31, np.float32)
+    body[:vals.size] = vals
+    g = np.concatenate([np.full((nblk32, 1), 256.0, np.float32), body.reshape(nblk32, 31)], axis=1).reshape(-1)
+    pad = (-g.size) % 256
+    g = np.concatenate([g, np.zeros(pad, np.float32)])
+    n = g.size
+    codes = torch.zeros(n, dtype=torch.int8, device=DEV)
+    absmax = torch.zeros(n // 256, dtype=torch.float32, device=DEV)
+    grad = torch.from_numpy(g).to(DEV)
+    plan = q.Plan([(codes, absmax, grad)], [(0, 0, n, 0)], 1)
+    say("e4m3 sweep", vals.size, "values")
+    car = q.qmuon_update_mxfp8_carrier(plan, 0.0, 1e-7)
+    torch.cuda.synchronize()
+    c, a, p, sc, _ = oracle.q8_update_carrier(np.zeros(n, np.int8), np.zeros(n // 256, np.float32), g, 0.0)
+    assert_bits_equal(host(car.data(0)), p, "payload")
+    assert_bits_equal(host(car.scale_inv(0)), sc, "scales")
+    assert_bits_equal(host(codes), c, "codes")
+    assert np.all(sc[:nblk32] == 127)
+    # the oracle's bytes for this sweep are the format's nearest codes (its own pins cover the encoder)
+    assert p.reshape(-1, 32)[0, 0] == 0x78
+
+
 def test_carrier_rejects_sizes_off_the_32_grid():
     qs = Q8Set([(1000,)], [torch.bfloat16], seed=46)
     plan = q.Plan(qs.triples(), [(0, 0, 1000, 0)], 1)
