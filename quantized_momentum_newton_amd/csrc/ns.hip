@@ -631,6 +631,229 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     }
 }
 
+// ------------------------------------------------------------ MX Gram
+// The first Gram product of an iteration whose input is an MXFP8 carrier
+// ("Quantized Muon Momentum", section "Wave18B MXFP8 Carrier Probe": the
+// carrier feeds the Gram GEMM): A = alpha X X^T, X = the carrier's E4M3
+// bytes (rows x K, K contiguous) with one E8M0 scale per 32 k of a row,
+// alpha = inv_norm^2, on gfx950's block-scaled v_mfma_scale_f32_32x32x64
+// (fp8 operands, fp32 accumulation), output bf16.
+//
+// Operand layout of that instruction (measured with an in-bounds probe:
+// one nonzero byte per test, all-ones other operand, distinct scales per
+// lane half): lane l holds row l % 32; its bytes 0..15 lie in the first
+// 32-k block of the 64-k step and bytes 16..31 in the second; the scale of
+// block 0 of row r comes from lane r, that of block 1 from lane r + 32.
+// So lane (r, h) of k-step s loads the 16-byte chunks 4s + h and 4s + 2 + h
+// of its row's 128-byte k-tile and supplies the scale of 32-k block
+// 2s + h (the order of k inside a block does not change the sum).
+//
+// Tiles as the bf16 Gram: 256 x 256 lower-triangle tiles, 8 waves of
+// 128 x 64, two LDS stages filled by LDS-DMA; a stage holds 512 rows x 128
+// bytes of data and each row's 4 scale bytes of the k-tile (one 4-byte DMA
+// per wave covers 64 rows).  Requires rows % 256 == 0, K % 128 == 0.
+struct MxItem {
+    const uint8_t *X;      // rows x K bytes, row pitch ldx bytes
+    const uint8_t *S;      // scales, row pitch lds bytes (K / 32 used)
+    bf16_t *C;             // A, row pitch ldc elements
+    const float *inv;      // device inverse norm: alpha = inv^2
+    int64_t ldx, lds, ldc;
+    int32_t tiles_m, tile_begin, k_tiles, pad;
+};
+
+struct MxGramArgs {
+    MxItem it[kMaxItems];
+    int32_t n_items;
+};
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+__global__ __launch_bounds__(512, 1) void gram_mx_kernel(MxGramArgs args) {
+    constexpr int BM = 256, BN = 256, WAVES_N = 4, NW = 8;
+    constexpr int WM = 128, WN = 64, FM = WM / 32, FN = WN / 32;
+    constexpr int ROWB = 128, CPR = 8, RPI = 8, SWD = 2, NSTAGE = 2, STEPS = 2;
+    constexpr int SROWS = BM + BN;
+    constexpr int DATA = SROWS * ROWB;
+    constexpr int STAGE = DATA + SROWS * 4;
+    constexpr int PI = BM / RPI / NW, QI = BN / RPI / NW;
+    constexpr int DPT = PI + QI + 1;                // + the scale DMA
+    constexpr int DPS = (DPT + STEPS - 1) / STEPS;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int L = wg_position(blockIdx.x, gridDim.x);
+    int item = 0;
+    while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+    const MxItem &I = args.it[item];
+    int bi, bj;
+    band_coords_tri(L - I.tile_begin, I.tiles_m, bi, bj);
+
+    const uint8_t *Pg = I.X + (int64_t)bi * BM * I.ldx, *Qg = I.X + (int64_t)bj * BN * I.ldx;
+    const uint8_t *Ps = I.S + (int64_t)bi * BM * I.lds, *Qs = I.S + (int64_t)bj * BN * I.lds;
+    const int lrw = lane / CPR, lch = lane % CPR;
+    // DMA instruction d of k-tile kt: d < PI + QI move 8 rows x 128 bytes
+    // (swizzled as the bf16 kernel: chunk c of row r at c ^ ((r / 2) % 8)),
+    // the last one the scale dwords of rows 64 wave .. 64 wave + 63.  The
+    // per-lane part of each address is a 32-bit offset from a wave-uniform
+    // panel base (a panel spans < 2^32 bytes: 256 rows of < 2^22 bytes).
+    uint32_t off[PI + QI];
+#pragma unroll
+    for (int d = 0; d < PI + QI; d++) {
+        const int row = (wave + (d >= PI ? d - PI : d) * NW) * RPI + lrw;
+        off[d] = (uint32_t)(row * I.ldx) + ((lch ^ ((row / SWD) % CPR)) << 4);
+    }
+    const int srow = wave * 64 + lane;             // stage row of this lane's scale dword: P rows, then Q rows
+    const uint8_t *sbase = srow < BM ? Ps : Qs;
+    const uint32_t soff = (uint32_t)((srow % BM) * I.lds);
+    // The k-tile's part of an address goes through a wave-uniform register
+    // (readfirstlane), so each load is a scalar base plus the 32-bit lane
+    // offset and the compiler keeps no 64-bit per-lane address per load.
+    auto uni = [](const uint8_t *p) -> const uint8_t * {
+        const uint64_t v = reinterpret_cast<uint64_t>(p);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo);
+    };
+    auto dma = [&](int kt, char *base, int d) {
+        if (d < PI + QI) {
+            const bool q = d >= PI;
+            const int r0 = (wave + (q ? d - PI : d) * NW) * RPI;
+            lds_dma16(uni((q ? Qg : Pg) + (int64_t)kt * ROWB) + off[d], base + ((q ? BM : 0) + r0) * ROWB);
+        } else {
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(uni(sbase + kt * 4) + soff),
+                                             (__attribute__((address_space(3))) void *)(base + DATA + wave * 256),
+                                             4, 0, 0);
+        }
+    };
+    auto issue_part = [&](int kt, int stage, int part) {
+        char *base = smem + stage * STAGE;
+#pragma unroll
+        for (int d = part * DPS; d < (part + 1) * DPS && d < DPT; d++) dma(kt, base, d);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
+
+    const int KT = I.k_tiles;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    auto frag = [&](const char *cp, int row, int s) -> i32x8 {
+        const int sw = (row / SWD) % CPR;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + (((4 * s + lhalf) ^ sw) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + (((4 * s + 2 + lhalf) ^ sw) << 4));
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_frags = [&](const char *cp, int s, i32x8 *a, i32x8 *b) {
+#pragma unroll
+        for (int i = 0; i < FM; i++) a[i] = frag(cp, wm * WM + i * 32 + lrow, s);
+#pragma unroll
+        for (int j = 0; j < FN; j++) b[j] = frag(cp, BM + wn * WN + j * 32 + lrow, s);
+    };
+    auto read_scales = [&](const char *cp, uint32_t *sa, uint32_t *sb) {
+        const uint32_t *sc = reinterpret_cast<const uint32_t *>(cp + DATA);
+#pragma unroll
+        for (int i = 0; i < FM; i++) sa[i] = sc[wm * WM + i * 32 + lrow];
+#pragma unroll
+        for (int j = 0; j < FN; j++) sb[j] = sc[BM + wn * WN + j * 32 + lrow];
+    };
+
+    // One register set of fragments (the 256 registers a wave has at two
+    // waves per SIMD hold the 128 accumulators, one set of fragments and the
+    // addresses); the other wave on the SIMD covers the LDS latency.
+    i32x8 fa[FM], fb[FN];
+    uint32_t sa[FM], sb[FN];
+    issue_part(0, 0, 0);
+    issue_part(0, 0, 1);
+    wait_vmcnt_tiles<DPT>(0);
+    kloop_barrier();
+    // k-tile kt from stage kt % 2 while tile kt + 1 streams into the other
+    // (the last tile is peeled off, so the loop body is branch-free and the
+    // scheduling barriers keep one step's fragments live at a time)
+    auto tile = [&](int kt, bool next) {
+        const char *cp = smem + (kt % NSTAGE) * STAGE;
+        read_scales(cp, sa, sb);
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(cp, s, fa, fb);
+            if (next) issue_part(kt + 1, (kt + 1) % NSTAGE, s);
+            const int sh = 8 * (2 * s + lhalf);      // this lane's 32-k block of the step
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fa[i], fb[j], acc[i][j], 0, 0, 0, (int)(sa[i] >> sh), 0, (int)(sb[j] >> sh));
+        }
+        wait_vmcnt_tiles<DPT>(0);
+        kloop_barrier();
+    };
+    for (int kt = 0; kt + 1 < KT; kt++) tile(kt, true);
+    tile(KT - 1, false);
+
+    // epilogue: C = alpha acc (bf16) through LDS, 64 rows per pass; the
+    // mirror tile (bi != bj) from the same rounded values
+    constexpr int ER = 64, EP = BN + 8, NTH = NW * 64;
+    constexpr int RIT = ER * (BN / 8) / NTH, CIT = BN * (ER / 8) / NTH;
+    static_assert((size_t)ER * EP * 4 <= (size_t)NSTAGE * STAGE, "epilogue tile must fit the stage buffers");
+    float *et = reinterpret_cast<float *>(smem);
+    const float alpha = I.inv[0] * I.inv[0];
+    const int64_t R0 = (int64_t)bi * BM, C0 = (int64_t)bj * BN;
+#pragma unroll
+    for (int p = 0; p < BM / ER; p++) {
+        const int pw = p * ER / WM, i0 = (p * ER % WM) / 32;
+        if (wm == pw) {
+#pragma unroll
+            for (int ii = 0; ii < ER / 32; ii++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) {
+                        const int row = ii * 32 + 8 * (r / 4) + 4 * lhalf + (r % 4);
+                        et[row * EP + wn * WN + j * 32 + lrow] = acc[i0 + ii][j][r];
+                    }
+        }
+        kloop_barrier();
+        const int64_t pr = R0 + p * ER;
+#pragma unroll
+        for (int it = 0; it < RIT; it++) {
+            const int idx = tid + it * NTH;
+            const int r = idx / (BN / 8), c = (idx % (BN / 8)) * 8;
+            float *e = et + r * EP + c;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) v[k] = alpha * e[k];
+            store8(I.C + (pr + r) * I.ldc + C0 + c, v);
+            if (bi != bj) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) e[k] = to_float(from_float<bf16_t>(v[k]));
+            }
+        }
+        if (bi != bj) {
+            kloop_barrier();
+#pragma unroll
+            for (int it = 0; it < CIT; it++) {
+                const int idx = tid + it * NTH;
+                const int c = idx % BN, r = (idx / BN) * 8;
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) v[k] = et[(r + k) * EP + c];
+                store8(I.C + (C0 + c) * I.ldc + pr + r, v);
+            }
+        }
+        kloop_barrier();
+    }
+}
+
+constexpr size_t kMxGramLds = 2 * (512 * 128 + 512 * 4);
+
 // ------------------------------------------------------- norm + prologue
 
 // Source format code of an MXFP8 carrier (payload bytes + per-32 E8M0
@@ -987,6 +1210,31 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     return QM_OK;
 }
 
+qm_status launch_gram_mx(const MxGramArgs &args, int grid, hipStream_t stream) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gram_mx_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGramLds) != hipSuccess)
+            return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", kMxGramLds);
+        attr_set = true;
+    }
+    Timed tm(stream, QM_K_NS_GRAM);
+    hipLaunchKernelGGL(gram_mx_kernel, dim3(grid), dim3(512), kMxGramLds, stream, args);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "mx gram launch: %s", hipGetErrorString(e));
+    return QM_OK;
+}
+
+// The first Gram product of a request can run on the carrier directly
+// (gram_mx_kernel) when the request is a carrier iterated as it is (not
+// tall), its rows a multiple of the 256-row tile, its K a multiple of the
+// 128-byte k-tile, and the carrier rows and scale rows aligned for the
+// 16-byte and 4-byte loads.
+bool mx_gram_ok(const NsRequest &r) {
+    return r.dtype == kSrcMx8 && r.inv && r.rows <= r.cols && r.rows % 256 == 0 && r.cols % 128 == 0 &&
+           aligned(r.src, 16) && r.ld % 16 == 0 && aligned(r.sc, 4) && r.sld % 4 == 0;
+}
+
 // bf16: X[0], X[1] ping-pong (X = aX + BX reads X in its K x N layout);
 // fp32: X[0] updated in place, X^T in XT[0], XT[1] ping-pong.
 struct ItemBufs {
@@ -1088,14 +1336,37 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     });
     std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
     for (int s = 0; s < steps; s++) {
-        // A = X X^T
+        // A = X X^T.  On the first iteration of a bf16 run whose requests
+        // are all carriers that qualify, the block-scaled fp8 product runs
+        // instead.  A chunk that mixes in other requests keeps one bf16
+        // launch: two smaller launches back to back fill the GPU worse than
+        // the fp8 product saves (measured on the 8B layer, whose tall gate
+        // and up matrices cannot take it).
+        bool all_mx = kQT && s == 0;
+        for (int k = 0; k < nit; k++) all_mx = all_mx && mx_gram_ok(req[chunk[k]]);
         GemmArgs<T> g1{};
-        g1.n_items = nit;
-        int tl = 0;
+        MxGramArgs gx{};
+        int tl = 0, tx = 0;
         for (int k = 0; k < nit; k++) {
             const ItemBufs &B = bufs[by_n[k]];
             const int tm = (int)(B.g.mp / CfgSym::BM);
-            GItem<T> &I = g1.it[k];
+            const NsRequest &r = req[chunk[by_n[k]]];
+            if (all_mx) {
+                MxItem &M = gx.it[gx.n_items++];
+                M.X = static_cast<const uint8_t *>(r.src);
+                M.S = r.sc;
+                M.C = reinterpret_cast<bf16_t *>(B.A);
+                M.inv = r.inv;
+                M.ldx = r.ld;
+                M.lds = r.sld;
+                M.ldc = B.g.ldm;
+                M.tiles_m = tm;
+                M.tile_begin = tx;
+                M.k_tiles = (int32_t)(r.cols / 128);
+                tx += tm * (tm + 1) / 2;
+                continue;
+            }
+            GItem<T> &I = g1.it[g1.n_items++];
             const char *X = kQT ? B.X[cur[by_n[k]]] : B.X[0];
             I.P = reinterpret_cast<const T *>(X); I.ldp = B.g.ldn;
             I.Q = reinterpret_cast<const T *>(X); I.ldq = B.g.ldn;
@@ -1106,7 +1377,10 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
             I.k_tiles = (int32_t)(B.g.np / kSymK);
             tl += tm * (tm + 1) / 2;
         }
-        qm_status st = launch_gemm<T, CfgSym, EPI_GRAM, true>(g1, tl, stream);
+        qm_status st = QM_OK;
+        if (g1.n_items) st = launch_gemm<T, CfgSym, EPI_GRAM, true>(g1, tl, stream);
+        if (st != QM_OK) return st;
+        if (gx.n_items) st = launch_gram_mx(gx, tx, stream);
         if (st != QM_OK) return st;
         // B = b A + c A A
         GemmArgs<T> g2{};

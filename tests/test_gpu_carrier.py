@@ -220,7 +220,10 @@ def test_ns_mxfp8_no_iteration_is_decode_times_inv(out_dtype):
         assert_bits_equal(host_grad(out).reshape(-1), oracle.round_to(exp.reshape(-1), oracle.BF16), "O")
 
 
-@pytest.mark.parametrize("rows,cols", [(96, 320), (320, 96), (256, 512), (640, 224), (1024, 1024)])
+# (256, 512), (1024, 1024), (512, 1536): the first Gram runs on block-scaled fp8
+# MFMA (rows a multiple of 256, cols of 128, not tall); the others on bf16
+@pytest.mark.parametrize("rows,cols", [(96, 320), (320, 96), (256, 512), (640, 224), (1024, 1024), (512, 1536),
+                                       (768, 640)])
 def test_ns_mxfp8_matches_oracle(rows, cols):
     data, scale, m, inv = _carrier_input(rows, cols, 48 + rows, gaussian=True)
     out = torch.empty(rows, cols, dtype=torch.bfloat16, device=DEV)
@@ -326,3 +329,70 @@ def test_muon_step_carrier_mode_llama8b_layer():
         sc = 0.2 * math.sqrt(max(r, c))
         dW = host(mats[i][4])[rows].astype(np.float64) - W0[i][rows]
         _within(dW, -0.02 * sc * ref, f"dW[{name}]")
+
+
+@pytest.mark.parametrize("steps", [1, 2])
+def test_ns_mxfp8_first_gram_few_steps(steps):
+    """T = 1, 2 on a shape whose first Gram runs on fp8 MFMA: the output is
+    dominated by that product, so an error in it (scale association, lane
+    layout, the alpha = inv^2 factor) shows directly."""
+    rows, cols = 512, 1024
+    data, scale, m, inv = _carrier_input(rows, cols, 50, gaussian=True)
+    out = torch.empty(rows, cols, dtype=torch.float32, device=DEV)
+    q.ns_orthogonalize_mxfp8(data, scale, inv, out, steps=steps, coeffs=COEF)
+    torch.cuda.synchronize()
+    ref = ns.ns_orthogonalize(m, steps, COEF, inv_norm=float(host(inv)[0]))
+    _within(host(out).astype(np.float64), ref, f"O T={steps}")
+
+
+def test_ns_mxfp8_scales_vary_per_block():
+    """Random bytes with scale bytes spread over 100..140 (per-32 scales that
+    differ by up to 2^40 within a row): each lane's fp8 values must meet their
+    own block's scale."""
+    rows, cols = 256, 1024
+    data, scale = H.carrier_bytes(rows, cols, DEV, 51, scale_lo=100, scale_hi=140)
+    torch.cuda.synchronize()
+    m = oracle.decode_carrier(host(data).reshape(-1), host(scale).reshape(-1)).reshape(rows, cols)
+    inv = torch.tensor([np.float32(1.0 / (np.sqrt(np.sum(m * m)) + 1e-7))], device=DEV)
+    out = torch.empty(rows, cols, dtype=torch.float32, device=DEV)
+    q.ns_orthogonalize_mxfp8(data, scale, inv, out, steps=1, coeffs=COEF)
+    torch.cuda.synchronize()
+    ref = ns.ns_orthogonalize(m, 1, COEF, inv_norm=float(host(inv)[0]))
+    _within(host(out).astype(np.float64), ref, "O T=1, wide scale spread")
+
+
+def test_muon_step_carrier_mode_fp8_gram():
+    """Carrier-mode steps where every matrix is wide with rows a multiple of
+    256 and cols of 128, so the first Gram of each step runs on fp8 MFMA:
+    state bit-exact, O and dW from the decoded carrier."""
+    shapes = [(256, 1024), (512, 2048), (768, 768)]
+    trip, mats, W_host, states = [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3201, i)
+        g = torch.empty(r * c, dtype=torch.bfloat16, device=DEV)
+        w = H.weights((r, c), DEV, 3201, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, w))
+        W_host.append(as_f64(w))
+        states.append((host(codes), host(absmax)))
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], len(shapes))
+    params = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, weight_decay=0.01, rms_scale=0.2,
+                            ns_steps=5, period=1, carrier=True)
+    for t in (1, 2):
+        for i, (r, c) in enumerate(shapes):
+            trip[i][2].copy_(H.grad((r, c), torch.bfloat16, DEV, 3201, i, t).reshape(-1))
+        torch.cuda.synchronize()
+        gh = [host_grad(trip[i][2]) for i in range(len(shapes))]
+        say("fp8-gram carrier step", t)
+        q.muon_step(plan, None, mats, t, params)
+        torch.cuda.synchronize()
+        for i, (r, c) in enumerate(shapes):
+            W2, c2, a2, O, _ = muonbp.muon_step(
+                W_host[i], states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c, r, c, 1, 0.95, 1e-7,
+                COEF, 5, 0.02, 0.02, 0.2, 0.01, carrier=True)
+            assert_bits_equal(host(trip[i][0]), c2, f"t{t} codes[{i}]")
+            assert_bits_equal(host(trip[i][1]), a2, f"t{t} absmax[{i}]")
+            states[i] = (c2, a2)
+            _within(as_f64(trip[i][2]).reshape(r, c), O, f"t{t} O[{i}]")
+            _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"t{t} dW[{i}]")
+            W_host[i] = as_f64(mats[i][4])
