@@ -498,11 +498,13 @@ __global__ __launch_bounds__(kThreads) void q8_scale_kernel(const PlanTensor *__
     }
 }
 
-// Workgroups per streaming launch: enough waves in flight to cover HBM
-// latency on 256 CUs, few enough that the grid-stride loop amortises setup.
+// Workgroups per streaming launch: one task per wave (the kernels keep
+// their grid-stride loop, which then runs once).  Measured on the 8B layer,
+// this beat grids capped at 8, 16 or 32 workgroups per CU by 5-10 %: the
+// hardware dispatcher keeps every CU's wave slots refilled as tasks finish.
 int stream_grid(int64_t n_tasks) {
     const int64_t want = (n_tasks + kWavesPerWG - 1) / kWavesPerWG;
-    const int64_t cap = 256 * 16;
+    const int64_t cap = (int64_t)1 << 30;
     return (int)(want < cap ? want : cap);
 }
 
