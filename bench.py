@@ -163,7 +163,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
     import quantized_momentum_newton_amd as q
@@ -172,11 +172,11 @@ def main():
     torch.cuda.init()
 
     if args.workload == "llama8b":
-        tensors, segments, ng = H.config3_layout()
+        tensors, segments, ng = H.llama8b_layer_layout()
     elif args.workload == "layerset28":
-        tensors, segments, ng = H.config2_layout()
+        tensors, segments, ng = H.layerset28_layout()
     else:
-        cfg = H.config4_shape()
+        cfg = H.muonbp_4096x14336_shape()
         tensors = [("w", cfg["rows"], cfg["cols"])]
         segments, ng = [(0, 0, cfg["rows"] * cfg["cols"], 0)], 1
     seed = {"llama8b": 1003, "layerset28": 1002, "muonbp": 1004}[args.workload]

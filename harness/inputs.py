@@ -95,12 +95,12 @@ NS_STEPS = 5
 BETA = 0.95
 
 
-def config1_shapes():
+def fp32_256x512_shapes():
     """Single 256x512 fp32 grad."""
     return [("w", 256, 512)]
 
 
-def config2_layout(layers=28, hidden=2048):
+def layerset28_layout(layers=28, hidden=2048):
     """One 2048-hidden layer set x28: fused QKV 2560x2048 (q 2048 rows, k 256,
     v 256), o 2048x2048, gate/up 6144x2048, down 2048x6144.  Returns
     (tensors, segments, ngroups): tensors = [(name, rows, cols)], segments =
@@ -123,7 +123,7 @@ def config2_layout(layers=28, hidden=2048):
     return tensors, segments, gid
 
 
-def config3_layout():
+def llama8b_layer_layout():
     """Llama-8B-shaped layer: q/o 4096x4096, k/v 1024x4096, gate/up
     14336x4096, down 4096x14336; one norm group per tensor."""
     tensors = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096),
@@ -148,14 +148,14 @@ def blocked_segments(rows, cols, block_rows, block_cols, tensor_index=0, group0=
     return segs, (rows // block_rows) * nbc
 
 
-def config4_shape():
+def muonbp_4096x14336_shape():
     """MuonBP-shaped momentum 4096x14336, 8 column blocks of 4096x1792, P=5."""
     return dict(rows=4096, cols=14336, block_rows=4096, block_cols=1792,
                 period=5, steps=20, lr_full=0.02, lr_block=0.01,
                 rms_scale=0.2, weight_decay=0.0)
 
 
-def config5_shape():
+def grasp_4096_shape():
     """GRASP-shaped 4096x4096, rank 8, 64x64 grid blocks, mu=0.95, 20 steps."""
     return dict(rows=4096, cols=4096, rank=8, grid=64, mu=0.95, steps=20,
                 lr=0.02, weight_decay=0.0)

@@ -135,7 +135,7 @@ def test_carrier_update_strided_grad_views(dtype):
 
 def test_carrier_update_llama8b_layer_full():
     """The Llama-8B layer (7 bf16 tensors, 218M elements): every byte checked."""
-    tensors, segments, ng = H.config3_layout()
+    tensors, segments, ng = H.llama8b_layer_layout()
     shapes = [(r, c) for (_, r, c) in tensors]
     qs = Q8Set(shapes, [torch.bfloat16] * len(shapes), seed=45)
     say("carrier update, llama-8B layer")
@@ -299,7 +299,7 @@ def test_muon_step_carrier_mode_muonbp():
 def test_muon_step_carrier_mode_llama8b_layer():
     """One full carrier-mode step on the Llama-8B layer: state bit-exact, O
     and dW on sampled rows against NS of the decoded carrier."""
-    tensors, segments, ng = H.config3_layout()
+    tensors, segments, ng = H.llama8b_layer_layout()
     trip, mats, hin = [], [], []
     for i, (name, r, c) in enumerate(tensors):
         codes, absmax = H.prior_state(r * c, DEV, 1103, i)

@@ -123,10 +123,10 @@ def test_grasp_ragged_shape_and_rank4():
         assert rel < 1e-4 and cos > 0.99999, (rel, cos)     # fp32 output, f32 NS
 
 
-def test_grasp_config5_full_size():
+def test_grasp_4096_full_size():
     """4096x4096, rank-8 spike of norm 10x the noise, mu = 0.95, 20 steps:
     state checked on every step, NS on sampled rows at the last step."""
-    cfg = H.config5_shape()
+    cfg = H.grasp_4096_shape()
     rows, cols, k, mu = cfg["rows"], cfg["cols"], cfg["rank"], cfg["mu"]
     spike = H.spike(rows, cols, k, DEV, 1005)
     warm = H.gaussian((cols, k), DEV, 1005)
@@ -138,7 +138,7 @@ def test_grasp_config5_full_size():
         g = _grad(rows, cols, spike, 1005, t)
         gh = g.float().cpu().numpy()
         prev = to_oracle(st)
-        say("config-5 step", t)
+        say("grasp 4096x4096 step", t)
         q.grasp_step(st, g, warm, mu=mu, ns_steps=5, coeffs=COEF, eps=H.NS_EPS, ws=ws)
         torch.cuda.synchronize()
         ref, M, P32, R32, _ = OG.grasp_step(prev, gh, mu, hw, 5, COEF, H.NS_EPS, with_ns=False)

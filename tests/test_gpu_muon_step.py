@@ -83,7 +83,7 @@ def test_reduced_muonbp_run_20_steps():
 def test_llama8b_layer_full_step():
     """One full Muon step on the Llama-8B layer: state bit-exact, O and the
     weight change on sampled rows of every matrix."""
-    tensors, segments, ng = H.config3_layout()
+    tensors, segments, ng = H.llama8b_layer_layout()
     trip, mats, hin = [], [], []
     for i, (name, r, c) in enumerate(tensors):
         codes, absmax = H.prior_state(r * c, DEV, 1003, i)
@@ -121,7 +121,7 @@ def test_muonbp_full_size_state_and_sampled_ns():
     """4096x14336, 8 column blocks, P = 5, 20 steps: the q8 state is
     bit-exact on all 20 steps (it does not depend on NS or W); NS is checked
     on sampled rows at a block step (4) and a full step (5)."""
-    cfg = H.config4_shape()
+    cfg = H.muonbp_4096x14336_shape()
     r, c, br, bc = cfg["rows"], cfg["cols"], cfg["block_rows"], cfg["block_cols"]
     codes, absmax = H.prior_state(r * c, DEV, 1004, 0)
     g = torch.empty(r * c, dtype=torch.bfloat16, device=DEV)

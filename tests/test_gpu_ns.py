@@ -39,7 +39,7 @@ def test_ns_small_shapes(shape, precision, dtype):
     _check(as_f64(x), ref, precision if dtype == torch.float32 else "bf16")
 
 
-def test_config1_f32_mode():
+def test_256x512_f32_mode():
     """256x512 fp32, F32 arithmetic, 5 quintic steps."""
     x = H.grad((256, 512), torch.float32, DEV, 1001, 7)
     x0 = as_f64(x)

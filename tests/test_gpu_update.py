@@ -86,7 +86,7 @@ def test_update_without_sums_matches():
         assert_bits_equal(host_grad(qs.grads[i]), m, "m")
 
 
-def test_config1_single_fp32():
+def test_single_256x512_fp32():
     qs = Q8Set([(256, 512)], [torch.float32], seed=1001)
     say("256x512 fp32 update+normalize")
     run_and_compare(qs, [(0, 0, 256 * 512, 0)], 1, H.BETA, H.NS_EPS)
@@ -126,10 +126,10 @@ def test_interleaved_qkv_segments():
     assert plan.n_blocks == 57344 and len(segs) == 3072
 
 
-def test_config2_full_size_sampled():
+def test_layerset28_full_size_sampled():
     """All 140 tensors of the 28-layer set in the benchmark's launch; layers 0
     and 27 checked element by element against the oracle."""
-    tensors, segments, ng = H.config2_layout()
+    tensors, segments, ng = H.layerset28_layout()
     shapes = [(r, c) for (_, r, c) in tensors]
     qs = Q8Set.__new__(Q8Set)
     qs.shapes, qs.dtypes = shapes, [torch.bfloat16] * len(shapes)
@@ -147,8 +147,8 @@ def test_config2_full_size_sampled():
     run_and_compare(qs, segments, ng, H.BETA, H.NS_EPS, check_idx=sample)
 
 
-def test_config3_update_full():
-    tensors, segments, ng = H.config3_layout()
+def test_llama8b_layer_update_full():
+    tensors, segments, ng = H.llama8b_layer_layout()
     shapes = [(r, c) for (_, r, c) in tensors]
     qs = Q8Set(shapes, [torch.bfloat16] * len(shapes), seed=1003)
     say("llama-8B layer update+normalize")
