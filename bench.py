@@ -28,7 +28,10 @@ E8M0 scales, 5.0625 B/element, and the NS prologue decodes them); the update
 
 Other workloads (not the headline): --workload layerset28 (the 28-layer
 2048-hidden set, grouped update + normalisation only), --workload muonbp
-(4096x14336, 8 column blocks, P = 5).
+(4096x14336, 8 column blocks, P = 5), --workload grasp (GRASP 4096x4096,
+rank 8: steps/s, state-path GB/s and f32 NS TFLOP/s against the fp32 peak),
+--workload fp32_256x512 (one small fp32 matrix, latency in us per step).
+per_step_ms gives the 10/50/90th percentiles of the per-step event times.
 """
 import argparse
 import hashlib
@@ -54,7 +57,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "layerset28", "muonbp"])
+    ap.add_argument("--workload", default="llama8b",
+                    choices=["llama8b", "layerset28", "muonbp", "grasp", "fp32_256x512"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="requantisation rounding of the update (the headline uses nearest)")
@@ -159,12 +163,104 @@ def cpu_baseline(host_q, host_ns, steps):
     }
 
 
+def percentiles(ms):
+    import numpy as np
+    p10, p50, p90 = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
+
+
+def bench_grasp(args, q, H, torch):
+    """GRASP 4096x4096 (rank 8): one grasp_step per step on a fresh bf16 grad
+    (noise + a fixed rank-8 spike); the state path and the f32 NS (T = 5)."""
+    cfg = H.grasp_4096_shape()
+    rows, cols, k = cfg["rows"], cfg["cols"], cfg["rank"]
+    dev = "cuda"
+    spike = H.spike(rows, cols, k, dev, 1005)
+    warm = H.gaussian((cols, k), dev, 1005)
+    grads = [(H.grad((rows, cols), torch.float32, dev, 1005, t) + spike).to(torch.bfloat16) for t in range(4)]
+    st = q.GraspState(rows, cols, k)
+    ws = torch.empty(q.grasp_workspace_bytes(rows, cols, k), dtype=torch.uint8, device=dev)
+    g = torch.empty_like(grads[0])
+    evs = []
+    for t in range(args.warmup + args.steps):
+        g.copy_(grads[t % 4])
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        if t == args.warmup:
+            torch.cuda.synchronize()
+            q.timing_enable(True)
+        e[0].record()
+        q.grasp_step(st, g, warm, mu=cfg["mu"], ns_steps=H.NS_STEPS, coeffs=H.NS_COEFFS, eps=H.NS_EPS, ws=ws)
+        e[1].record()
+        if t >= args.warmup:
+            evs.append(e)
+    torch.cuda.synchronize()
+    q.timing_enable(False)
+    ms = [a.elapsed_time(b) for a, b in evs]
+    step_ms = sum(ms) / len(ms)
+    ns_ms = sum(q.timing_read(c)[0] for c in ("ns_norm", "ns_prologue", "ns_gram", "ns_poly", "ns_xupdate",
+                                                "ns_writeback")) / args.steps
+    state_ms = step_ms - ns_ms
+    numel = rows * cols
+    state_bytes = numel * 15.25             # three passes over the fp32 momentum plus the codes
+    ns_fl = ns_sym_flops(rows, cols, H.NS_STEPS)
+    return {"metric": METRIC, "value": round(1000.0 / step_ms, 3), "unit": "steps/s", "dtype": "f32",
+            "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
+            "config": {"workload": "grasp_4096x4096_rank8", "ns_steps": H.NS_STEPS, "ns_precision": "f32",
+                       "state_ms": round(state_ms, 4), "ns_ms": round(ns_ms, 4),
+                       "state_gbs": round(state_bytes / (state_ms * 1e-3) / 1e9, 1),
+                       "ns_tflops": round(ns_fl / (ns_ms * 1e-3) / 1e12, 2),
+                       "ns_frac_of_fp32_peak": round(ns_fl / (ns_ms * 1e-3) / 1e12 / F32_PEAK_TFLOPS, 4)}}
+
+
+def bench_small(args, q, H, torch):
+    """One 256x512 fp32 matrix: update + normalise + f32 NS (T = 5) + weight
+    apply through muon_step.  Latency-bound (1.3 MB, 0.6 GFLOP): reported as
+    microseconds per step."""
+    (_, r, c), = H.fp32_256x512_shapes()
+    dev = "cuda"
+    codes, absmax = H.prior_state(r * c, dev, 1001, 0)
+    g0 = H.grad((r, c), torch.float32, dev, 1001, 0).reshape(-1)
+    g = g0.clone()
+    w = H.weights((r, c), dev, 1001, 0)
+    plan = q.Plan([(codes, absmax, g)], [(0, 0, r * c, 0)], 1)
+    mats = [(r, c, r, c, w)]
+    hp = q.make_hparams(beta=H.BETA, eps=H.NS_EPS, coeffs=H.NS_COEFFS, ns_steps=H.NS_STEPS, period=1,
+                        precision="f32")
+    ws = torch.empty(q.muon_step_workspace_bytes(plan, None, mats, hparams=hp), dtype=torch.uint8, device=dev)
+    evs = []
+    for t in range(args.warmup + args.steps):
+        g.copy_(g0)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        q.muon_step(plan, None, mats, t + 1, hp, ws=ws)
+        e[1].record()
+        if t >= args.warmup:
+            evs.append(e)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    step_ms = sum(ms) / len(ms)
+    return {"metric": METRIC, "value": round(step_ms * 1e3, 2), "unit": "us/step", "dtype": "f32",
+            "higher_is_better": False, "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
+            "config": {"workload": "fp32_256x512_muon_step", "ns_steps": H.NS_STEPS, "ns_precision": "f32"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if args.workload in ("grasp", "fp32_256x512"):
+        import torch
+        import quantized_momentum_newton_amd as q
+        from harness import inputs as H
+        torch.cuda.init()
+        fn = bench_grasp if args.workload == "grasp" else bench_small
+        out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+        out.update(fn(args, q, H, torch))
+        print(json.dumps(out), flush=True)
+        return
     import torch
     import quantized_momentum_newton_amd as q
     from harness import inputs as H
@@ -278,10 +374,11 @@ def main():
         upd_ms = (per_class["q8_update"][0] + per_class["group_reduce"][0]) / args.steps
         ns_ms = call_ms - upd_ms
     ms_per_step = total_ms / args.steps
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "data": "synthetic"}
+           "ms_per_step": round(ms_per_step, 4), "per_step_ms": percentiles(step_ms), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
     if args.workload == "layerset28":
         bytes_ = numel * (BYTES_PER_ELEM_UPDATE + BYTES_PER_ELEM_SCALE)
         gbs = bytes_ / (upd_ms * 1e-3) / 1e9

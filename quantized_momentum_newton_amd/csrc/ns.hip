@@ -533,7 +533,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     //     stores them as a segment of the transposed target; the lanes of a
     //     wave read consecutive columns of one LDS row per instruction.
     // The loop's last barrier has passed, so every stage buffer is free.
-    constexpr int ER = 64;           // tile rows per pass
+    constexpr int ER = WM < 64 ? WM : 64;   // tile rows per pass
     constexpr int EP = BN + 8;       // fp32 pitch; 4 EP = 32 mod 64 banks separates the two half-waves
     constexpr int NTH = NW * 64;
     constexpr int RIT = ER * (BN / 8) / NTH;   // row-phase items per thread
@@ -1190,6 +1190,29 @@ struct CfgSym {
 struct CfgRect {
     static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
 };
+// fp32 runs on matrices too small to give every CU a 256 x 256 tile: the
+// fp32 MFMA needs 16x fewer operand bytes per second than bf16, so smaller
+// tiles cost little and keep all CUs busy (128 x 128: 4 waves of 64 x 64,
+// two workgroups per CU; 64 x 64: 4 waves of 32 x 32, four per CU).
+struct CfgF32Mid {
+    static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, ROWB = 128, NST = 2, MINB = 2;
+};
+struct CfgF32Small {
+    static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, ROWB = 128, NST = 2, MINB = 4;
+};
+
+// Compute units of the current device (cached per device).
+int64_t cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
 
 template <typename T, typename C, int EPI, bool SYM, bool QT = false>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
@@ -1243,6 +1266,125 @@ struct ItemBufs {
     char *XT[2] = {nullptr, nullptr};
     char *A = nullptr, *B = nullptr;
 };
+
+// The T iterations of one chunk: A = X X^T, B = b A + c A A, X = a X + B X,
+// with the symmetric products on tile configuration CS and the last on CR.
+template <typename T, typename CS, typename CR>
+qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk,
+                       const std::vector<ItemBufs> &bufs, const std::vector<int> &by_n, const std::vector<int> &by_m,
+                       std::vector<int> &cur, int steps, float a, float b, float c, hipStream_t stream) {
+    const int nit = (int)chunk.size();
+    constexpr bool kQT = sizeof(T) == 2;   // bf16: transposing reads, no X^T copy
+    constexpr int64_t kSymK = CS::ROWB / (int64_t)sizeof(T);    // K elements per k-tile
+    constexpr int64_t kRectK = CR::ROWB / (int64_t)sizeof(T);
+    for (int s = 0; s < steps; s++) {
+        // A = X X^T.  On the first iteration of a bf16 run whose requests
+        // are all carriers that qualify, the block-scaled fp8 product runs
+        // instead.  A chunk that mixes in other requests keeps one bf16
+        // launch: two smaller launches back to back fill the GPU worse than
+        // the fp8 product saves (measured on the 8B layer, whose tall gate
+        // and up matrices cannot take it).
+        bool all_mx = kQT && s == 0;
+        for (int k = 0; k < nit; k++) all_mx = all_mx && mx_gram_ok(req[chunk[k]]);
+        GemmArgs<T> g1{};
+        MxGramArgs gx{};
+        int tl = 0, tx = 0;
+        for (int k = 0; k < nit; k++) {
+            const ItemBufs &B = bufs[by_n[k]];
+            const int tm = (int)(B.g.mp / CS::BM);
+            const NsRequest &r = req[chunk[by_n[k]]];
+            if (all_mx) {
+                MxItem &M = gx.it[gx.n_items++];
+                M.X = static_cast<const uint8_t *>(r.src);
+                M.S = r.sc;
+                M.C = reinterpret_cast<bf16_t *>(B.A);
+                M.inv = r.inv;
+                M.ldx = r.ld;
+                M.lds = r.sld;
+                M.ldc = B.g.ldm;
+                M.tiles_m = tm;
+                M.tile_begin = tx;
+                M.k_tiles = (int32_t)(r.cols / 128);
+                tx += tm * (tm + 1) / 2;
+                continue;
+            }
+            GItem<T> &I = g1.it[g1.n_items++];
+            const char *X = kQT ? B.X[cur[by_n[k]]] : B.X[0];
+            I.P = reinterpret_cast<const T *>(X); I.ldp = B.g.ldn;
+            I.Q = reinterpret_cast<const T *>(X); I.ldq = B.g.ldn;
+            I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.ldm;
+            I.tiles_m = tm;
+            I.tiles_n = tm;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.np / kSymK);
+            tl += tm * (tm + 1) / 2;
+        }
+        qm_status st = QM_OK;
+        if (g1.n_items) st = launch_gemm<T, CS, EPI_GRAM, true>(g1, tl, stream);
+        if (st != QM_OK) return st;
+        if (gx.n_items) st = launch_gram_mx(gx, tx, stream);
+        if (st != QM_OK) return st;
+        // B = b A + c A A
+        GemmArgs<T> g2{};
+        g2.n_items = nit;
+        g2.alpha = b;
+        g2.beta = c;
+        g2.dloop = c != 0.0f;
+        g2.dgain = c != 0.0f ? b / c : 0.0f;
+        tl = 0;
+        for (int k = 0; k < nit; k++) {
+            const ItemBufs &B = bufs[by_m[k]];
+            const int tm = (int)(B.g.mp / CS::BM);
+            GItem<T> &I = g2.it[k];
+            I.P = reinterpret_cast<const T *>(B.A); I.ldp = B.g.ldm;
+            I.Q = reinterpret_cast<const T *>(B.A); I.ldq = B.g.ldm;
+            I.C = reinterpret_cast<T *>(B.B); I.ldc = B.g.ldm;
+            I.D = reinterpret_cast<const T *>(B.A); I.ldd = B.g.ldm;
+            I.tiles_m = tm;
+            I.tiles_n = tm;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.mp / kSymK);
+            tl += tm * (tm + 1) / 2;
+        }
+        st = launch_gemm<T, CS, EPI_POLY, true>(g2, tl, stream);
+        if (st != QM_OK) return st;
+        // X = a X + B X: bf16 reads Q = X (K x N) and writes the other X
+        // buffer; fp32 reads Q = X^T and updates X in place, writing X^T.
+        GemmArgs<T> g3{};
+        g3.n_items = nit;
+        g3.alpha = a;
+        g3.dloop = 1;
+        g3.dgain = a;
+        tl = 0;
+        for (int k = 0; k < nit; k++) {
+            const int i = by_m[k];
+            const ItemBufs &B = bufs[i];
+            const int tm = (int)(B.g.mp / CR::BM), tn = (int)(B.g.np / CR::BN);
+            GItem<T> &I = g3.it[k];
+            I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.ldm;
+            if constexpr (kQT) {
+                I.Q = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldq = B.g.ldn;
+                I.C = reinterpret_cast<T *>(B.X[cur[i] ^ 1]); I.ldc = B.g.ldn;
+                I.D = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldd = B.g.ldn;
+            } else {
+                I.Q = reinterpret_cast<const T *>(B.XT[cur[i]]); I.ldq = B.g.ldm;
+                I.C = reinterpret_cast<T *>(B.X[0]); I.ldc = B.g.ldn;
+                I.CT = reinterpret_cast<T *>(B.XT[cur[i] ^ 1]); I.ldct = B.g.ldm;
+                I.D = reinterpret_cast<const T *>(B.X[0]); I.ldd = B.g.ldn;
+            }
+            I.tiles_m = tm;
+            I.tiles_n = tn;
+            I.tile_begin = tl;
+            I.k_tiles = (int32_t)(B.g.mp / kRectK);
+            tl += tm * tn;
+            if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
+        }
+        st = launch_gemm<T, CR, EPI_UPDATE, false, kQT>(g3, tl, stream);
+        if (st != QM_OK) return st;
+        for (int i = 0; i < nit; i++) cur[i] ^= 1;
+    }
+    return QM_OK;
+}
 
 template <typename T>
 qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int steps, float a,
@@ -1325,8 +1467,6 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     for (int i = 0; i < nit; i++) wb.fo[i] = fo[i];
 
     // Per-product item order: longest K first (all tiles of a matrix share K).
-    constexpr int64_t kSymK = CfgSym::ROWB / (int64_t)sizeof(T);    // K elements per k-tile
-    constexpr int64_t kRectK = CfgRect::ROWB / (int64_t)sizeof(T);
     std::vector<int> by_n(nit), by_m(nit);
     std::iota(by_n.begin(), by_n.end(), 0);
     std::iota(by_m.begin(), by_m.end(), 0);
@@ -1335,112 +1475,26 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         return bufs[x].g.mp * bufs[x].g.np > bufs[y].g.mp * bufs[y].g.np;
     });
     std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
-    for (int s = 0; s < steps; s++) {
-        // A = X X^T.  On the first iteration of a bf16 run whose requests
-        // are all carriers that qualify, the block-scaled fp8 product runs
-        // instead.  A chunk that mixes in other requests keeps one bf16
-        // launch: two smaller launches back to back fill the GPU worse than
-        // the fp8 product saves (measured on the 8B layer, whose tall gate
-        // and up matrices cannot take it).
-        bool all_mx = kQT && s == 0;
-        for (int k = 0; k < nit; k++) all_mx = all_mx && mx_gram_ok(req[chunk[k]]);
-        GemmArgs<T> g1{};
-        MxGramArgs gx{};
-        int tl = 0, tx = 0;
-        for (int k = 0; k < nit; k++) {
-            const ItemBufs &B = bufs[by_n[k]];
-            const int tm = (int)(B.g.mp / CfgSym::BM);
-            const NsRequest &r = req[chunk[by_n[k]]];
-            if (all_mx) {
-                MxItem &M = gx.it[gx.n_items++];
-                M.X = static_cast<const uint8_t *>(r.src);
-                M.S = r.sc;
-                M.C = reinterpret_cast<bf16_t *>(B.A);
-                M.inv = r.inv;
-                M.ldx = r.ld;
-                M.lds = r.sld;
-                M.ldc = B.g.ldm;
-                M.tiles_m = tm;
-                M.tile_begin = tx;
-                M.k_tiles = (int32_t)(r.cols / 128);
-                tx += tm * (tm + 1) / 2;
-                continue;
-            }
-            GItem<T> &I = g1.it[g1.n_items++];
-            const char *X = kQT ? B.X[cur[by_n[k]]] : B.X[0];
-            I.P = reinterpret_cast<const T *>(X); I.ldp = B.g.ldn;
-            I.Q = reinterpret_cast<const T *>(X); I.ldq = B.g.ldn;
-            I.C = reinterpret_cast<T *>(B.A); I.ldc = B.g.ldm;
-            I.tiles_m = tm;
-            I.tiles_n = tm;
-            I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.np / kSymK);
-            tl += tm * (tm + 1) / 2;
+    qm_status st;
+    if constexpr (sizeof(T) == 4) {
+        // the largest tile whose Gram launch still gives every CU a tile
+        int64_t big = 0, mid = 0;
+        for (int i = 0; i < nit; i++) {
+            const int64_t t256 = bufs[i].g.mp / 256, t128 = bufs[i].g.mp / 128;
+            big += t256 * (t256 + 1) / 2;
+            mid += t128 * (t128 + 1) / 2;
         }
-        qm_status st = QM_OK;
-        if (g1.n_items) st = launch_gemm<T, CfgSym, EPI_GRAM, true>(g1, tl, stream);
-        if (st != QM_OK) return st;
-        if (gx.n_items) st = launch_gram_mx(gx, tx, stream);
-        if (st != QM_OK) return st;
-        // B = b A + c A A
-        GemmArgs<T> g2{};
-        g2.n_items = nit;
-        g2.alpha = b;
-        g2.beta = c;
-        g2.dloop = c != 0.0f;
-        g2.dgain = c != 0.0f ? b / c : 0.0f;
-        tl = 0;
-        for (int k = 0; k < nit; k++) {
-            const ItemBufs &B = bufs[by_m[k]];
-            const int tm = (int)(B.g.mp / CfgSym::BM);
-            GItem<T> &I = g2.it[k];
-            I.P = reinterpret_cast<const T *>(B.A); I.ldp = B.g.ldm;
-            I.Q = reinterpret_cast<const T *>(B.A); I.ldq = B.g.ldm;
-            I.C = reinterpret_cast<T *>(B.B); I.ldc = B.g.ldm;
-            I.D = reinterpret_cast<const T *>(B.A); I.ldd = B.g.ldm;
-            I.tiles_m = tm;
-            I.tiles_n = tm;
-            I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.mp / kSymK);
-            tl += tm * (tm + 1) / 2;
-        }
-        st = launch_gemm<T, CfgSym, EPI_POLY, true>(g2, tl, stream);
-        if (st != QM_OK) return st;
-        // X = a X + B X: bf16 reads Q = X (K x N) and writes the other X
-        // buffer; fp32 reads Q = X^T and updates X in place, writing X^T.
-        GemmArgs<T> g3{};
-        g3.n_items = nit;
-        g3.alpha = a;
-        g3.dloop = 1;
-        g3.dgain = a;
-        tl = 0;
-        for (int k = 0; k < nit; k++) {
-            const int i = by_m[k];
-            const ItemBufs &B = bufs[i];
-            const int tm = (int)(B.g.mp / CfgRect::BM), tn = (int)(B.g.np / CfgRect::BN);
-            GItem<T> &I = g3.it[k];
-            I.P = reinterpret_cast<const T *>(B.B); I.ldp = B.g.ldm;
-            if constexpr (kQT) {
-                I.Q = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldq = B.g.ldn;
-                I.C = reinterpret_cast<T *>(B.X[cur[i] ^ 1]); I.ldc = B.g.ldn;
-                I.D = reinterpret_cast<const T *>(B.X[cur[i]]); I.ldd = B.g.ldn;
-            } else {
-                I.Q = reinterpret_cast<const T *>(B.XT[cur[i]]); I.ldq = B.g.ldm;
-                I.C = reinterpret_cast<T *>(B.X[0]); I.ldc = B.g.ldn;
-                I.CT = reinterpret_cast<T *>(B.XT[cur[i] ^ 1]); I.ldct = B.g.ldm;
-                I.D = reinterpret_cast<const T *>(B.X[0]); I.ldd = B.g.ldn;
-            }
-            I.tiles_m = tm;
-            I.tiles_n = tn;
-            I.tile_begin = tl;
-            I.k_tiles = (int32_t)(B.g.mp / kRectK);
-            tl += tm * tn;
-            if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
-        }
-        st = launch_gemm<T, CfgRect, EPI_UPDATE, false, kQT>(g3, tl, stream);
-        if (st != QM_OK) return st;
-        for (int i = 0; i < nit; i++) cur[i] ^= 1;
+        const int64_t n_cu = cu_count();
+        if (big >= n_cu)
+            st = run_products<T, CfgSym, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+        else if (mid >= n_cu)
+            st = run_products<T, CfgF32Mid, CfgF32Mid>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+        else
+            st = run_products<T, CfgF32Small, CfgF32Small>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+    } else {
+        st = run_products<T, CfgSym, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
     }
+    if (st != QM_OK) return st;
     if constexpr (kQT)
         for (int i = 0; i < nit; i++) pa.it[i].X = bufs[i].X[cur[i]];
     {
