@@ -79,26 +79,61 @@ __global__ __launch_bounds__(kThreads) void deq_factors_kernel(const int8_t *pc,
 
 // ------------------------------------------------------------ ColNorm
 __global__ __launch_bounds__(kThreads) void colnorm_kernel(const float *Rd, const float *warm, Dims d, double *Q) {
-    __shared__ double scratch[4];
-    for (int c = 0; c < d.rank; c++) {
-        double s = 0.0;
-        for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
-            const double v = (double)Rd[j * d.rank + c];
-            s += v * v;
-        }
-        const double nrm = sqrt(block_sum(s, scratch));
-        if (nrm > 0.0) {
-            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) Q[j * d.rank + c] = (double)Rd[j * d.rank + c] / nrm;
-        } else {
-            double w = 0.0;
-            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
-                const double v = (double)warm[j * d.rank + c];
-                w += v * v;
+    // every column's sum of squares in one pass over Rd (per column: thread
+    // t adds rows t, t + 256, ... in order, then the block sum's fixed order)
+    __shared__ double part[4][16];
+    __shared__ double nrm[16], wnrm[16];
+    const int K = d.rank;
+    double s[16];
+#pragma unroll
+    for (int c = 0; c < 16; c++) s[c] = 0.0;
+    for (int64_t j = threadIdx.x; j < d.cols; j += kThreads)
+#pragma unroll
+        for (int c = 0; c < 16; c++)
+            if (c < K) {
+                const double v = (double)Rd[j * K + c];
+                s[c] += v * v;
             }
-            const double nw = sqrt(block_sum(w, scratch));
-            for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) Q[j * d.rank + c] = (double)warm[j * d.rank + c] / nw;
-        }
+#pragma unroll
+    for (int c = 0; c < 16; c++) {
+        double v = s[c];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = v;
     }
+    __syncthreads();
+    if (threadIdx.x < K) nrm[threadIdx.x] = sqrt(((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                                                part[3][threadIdx.x]);
+    __syncthreads();
+    bool any_zero = false;
+    for (int c = 0; c < K; c++) any_zero |= !(nrm[c] > 0.0);
+    if (any_zero) {   // warm-start columns: their norms, same order
+#pragma unroll
+        for (int c = 0; c < 16; c++) s[c] = 0.0;
+        for (int64_t j = threadIdx.x; j < d.cols; j += kThreads)
+#pragma unroll
+            for (int c = 0; c < 16; c++)
+                if (c < K) {
+                    const double v = (double)warm[j * K + c];
+                    s[c] += v * v;
+                }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < 16; c++) {
+            double v = s[c];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x < K)
+            wnrm[threadIdx.x] = sqrt(((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                                     part[3][threadIdx.x]);
+        __syncthreads();
+    }
+    for (int64_t j = threadIdx.x; j < d.cols; j += kThreads)
+        for (int c = 0; c < K; c++)
+            Q[j * K + c] = nrm[c] > 0.0 ? (double)Rd[j * K + c] / nrm[c] : (double)warm[j * K + c] / wnrm[c];
 }
 
 // ------------------------------------------------- momentum and Y = M Q
@@ -163,46 +198,131 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const uint8_t *res_c
 }
 
 // ------------------------------------------------------------ MGS
-// One workgroup: P = Y column by column, each earlier column projected out
-// with the current remainder (modified Gram-Schmidt), then normalised.
-__global__ __launch_bounds__(kThreads) void mgs_kernel(const double *Y, Dims d, double *P, float *P32) {
-    __shared__ double scratch[4];
+// One workgroup of 1024 threads: P = Y column by column, each earlier column
+// projected out with the current remainder (modified Gram-Schmidt), then
+// normalised.  The columns are worked on in a column-major copy Pc (rows x k
+// as k rows of `rows`), so every pass reads consecutive addresses; thread t
+// takes rows t, t + 1024, ... and the 16 waves' partial sums are added in
+// wave order.
+constexpr int kMgsThreads = 1024;
+
+__device__ __forceinline__ double block_sum_1024(double v, double *scratch) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = scratch[0];
+#pragma unroll
+    for (int w = 1; w < kMgsThreads / 64; w++) s += scratch[w];
+    __syncthreads();
+    return s;
+}
+
+__global__ __launch_bounds__(kMgsThreads) void mgs_kernel(const double *Y, Dims d, double *Pc, double *P, float *P32) {
+    __shared__ double scratch[kMgsThreads / 64];
     const int K = d.rank;
-    for (int64_t e = threadIdx.x; e < d.rows * K; e += kThreads) P[e] = Y[e];
+    const int64_t n = d.rows;
+    for (int64_t e = threadIdx.x; e < n * K; e += kMgsThreads) Pc[(e % K) * n + e / K] = Y[e];
     __syncthreads();
     for (int c = 0; c < K; c++) {
+        double *pc = Pc + c * n;
         for (int p = 0; p < c; p++) {
+            const double *pp = Pc + p * n;
             double s = 0.0;
-            for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) s += P[i * K + p] * P[i * K + c];
-            const double dot = block_sum(s, scratch);
-            for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) {
-                const double t = dot * P[i * K + p];
-                P[i * K + c] = P[i * K + c] - t;
+            for (int64_t i = threadIdx.x; i < n; i += kMgsThreads) s += pp[i] * pc[i];
+            const double dot = block_sum_1024(s, scratch);
+            for (int64_t i = threadIdx.x; i < n; i += kMgsThreads) {
+                const double t = dot * pp[i];
+                pc[i] = pc[i] - t;
             }
             __syncthreads();
         }
         double s = 0.0;
-        for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) s += P[i * K + c] * P[i * K + c];
-        const double nrm = sqrt(block_sum(s, scratch));
-        for (int64_t i = threadIdx.x; i < d.rows; i += kThreads) P[i * K + c] = nrm > 0.0 ? P[i * K + c] / nrm : 0.0;
+        for (int64_t i = threadIdx.x; i < n; i += kMgsThreads) s += pc[i] * pc[i];
+        const double nrm = sqrt(block_sum_1024(s, scratch));
+        for (int64_t i = threadIdx.x; i < n; i += kMgsThreads) pc[i] = nrm > 0.0 ? pc[i] / nrm : 0.0;
         __syncthreads();
     }
-    for (int64_t e = threadIdx.x; e < d.rows * K; e += kThreads) P32[e] = (float)P[e];
+    for (int64_t e = threadIdx.x; e < n * K; e += kMgsThreads) {
+        const double v = Pc[(e % K) * n + e / K];
+        P[e] = v;
+        P32[e] = (float)v;
+    }
+}
+
+// The same computation with the columns in registers, for rows <= 4 * 1024
+// and k <= 8: thread t holds rows t + 1024 r (r < 4) of every column, so a
+// pass is thread-local arithmetic plus one workgroup sum (the operations
+// and their order are those of mgs_kernel).
+template <int K>
+__global__ __launch_bounds__(kMgsThreads) void mgs_reg_kernel(const double *Y, Dims d, double *P, float *P32) {
+    constexpr int R = 4;
+    __shared__ double scratch[kMgsThreads / 64];
+    const int64_t n = d.rows;
+    double v[R][K];
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int64_t i = threadIdx.x + (int64_t)r * kMgsThreads;
+#pragma unroll
+        for (int c = 0; c < K; c++) v[r][c] = i < n ? Y[i * K + c] : 0.0;
+    }
+#pragma unroll
+    for (int c = 0; c < K; c++) {
+#pragma unroll
+        for (int p = 0; p < c; p++) {
+            double s = 0.0;
+#pragma unroll
+            for (int r = 0; r < R; r++)
+                if (threadIdx.x + (int64_t)r * kMgsThreads < n) s += v[r][p] * v[r][c];
+            const double dot = block_sum_1024(s, scratch);
+#pragma unroll
+            for (int r = 0; r < R; r++) {
+                const double t = dot * v[r][p];
+                v[r][c] = v[r][c] - t;
+            }
+        }
+        double s = 0.0;
+#pragma unroll
+        for (int r = 0; r < R; r++)
+            if (threadIdx.x + (int64_t)r * kMgsThreads < n) s += v[r][c] * v[r][c];
+        const double nrm = sqrt(block_sum_1024(s, scratch));
+#pragma unroll
+        for (int r = 0; r < R; r++) v[r][c] = nrm > 0.0 ? v[r][c] / nrm : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+        const int64_t i = threadIdx.x + (int64_t)r * kMgsThreads;
+        if (i < n)
+#pragma unroll
+            for (int c = 0; c < K; c++) {
+                P[i * K + c] = v[r][c];
+                P32[i * K + c] = (float)v[r][c];
+            }
+    }
 }
 
 // ------------------------------------------------------------ R = M^T P
-// 64 columns per workgroup; lane (c, g) = (t % 64, t / 64) sums rows g, g+4,
-// ... (fp64), then the four row groups are added in order.
+// Workgroup (bx, by) covers columns 64 bx .. 64 bx + 63 and rows
+// kRtRows by .. kRtRows (by + 1) - 1: lane (c, g) = (t % 64, t / 64) sums rows
+// g, g+4, ... of the chunk (fp64), the four row groups are added in order,
+// and the chunk's partial goes to Rpart[by].  rt_combine adds the chunks in
+// order and rounds to fp32.
+constexpr int kRtRows = 128;
+
 template <int K>
-__global__ __launch_bounds__(kThreads) void rt_kernel(const float *M, const double *P, Dims d, float *R32) {
+__global__ __launch_bounds__(kThreads) void rt_partial_kernel(const float *M, const double *P, Dims d,
+                                                              double *Rpart) {
     __shared__ double part[4][64 * K];
     const int c = threadIdx.x & 63, grp = threadIdx.x >> 6;
     const int64_t j = (int64_t)blockIdx.x * 64 + c;
+    const int64_t i0 = (int64_t)blockIdx.y * kRtRows;
+    const int64_t i1 = min(d.rows, i0 + kRtRows);
     double acc[K];
 #pragma unroll
     for (int k = 0; k < K; k++) acc[k] = 0.0;
     if (j < d.cols)
-        for (int64_t i = grp; i < d.rows; i += 4) {
+        for (int64_t i = i0 + grp; i < i1; i += 4) {
             const double m = (double)M[i * d.cols + j];
 #pragma unroll
             for (int k = 0; k < K; k++) acc[k] += m * P[i * K + k];
@@ -210,10 +330,21 @@ __global__ __launch_bounds__(kThreads) void rt_kernel(const float *M, const doub
 #pragma unroll
     for (int k = 0; k < K; k++) part[grp][c * K + k] = acc[k];
     __syncthreads();
+    double *out = Rpart + (int64_t)blockIdx.y * d.cols * K;
     for (int e = threadIdx.x; e < 64 * K; e += kThreads) {
         const int64_t jj = (int64_t)blockIdx.x * 64 + e / K;
-        if (jj < d.cols) R32[jj * K + e % K] = (float)(((part[0][e] + part[1][e]) + part[2][e]) + part[3][e]);
+        if (jj < d.cols) out[jj * K + e % K] = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
     }
+}
+
+__global__ __launch_bounds__(kThreads) void rt_combine_kernel(const double *Rpart, int64_t chunks, Dims d,
+                                                              float *R32) {
+    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t n = d.cols * d.rank;
+    if (e >= n) return;
+    double s = 0.0;
+    for (int64_t ch = 0; ch < chunks; ch++) s += Rpart[ch * n + e];
+    R32[e] = (float)s;
 }
 
 // ------------------------------------------------ residual, 4-bit codes
@@ -221,22 +352,30 @@ __global__ __launch_bounds__(kThreads) void rt_kernel(const float *M, const doub
 //   res = (float)(M - sum_c P32[i][c] R32[j][c])   (fp64, c in order)
 //   row / column maxima of |res| inside the block; code = d == 0 ? 0 :
 //   clamp(rint((res / d) * 7), -7, 7), two codes per byte (even column low).
+template <int K>
 __global__ __launch_bounds__(kThreads) void residual_q4_kernel(const float *M, const float *P32, const float *R32,
                                                                Dims d, uint8_t *codes, float *rmax_out,
                                                                float *cmax_out) {
     __shared__ float tile[64][65];
     __shared__ float rm[64], cm[64];
+    __shared__ float ps[64][K], rs[64][K];   // the block's rows of P32 and of R32
     const int64_t bi = blockIdx.y, bj = blockIdx.x;
     const int64_t r0 = bi * 64, c0 = bj * 64;
     const int br = (int)min<int64_t>(64, d.rows - r0), bc = (int)min<int64_t>(64, d.cols - c0);
-    const int K = d.rank;
+    for (int e = threadIdx.x; e < 64 * K; e += kThreads) {
+        const int r = e / K, c = e % K;
+        ps[r][c] = r < br ? P32[(r0 + r) * K + c] : 0.0f;
+        rs[r][c] = r < bc ? R32[(c0 + r) * K + c] : 0.0f;
+    }
+    __syncthreads();
     for (int idx = threadIdx.x; idx < 4096; idx += kThreads) {
         const int ii = idx >> 6, jj = idx & 63;
         float v = 0.0f;
         if (ii < br && jj < bc) {
             const int64_t i = r0 + ii, j = c0 + jj;
             double acc = (double)M[i * d.cols + j];
-            for (int c = 0; c < K; c++) acc = acc - (double)P32[i * K + c] * (double)R32[j * K + c];
+#pragma unroll
+            for (int c = 0; c < K; c++) acc = acc - (double)ps[ii][c] * (double)rs[jj][c];
             v = (float)acc;
         }
         tile[ii][jj] = v;
@@ -311,7 +450,8 @@ __global__ __launch_bounds__(kThreads) void factor_q8_kernel(const float *X, int
 
 struct Ws {
     float *M, *Pd, *Rd, *P32, *R32;
-    double *Q, *Y, *P;
+    double *Q, *Y, *P, *Pc, *Rpart;
+    int64_t rt_chunks;
     void *ns;
     size_t bytes;
 };
@@ -333,6 +473,9 @@ Ws carve(const Dims &d, void *base) {
     w.Q = reinterpret_cast<double *>(take(ck * 8));
     w.Y = reinterpret_cast<double *>(take(rk * 8));
     w.P = reinterpret_cast<double *>(take(rk * 8));
+    w.Pc = reinterpret_cast<double *>(take(rk * 8));
+    w.rt_chunks = (d.rows + kRtRows - 1) / kRtRows;
+    w.Rpart = reinterpret_cast<double *>(take(w.rt_chunks * ck * 8));
     w.ns = p;
     w.bytes = (size_t)(p - static_cast<char *>(base));
     return w;
@@ -363,8 +506,13 @@ void launch_rank_kernels(const qm_grasp_state *s, const Dims &d, const Ws &w, co
 }
 
 template <int K>
-void launch_rt(const Dims &d, const Ws &w, hipStream_t st) {
-    rt_kernel<K><<<(unsigned)((d.cols + 63) / 64), kThreads, 0, st>>>(w.M, w.P, d, w.R32);
+void launch_rt_residual(const qm_grasp_state *s, const Dims &d, const Ws &w, hipStream_t st) {
+    rt_partial_kernel<K><<<dim3((unsigned)((d.cols + 63) / 64), (unsigned)w.rt_chunks), kThreads, 0, st>>>(
+        w.M, w.P, d, w.Rpart);
+    rt_combine_kernel<<<(unsigned)((d.cols * K + kThreads - 1) / kThreads), kThreads, 0, st>>>(w.Rpart, w.rt_chunks,
+                                                                                              d, w.R32);
+    residual_q4_kernel<K><<<dim3((unsigned)d.nbc, (unsigned)d.nbr), kThreads, 0, st>>>(
+        w.M, w.P32, w.R32, d, s->res_codes, s->res_rmax, s->res_cmax);
 }
 
 }  // namespace
@@ -420,16 +568,23 @@ extern "C" qm_status grasp_step(const qm_grasp_state *state, int64_t rows, int64
         case 8: launch_rank_kernels<8>(s, d, w, grad, grad_dtype, mu, st); break;
         default: launch_rank_kernels<16>(s, d, w, grad, grad_dtype, mu, st); break;
     }
-    mgs_kernel<<<1, kThreads, 0, st>>>(w.Y, d, w.P, w.P32);
-    switch (rank) {
-        case 1: launch_rt<1>(d, w, st); break;
-        case 2: launch_rt<2>(d, w, st); break;
-        case 4: launch_rt<4>(d, w, st); break;
-        case 8: launch_rt<8>(d, w, st); break;
-        default: launch_rt<16>(d, w, st); break;
+    if (rows <= 4 * kMgsThreads && rank <= 8) {
+        switch (rank) {
+            case 1: mgs_reg_kernel<1><<<1, kMgsThreads, 0, st>>>(w.Y, d, w.P, w.P32); break;
+            case 2: mgs_reg_kernel<2><<<1, kMgsThreads, 0, st>>>(w.Y, d, w.P, w.P32); break;
+            case 4: mgs_reg_kernel<4><<<1, kMgsThreads, 0, st>>>(w.Y, d, w.P, w.P32); break;
+            default: mgs_reg_kernel<8><<<1, kMgsThreads, 0, st>>>(w.Y, d, w.P, w.P32); break;
+        }
+    } else {
+        mgs_kernel<<<1, kMgsThreads, 0, st>>>(w.Y, d, w.Pc, w.P, w.P32);
     }
-    residual_q4_kernel<<<dim3((unsigned)d.nbc, (unsigned)d.nbr), kThreads, 0, st>>>(
-        w.M, w.P32, w.R32, d, s->res_codes, s->res_rmax, s->res_cmax);
+    switch (rank) {
+        case 1: launch_rt_residual<1>(s, d, w, st); break;
+        case 2: launch_rt_residual<2>(s, d, w, st); break;
+        case 4: launch_rt_residual<4>(s, d, w, st); break;
+        case 8: launch_rt_residual<8>(s, d, w, st); break;
+        default: launch_rt_residual<16>(s, d, w, st); break;
+    }
     factor_q8_kernel<<<(unsigned)d.nbr, kThreads, 0, st>>>(w.P32, rows, rank, s->p_codes, s->p_rmax, s->p_cmax);
     factor_q8_kernel<<<(unsigned)d.nbc, kThreads, 0, st>>>(w.R32, cols, rank, s->r_codes, s->r_rmax, s->r_cmax);
     qm_status stt = launched("grasp state kernels");

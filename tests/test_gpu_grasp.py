@@ -123,6 +123,26 @@ def test_grasp_ragged_shape_and_rank4():
         assert rel < 1e-4 and cos > 0.99999, (rel, cos)     # fp32 output, f32 NS
 
 
+@pytest.mark.parametrize("rows,cols,k", [(4160, 256, 8), (320, 192, 16)])
+def test_grasp_generic_mgs_path(rows, cols, k):
+    """More than 4096 rows, or rank 16: the MGS that keeps its columns in
+    global memory rather than in registers; state and NS as elsewhere."""
+    spike = H.spike(rows, cols, min(k, 8), DEV, 5003)
+    warm = H.gaussian((cols, k), DEV, 5003)
+    st = q.GraspState(rows, cols, k)
+    hw = host(warm)
+    for t in range(1, 4):
+        g = _grad(rows, cols, spike, 5003, t)
+        gh = g.float().cpu().numpy()
+        prev = to_oracle(st)
+        say("grasp generic-mgs step", rows, cols, k, t)
+        q.grasp_step(st, g, warm, ns_steps=5, coeffs=COEF, eps=H.NS_EPS)
+        torch.cuda.synchronize()
+        ref, M, P32, R32, O = OG.grasp_step(prev, gh, 0.95, hw, 5, COEF, H.NS_EPS)
+        compare_step(st, ref, M, P32, R32)
+        _within(as_f64(g), O, f"t{t} O")
+
+
 def test_grasp_4096_full_size():
     """4096x4096, rank-8 spike of norm 10x the noise, mu = 0.95, 20 steps:
     state checked on every step, NS on sampled rows at the last step."""
