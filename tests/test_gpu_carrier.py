@@ -396,3 +396,74 @@ def test_muon_step_carrier_mode_fp8_gram():
             _within(as_f64(trip[i][2]).reshape(r, c), O, f"t{t} O[{i}]")
             _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"t{t} dW[{i}]")
             W_host[i] = as_f64(mats[i][4])
+
+
+def test_muon_step_carrier_mode_strided_views():
+    """Carrier mode with grads as column slices of one fused buffer, P = 2
+    over 4 steps: the carrier is dense whatever the grad's pitch, O lands in
+    the views, the buffer's other columns stay untouched."""
+    rows, widths, pad = 512, [256, 512], 64
+    blocks = [(256, 256), (512, 256)]
+    buf = torch.zeros((rows, sum(widths) + pad), dtype=torch.bfloat16, device=DEV)
+    views = [buf[:, 0:256], buf[:, 256:768]]
+    buf[:, 768:] = 7.0
+    trip, mats, W_host, states = [], [], [], []
+    for i, (v, (br, bc)) in enumerate(zip(views, blocks)):
+        r, c = v.shape
+        codes, absmax = H.prior_state(r * c, DEV, 3301, i)
+        w = H.weights((r, c), DEV, 3301, i)
+        trip.append((codes, absmax, v))
+        mats.append((r, c, br, bc, w))
+        W_host.append(as_f64(w))
+        states.append((host(codes), host(absmax)))
+    full, block = _plans(trip, mats)
+    params = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, lr_block=0.01, rms_scale=0.2,
+                            ns_steps=5, period=2, carrier=True)
+    for t in range(1, 5):
+        for i, v in enumerate(views):
+            v.copy_(H.grad(tuple(v.shape), torch.bfloat16, DEV, 3301, i, t))
+        torch.cuda.synchronize()
+        gh = [host_grad(v) for v in views]
+        say("carrier strided step", t)
+        q.muon_step(full, block, mats, t, params)
+        torch.cuda.synchronize()
+        for i, v in enumerate(views):
+            r, c = v.shape
+            br, bc = blocks[i]
+            W2, c2, a2, O, _ = muonbp.muon_step(W_host[i], states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c,
+                                                br, bc, 2, 0.95, 1e-7, COEF, 5, 0.02, 0.01, 0.2, 0.0, carrier=True)
+            assert_bits_equal(host(trip[i][0]), c2, f"t{t} codes[{i}]")
+            assert_bits_equal(host(trip[i][1]), a2, f"t{t} absmax[{i}]")
+            states[i] = (c2, a2)
+            _within(as_f64(v), O, f"t{t} O[{i}]")
+            _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"t{t} dW[{i}]")
+            W_host[i] = as_f64(mats[i][4])
+        assert bool((buf[:, 768:] == 7.0).all())
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+def test_muon_step_carrier_mode_other_grad_dtypes(dtype):
+    """Carrier mode with fp32 and f16 grads: the update reads them, the carrier
+    is the same format, O is written back in the grad's dtype."""
+    shapes = [(256, 512), (512, 256)]
+    trip, mats, states = [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3401, i)
+        g = H.grad((r, c), dtype, DEV, 3401, i).reshape(-1)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, None))
+        states.append((host(codes), host(absmax)))
+    torch.cuda.synchronize()
+    gh = [host_grad(t[2]) for t in trip]
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], len(shapes))
+    params = q.make_hparams(coeffs=COEF, period=1, carrier=True)
+    say("carrier step, grads", dtype)
+    q.muon_step(plan, None, mats, 1, params)
+    torch.cuda.synchronize()
+    odt = TORCH_TO_ORACLE[dtype]
+    for i, (r, c) in enumerate(shapes):
+        _, c2, a2, O, _ = muonbp.muon_step(np.zeros((r, c), np.float32), states[i][0], states[i][1], gh[i], odt, 1,
+                                           r, c, r, c, 1, H.BETA, H.NS_EPS, COEF, 5, 0.0, 0.0, 0.2, carrier=True)
+        assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
+        _within(as_f64(trip[i][2]).reshape(r, c), O, f"O[{i}] ({dtype})")
