@@ -382,11 +382,16 @@ def main():
     if args.workload == "layerset28":
         bytes_ = numel * (BYTES_PER_ELEM_UPDATE + BYTES_PER_ELEM_SCALE)
         gbs = bytes_ / (upd_ms * 1e-3) / 1e9
+        kernels = {k: {"ms_per_launch": round(ms / n, 4), "launches": n,
+                       "gbs": round(numel * {"q8_update": BYTES_PER_ELEM_UPDATE, "q8_scale": BYTES_PER_ELEM_SCALE}
+                                    .get(k, 0.0) / (ms / n * 1e-3) / 1e9, 1)}
+                   for k, (ms, n) in per_class.items() if n}
         out.update({"value": round(gbs, 2), "unit": "GB/s", "dtype": "f32",
                     "config": {"workload": "layerset28_grouped_update_normalize", "tensors": len(tensors),
                                "groups": ng, "elements": numel, "grad_dtype": "bf16", "state": "int8"},
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}})
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                    "kernels": kernels})
     elif args.workload == "llama8b":
         bytes_ = numel * (BYTES_PER_ELEM_CARRIER if args.carrier else BYTES_PER_ELEM_UPDATE)
         gbs = bytes_ / (upd_ms * 1e-3) / 1e9
