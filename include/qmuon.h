@@ -216,9 +216,9 @@ QM_API qm_status qmuon_update_normalize_groups_ex(const void *host_plan,
  *   group_sumsq:       nullable [n_groups] fp64 out.
  *   ws: >= qm_update_workspace_bytes(host_plan) bytes, 256-byte aligned.
  * Every tensor's numel must be a multiple of 32 (else QM_E_SHAPE); the
- * carrier arrays must not overlap each other (QM_E_ARG) or the plan's
- * buffers.  Errors: QM_E_ARG, QM_E_ALIGN, QM_E_SHAPE, QM_E_PLAN,
- * QM_E_WORKSPACE, QM_E_HIP. */
+ * carrier arrays must not overlap each other or any tensor's codes, absmax
+ * or grad span (QM_E_ARG).  Errors: QM_E_ARG, QM_E_ALIGN, QM_E_SHAPE,
+ * QM_E_PLAN, QM_E_WORKSPACE, QM_E_HIP. */
 QM_API qm_status qmuon_update_mxfp8_carrier(const void *host_plan,
                                             const void *dev_plan, float beta,
                                             float eps, uint8_t *rowwise_data,

@@ -637,7 +637,20 @@ qm_status check_carrier(const PlanHeader *h, const void *host_plan, const void *
                         (long long)pt[i].numel);
     const uintptr_t d0 = reinterpret_cast<uintptr_t>(data), s0 = reinterpret_cast<uintptr_t>(scale);
     const uintptr_t dn = (uintptr_t)h->n_blocks * kBlock, sn = (uintptr_t)h->n_blocks * (kBlock / 32);
-    if (d0 < s0 + sn && s0 < d0 + dn) return fail(QM_E_ARG, "carrier data and scales overlap");
+    auto meets = [](uintptr_t a, uintptr_t an, uintptr_t b, uintptr_t bn) { return a < b + bn && b < a + an; };
+    if (meets(d0, dn, s0, sn)) return fail(QM_E_ARG, "carrier data and scales overlap");
+    // neither array may overlap a tensor's codes, absmax or grad span
+    for (int32_t i = 0; i < h->n_tensors; i++) {
+        const PlanTensor &T = pt[i];
+        const uintptr_t esz = T.dtype == QM_F32 ? 4 : 2;
+        const uintptr_t nblk = (uintptr_t)((T.numel + kBlock - 1) / kBlock);
+        const uintptr_t gspan = T.grad_cols ? (uintptr_t)((T.numel / T.grad_cols - 1) * T.grad_ld + T.grad_cols) * esz
+                                            : (uintptr_t)T.numel * esz;
+        const uintptr_t r[3][2] = {{T.codes, (uintptr_t)T.numel}, {T.absmax, nblk * 4}, {T.grad, gspan}};
+        for (const auto &b : r)
+            if (meets(d0, dn, b[0], b[1]) || meets(s0, sn, b[0], b[1]))
+                return fail(QM_E_ARG, "carrier arrays overlap tensor %d's state or grad", i);
+    }
     return QM_OK;
 }
 

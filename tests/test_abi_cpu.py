@@ -231,6 +231,8 @@ def test_carrier_update_validates_before_launch():
     assert _carrier_call(hp, need, inv=None) == 1
     assert _carrier_call(hp, need, eps=-1.0) == 1
     assert _carrier_call(hp, need, ws_bytes=need - 1) == 5
+    assert _carrier_call(hp, need, data=tens[1].grad) == 1                  # data over a grad
+    assert _carrier_call(hp, need, scale=tens[0].codes + 64) == 1           # scales inside codes
 
 
 def test_ns_mxfp8_validates_before_launch():
