@@ -107,6 +107,21 @@ def test_llama8b_shapes_full_size_sampled(name, shape):
     _check(as_f64(x)[rows], ref, "bf16")
 
 
+@pytest.mark.parametrize("shape", [(3000, 3300), (3300, 3000), (2048, 2048)])
+def test_f32_mid_and_small_tile_runs(shape):
+    """fp32 runs whose Gram leaves CUs idle at 256 x 256 tiles: 3000 x 3300
+    (padded to 3072 x 3328) takes the 128 x 128 tiles, 2048 x 2048 the
+    64 x 64 ones; sampled rows against the exact iterate."""
+    say("f32 NS", shape)
+    x = H.grad(shape, torch.float32, DEV, 2101, *shape)
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision="f32")
+    torch.cuda.synchronize()
+    rows = _sample_rows(shape[0], 32, 5)
+    ref = ns.spectral_rows(x0, rows, 5, COEF, H.NS_EPS)
+    _check(as_f64(x)[rows], ref, "f32")
+
+
 def test_blocked_muonbp_shape_sampled():
     """4096x14336 cut into 8 column blocks of 4096x1792, one batched NS."""
     x = H.grad((4096, 14336), torch.bfloat16, DEV, 1004)
