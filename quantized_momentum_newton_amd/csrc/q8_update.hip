@@ -392,11 +392,14 @@ __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_up
 }
 
 // ------------------------------------------------- K2: group sums, inverse norms
-// K2a: one workgroup per chunk (<= 256 runs of one group, each <= 16 blocks):
-// lane k sums run k of the chunk in block order, then a fixed butterfly and a
-// fixed-order combine of the four waves.  K2b: per group, the chunk partials
-// are added in chunk order.  Results depend only on the plan, never on
-// scheduling, and no atomics are used.
+// K2a: one workgroup per chunk (<= 256 runs of one group, each <= 16
+// blocks).  Sixteen lanes take one run, one block each, so a wave reads four
+// runs' block sums as four contiguous 128-byte pieces; a fixed butterfly
+// over the sixteen lanes gives the run's sum.  The 16 run slots of the
+// workgroup (4 waves x 4) each add their runs in pass order, and the slots
+// are added in slot order.  K2b: per group, the chunk partials are added in
+// chunk order.  Results depend only on the plan, never on scheduling, and no
+// atomics are used.
 
 __global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *__restrict__ run_offsets,
                                                                 const PlanRun *__restrict__ runs,
@@ -404,22 +407,31 @@ __global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *_
                                                                 const int32_t *__restrict__ chunk_group,
                                                                 const double *__restrict__ block_sums,
                                                                 double *__restrict__ partials) {
+    static_assert(kRunMax == 16 && kChunkRuns % 16 == 0, "sixteen lanes per run");
     const int64_t c = blockIdx.x;
     const int g = chunk_group[c];
-    const int64_t r = run_offsets[g] + (c - chunk_offsets[g]) * kChunkRuns + threadIdx.x;
+    const int64_t r0 = run_offsets[g] + (c - chunk_offsets[g]) * kChunkRuns;
+    const int64_t r_end = run_offsets[g + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int slot = wave * 4 + (lane >> 4), b = lane & 15;
     double acc = 0.0;
-    if (r < run_offsets[g + 1]) {
-        const PlanRun R = runs[r];
-        for (int k = 0; k < R.count; k++) acc += block_sums[R.start_block + k];
-    }
+    for (int pass = 0; pass < kChunkRuns / 16; pass++) {
+        const int64_t r = r0 + pass * 16 + slot;
+        double v = 0.0;
+        if (r < r_end) {
+            const PlanRun R = runs[r];
+            if (b < R.count) v = block_sums[R.start_block + b];
+        }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    __shared__ double part[kWavesPerWG];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        acc += v;
+    }
+    __shared__ double part[16];
+    if (b == 0) part[slot] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         double S = part[0];
-        for (int w = 1; w < kWavesPerWG; w++) S += part[w];
+        for (int k = 1; k < 16; k++) S += part[k];
         partials[c] = S;
     }
 }
