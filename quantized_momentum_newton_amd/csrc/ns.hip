@@ -269,8 +269,8 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
-template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int MINB, int EPI, bool SYM,
-          bool QT>
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
+          bool SYM, bool QT>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -292,6 +292,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     static_assert(!QT || (sizeof(T) == 2 && KK * QRB == BN * ROWB && KK % (QRPI * NW) == 0 && KK / QRPI / NW == QI),
                   "QT layout: bf16, same stage size and DMA count as the NT layout");
     static_assert(FM >= 1 && FN >= 1 && NSTAGE >= 2 && NSTAGE <= 5, "config");
+    // SLOTS > 0: the LDS holds SLOTS buffers of one operand's k-tile each
+    // (P of tile kt in slot 2 kt mod SLOTS, Q in 2 kt + 1), instead of
+    // NSTAGE stages of both operands; see the pipeline below.
+    constexpr bool RING = SLOTS > 0;
+    constexpr int HS = BM * ROWB;                   // one operand's k-tile
+    static_assert(!RING || (SLOTS == 5 && BM == BN), "ring: five slots of equal operand tiles");
+    constexpr size_t LDS_BYTES = RING ? (size_t)SLOTS * HS : (size_t)NSTAGE * STAGE;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
@@ -313,21 +320,36 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     const int64_t ldpb = I.ldp * (int64_t)sizeof(T), ldqb = I.ldq * (int64_t)sizeof(T);
     const int lrw = lane / CPR, lch = lane % CPR;
 
-    // One DMA instruction of the Q operand's k-tile kt (i < QI) into the
-    // stage at base.  QT: QRPI rows of QRB bytes; the 16-byte chunk c of LDS
+    // One DMA instruction of the Q operand's k-tile kt (i < QI) into the Q
+    // buffer qb.  QT: QRPI rows of QRB bytes; the 16-byte chunk c of LDS
     // row k sits at position c ^ 4 (k % 4), so the transposing fragment
     // reads (4 rows x 64 bytes per half-wave) cover all 64 banks.
-    auto dma_q = [&](int kt, char *base, int i) {
+    auto dma_q = [&](int kt, char *qb, int i) {
         if constexpr (QT) {
             const int r0 = (wave + i * NW) * QRPI;
             const int row = r0 + lane / QCPR, pos = lane % QCPR;
-            lds_dma16(Qg + ((int64_t)kt * KK + row) * ldqb + ((pos ^ (4 * (row & 3))) << 4), base + BM * ROWB + r0 * QRB);
+            lds_dma16(Qg + ((int64_t)kt * KK + row) * ldqb + ((pos ^ (4 * (row & 3))) << 4), qb + r0 * QRB);
         } else {
             const int r0 = (wave + i * NW) * RPI;
             const int row = r0 + lrw;
-            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
-                      base + (BM + r0) * ROWB);
+            lds_dma16(Qg + row * ldqb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4), qb + r0 * ROWB);
         }
+    };
+    // One DMA instruction of the P operand's k-tile kt (i < PI) into pb.
+    auto dma_p = [&](int kt, char *pb, int i) {
+        const int r0 = (wave + i * NW) * RPI;
+        const int row = r0 + lrw;
+        lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4), pb + r0 * ROWB);
+    };
+    // operand buffers of k-tile kt
+    // (slot offsets are wave-uniform: kept in scalar registers)
+    auto pbuf = [&](int kt) -> char * {
+        if constexpr (RING) return smem + __builtin_amdgcn_readfirstlane((2 * kt) % SLOTS * HS);
+        else return smem + (kt % NSTAGE) * STAGE;
+    };
+    auto qbuf = [&](int kt) -> char * {
+        if constexpr (RING) return smem + __builtin_amdgcn_readfirstlane((2 * kt + 1) % SLOTS * HS);
+        else return smem + (kt % NSTAGE) * STAGE + BM * ROWB;
     };
 
     // Direct loads: one instruction moves RPI tile rows (1 KiB) into LDS;
@@ -336,16 +358,13 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     // sw(row) = (row / SWD) % CPR gives 16 consecutive rows' copies of one
     // logical chunk 16 distinct 16-byte slots of a 256-byte bank row: the 16
     // lanes a fragment read serves together never collide (64 banks).
-    auto issue = [&](int kt, int stage) {
-        char *base = smem + stage * STAGE;
+    auto issue_p = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < PI; i++) {
-            const int r0 = (wave + i * NW) * RPI;
-            const int row = r0 + lrw;
-            lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4), base + r0 * ROWB);
-        }
+        for (int i = 0; i < PI; i++) dma_p(kt, pbuf(kt), i);
+    };
+    auto issue_q = [&](int kt) {
 #pragma unroll
-        for (int i = 0; i < QI; i++) dma_q(kt, base, i);
+        for (int i = 0; i < QI; i++) dma_q(kt, qbuf(kt), i);
     };
 
     f32x16 acc[FM][FN];
@@ -387,8 +406,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         const u32x2 lo = read_qt4(cq, k0, nb), hi = read_qt4(cq, k0 + 4, nb);
         return u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    auto read_frags = [&](const char *cp, int s, u32x4 *a, u32x4 *b) {
-        const char *cq = cp + BM * ROWB;
+    auto read_frags = [&](const char *cp, const char *cq, int s, u32x4 *a, u32x4 *b) {
         const int ch = 2 * s + lhalf;
 #pragma unroll
         for (int i = 0; i < FM; i++) {
@@ -405,66 +423,73 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
             }
         }
     };
-    // Software pipeline.  NSTAGE LDS stages: tiles kt+1 .. kt+NSTAGE-1 are in
-    // flight while tile kt is multiplied, and each iteration waits only for
-    // tile kt+1.  The next tile's DMA is spread over the k-steps (one slice
-    // per step), and fragments for k-step s+1 are read into a second
+    // Software pipeline.  Fragments for k-step s+1 are read into a second
     // register set while the MFMAs of step s run; the next tile's first
     // fragments are read right after the barrier, while the last MFMAs of
-    // this tile drain.
+    // this tile drain.  The DMA issued during a tile is spread over its
+    // k-steps (one slice per step).
+    //  * NSTAGE stages: tiles kt+1 .. kt+NSTAGE-1 are in flight while tile kt
+    //    is multiplied, and each iteration waits only for tile kt+1.
+    //  * ring (five one-operand slots): while tile kt is multiplied, P of
+    //    tile kt+1 is already in flight (issued during tile kt-1), and Q of
+    //    kt+1 and P of kt+2 are issued into the two slots tile kt-1 freed;
+    //    the iteration waits for everything but P of kt+2.  P loads thus get
+    //    two tiles of lead and Q loads one, where two full stages give each
+    //    load between a quarter and all of one tile.
     u32x4 fa[2][FM], fb[2][FN];
     constexpr int DPS = (DPT + STEPS - 1) / STEPS;  // DMA instructions per k-step
-    auto issue_part = [&](int kt, int stage, int part) {
-        char *base = smem + stage * STAGE;
+    auto issue_part = [&](int kt, int part) {
 #pragma unroll
         for (int d = part * DPS; d < (part + 1) * DPS && d < DPT; d++) {
-            if (d < PI) {
-                const int r0 = (wave + d * NW) * RPI;
-                const int row = r0 + lrw;
-                lds_dma16(Pg + row * ldpb + (int64_t)kt * ROWB + ((lch ^ ((row / SWD) % CPR)) << 4),
-                          base + r0 * ROWB);
+            if constexpr (RING) {
+                if (d < QI) {
+                    if (kt + 1 < KT) dma_q(kt + 1, qbuf(kt + 1), d);
+                } else {
+                    if (kt + 2 < KT) dma_p(kt + 2, pbuf(kt + 2), d - QI);
+                }
             } else {
-                dma_q(kt, base, d - PI);
+                const int nk = kt + NSTAGE - 1;
+                if (nk < KT) {
+                    if (d < PI) dma_p(nk, pbuf(nk), d);
+                    else dma_q(nk, qbuf(nk), d - PI);
+                }
             }
         }
     };
+    if constexpr (RING) {
+        issue_p(0);
+        issue_q(0);
+        if (KT > 1) issue_p(1);
+        wait_vmcnt_tiles<PI>(KT > 1 ? 1 : 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < NSTAGE - 1; k++)
-        if (k < KT) issue(k, k);
-    wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
+        for (int k = 0; k < NSTAGE - 1; k++)
+            if (k < KT) {
+                issue_p(k);
+                issue_q(k);
+            }
+        wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
+    }
     kloop_barrier();
-    read_frags(smem, 0, fa[0], fb[0]);
-    // D gathered from the Q operand.  For X = aX + BX (Q = X^T) and for
-    // B = bA + cA^2 (Q = A, symmetric), D's tile (bi, bj) equals the Q panel
-    // bj at k in [bi BM, bi BM + BM): element (row R, column C) of the tile
-    // is Q row bj BN + C at k = bi BM + R.  While such a k-tile is in LDS,
-    // the waves owning rows R add dgain * D to their accumulators: four
-    // consecutive rows of one column are four consecutive k, one 8-byte
-    // (bf16) or 16-byte (fp32) LDS read.  No D is read from memory.
+    read_frags(pbuf(0), qbuf(0), 0, fa[0], fb[0]);
+    // The D term in the k-loop.  For X = aX + BX (Q = X, or X^T in fp32
+    // runs) and for B = bA + cA^2 (Q = A, symmetric), D's tile (bi, bj)
+    // equals the Q panel bj at k in [bi BM, bi BM + BM): element (row R,
+    // column C) of the tile is Q at (n = bj BN + C, k = bi BM + R).  While
+    // such a k-tile is in LDS, the waves owning rows R add dgain * D to their
+    // accumulators, so the epilogue reads no D from memory.  fp32 runs gather
+    // it with VALU adds (four consecutive rows of one column are four
+    // consecutive k: one 16-byte LDS read); bf16 runs add it with MFMAs
+    // (below).
     static_assert(32 % KK == 0 || KK % 32 == 0, "k-tile vs sub-tile rows");
     const bool dloop = EPI != EPI_GRAM && args.dloop;
-    auto gather_d = [&](const char *cp, int kt) {
-        const char *cq = cp + BM * ROWB;
+    auto gather_d = [&](const char *cq, int kt) {
+        if constexpr (sizeof(T) == 4 && !QT)
 #pragma unroll
         for (int i = 0; i < FM; i++) {
             const int64_t rb = (int64_t)bi * BM + wm * WM + i * 32;  // first k of sub-tile i
             if (rb / KK != kt) continue;
             const int kk0 = (int)(rb % KK) + 4 * lhalf;
-            if constexpr (QT) {
-                // rows kk0 + 8 g .. +3 of column lrow: one transposing read
-#pragma unroll
-                for (int j = 0; j < FN; j++)
-#pragma unroll
-                    for (int g = 0; g < 4; g++) {
-                        u32x2 w = read_qt4(cq, (int)(rb % KK) + 8 * g + 4 * lhalf, wn * WN + j * 32);
-                        lds_wait(w);
-                        const float d[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-#pragma unroll
-                        for (int q = 0; q < 4; q++) acc[i][j][4 * g + q] += args.dgain * d[q];
-                    }
-                continue;
-            }
 #pragma unroll
             for (int j = 0; j < FN; j++) {
                 const int row = wn * WN + j * 32 + lrow;
@@ -473,29 +498,39 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 #pragma unroll
                 for (int g = 0; g < 4; g++) {
                     const int ob = (kk0 + 8 * g) * (int)sizeof(T);
-                    const char *src = qr + (((ob >> 4) ^ sw) << 4) + (ob & 15);
                     float d[4];
-                    if constexpr (sizeof(T) == 2) {
-                        const uint2 w = *reinterpret_cast<const uint2 *>(src);
-                        d[0] = __uint_as_float(w.x << 16);
-                        d[1] = __uint_as_float(w.x & 0xffff0000u);
-                        d[2] = __uint_as_float(w.y << 16);
-                        d[3] = __uint_as_float(w.y & 0xffff0000u);
-                    } else {
-                        *reinterpret_cast<float4 *>(d) = *reinterpret_cast<const float4 *>(src);
-                    }
+                    *reinterpret_cast<float4 *>(d) =
+                        *reinterpret_cast<const float4 *>(qr + (((ob >> 4) ^ sw) << 4) + (ob & 15));
 #pragma unroll
                     for (int q = 0; q < 4; q++) acc[i][j][4 * g + q] += args.dgain * d[q];
                 }
             }
         }
     };
+    // bf16: the D term as MFMAs.  D's tile row R is the Q operand at
+    // k = bi BM + R (above), so dgain D = (dgain I) Q over those k: in the
+    // k-step whose 16 k are rows 16 h .. 16 h + 15 of sub-tile i, an A
+    // fragment holding dgain at (row 16 h + e, k e) times the step's B
+    // fragments adds the term to acc[i][.].  dgain is split into bf16
+    // hi = bf16(dgain) and lo = bf16(dgain - hi): two MFMAs whose products are
+    // exact in fp32, |dgain - hi - lo| <= 2^-17 |dgain|.
+    constexpr bool DMF = sizeof(T) == 2;
+    static_assert(!DMF || (WM % KK == 0 && KK % 32 == 0), "D by MFMA: wave rows span whole k-tiles");
+    const uint16_t dhi = to_bf16_bits(args.dgain);
+    const uint16_t dlo = to_bf16_bits(args.dgain - __uint_as_float((uint32_t)dhi << 16));
+    // A-fragment lane l holds row l % 32 at k 8 (l / 32) .. +7
+    auto eye_frag = [&](int h, uint16_t v) -> u32x4 {
+        const int e = lrow - 16 * h - 8 * lhalf;
+        const uint32_t w = (e >= 0 && e < 8) ? ((uint32_t)v << (16 * (e & 1))) : 0u;
+        const int q = e >> 1;
+        return u32x4{q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
+    };
+    const int dkt0 = (int)(((int64_t)bi * BM + wm * WM) / KK);   // first k-tile of this wave's D rows
     for (int kt = 0; kt < KT; kt++) {
-        const char *cp = smem + (kt % NSTAGE) * STAGE;
-        if (dloop) gather_d(cp, kt);
-        const int nk = kt + NSTAGE - 1;
-        const bool more = nk < KT;
-        const int nstage = nk % NSTAGE;
+        const char *cp = pbuf(kt), *cq = qbuf(kt);
+        if constexpr (!DMF) {
+            if (dloop) gather_d(cq, kt);
+        }
 #pragma unroll
         for (int s = 0; s < STEPS; s++) {
             // QT: fragments of this step came from assembly reads issued a
@@ -505,8 +540,8 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 #pragma unroll
                 for (int j = 0; j < FN; j++) lds_wait(fb[s & 1][j]);
             }
-            if (s + 1 < STEPS) read_frags(cp, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-            if (more) issue_part(nk, nstage, s);
+            if (s + 1 < STEPS) read_frags(cp, cq, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            issue_part(kt, s);
             // raised wave priority while the step's MFMAs issue: with two
             // waves per SIMD, the one holding ready MFMAs goes first (about
             // 1 % on the NS products)
@@ -515,12 +550,31 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++) Mfma<T>::step(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+            if constexpr (DMF) {
+                if (dloop) {
+                    const int t = kt - dkt0;
+#pragma unroll
+                    for (int tt = 0; tt < WM / KK; tt++)
+                        if (t == tt) {
+                            const int i = tt * (KK / 32) + s / 2, h = s % 2;
+                            const u32x4 eh = eye_frag(h, dhi), el = eye_frag(h, dlo);
+#pragma unroll
+                            for (int j = 0; j < FN; j++) {
+                                Mfma<T>::step(eh, fb[s & 1][j], acc[i][j]);
+                                Mfma<T>::step(el, fb[s & 1][j], acc[i][j]);
+                            }
+                        }
+                }
+            }
             __builtin_amdgcn_s_setprio(0);
         }
-        // tiles still allowed in flight: those issued after kt+1
-        wait_vmcnt_tiles<DPT>(min(KT - 1, kt + NSTAGE - 1) - (kt + 1));
+        // loads still allowed in flight: those of later tiles than kt+1
+        if constexpr (RING)
+            wait_vmcnt_tiles<PI>(kt + 2 < KT ? 1 : 0);
+        else
+            wait_vmcnt_tiles<DPT>(min(KT - 1, kt + NSTAGE - 1) - (kt + 1));
         kloop_barrier();
-        if (kt + 1 < KT) read_frags(smem + ((kt + 1) % NSTAGE) * STAGE, 0, fa[STEPS & 1], fb[STEPS & 1]);
+        if (kt + 1 < KT) read_frags(pbuf(kt + 1), qbuf(kt + 1), 0, fa[STEPS & 1], fb[STEPS & 1]);
     }
 
     // ---------------------------------------------------------- epilogue
@@ -544,7 +598,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     constexpr int RIT = ER * (BN / 8) / NTH;   // row-phase items per thread
     constexpr int CIT = BN * (ER / 8) / NTH;   // column-phase items per thread
     static_assert(WM % ER == 0 && ER % 32 == 0 && BM % ER == 0, "epilogue pass rows");
-    static_assert((size_t)ER * EP * 4 <= (size_t)NSTAGE * STAGE, "epilogue tile must fit the stage buffers");
+    static_assert((size_t)ER * EP * 4 <= LDS_BYTES, "epilogue tile must fit the stage buffers");
     static_assert(RIT * NTH == ER * (BN / 8) && CIT * NTH == BN * (ER / 8), "epilogue work split");
     float *et = reinterpret_cast<float *>(smem);
     T *tgt = nullptr;                // transposed target
@@ -1190,20 +1244,20 @@ size_t ns_ws_bytes_uniform(int64_t rows, int64_t cols, int64_t items, int precis
 // Tile configurations: <BM, BN, waves_m, waves_n, row bytes per k-tile,
 // LDS stages, workgroups per CU>.  The symmetric products need square tiles.
 struct CfgSym {
-    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, SLOTS = 5, MINB = 1;
 };
 struct CfgRect {
-    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, MINB = 1;
+    static constexpr int BM = 256, BN = 256, WM = 2, WN = 4, ROWB = 128, NST = 2, SLOTS = 5, MINB = 1;
 };
 // fp32 runs on matrices too small to give every CU a 256 x 256 tile: the
 // fp32 MFMA needs 16x fewer operand bytes per second than bf16, so smaller
 // tiles cost little and keep all CUs busy (128 x 128: 4 waves of 64 x 64,
 // two workgroups per CU; 64 x 64: 4 waves of 32 x 32, four per CU).
 struct CfgF32Mid {
-    static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, ROWB = 128, NST = 2, MINB = 2;
+    static constexpr int BM = 128, BN = 128, WM = 2, WN = 2, ROWB = 128, NST = 2, SLOTS = 0, MINB = 2;
 };
 struct CfgF32Small {
-    static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, ROWB = 128, NST = 2, MINB = 4;
+    static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, ROWB = 128, NST = 2, SLOTS = 0, MINB = 4;
 };
 
 // Compute units of the current device (cached per device).
@@ -1222,8 +1276,8 @@ int64_t cu_count() {
 template <typename T, typename C, int EPI, bool SYM, bool QT = false>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
-    constexpr size_t lds = (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
-    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::MINB, EPI, SYM, QT>;
+    constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
+    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
