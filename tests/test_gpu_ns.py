@@ -136,6 +136,33 @@ def test_blocked_muonbp_shape_sampled():
         _check(out[rows, 1792 * j:1792 * (j + 1)], ref, "bf16")
 
 
+@pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32)])
+def test_degenerate_inputs(precision, dtype):
+    """Degenerate inputs the iteration keeps exact in any arithmetic:
+      * a zero matrix stays exactly zero (eps keeps the inverse norm finite,
+        0 * 1/eps = 0, and every product of zeros is zero);
+      * zero rows of the input are exactly zero rows of every iterate, and
+        the other rows match the oracle.
+    Other rank-deficient inputs (duplicate rows, low rank) are not parity
+    cases: rounding gives their zero singular values tiny nonzero parts,
+    which the iteration multiplies by about a = 3.44 per step towards one,
+    as it does any small singular value."""
+    say("ns degenerate", precision)
+    z = torch.zeros((300, 200), dtype=dtype, device=DEV)
+    q.ns_orthogonalize(z, 5, COEF, H.NS_EPS, precision=precision)
+    torch.cuda.synchronize()
+    assert torch.all(z == 0) and not torch.any(torch.isnan(z))
+
+    x = H.grad((256, 384), dtype, DEV, 2203)
+    x[::3] = 0
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
+    torch.cuda.synchronize()
+    out = as_f64(x)
+    assert np.all(out[::3] == 0)
+    _check(out, ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS), precision)
+
+
 def test_validation_errors():
     x = torch.zeros((16, 16), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(q.QmuonError):
