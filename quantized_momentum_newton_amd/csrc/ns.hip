@@ -1273,18 +1273,29 @@ int64_t cu_count() {
     return cached[dev];
 }
 
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (done[] indexed by device; devices beyond the table are set on
+// every call).
+constexpr int kMaxDevices = 64;
+qm_status reserve_lds(const void *kern, size_t bytes, bool *done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(QM_E_HIP, "no current device");
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    if (cached && done[dev]) return QM_OK;
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+        return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", bytes);
+    if (cached) done[dev] = true;
+    return QM_OK;
+}
+
 template <typename T, typename C, int EPI, bool SYM, bool QT = false>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
     constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
     auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
-            return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", lds);
-        attr_set = true;
-    }
+    static bool attr_set[kMaxDevices] = {};
+    const qm_status st = reserve_lds(reinterpret_cast<const void *>(kern), lds, attr_set);
+    if (st != QM_OK) return st;
     Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, stream, args);
     const hipError_t e = hipGetLastError();
@@ -1293,13 +1304,9 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
 }
 
 qm_status launch_gram_mx(const MxGramArgs &args, int grid, hipStream_t stream) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gram_mx_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxGramLds) != hipSuccess)
-            return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", kMxGramLds);
-        attr_set = true;
-    }
+    static bool attr_set[kMaxDevices] = {};
+    const qm_status st = reserve_lds(reinterpret_cast<const void *>(gram_mx_kernel), kMxGramLds, attr_set);
+    if (st != QM_OK) return st;
     Timed tm(stream, QM_K_NS_GRAM);
     hipLaunchKernelGGL(gram_mx_kernel, dim3(grid), dim3(512), kMxGramLds, stream, args);
     const hipError_t e = hipGetLastError();
