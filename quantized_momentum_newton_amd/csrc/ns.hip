@@ -1452,6 +1452,34 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
     return QM_OK;
 }
 
+// fp32 runs: the tile size of the symmetric products (sym) or of X = aX + BX
+// from a model of the launch time: the tiles the busiest CU runs,
+// ceil(tiles / CUs), x tile area / the tile's relative throughput (measured
+// on the 4096-square NS: 256 x 256 0.76, 128 x 128 1, 64 x 64 0.94).  The
+// fp32 MFMA needs 16x fewer operand bytes per second than bf16, so small
+// tiles lose little, and a launch whose tiles do not fill the CUs evenly
+// loses most of a round.  0: 256 x 256, 1: 128 x 128, 2: 64 x 64.
+int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym) {
+    static constexpr int kS[3] = {256, 128, 64};
+    static constexpr double kEff[3] = {0.76, 1.0, 0.94};
+    const int64_t n_cu = cu_count();
+    int best = 0;
+    double best_t = 0;
+    for (int k = 0; k < 3; k++) {
+        int64_t tiles = 0;
+        for (const ItemBufs &b : bufs) {
+            const int64_t tm = b.g.mp / kS[k], tn = b.g.np / kS[k];
+            tiles += sym ? tm * (tm + 1) / 2 : tm * tn;
+        }
+        const double t = (double)((tiles + n_cu - 1) / n_cu) * kS[k] * kS[k] / kEff[k];
+        if (k == 0 || t < best_t) {
+            best = k;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 template <typename T>
 qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int steps, float a,
                     float b, float c, float eps, void *ws, hipStream_t stream) {
@@ -1543,20 +1571,14 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
     qm_status st;
     if constexpr (sizeof(T) == 4) {
-        // the largest tile whose Gram launch still gives every CU a tile
-        int64_t big = 0, mid = 0;
-        for (int i = 0; i < nit; i++) {
-            const int64_t t256 = bufs[i].g.mp / 256, t128 = bufs[i].g.mp / 128;
-            big += t256 * (t256 + 1) / 2;
-            mid += t128 * (t128 + 1) / 2;
-        }
-        const int64_t n_cu = cu_count();
-        if (big >= n_cu)
-            st = run_products<T, CfgSym, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
-        else if (mid >= n_cu)
-            st = run_products<T, CfgF32Mid, CfgF32Mid>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
-        else
-            st = run_products<T, CfgF32Small, CfgF32Small>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+        const int ts = pick_f32_tile(bufs, true), tr = pick_f32_tile(bufs, false);
+        auto run = [&](auto cs) -> qm_status {
+            using CS = decltype(cs);
+            if (tr == 0) return run_products<T, CS, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            if (tr == 1) return run_products<T, CS, CfgF32Mid>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            return run_products<T, CS, CfgF32Small>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+        };
+        st = ts == 0 ? run(CfgSym{}) : ts == 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
     } else {
         st = run_products<T, CfgSym, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
     }
