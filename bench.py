@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--carrier", action="store_true",
                     help="hand m to Newton-Schulz as the MXFP8 carrier (muon_step with hparams.carrier = 1) "
                          "instead of bf16 in the grads (llama8b and muonbp workloads)")
+    ap.add_argument("--ns-precision", default="f32", choices=["f32", "bf16x3"],
+                    help="fp32-operand NS arithmetic of the grasp and fp32_256x512 workloads: fp32 MFMAs, or "
+                         "bf16 MFMAs on a hi + lo split of each operand")
     ap.add_argument("--ref-copy-mib", type=int, default=0,
                     help="after the timed region, copy a buffer of this many MiB once (a kernel of "
                          "known traffic, to calibrate HBM byte counters in a profiler run)")
@@ -171,7 +174,8 @@ def percentiles(ms):
 
 def bench_grasp(args, q, H, torch):
     """GRASP 4096x4096 (rank 8): one grasp_step per step on a fresh bf16 grad
-    (noise + a fixed rank-8 spike); the state path and the f32 NS (T = 5)."""
+    (noise + a fixed rank-8 spike); the state path and the fp32-operand NS
+    (T = 5) in the arithmetic --ns-precision names."""
     cfg = H.grasp_4096_shape()
     rows, cols, k = cfg["rows"], cfg["cols"], cfg["rank"]
     dev = "cuda"
@@ -189,7 +193,8 @@ def bench_grasp(args, q, H, torch):
             torch.cuda.synchronize()
             q.timing_enable(True)
         e[0].record()
-        q.grasp_step(st, g, warm, mu=cfg["mu"], ns_steps=H.NS_STEPS, coeffs=H.NS_COEFFS, eps=H.NS_EPS, ws=ws)
+        q.grasp_step(st, g, warm, mu=cfg["mu"], ns_steps=H.NS_STEPS, coeffs=H.NS_COEFFS, eps=H.NS_EPS, ws=ws,
+                     ns_precision=args.ns_precision)
         e[1].record()
         if t >= args.warmup:
             evs.append(e)
@@ -203,13 +208,17 @@ def bench_grasp(args, q, H, torch):
     numel = rows * cols
     state_bytes = numel * 15.25             # three passes over the fp32 momentum plus the codes
     ns_fl = ns_sym_flops(rows, cols, H.NS_STEPS)
+    # the arithmetic's own ceiling: the fp32 MFMA peak, or a third of the
+    # bf16 MFMA peak for bf16x3 (three bf16 products per fp32 product)
+    peak = F32_PEAK_TFLOPS if args.ns_precision == "f32" else BF16_PEAK_TFLOPS / 3
     return {"metric": METRIC, "value": round(1000.0 / step_ms, 3), "unit": "steps/s", "dtype": "f32",
             "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
-            "config": {"workload": "grasp_4096x4096_rank8", "ns_steps": H.NS_STEPS, "ns_precision": "f32",
+            "config": {"workload": "grasp_4096x4096_rank8", "ns_steps": H.NS_STEPS, "ns_precision": args.ns_precision,
                        "state_ms": round(state_ms, 4), "ns_ms": round(ns_ms, 4),
                        "state_gbs": round(state_bytes / (state_ms * 1e-3) / 1e9, 1),
                        "ns_tflops": round(ns_fl / (ns_ms * 1e-3) / 1e12, 2),
-                       "ns_frac_of_fp32_peak": round(ns_fl / (ns_ms * 1e-3) / 1e12 / F32_PEAK_TFLOPS, 4)}}
+                       "ns_peak_tflops": round(peak, 1),
+                       "ns_frac_of_peak": round(ns_fl / (ns_ms * 1e-3) / 1e12 / peak, 4)}}
 
 
 def bench_small(args, q, H, torch):
@@ -225,7 +234,7 @@ def bench_small(args, q, H, torch):
     plan = q.Plan([(codes, absmax, g)], [(0, 0, r * c, 0)], 1)
     mats = [(r, c, r, c, w)]
     hp = q.make_hparams(beta=H.BETA, eps=H.NS_EPS, coeffs=H.NS_COEFFS, ns_steps=H.NS_STEPS, period=1,
-                        precision="f32")
+                        precision=args.ns_precision)
     ws = torch.empty(q.muon_step_workspace_bytes(plan, None, mats, hparams=hp), dtype=torch.uint8, device=dev)
     evs = []
     for t in range(args.warmup + args.steps):
@@ -241,7 +250,8 @@ def bench_small(args, q, H, torch):
     step_ms = sum(ms) / len(ms)
     return {"metric": METRIC, "value": round(step_ms * 1e3, 2), "unit": "us/step", "dtype": "f32",
             "higher_is_better": False, "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
-            "config": {"workload": "fp32_256x512_muon_step", "ns_steps": H.NS_STEPS, "ns_precision": "f32"}}
+            "config": {"workload": "fp32_256x512_muon_step", "ns_steps": H.NS_STEPS,
+                       "ns_precision": args.ns_precision}}
 
 
 def main():

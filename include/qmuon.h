@@ -27,7 +27,7 @@
 extern "C" {
 #endif
 
-#define QM_ABI_VERSION 3
+#define QM_ABI_VERSION 4
 #define QM_BLOCK 256           /* quantisation block: elements per absmax */
 
 typedef void *qm_stream_t;     /* hipStream_t */
@@ -51,8 +51,12 @@ typedef enum {
 typedef enum { QM_F32 = 0, QM_BF16 = 1, QM_F16 = 2 } qm_dtype;
 
 /* Newton-Schulz arithmetic: bf16 operands with fp32 accumulation (X, A, B
- * all held in bf16), or fp32 operands with fp32 accumulation. */
-typedef enum { QM_NS_BF16 = 0, QM_NS_F32 = 1 } qm_ns_precision;
+ * all held in bf16); fp32 operands with fp32 accumulation on fp32 MFMAs; or
+ * fp32 operands held in fp32, each product formed on bf16 MFMAs from a
+ * hi + lo split of both factors (hi = bf16(x), lo = bf16(x - hi); terms
+ * hi hi' + hi lo' + lo hi', fp32 accumulation; the dropped lo lo' is below
+ * 2^-16 of each product), "bf16x3". */
+typedef enum { QM_NS_BF16 = 0, QM_NS_F32 = 1, QM_NS_BF16X3 = 2 } qm_ns_precision;
 
 /* ------------------------------------------------------------------------
  * q8 momentum state and norm plans
@@ -399,8 +403,9 @@ QM_API size_t grasp_workspace_bytes(int64_t rows, int64_t cols, int32_t rank);
  *   Q = R_{t-1} with unit columns (a zero column is replaced by the same
  *   column of `warm`, cols x k fp32, normalised);  P = MGS(M_t Q) (modified
  *   Gram-Schmidt, positive diagonal);  R = M_t^T P;  residual M_t - P R^T;
- *   requantise residual, P, R;  O = NS_T(M_t) in f32 arithmetic, written
- *   over grad in its dtype;  W <- W - lr (O + weight_decay W) if weight.
+ *   requantise residual, P, R;  O = NS_T(M_t) on fp32 operands (ns_precision
+ *   QM_NS_F32 or QM_NS_BF16X3), written over grad in its dtype;
+ *   W <- W - lr (O + weight_decay W) if weight.
  * Reductions accumulate in fp64 in a fixed order; P, R are rounded to fp32
  * before the residual.  rank in {1, 2, 4, 8, 16}; grid must be 64.
  *   grad: in g, out O (rows x cols contiguous, dtype grad_dtype).
@@ -411,9 +416,9 @@ QM_API qm_status grasp_step(const qm_grasp_state *state, int64_t rows,
                             int64_t cols, int32_t rank, int32_t grid,
                             void *grad, int32_t grad_dtype, const float *warm,
                             float mu, int32_t ns_steps, float a, float b,
-                            float c, float eps, float *weight, float lr,
-                            float weight_decay, void *ws, size_t ws_bytes,
-                            qm_stream_t stream);
+                            float c, float eps, int32_t ns_precision,
+                            float *weight, float lr, float weight_decay,
+                            void *ws, size_t ws_bytes, qm_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Launch timing (measurement aid, off by default).

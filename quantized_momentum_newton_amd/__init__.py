@@ -29,7 +29,7 @@ _LIB = L.load()
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
 BLOCK = 256      # elements per absmax block
-PRECISION = {"bf16": L.QM_NS_BF16, "f32": L.QM_NS_F32}
+PRECISION = {"bf16": L.QM_NS_BF16, "f32": L.QM_NS_F32, "bf16x3": L.QM_NS_BF16X3}
 _DTYPES = {torch.float32: L.QM_F32, torch.bfloat16: L.QM_BF16, torch.float16: L.QM_F16}
 
 
@@ -372,9 +372,10 @@ def grasp_workspace_bytes(rows, cols, rank):
 
 
 def grasp_step(state, grad, warm, mu=0.95, ns_steps=5, coeffs=QUINTIC, eps=1e-7, weight=None,
-               lr=0.02, weight_decay=0.0, ws=None, stream=None):
+               lr=0.02, weight_decay=0.0, ws=None, stream=None, ns_precision="f32"):
     """One GRASP step: state updated in place, grad (in: g) overwritten with
-    O = NS(M_t), weight (optional) updated."""
+    O = NS(M_t), weight (optional) updated.  ns_precision: "f32" (fp32
+    MFMAs) or "bf16x3" (fp32 operands, products from a bf16 hi + lo split)."""
     rows, cols = grad.shape
     if ws is None:
         ws = torch.empty(_LIB.grasp_workspace_bytes(rows, cols, state.rank), dtype=torch.uint8,
@@ -382,5 +383,6 @@ def grasp_step(state, grad, warm, mu=0.95, ns_steps=5, coeffs=QUINTIC, eps=1e-7,
     a, b, c = coeffs
     st = state.c_struct()
     _check(_LIB.grasp_step(ctypes.byref(st), rows, cols, state.rank, GRASP_GRID, _ptr(grad),
-                           _dtype(grad), _ptr(warm), mu, ns_steps, a, b, c, eps, _ptr(weight), lr,
+                           _dtype(grad), _ptr(warm), mu, ns_steps, a, b, c, eps, PRECISION[ns_precision],
+                           _ptr(weight), lr,
                            weight_decay, _ptr(ws), ws.numel(), _stream(stream)))

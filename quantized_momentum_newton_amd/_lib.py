@@ -14,7 +14,7 @@ STATUS_NAMES = {0: "QM_OK", 1: "QM_E_ARG", 2: "QM_E_ALIGN", 3: "QM_E_DTYPE",
                 4: "QM_E_SHAPE", 5: "QM_E_WORKSPACE", 6: "QM_E_HIP",
                 7: "QM_E_UNSUPPORTED", 8: "QM_E_PLAN"}
 QM_F32, QM_BF16, QM_F16 = 0, 1, 2
-QM_NS_BF16, QM_NS_F32 = 0, 1
+QM_NS_BF16, QM_NS_F32, QM_NS_BF16X3 = 0, 1, 2
 
 c_void_p = ctypes.c_void_p
 c_i32 = ctypes.c_int32
@@ -95,7 +95,7 @@ SIGNATURES = {
                            ctypes.POINTER(MuonHparams), c_void_p, c_size, c_void_p]),
     "grasp_workspace_bytes": (c_size, [c_i64, c_i64, c_i32]),
     "grasp_step": (c_i32, [ctypes.POINTER(GraspStateC), c_i64, c_i64, c_i32, c_i32, c_void_p, c_i32,
-                           c_void_p, c_f32, c_i32, c_f32, c_f32, c_f32, c_f32, c_void_p, c_f32, c_f32,
+                           c_void_p, c_f32, c_i32, c_f32, c_f32, c_f32, c_f32, c_i32, c_void_p, c_f32, c_f32,
                            c_void_p, c_size, c_void_p]),
     "qm_timing_enable": (c_i32, [c_i32]),
     "qm_timing_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),

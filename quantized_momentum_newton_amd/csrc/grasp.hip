@@ -529,8 +529,9 @@ extern "C" size_t grasp_workspace_bytes(int64_t rows, int64_t cols, int32_t rank
 
 extern "C" qm_status grasp_step(const qm_grasp_state *state, int64_t rows, int64_t cols, int32_t rank,
                                 int32_t grid, void *grad, int32_t grad_dtype, const float *warm, float mu,
-                                int32_t ns_steps, float a, float b, float c, float eps, float *weight, float lr,
-                                float weight_decay, void *ws, size_t ws_bytes, qm_stream_t stream) {
+                                int32_t ns_steps, float a, float b, float c, float eps, int32_t ns_precision,
+                                float *weight, float lr, float weight_decay, void *ws, size_t ws_bytes,
+                                qm_stream_t stream) {
     clear_error();
     if (!state || !grad || !warm) return fail(QM_E_ARG, "state, grad and warm are required");
     if (!state->res_codes || !state->res_rmax || !state->res_cmax || !state->p_codes || !state->p_rmax ||
@@ -548,6 +549,8 @@ extern "C" qm_status grasp_step(const qm_grasp_state *state, int64_t rows, int64
         !std::isfinite(b) || !std::isfinite(c) || !(eps >= 0.0f) || std::isinf(eps))
         return fail(QM_E_ARG, "hyperparameters must be finite (eps >= 0)");
     if (ns_steps < 0 || ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
+    if (ns_precision != QM_NS_F32 && ns_precision != QM_NS_BF16X3)
+        return fail(QM_E_ARG, "ns_precision must be QM_NS_F32 or QM_NS_BF16X3");
     if (std::min(rows, cols) > (1 << 16) || std::max(rows, cols) > (1 << 22))
         return fail(QM_E_UNSUPPORTED, "matrix too large");
     const size_t need = grasp_workspace_bytes(rows, cols, rank);
@@ -589,7 +592,7 @@ extern "C" qm_status grasp_step(const qm_grasp_state *state, int64_t rows, int64
     factor_q8_kernel<<<(unsigned)d.nbc, kThreads, 0, st>>>(w.R32, cols, rank, s->r_codes, s->r_rmax, s->r_cmax);
     qm_status stt = launched("grasp state kernels");
     if (stt != QM_OK) return stt;
-    // O = NS(M_t) in f32 arithmetic, written over the grad; W <- W - lr (O + wd W)
+    // O = NS(M_t) on fp32 operands, written over the grad; W <- W - lr (O + wd W)
     return run_ns_f32_into(w.M, rows, cols, grad, grad_dtype, weight, lr, lr * weight_decay, ns_steps, a, b, c, eps,
-                           w.ns, st);
+                           ns_precision, w.ns, st);
 }

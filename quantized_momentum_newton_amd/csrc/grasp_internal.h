@@ -9,11 +9,11 @@ namespace qm {
 
 size_t ns_f32_workspace_bytes(int64_t rows, int64_t cols);
 
-// NS (f32 arithmetic, norm computed from M) of the fp32 rows x cols matrix M
-// into `out` (same shape, contiguous, out_dtype), with W <- W - lr_s O -
-// lr_wd W when w is not null.
+// NS (fp32 operands: precision QM_NS_F32 or QM_NS_BF16X3; norm computed
+// from M) of the fp32 rows x cols matrix M into `out` (same shape,
+// contiguous, out_dtype), with W <- W - lr_s O - lr_wd W when w is not null.
 qm_status run_ns_f32_into(const float *M, int64_t rows, int64_t cols, void *out, int32_t out_dtype, float *w,
-                          float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, void *ws,
-                          hipStream_t stream);
+                          float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, int32_t precision,
+                          void *ws, hipStream_t stream);
 
 }  // namespace qm

@@ -116,6 +116,37 @@ template <> struct Mfma<float> {
     }
 };
 
+// bf16x3 ("fp32 operands, bf16 MFMA"): an fp32 value x is split into
+// hi = bf16(x) and lo = bf16(x - hi), both rounded to nearest even (x - hi
+// is exact in fp32).  A product x y is taken as hi hi' + hi lo' + lo hi':
+// each term an exact bf16 x bf16 product, accumulated in fp32 by the MFMA;
+// the dropped lo lo' is below 2^-16 |x y|.  One fragment holds the 8
+// consecutive k of a lane (two 16-byte chunks of fp32).
+struct F8 {
+    u32x4 x, y;
+};
+__device__ __forceinline__ void split_bf16x3(const F8 &f, u32x4 &hi, u32x4 &lo) {
+    typedef __attribute__((ext_vector_type(2))) float f2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+    const uint32_t w[8] = {f.x.x, f.x.y, f.x.z, f.x.w, f.y.x, f.y.y, f.y.z, f.y.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const f2 v = {__uint_as_float(w[2 * k]), __uint_as_float(w[2 * k + 1])};
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+        const f2 r = {v.x - __uint_as_float(h << 16), v.y - __uint_as_float(h & 0xffff0000u)};
+        hi[k] = h;
+        lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, b2));
+    }
+}
+__device__ __forceinline__ void mfma_bf16x3(const F8 &a, const F8 &b, f32x16 &c) {
+    u32x4 ah, al, bh, bl;
+    split_bf16x3(a, ah, al);
+    split_bf16x3(b, bh, bl);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al), __builtin_bit_cast(bf16x8, bh), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, bl), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah), __builtin_bit_cast(bf16x8, bh), c, 0, 0, 0);
+}
+
 // ------------------------------------------------------------ GEMM kernel
 
 enum Epi { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2 };
@@ -270,7 +301,7 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
 }
 
 template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
-          bool SYM, bool QT>
+          bool SYM, bool QT, bool X3>
 __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -278,7 +309,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     constexpr int CPR = ROWB / 16;                  // 16-byte chunks per tile row (one k-tile)
     constexpr int RPI = 64 / CPR;                   // tile rows per DMA instruction
     constexpr int SWD = 16 / CPR;                   // rows sharing one 256-byte bank row
-    constexpr int STEPS = CPR / 2;                  // MFMA k-steps per k-tile
+    // MFMA k-steps per k-tile (X3: fp32 data, 16 k per bf16x3 step)
+    constexpr int STEPS = X3 ? CPR / 4 : CPR / 2;
+    static_assert(!X3 || (sizeof(T) == 4 && !QT), "bf16x3: fp32 operands, K-contiguous");
     constexpr int STAGE = (BM + BN) * ROWB;
     constexpr int PI = BM / RPI / NW, QI = BN / RPI / NW;  // DMA instructions per wave per operand
     constexpr int DPT = PI + QI;                    // per wave per k-tile
@@ -406,20 +439,30 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         const u32x2 lo = read_qt4(cq, k0, nb), hi = read_qt4(cq, k0 + 4, nb);
         return u32x4{lo.x, lo.y, hi.x, hi.y};
     };
-    auto read_frags = [&](const char *cp, const char *cq, int s, u32x4 *a, u32x4 *b) {
+    using Frag = std::conditional_t<X3, F8, u32x4>;
+    // X3: lane half h of step s takes k 16 s + 8 h .. + 7: chunks 4 s + 2 h and 4 s + 2 h + 1
+    auto read_frag = [&](const char *base, int row, int s) -> Frag {
+        const int sw = (row / SWD) % CPR;
+        if constexpr (X3) {
+            const int c0 = 4 * s + 2 * lhalf;
+            return F8{*reinterpret_cast<const u32x4 *>(base + row * ROWB + ((c0 ^ sw) << 4)),
+                      *reinterpret_cast<const u32x4 *>(base + row * ROWB + (((c0 + 1) ^ sw) << 4))};
+        } else {
+            return *reinterpret_cast<const u32x4 *>(base + row * ROWB + (((2 * s + lhalf) ^ sw) << 4));
+        }
+    };
+    auto read_frags = [&](const char *cp, const char *cq, int s, Frag *a, Frag *b) {
         const int ch = 2 * s + lhalf;
 #pragma unroll
         for (int i = 0; i < FM; i++) {
-            const int row = wm * WM + i * 32 + lrow;
-            a[i] = *reinterpret_cast<const u32x4 *>(cp + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+            a[i] = read_frag(cp, wm * WM + i * 32 + lrow, s);
         }
 #pragma unroll
         for (int j = 0; j < FN; j++) {
             if constexpr (QT) {
                 b[j] = read_qt8(cq, 16 * s + 8 * (lane >> 5), wn * WN + j * 32);
             } else {
-                const int row = wn * WN + j * 32 + lrow;
-                b[j] = *reinterpret_cast<const u32x4 *>(cq + row * ROWB + ((ch ^ ((row / SWD) % CPR)) << 4));
+                b[j] = read_frag(cq, wn * WN + j * 32 + lrow, s);
             }
         }
     };
@@ -436,7 +479,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     //    the iteration waits for everything but P of kt+2.  P loads thus get
     //    two tiles of lead and Q loads one, where two full stages give each
     //    load between a quarter and all of one tile.
-    u32x4 fa[2][FM], fb[2][FN];
+    Frag fa[2][FM], fb[2][FN];
     constexpr int DPS = (DPT + STEPS - 1) / STEPS;  // DMA instructions per k-step
     auto issue_part = [&](int kt, int part) {
 #pragma unroll
@@ -549,7 +592,10 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
-                for (int j = 0; j < FN; j++) Mfma<T>::step(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+                for (int j = 0; j < FN; j++) {
+                    if constexpr (X3) mfma_bf16x3(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+                    else Mfma<T>::step(fa[s & 1][i], fb[s & 1][j], acc[i][j]);
+                }
             if constexpr (DMF) {
                 if (dloop) {
                     const int t = kt - dkt0;
@@ -1204,7 +1250,7 @@ Geometry geometry(int64_t rows, int64_t cols, size_t esz) {
     return g;
 }
 
-size_t elem_size(int precision) { return precision == QM_NS_F32 ? 4 : 2; }
+size_t elem_size(int precision) { return precision == QM_NS_BF16 ? 2 : 4; }
 
 // Requests are processed in chunks of up to kMaxItems, largest first; the
 // workspace holds the largest chunk plus the norm scratch.
@@ -1288,11 +1334,11 @@ qm_status reserve_lds(const void *kern, size_t bytes, bool *done) {
     return QM_OK;
 }
 
-template <typename T, typename C, int EPI, bool SYM, bool QT = false>
+template <typename T, typename C, int EPI, bool SYM, bool QT = false, bool X3 = false>
 qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
     constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
-    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT>;
+    auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT, X3>;
     static bool attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(kern), lds, attr_set);
     if (st != QM_OK) return st;
@@ -1335,7 +1381,7 @@ struct ItemBufs {
 
 // The T iterations of one chunk: A = X X^T, B = b A + c A A, X = a X + B X,
 // with the symmetric products on tile configuration CS and the last on CR.
-template <typename T, typename CS, typename CR>
+template <typename T, typename CS, typename CR, bool X3>
 qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk,
                        const std::vector<ItemBufs> &bufs, const std::vector<int> &by_n, const std::vector<int> &by_m,
                        std::vector<int> &cur, int steps, float a, float b, float c, hipStream_t stream) {
@@ -1386,7 +1432,7 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
             tl += tm * (tm + 1) / 2;
         }
         qm_status st = QM_OK;
-        if (g1.n_items) st = launch_gemm<T, CS, EPI_GRAM, true>(g1, tl, stream);
+        if (g1.n_items) st = launch_gemm<T, CS, EPI_GRAM, true, false, X3>(g1, tl, stream);
         if (st != QM_OK) return st;
         if (gx.n_items) st = launch_gram_mx(gx, tx, stream);
         if (st != QM_OK) return st;
@@ -1412,7 +1458,7 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
             I.k_tiles = (int32_t)(B.g.mp / kSymK);
             tl += tm * (tm + 1) / 2;
         }
-        st = launch_gemm<T, CS, EPI_POLY, true>(g2, tl, stream);
+        st = launch_gemm<T, CS, EPI_POLY, true, false, X3>(g2, tl, stream);
         if (st != QM_OK) return st;
         // X = a X + B X: bf16 reads Q = X (K x N) and writes the other X
         // buffer; fp32 reads Q = X^T and updates X in place, writing X^T.
@@ -1445,7 +1491,7 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
             tl += tm * tn;
             if (s + 1 == steps) I.CT = nullptr;   // no further product reads X^T
         }
-        st = launch_gemm<T, CR, EPI_UPDATE, false, kQT>(g3, tl, stream);
+        st = launch_gemm<T, CR, EPI_UPDATE, false, kQT, X3>(g3, tl, stream);
         if (st != QM_OK) return st;
         for (int i = 0; i < nit; i++) cur[i] ^= 1;
     }
@@ -1458,21 +1504,23 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
 // on the 4096-square NS: 256 x 256 0.76, 128 x 128 1, 64 x 64 0.94).  The
 // fp32 MFMA needs 16x fewer operand bytes per second than bf16, so small
 // tiles lose little, and a launch whose tiles do not fill the CUs evenly
-// loses most of a round.  0: 256 x 256, 1: 128 x 128, 2: 64 x 64.
-int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym) {
+// loses most of a round.  0: 256 x 256, 1: 128 x 128, 2: 64 x 64; bf16x3
+// runs choose from the last two (with 256 x 256 tiles their fragments of
+// 8 fp32 do not fit the registers).
+int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym, int first) {
     static constexpr int kS[3] = {256, 128, 64};
     static constexpr double kEff[3] = {0.76, 1.0, 0.94};
     const int64_t n_cu = cu_count();
-    int best = 0;
+    int best = first;
     double best_t = 0;
-    for (int k = 0; k < 3; k++) {
+    for (int k = first; k < 3; k++) {
         int64_t tiles = 0;
         for (const ItemBufs &b : bufs) {
             const int64_t tm = b.g.mp / kS[k], tn = b.g.np / kS[k];
             tiles += sym ? tm * (tm + 1) / 2 : tm * tn;
         }
         const double t = (double)((tiles + n_cu - 1) / n_cu) * kS[k] * kS[k] / kEff[k];
-        if (k == 0 || t < best_t) {
+        if (k == first || t < best_t) {
             best = k;
             best_t = t;
         }
@@ -1480,7 +1528,8 @@ int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym) {
     return best;
 }
 
-template <typename T>
+// X3: fp32 runs on bf16x3 products (precision QM_NS_BF16X3).
+template <typename T, bool X3 = false>
 qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int steps, float a,
                     float b, float c, float eps, void *ws, hipStream_t stream) {
     const int nit = (int)chunk.size();
@@ -1571,16 +1620,20 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
     qm_status st;
     if constexpr (sizeof(T) == 4) {
-        const int ts = pick_f32_tile(bufs, true), tr = pick_f32_tile(bufs, false);
+        const int first = X3 ? 1 : 0;
+        const int ts = pick_f32_tile(bufs, true, first), tr = pick_f32_tile(bufs, false, first);
         auto run = [&](auto cs) -> qm_status {
             using CS = decltype(cs);
-            if (tr == 0) return run_products<T, CS, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
-            if (tr == 1) return run_products<T, CS, CfgF32Mid>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
-            return run_products<T, CS, CfgF32Small>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            if constexpr (!X3) {
+                if (tr == 0) return run_products<T, CS, CfgRect, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            }
+            if (tr <= 1) return run_products<T, CS, CfgF32Mid, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            return run_products<T, CS, CfgF32Small, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
         };
-        st = ts == 0 ? run(CfgSym{}) : ts == 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
+        if constexpr (X3) st = ts <= 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
+        else st = ts == 0 ? run(CfgSym{}) : ts == 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
     } else {
-        st = run_products<T, CfgSym, CfgRect>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+        st = run_products<T, CfgSym, CfgRect, false>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
     }
     if (st != QM_OK) return st;
     if constexpr (kQT)
@@ -1597,9 +1650,9 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
 qm_status run_ns(const std::vector<NsRequest> &req, int steps, float a, float b, float c, float eps,
                  int precision, void *ws, hipStream_t stream) {
     for (const auto &chunk : make_chunks(req)) {
-        const qm_status st = precision == QM_NS_F32
-                                 ? run_chunk<float>(req, chunk, steps, a, b, c, eps, ws, stream)
-                                 : run_chunk<bf16_t>(req, chunk, steps, a, b, c, eps, ws, stream);
+        const qm_status st = precision == QM_NS_F32      ? run_chunk<float>(req, chunk, steps, a, b, c, eps, ws, stream)
+                             : precision == QM_NS_BF16X3 ? run_chunk<float, true>(req, chunk, steps, a, b, c, eps, ws, stream)
+                                                         : run_chunk<bf16_t>(req, chunk, steps, a, b, c, eps, ws, stream);
         if (st != QM_OK) return st;
     }
     return QM_OK;
@@ -1609,7 +1662,8 @@ qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, in
                           float a, float b, float c, float eps, int32_t precision) {
     if (!x) return fail(QM_E_ARG, "x is null");
     if (dtype != QM_F32 && dtype != QM_BF16 && dtype != QM_F16) return fail(QM_E_DTYPE, "unknown dtype %d", dtype);
-    if (precision != QM_NS_BF16 && precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision %d", precision);
+    if (precision != QM_NS_BF16 && precision != QM_NS_F32 && precision != QM_NS_BF16X3)
+        return fail(QM_E_ARG, "unknown precision %d", precision);
     if (rows <= 0 || cols <= 0) return fail(QM_E_SHAPE, "rows and cols must be positive");
     if (ld < cols) return fail(QM_E_SHAPE, "ld must be >= cols");
     if (std::min(rows, cols) > (1 << 16) || std::max(rows, cols) > (1 << 22))
@@ -1627,10 +1681,10 @@ qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, in
 size_t ns_f32_workspace_bytes(int64_t rows, int64_t cols) { return ns_ws_bytes_uniform(rows, cols, 1, QM_NS_F32); }
 
 qm_status run_ns_f32_into(const float *M, int64_t rows, int64_t cols, void *out, int32_t out_dtype, float *w,
-                          float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, void *ws,
-                          hipStream_t stream) {
+                          float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, int32_t precision,
+                          void *ws, hipStream_t stream) {
     std::vector<NsRequest> req{NsRequest{M, out, rows, cols, cols, QM_F32, out_dtype, nullptr, w, cols, lr_s, lr_wd}};
-    return run_ns(req, steps, a, b, c, eps, QM_NS_F32, ws, stream);
+    return run_ns(req, steps, a, b, c, eps, precision, ws, stream);
 }
 
 }  // namespace qm
@@ -1833,7 +1887,8 @@ size_t step_ws_total(const void *host_plan_full, const void *host_plan_block, co
 
 qm_status check_hparams(const qm_muon_hparams *hp) {
     if (!hp) return fail(QM_E_ARG, "hparams is null");
-    if (hp->precision != QM_NS_BF16 && hp->precision != QM_NS_F32) return fail(QM_E_ARG, "unknown precision");
+    if (hp->precision != QM_NS_BF16 && hp->precision != QM_NS_F32 && hp->precision != QM_NS_BF16X3)
+        return fail(QM_E_ARG, "unknown precision");
     if (hp->ns_steps < 0 || hp->ns_steps > 100) return fail(QM_E_ARG, "ns_steps must lie in [0, 100]");
     if (!std::isfinite(hp->lr_full) || !std::isfinite(hp->lr_block) || !std::isfinite(hp->weight_decay) ||
         !std::isfinite(hp->rms_scale) || !std::isfinite(hp->a) || !std::isfinite(hp->b) || !std::isfinite(hp->c))

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(LIB, n), n
     assert names == set(L.SIGNATURES), names ^ set(L.SIGNATURES)
-    assert LIB.qm_abi_version() == 3
+    assert LIB.qm_abi_version() == 4
     assert LIB.qm_status_string(0) == b"ok"
 
 
@@ -276,3 +276,17 @@ def test_carrier_hparams_and_workspace():
     st, buf = _encode(tens, _segs([(0, 0, 64 * 48, 0)]), 1)
     mats[0] = L.MuonMatrix(64, 48, 64, 48, None)
     assert LIB.muon_step_workspace_bytes_ex(ctypes.cast(buf, ctypes.c_void_p), None, mats, 1, ctypes.byref(h)) == 0
+
+
+def test_ns_precisions_workspace_and_validation():
+    """bf16x3 holds X, A, B in fp32 like the f32 mode (same workspace); an
+    unknown precision is refused before any launch."""
+    for rows, cols in ((64, 256), (300, 200), (4096, 14336)):
+        f32 = LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_F32)
+        assert LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16X3) == f32
+        assert f32 > LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16)
+    x = ctypes.c_void_p(BASE)
+    ws = ctypes.c_void_p(BASE + (1 << 34))
+    for prec in (3, -1):
+        assert LIB.ns_orthogonalize(x, L.QM_F32, 64, 256, 256, 1, 0, 5, 3.4445, -4.775, 2.0315, 1e-7, None, prec,
+                                    ws, 1 << 40, None) == 1

@@ -106,8 +106,10 @@ def test_grasp_small_chain_20_steps():
     say("code mismatches over 20 steps:", mism)
 
 
-def test_grasp_ragged_shape_and_rank4():
-    """Edge blocks clipped on both sides (rows 100, cols 77 -> odd packing)."""
+@pytest.mark.parametrize("ns_precision", ["f32", "bf16x3"])
+def test_grasp_ragged_shape_and_rank4(ns_precision):
+    """Edge blocks clipped on both sides (rows 100, cols 77 -> odd packing);
+    the NS on fp32 operands, fp32 MFMAs or bf16 MFMAs on a hi + lo split."""
     rows, cols, k = 100, 77, 4
     st = q.GraspState(rows, cols, k)
     warm = H.gaussian((cols, k), DEV, 5002)
@@ -115,7 +117,7 @@ def test_grasp_ragged_shape_and_rank4():
         g = H.grad((rows, cols), torch.float32, DEV, 5002, t)
         gh = host(g)
         prev = to_oracle(st)
-        q.grasp_step(st, g, warm, ns_steps=5, coeffs=COEF)
+        q.grasp_step(st, g, warm, ns_steps=5, coeffs=COEF, ns_precision=ns_precision)
         torch.cuda.synchronize()
         ref, M, P32, R32, O = OG.grasp_step(prev, gh, 0.95, host(warm), 5, COEF, H.NS_EPS)
         compare_step(st, ref, M, P32, R32)
@@ -143,7 +145,8 @@ def test_grasp_generic_mgs_path(rows, cols, k):
         _within(as_f64(g), O, f"t{t} O")
 
 
-def test_grasp_4096_full_size():
+@pytest.mark.parametrize("ns_precision", ["f32", "bf16x3"])
+def test_grasp_4096_full_size(ns_precision):
     """4096x4096, rank-8 spike of norm 10x the noise, mu = 0.95, 20 steps:
     state checked on every step, NS on sampled rows at the last step."""
     cfg = H.grasp_4096_shape()
@@ -159,7 +162,7 @@ def test_grasp_4096_full_size():
         gh = g.float().cpu().numpy()
         prev = to_oracle(st)
         say("grasp 4096x4096 step", t)
-        q.grasp_step(st, g, warm, mu=mu, ns_steps=5, coeffs=COEF, eps=H.NS_EPS, ws=ws)
+        q.grasp_step(st, g, warm, mu=mu, ns_steps=5, coeffs=COEF, eps=H.NS_EPS, ws=ws, ns_precision=ns_precision)
         torch.cuda.synchronize()
         ref, M, P32, R32, _ = OG.grasp_step(prev, gh, mu, hw, 5, COEF, H.NS_EPS, with_ns=False)
         mism += compare_step(st, ref, M, P32, R32)

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import quantized_momentum_newton_amd as q
-from gpu_util import (NS_BF16_COS, NS_BF16_REL, as_f64, assert_bits_equal, host, host_grad,
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, assert_bits_equal, host, host_grad,
                       ns_parity, say)
 from harness import inputs as H
 from oracle import muonbp, ns
@@ -238,3 +238,37 @@ def test_muon_step_stochastic_rounding_state():
             assert_bits_equal(host(trip[i][0]), st[i][0], f"t{t} codes[{i}]")
             assert_bits_equal(host(trip[i][1]), st[i][1], f"t{t} absmax[{i}]")
         states = [(c, a) for c, a in st]
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+def test_fp32_256x512_step_fp32_operands(precision):
+    """The single 256x512 fp32 matrix: update, normalise, NS on fp32 operands
+    (fp32 MFMAs, or bf16 MFMAs on a hi + lo split) and the weight apply,
+    three full steps: state bit-exact, O and dW within the f32 bound."""
+    (_, r, c), = H.fp32_256x512_shapes()
+    codes, absmax = H.prior_state(r * c, DEV, 3101, 0)
+    g = torch.empty(r * c, dtype=torch.float32, device=DEV)
+    w = H.weights((r, c), DEV, 3101, 0)
+    trip, mats = [(codes, absmax, g)], [(r, c, r, c, w)]
+    plan = q.Plan(trip, [(0, 0, r * c, 0)], 1)
+    params = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, weight_decay=0.01, ns_steps=5, period=1,
+                            precision=precision)
+    W_host, state = as_f64(w), (host(codes), host(absmax))
+    for t in range(1, 4):
+        g.copy_(H.grad((r, c), torch.float32, DEV, 3101, 0, t).reshape(-1))
+        torch.cuda.synchronize()
+        gh = host_grad(g)
+        say("fp32 step", precision, t)
+        q.muon_step(plan, None, mats, t, params)
+        torch.cuda.synchronize()
+        W2, c2, a2, O, is_full = muonbp.muon_step(W_host, state[0], state[1], gh, oracle.F32, t, r, c, r, c, 1, 0.95,
+                                                  1e-7, COEF, 5, 0.02, 0.01, 0.2, 0.01)
+        assert is_full
+        assert_bits_equal(host(codes), c2, f"t{t} codes")
+        assert_bits_equal(host(absmax), a2, f"t{t} absmax")
+        state = (c2, a2)
+        for got, ref, what in ((as_f64(g).reshape(r, c), O, "O"), (as_f64(w) - W_host, W2 - W_host, "dW")):
+            rel, cos = ns_parity(got, ref)
+            say(f"   t{t} {what}: relF {rel:.3e} min cos {cos:.7f}")
+            assert rel <= NS_F32_REL and cos >= NS_F32_COS, (what, rel, cos)
+        W_host = as_f64(w)

@@ -1,8 +1,9 @@
 """GPU parity of Newton-Schulz orthogonalisation against the fp64 oracle.
 
 bf16 mode: relative Frobenius error <= 2e-2 and every row's cosine >= 0.999
-(the workload's stated bound); f32 mode: <= 1e-4.  At full size the oracle
-runs through its spectral route on sampled rows.
+(the workload's stated bound); f32 and bf16x3 modes (fp32 operands; fp32
+MFMAs, or bf16 MFMAs on a hi + lo split): <= 1e-4 and >= 0.99999.  At full
+size the oracle runs through its spectral route on sampled rows.
 """
 import numpy as np
 import pytest
@@ -28,7 +29,7 @@ def _check(got, ref, precision):
 @pytest.mark.parametrize("shape", [(256, 512), (512, 256), (100, 300), (300, 100), (128, 128),
                                    (1, 7), (7, 1), (257, 513)])
 @pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32),
-                                             ("bf16", torch.float16)])
+                                             ("bf16", torch.float16), ("bf16x3", torch.float32)])
 def test_ns_small_shapes(shape, precision, dtype):
     say("ns", shape, precision, dtype)
     x = H.grad(shape, dtype, DEV, 2001, *shape)
@@ -39,13 +40,26 @@ def test_ns_small_shapes(shape, precision, dtype):
     _check(as_f64(x), ref, precision if dtype == torch.float32 else "bf16")
 
 
-def test_256x512_f32_mode():
-    """256x512 fp32, F32 arithmetic, 5 quintic steps."""
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+def test_256x512_f32_mode(precision):
+    """256x512 fp32, fp32-operand arithmetic, 5 quintic steps."""
     x = H.grad((256, 512), torch.float32, DEV, 1001, 7)
     x0 = as_f64(x)
-    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision="f32")
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
     torch.cuda.synchronize()
-    _check(as_f64(x), ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS), "f32")
+    _check(as_f64(x), ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS), precision)
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+def test_rank8_spike_needs_fp32_operands(precision):
+    """The GRASP gradient's shape, a rank-8 spike of 10x the noise norm on
+    Gaussian noise: both fp32-operand modes within the f32 bound."""
+    rows, cols = 1024, 768
+    x = (H.grad((rows, cols), torch.float32, DEV, 2301) + H.spike(rows, cols, 8, DEV, 2301)).contiguous()
+    x0 = as_f64(x)
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
+    torch.cuda.synchronize()
+    _check(as_f64(x), ns.ns_orthogonalize(x0, 5, COEF, H.NS_EPS), precision)
 
 
 def test_given_inverse_norm_and_zero_steps():
@@ -107,19 +121,21 @@ def test_llama8b_shapes_full_size_sampled(name, shape):
     _check(as_f64(x)[rows], ref, "bf16")
 
 
-@pytest.mark.parametrize("shape", [(3000, 3300), (3300, 3000), (2048, 2048)])
-def test_f32_mid_and_small_tile_runs(shape):
-    """fp32 runs whose Gram leaves CUs idle at 256 x 256 tiles: 3000 x 3300
-    (padded to 3072 x 3328) takes the 128 x 128 tiles, 2048 x 2048 the
-    64 x 64 ones; sampled rows against the exact iterate."""
-    say("f32 NS", shape)
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+@pytest.mark.parametrize("shape", [(3000, 3300), (3300, 3000), (2048, 2048), (4096, 4096)])
+def test_f32_mid_and_small_tile_runs(shape, precision):
+    """fp32-operand runs on the sizes whose products take 128 x 128 or 64 x 64
+    tiles (3000 x 3300 is padded to 3072 x 3328; the 4096-square Gram takes
+    64 x 64, its X = aX + BX 128 x 128); sampled rows against the exact
+    iterate."""
+    say("fp32-operand NS", shape, precision)
     x = H.grad(shape, torch.float32, DEV, 2101, *shape)
     x0 = as_f64(x)
-    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision="f32")
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
     torch.cuda.synchronize()
     rows = _sample_rows(shape[0], 32, 5)
     ref = ns.spectral_rows(x0, rows, 5, COEF, H.NS_EPS)
-    _check(as_f64(x)[rows], ref, "f32")
+    _check(as_f64(x)[rows], ref, precision)
 
 
 def test_blocked_muonbp_shape_sampled():
@@ -136,7 +152,8 @@ def test_blocked_muonbp_shape_sampled():
         _check(out[rows, 1792 * j:1792 * (j + 1)], ref, "bf16")
 
 
-@pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32)])
+@pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32),
+                                             ("bf16x3", torch.float32)])
 def test_degenerate_inputs(precision, dtype):
     """Degenerate inputs the iteration keeps exact in any arithmetic:
       * a zero matrix stays exactly zero (eps keeps the inverse norm finite,
