@@ -1504,23 +1504,30 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
 // on the 4096-square NS: 256 x 256 0.76, 128 x 128 1, 64 x 64 0.94).  The
 // fp32 MFMA needs 16x fewer operand bytes per second than bf16, so small
 // tiles lose little, and a launch whose tiles do not fill the CUs evenly
-// loses most of a round.  0: 256 x 256, 1: 128 x 128, 2: 64 x 64; bf16x3
-// runs choose from the last two (with 256 x 256 tiles their fragments of
-// 8 fp32 do not fit the registers).
-int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym, int first) {
+// loses most of a round.  0: 256 x 256, 1: 128 x 128, 2: 64 x 64.
+// bf16x3 runs (x3) take 128 x 128 when that gives every CU a tile, else
+// 64 x 64: their tiles compute 2x faster, so the small tiles' overheads weigh
+// more (64 x 64 ran at 0.54 - 0.87 of the 128 x 128 rate), and with 256 x 256
+// tiles their fragments of 8 fp32 do not fit the registers.
+int64_t tile_count(const std::vector<ItemBufs> &bufs, bool sym, int64_t s) {
+    int64_t tiles = 0;
+    for (const ItemBufs &b : bufs) {
+        const int64_t tm = b.g.mp / s, tn = b.g.np / s;
+        tiles += sym ? tm * (tm + 1) / 2 : tm * tn;
+    }
+    return tiles;
+}
+int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym, bool x3) {
     static constexpr int kS[3] = {256, 128, 64};
     static constexpr double kEff[3] = {0.76, 1.0, 0.94};
     const int64_t n_cu = cu_count();
-    int best = first;
+    if (x3) return tile_count(bufs, sym, 128) >= n_cu ? 1 : 2;
+    int best = 0;
     double best_t = 0;
-    for (int k = first; k < 3; k++) {
-        int64_t tiles = 0;
-        for (const ItemBufs &b : bufs) {
-            const int64_t tm = b.g.mp / kS[k], tn = b.g.np / kS[k];
-            tiles += sym ? tm * (tm + 1) / 2 : tm * tn;
-        }
+    for (int k = 0; k < 3; k++) {
+        const int64_t tiles = tile_count(bufs, sym, kS[k]);
         const double t = (double)((tiles + n_cu - 1) / n_cu) * kS[k] * kS[k] / kEff[k];
-        if (k == first || t < best_t) {
+        if (k == 0 || t < best_t) {
             best = k;
             best_t = t;
         }
@@ -1620,8 +1627,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     std::vector<int> cur(nit, 0);  // bf16: which X buffer is current; fp32: which X^T buffer
     qm_status st;
     if constexpr (sizeof(T) == 4) {
-        const int first = X3 ? 1 : 0;
-        const int ts = pick_f32_tile(bufs, true, first), tr = pick_f32_tile(bufs, false, first);
+        const int ts = pick_f32_tile(bufs, true, X3), tr = pick_f32_tile(bufs, false, X3);
         auto run = [&](auto cs) -> qm_status {
             using CS = decltype(cs);
             if constexpr (!X3) {
