@@ -374,3 +374,25 @@ def test_stochastic_rounding_matches_oracle():
         torch.cuda.synchronize()
         runs.append(host(q2.codes[0]))
     assert np.array_equal(runs[0], runs[1]) and not np.array_equal(runs[0], runs[2])
+
+
+def test_nonfinite_grad_stays_in_its_block():
+    """Non-finite momentum is outside the method's contract, but it must
+    neither fault nor spread: with a NaN in block 3 and an Inf in block 5 of
+    one tensor, its other blocks (codes, absmax) and the other tensors and
+    their groups stay bit-exact with the oracle; the two blocks keep codes
+    inside [-127, 127]."""
+    qs = Q8Set([(4096,), (2048,), (777,)], [torch.bfloat16, torch.bfloat16, torch.float32], seed=1011)
+    qs.grads[0][3 * 256 + 17] = float("nan")
+    qs.grads[0][5 * 256 + 200] = float("inf")
+    torch.cuda.synchronize()
+    qs.snapshot()
+    run_and_compare(qs, [(0, 0, 4096, 0), (1, 0, 2048, 1), (2, 0, 777, 2)], 3, 0.95, 1e-7, check_idx=[1, 2])
+    c_ref, a_ref, _, _ = oracle.q8_update(qs.h_codes[0], qs.h_absmax[0], qs.h_grads[0].copy(), 0.95,
+                                          dtype=qs.odt(0))
+    codes, absmax = host(qs.codes[0]), host(qs.absmax[0])
+    keep = np.ones(16, bool)
+    keep[[3, 5]] = False
+    assert_bits_equal(codes.reshape(16, 256)[keep].ravel(), c_ref.reshape(16, 256)[keep].ravel(), "codes, finite blocks")
+    assert_bits_equal(absmax[keep], a_ref[keep], "absmax, finite blocks")
+    assert codes.min() >= -127 and codes.max() <= 127
