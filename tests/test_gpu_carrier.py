@@ -16,8 +16,8 @@ import torch
 
 import oracle
 import quantized_momentum_newton_amd as q
-from gpu_util import (NS_BF16_COS, NS_BF16_REL, TORCH_TO_ORACLE, Q8Set, as_f64, assert_bits_equal, host,
-                      host_grad, ns_parity, say)
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, TORCH_TO_ORACLE, Q8Set, as_f64,
+                      assert_bits_equal, host, host_grad, ns_parity, say)
 from harness import inputs as H
 from oracle import muonbp, ns
 
@@ -467,3 +467,34 @@ def test_muon_step_carrier_mode_other_grad_dtypes(dtype):
         assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
         assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
         _within(as_f64(trip[i][2]).reshape(r, c), O, f"O[{i}] ({dtype})")
+
+
+@pytest.mark.parametrize("precision", ["f32", "bf16x3"])
+def test_muon_step_carrier_mode_fp32_operand_ns(precision):
+    """Carrier mode with an NS on fp32 operands: the prologue decodes the
+    carrier times the group inverse norm into fp32 X (exact decode, one fp32
+    rounding), the products run in f32 or bf16x3; O within the f32 bound."""
+    shapes = [(256, 512), (512, 256)]
+    trip, mats, states = [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3501, i)
+        g = H.grad((r, c), torch.float32, DEV, 3501, i).reshape(-1)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, None))
+        states.append((host(codes), host(absmax)))
+    torch.cuda.synchronize()
+    gh = [host_grad(t[2]) for t in trip]
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], len(shapes))
+    params = q.make_hparams(coeffs=COEF, period=1, carrier=True, precision=precision)
+    say("carrier step, fp32-operand NS", precision)
+    q.muon_step(plan, None, mats, 1, params)
+    torch.cuda.synchronize()
+    for i, (r, c) in enumerate(shapes):
+        _, c2, a2, O, _ = muonbp.muon_step(np.zeros((r, c), np.float32), states[i][0], states[i][1], gh[i],
+                                           oracle.F32, 1, r, c, r, c, 1, H.BETA, H.NS_EPS, COEF, 5, 0.0, 0.0, 0.2,
+                                           carrier=True)
+        assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
+        rel, cos = ns_parity(as_f64(trip[i][2]).reshape(r, c), O)
+        say(f"   O[{i}]: relF {rel:.3e} min cos {cos:.7f}")
+        assert rel <= NS_F32_REL and cos >= NS_F32_COS, (i, rel, cos)
