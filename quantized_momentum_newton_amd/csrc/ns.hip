@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <numeric>
 #include <vector>
 
@@ -1306,31 +1307,35 @@ struct CfgF32Small {
     static constexpr int BM = 64, BN = 64, WM = 2, WN = 2, ROWB = 128, NST = 2, SLOTS = 0, MINB = 4;
 };
 
+// Per-device caches below are indexed by device ordinal; they are atomics
+// because entry points may run on several host threads at once (the values
+// written are the same whichever thread writes first).
+constexpr int kMaxDevices = 64;
+
 // Compute units of the current device (cached per device).
 int64_t cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 // Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per device (done[] indexed by device; devices beyond the table are set on
 // every call).
-constexpr int kMaxDevices = 64;
-qm_status reserve_lds(const void *kern, size_t bytes, bool *done) {
+qm_status reserve_lds(const void *kern, size_t bytes, std::atomic<bool> *done) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(QM_E_HIP, "no current device");
     const bool cached = dev >= 0 && dev < kMaxDevices;
-    if (cached && done[dev]) return QM_OK;
+    if (cached && done[dev].load(std::memory_order_acquire)) return QM_OK;
     if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
         return fail(QM_E_HIP, "cannot reserve %zu bytes of LDS", bytes);
-    if (cached) done[dev] = true;
+    if (cached) done[dev].store(true, std::memory_order_release);
     return QM_OK;
 }
 
@@ -1339,7 +1344,7 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
     constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
     auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT, X3>;
-    static bool attr_set[kMaxDevices] = {};
+    static std::atomic<bool> attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(kern), lds, attr_set);
     if (st != QM_OK) return st;
     Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
@@ -1350,7 +1355,7 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
 }
 
 qm_status launch_gram_mx(const MxGramArgs &args, int grid, hipStream_t stream) {
-    static bool attr_set[kMaxDevices] = {};
+    static std::atomic<bool> attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(gram_mx_kernel), kMxGramLds, attr_set);
     if (st != QM_OK) return st;
     Timed tm(stream, QM_K_NS_GRAM);
