@@ -16,6 +16,9 @@
  *   - qm_last_error() gives a per-thread description of the last failure.
  *   - Calls that share buffers or workspace on one stream run in order; the
  *     same workspace must not be used by two streams at once.
+ *   - Entry points may be called from several host threads at once, each
+ *     with its own buffers, workspace and stream; results do not depend on
+ *     what else runs (every reduction has one fixed order).
  */
 #ifndef QMUON_H
 #define QMUON_H
