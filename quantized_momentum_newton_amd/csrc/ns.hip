@@ -26,9 +26,12 @@
 //     direct global-to-LDS loads (no staging registers); a 16-byte XOR
 //     swizzle keeps the 16-byte fragment reads free of bank conflicts
 //     (64 banks: 16 lanes per cycle).
-//   * Tiles are ordered in bands of 4 tile rows walked column by column and
-//     workgroups remapped so each XCD's 32 concurrent workgroups cover a 4x8
-//     block of tiles (12 operand panels shared in that XCD's L2).
+//   * Tiles are ordered in bands of 4 tile rows walked column by column, and
+//     each XCD's 32 concurrent workgroups cover a 4x8 block of tiles (12
+//     operand panels shared in that XCD's L2).  A symmetric product of
+//     several rounds over matrices that differ in K gives each XCD an equal
+//     share of every matrix's tiles (xcd_tile); other launches deal rounds
+//     of 256 tiles (wg_position).
 //   * Internal buffers are zero-padded to multiples of 256: zero rows and
 //     columns stay zero through the iteration, so no kernel needs bounds
 //     checks in its main loop.
@@ -181,6 +184,8 @@ template <typename T> struct GItem {
 template <typename T> struct GemmArgs {
     GItem<T> it[kMaxItems];
     int32_t n_items;
+    int32_t total_tiles;   // tiles of all items (set at launch)
+    int32_t xcd;           // 1: tiles dealt by xcd_tile, else by wg_position (set at launch)
     float alpha, beta;     // epilogue: C = alpha D + beta acc (beta = 1 for X = aX + BX)
     // dloop != 0: the D term is gathered inside the k-loop instead (acc +=
     // dgain D, dgain = alpha / beta), then C = beta acc.  Valid because D's
@@ -189,7 +194,40 @@ template <typename T> struct GemmArgs {
     float dgain;
 };
 
-// Workgroup -> position in the tile order.  Workgroups go to the 8 XCDs
+// Workgroup -> (item, tile position in the item's band order).  Workgroups
+// go to the 8 XCDs round robin (w % 8).  XCD x takes the x-th contiguous
+// eighth of every item's tiles, items in launch order (longest K first), so
+// each XCD gets the same share of long-K and short-K tiles and none runs
+// out of work while another still holds a second round of long ones.  An
+// item's tiles beyond a multiple of 8 go one each to the XCDs after those
+// that took the previous item's, so XCD totals differ by at most one.  Its
+// 32 concurrent workgroups walk consecutive band positions: a 4 x 8 block
+// of tiles whose 4 + 8 operand panels are shared through that XCD's L2.
+// The grid holds 8 x the largest XCD total; a workgroup past its XCD's
+// total has no tile.
+template <typename Args>
+__device__ __forceinline__ bool xcd_tile(int w, const Args &args, int &item, int &t) {
+    const int x = w & 7, l = w >> 3;
+    int seen = 0, s = 0;
+    for (int i = 0; i < args.n_items; i++) {
+        const int begin = args.it[i].tile_begin;
+        const int cnt = (i + 1 < args.n_items ? args.it[i + 1].tile_begin : args.total_tiles) - begin;
+        const int q = cnt >> 3, r = cnt & 7;
+        const int v = (x - s) & 7;   // which eighth of this item XCD x takes
+        const int share = q + (v < r ? 1 : 0);
+        if (l < seen + share) {
+            item = i;
+            t = v * q + min(v, r) + (l - seen);
+            return true;
+        }
+        seen += share;
+        s = (s + r) & 7;             // the next item's extra tiles start where these end
+    }
+    return false;
+}
+
+// Workgroup -> position in the tile order (launches that do not take
+// xcd_tile).  Workgroups go to the 8 XCDs
 // round robin (w % 8) and each XCD runs 32 at a time (one per CU); in every
 // round of 256, XCD x takes positions [32x, 32x + 32).  With the band order
 // below, those 32 positions are a 4 x 8 block of tiles: 4 + 8 operand
@@ -340,11 +378,15 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    const int L = wg_position(blockIdx.x, gridDim.x);
-    int item = 0;
-    while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+    int item = 0, t = 0;
+    if (SYM && args.xcd) {
+        if (!xcd_tile(blockIdx.x, args, item, t)) return;   // uniform: the whole workgroup
+    } else {
+        const int L = wg_position(blockIdx.x, gridDim.x);
+        while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+        t = L - args.it[item].tile_begin;
+    }
     const GItem<T> &I = args.it[item];
-    const int t = L - I.tile_begin;
     int bi, bj;
     if constexpr (SYM) band_coords_tri(t, I.tiles_n, bi, bj);
     else band_coords(t, I.tiles_m, I.tiles_n, bi, bj);
@@ -770,6 +812,8 @@ struct MxItem {
 struct MxGramArgs {
     MxItem it[kMaxItems];
     int32_t n_items;
+    int32_t total_tiles;   // tiles of all items (set at launch)
+    int32_t xcd;           // as in GemmArgs
 };
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -790,12 +834,17 @@ __global__ __launch_bounds__(512, 1) void gram_mx_kernel(MxGramArgs args) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int L = wg_position(blockIdx.x, gridDim.x);
-    int item = 0;
-    while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+    int item = 0, t = 0;
+    if (args.xcd) {
+        if (!xcd_tile(blockIdx.x, args, item, t)) return;   // uniform: the whole workgroup
+    } else {
+        const int L = wg_position(blockIdx.x, gridDim.x);
+        while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+        t = L - args.it[item].tile_begin;
+    }
     const MxItem &I = args.it[item];
     int bi, bj;
-    band_coords_tri(L - I.tile_begin, I.tiles_m, bi, bj);
+    band_coords_tri(t, I.tiles_m, bi, bj);
 
     const uint8_t *Pg = I.X + (int64_t)bi * BM * I.ldx, *Qg = I.X + (int64_t)bj * BN * I.ldx;
     const uint8_t *Ps = I.S + (int64_t)bi * BM * I.lds, *Qs = I.S + (int64_t)bj * BN * I.lds;
@@ -1339,14 +1388,41 @@ qm_status reserve_lds(const void *kern, size_t bytes, std::atomic<bool> *done) {
     return QM_OK;
 }
 
+// Whether a symmetric launch deals its tiles by xcd_tile: only when it has
+// more tiles than the GPU runs at once and its matrices differ in K.
+// Measured: the Gram of the Llama-8B layer (700 tiles, K 14336 and 4096)
+// ran 7 % faster; launches of a single round (MuonBP's block and full
+// steps) ran 3-5 % slower than with tiles spread round robin, and so did
+// X = aX + BX (equal K) by 1-2 %.
+template <typename Args> bool use_xcd(const Args &args, int tiles, int per_cu) {
+    bool k_differs = false;
+    for (int i = 1; i < args.n_items; i++) k_differs |= args.it[i].k_tiles != args.it[0].k_tiles;
+    return k_differs && tiles > cu_count() * per_cu;
+}
+
+// Grid for xcd_tile: 8 x the largest XCD total, i.e. the whole eighths of
+// every item plus the extra tiles spread one per XCD.
+template <typename Args> int xcd_grid(const Args &args, int total) {
+    int64_t whole = 0, extra = 0;
+    for (int i = 0; i < args.n_items; i++) {
+        const int cnt = (i + 1 < args.n_items ? args.it[i + 1].tile_begin : total) - args.it[i].tile_begin;
+        whole += cnt / 8;
+        extra += cnt % 8;
+    }
+    return (int)(8 * (whole + (extra + 7) / 8));
+}
+
 template <typename T, typename C, int EPI, bool SYM, bool QT = false, bool X3 = false>
-qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
+qm_status launch_gemm(GemmArgs<T> args, int tiles, hipStream_t stream) {
     constexpr int NT = C::WM * C::WN * 64;
     constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
     auto kern = gemm_nt_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT, X3>;
     static std::atomic<bool> attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(kern), lds, attr_set);
     if (st != QM_OK) return st;
+    args.total_tiles = tiles;
+    args.xcd = SYM && use_xcd(args, tiles, C::MINB) ? 1 : 0;
+    const int grid = args.xcd ? xcd_grid(args, tiles) : tiles;
     Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, stream, args);
     const hipError_t e = hipGetLastError();
@@ -1354,10 +1430,13 @@ qm_status launch_gemm(const GemmArgs<T> &args, int grid, hipStream_t stream) {
     return QM_OK;
 }
 
-qm_status launch_gram_mx(const MxGramArgs &args, int grid, hipStream_t stream) {
+qm_status launch_gram_mx(MxGramArgs args, int tiles, hipStream_t stream) {
     static std::atomic<bool> attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(gram_mx_kernel), kMxGramLds, attr_set);
     if (st != QM_OK) return st;
+    args.total_tiles = tiles;
+    args.xcd = use_xcd(args, tiles, 1) ? 1 : 0;
+    const int grid = args.xcd ? xcd_grid(args, tiles) : tiles;
     Timed tm(stream, QM_K_NS_GRAM);
     hipLaunchKernelGGL(gram_mx_kernel, dim3(grid), dim3(512), kMxGramLds, stream, args);
     const hipError_t e = hipGetLastError();
