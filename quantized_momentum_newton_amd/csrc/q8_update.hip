@@ -397,9 +397,11 @@ __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_up
 // runs' block sums as four contiguous 128-byte pieces; a fixed butterfly
 // over the sixteen lanes gives the run's sum.  The 16 run slots of the
 // workgroup (4 waves x 4) each add their runs in pass order, and the slots
-// are added in slot order.  K2b: per group, the chunk partials are added in
-// chunk order.  Results depend only on the plan, never on scheduling, and no
-// atomics are used.
+// are added in slot order.  K2b: one wave per group; lane l adds the
+// group's chunk partials l, l + 64, ... in chunk order, then a butterfly over
+// the 64 lanes adds the lane sums (every lane ends with the same bits: each
+// level adds the same two values in either order).  Results depend only on
+// the plan, never on scheduling, and no atomics are used.
 
 __global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *__restrict__ run_offsets,
                                                                 const PlanRun *__restrict__ runs,
@@ -414,17 +416,33 @@ __global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *_
     const int64_t r_end = run_offsets[g + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int slot = wave * 4 + (lane >> 4), b = lane & 15;
-    double acc = 0.0;
-    for (int pass = 0; pass < kChunkRuns / 16; pass++) {
+    // All run descriptors of the chunk are loaded first, then all block
+    // sums, so a workgroup waits for two memory latencies instead of two
+    // per pass; the sums are then added in the same pass order as ever.
+    constexpr int NP = kChunkRuns / 16;
+    int64_t start[NP];
+    int count[NP];
+#pragma unroll
+    for (int pass = 0; pass < NP; pass++) {
         const int64_t r = r0 + pass * 16 + slot;
-        double v = 0.0;
+        start[pass] = 0;
+        count[pass] = 0;
         if (r < r_end) {
             const PlanRun R = runs[r];
-            if (b < R.count) v = block_sums[R.start_block + b];
+            start[pass] = R.start_block;
+            count[pass] = R.count;
         }
+    }
+    double v[NP];
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        acc += v;
+    for (int pass = 0; pass < NP; pass++) v[pass] = b < count[pass] ? block_sums[start[pass] + b] : 0.0;
+    double acc = 0.0;
+#pragma unroll
+    for (int pass = 0; pass < NP; pass++) {
+        double x = v[pass];
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        acc += x;
     }
     __shared__ double part[16];
     if (b == 0) part[slot] = acc;
@@ -436,16 +454,19 @@ __global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const int64_t *_
     }
 }
 
-__global__ __launch_bounds__(kThreads) void group_final_kernel(const int64_t *__restrict__ chunk_offsets,
-                                                               const double *__restrict__ partials, int n_groups,
-                                                               float eps, double *__restrict__ group_sums,
-                                                               float *__restrict__ inv_norm) {
-    const int g = blockIdx.x * kThreads + threadIdx.x;
-    if (g >= n_groups) return;
+__global__ __launch_bounds__(64) void group_final_kernel(const int64_t *__restrict__ chunk_offsets,
+                                                         const double *__restrict__ partials, float eps,
+                                                         double *__restrict__ group_sums,
+                                                         float *__restrict__ inv_norm) {
+    const int g = blockIdx.x, lane = threadIdx.x;
     double S = 0.0;
-    for (int64_t c = chunk_offsets[g]; c < chunk_offsets[g + 1]; c++) S += partials[c];
-    if (group_sums) group_sums[g] = S;
-    inv_norm[g] = (float)(1.0 / (sqrt(S) + (double)eps));
+    for (int64_t c = chunk_offsets[g] + lane; c < chunk_offsets[g + 1]; c += 64) S += partials[c];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+    if (lane == 0) {
+        if (group_sums) group_sums[g] = S;
+        inv_norm[g] = (float)(1.0 / (sqrt(S) + (double)eps));
+    }
 }
 
 // ------------------------------------------------------------ K3: scale pass
@@ -594,8 +615,7 @@ qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const d
         block_sums, partials);
     qm_status st = check_launch("chunk reduce");
     if (st != QM_OK) return st;
-    group_final_kernel<<<(h->n_groups + kThreads - 1) / kThreads, kThreads, 0, stream>>>(co, partials, h->n_groups,
-                                                                                       eps, group_sums, inv);
+    group_final_kernel<<<(unsigned)h->n_groups, 64, 0, stream>>>(co, partials, eps, group_sums, inv);
     return check_launch("group reduce");
 }
 
