@@ -272,3 +272,37 @@ def test_fp32_256x512_step_fp32_operands(precision):
             say(f"   t{t} {what}: relF {rel:.3e} min cos {cos:.7f}")
             assert rel <= NS_F32_REL and cos >= NS_F32_COS, (what, rel, cos)
         W_host = as_f64(w)
+
+
+def test_grouped_products_equal_single_matrix_products():
+    """Four matrices of different K in one chunk: 136 + 78 + 36 + 10 = 260
+    lower-triangle tiles, more than one round of 256, so the Gram and A^2
+    launches deal their tiles evenly over the XCDs.  Each tile's arithmetic
+    does not depend on which workgroup computes it, so every output must equal,
+    bit for bit, the same matrix orthogonalised alone (one matrix per launch,
+    tiles dealt round robin); a tile dealt twice or never would show here."""
+    shapes = [(4096, 4096), (3072, 3072), (2048, 8192), (1024, 6144)]
+    trip = []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 4401, i)
+        trip.append((codes, absmax, H.grad((r, c), torch.bfloat16, DEV, 4401, i).reshape(-1)))
+    mats = [(r, c, r, c, None) for r, c in shapes]
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], len(shapes))
+    inv = torch.empty(len(shapes), dtype=torch.float32, device=DEV)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, False, group_inv_norm=inv)
+    m = [t[2].clone() for t in trip]
+    hp = q.make_hparams(period=1)
+    ws = torch.empty(q.muon_step_workspace_bytes(plan, None, mats, hparams=hp), dtype=torch.uint8, device=DEV)
+    say("grouped:", shapes)
+    q.muon_apply(plan, mats, True, inv, hp, ws)
+    torch.cuda.synchronize()
+    grouped = [t[2].clone() for t in trip]
+    for i, (r, c) in enumerate(shapes):
+        trip[i][2].copy_(m[i])
+        one = q.Plan([trip[i]], [(0, 0, r * c, 0)], 1)
+        ws1 = torch.empty(q.muon_step_workspace_bytes(one, None, [mats[i]], hparams=hp), dtype=torch.uint8,
+                          device=DEV)
+        q.muon_apply(one, [mats[i]], True, inv[i:i + 1].clone(), hp, ws1)
+        torch.cuda.synchronize()
+        say("  alone:", (r, c))
+        assert torch.equal(trip[i][2].view(torch.int16), grouped[i].view(torch.int16)), (r, c)
