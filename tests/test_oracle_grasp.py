@@ -144,3 +144,36 @@ def test_ns_output_is_ns_of_unquantised_momentum():
     st = grasp.State(m, n, k)
     _, M, _, _, O = grasp.grasp_step(st, g, 0.95, RNG.standard_normal((n, k)))
     assert np.allclose(O, ns.ns_orthogonalize(M.astype(np.float64)), atol=1e-14)
+
+
+def test_apply_weights_hand_worked_2x2():
+    """W' = W - lr (O + lambda W) on a 2 x 2 case worked by hand
+    ("4-bit-Muon-GRASP", update equations; decoupled weight decay):
+    lr = lambda = 0.5 gives W' = 0.75 W - 0.5 O."""
+    W = np.array([[1.0, 2.0], [3.0, 4.0]])
+    O = np.array([[0.5, 0.0], [0.0, -0.5]])
+    got = grasp.apply_weights(W, O, 0.5, 0.5)
+    assert np.array_equal(got, np.array([[0.5, 1.5], [2.25, 3.25]]))
+    assert np.array_equal(grasp.apply_weights(W, O, 0.5), np.array([[0.75, 2.0], [3.0, 4.25]]))
+
+
+def test_first_step_with_weight_decay_closed_form():
+    """From the zero state M_1 = g exactly.  g = rows 0..15 of a 256-order
+    Hadamard matrix / 16 has orthonormal rows, so with eps = 0 the NS output
+    is p^5(1/4) g, and the weights move by -lr (p^5(1/4) g + lambda W)."""
+    H = np.array([[1.0]])
+    while H.shape[0] < 256:
+        H = np.block([[H, H], [H, -H]])
+    g = (H[:16] / 16.0).astype(np.float32)
+    st = grasp.State(16, 256, 2)
+    warm = RNG.standard_normal((256, 2)).astype(np.float32)
+    _, M, _, _, O = grasp.grasp_step(st, g, 0.95, warm, eps=0.0)
+    assert np.array_equal(M, g)
+    s = 0.25
+    for _ in range(5):
+        s = ns.QUINTIC[0] * s + ns.QUINTIC[1] * s ** 3 + ns.QUINTIC[2] * s ** 5
+    assert np.allclose(O, s * g.astype(np.float64), rtol=0, atol=1e-13)
+    W = (RNG.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    W2 = grasp.apply_weights(W, O, 0.02, 0.1)
+    exp = W.astype(np.float64) - 0.02 * (s * g.astype(np.float64) + 0.1 * W.astype(np.float64))
+    assert np.allclose(W2, exp, rtol=0, atol=1e-15)
