@@ -355,7 +355,13 @@ QM_API size_t muon_step_workspace_bytes_ex(const void *host_plan_full,
  *   m * inv_g, output written over the grad buffer in its dtype;
  *   W <- W - lr (s O + weight_decay W), lr = lr_full or lr_block,
  *   s = rms_scale * sqrt(max(p, q)) for the p x q matrix orthogonalised.
- * step is 1-based.  Errors: as the calls above. */
+ * step is 1-based.  With more than one block per matrix, every block must
+ * consist of whole 256-element quantisation blocks (cols and block_cols
+ * multiples of 256, or one column block with block_rows * cols a multiple
+ * of 256), else QM_E_SHAPE; the block plan must give each quantisation block
+ * the group of the block holding it, and both plans must name the same
+ * tensors (codes, absmax, grad, size, dtype), else QM_E_PLAN.
+ * Errors: as the calls above. */
 QM_API qm_status muon_step(const void *host_plan_full, const void *dev_plan_full,
                     const void *host_plan_block, const void *dev_plan_block,
                     const qm_muon_matrix *mats, int32_t n_mats, int64_t step,

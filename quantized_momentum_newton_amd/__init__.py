@@ -55,6 +55,24 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _require(t, name, dtype, device, numel=None, shape=None):
+    """Raise unless t is a contiguous `dtype` tensor on `device` with exactly
+    `numel` elements / this shape (the C side reads that many elements at
+    t.data_ptr())."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
 def _dtype(t):
     try:
         return _DTYPES[t.dtype]
@@ -300,15 +318,19 @@ def make_hparams(beta=0.95, eps=1e-7, coeffs=QUINTIC, lr_full=0.02, lr_block=0.0
                          ns_steps, period, PRECISION[precision], ROUNDING[rounding], int(carrier), seed)
 
 
-def _matrices(mats):
+def _matrices(mats, device):
+    """qm_muon_matrix array; each weight (optional) must be a contiguous fp32
+    tensor of rows x cols elements on the plan's device."""
     arr = (L.MuonMatrix * len(mats))()
     for i, (rows, cols, br, bc, w) in enumerate(mats):
+        if w is not None:
+            _require(w, f"weight {i}", torch.float32, device, numel=rows * cols)
         arr[i] = L.MuonMatrix(rows, cols, br, bc, w.data_ptr() if w is not None else None)
     return arr
 
 
 def muon_step_workspace_bytes(plan_full, plan_block, mats, precision="bf16", hparams=None):
-    arr = _matrices(mats)
+    arr = _matrices(mats, plan_full.device)
     if hparams is not None:
         return _LIB.muon_step_workspace_bytes_ex(plan_full.hptr, plan_block.hptr if plan_block else None,
                                                  arr, len(mats), ctypes.byref(hparams))
@@ -319,7 +341,7 @@ def muon_step_workspace_bytes(plan_full, plan_block, mats, precision="bf16", hpa
 def muon_step(plan_full, plan_block, mats, step, hparams, ws=None, stream=None):
     """One block-periodic Muon step.  mats: list of (rows, cols, block_rows,
     block_cols, weight fp32 tensor or None), tensor i of both plans."""
-    arr = _matrices(mats)
+    arr = _matrices(mats, plan_full.device)
     if ws is None:
         nbytes = _LIB.muon_step_workspace_bytes_ex(plan_full.hptr,
                                                    plan_block.hptr if plan_block else None,
@@ -335,7 +357,8 @@ def muon_step(plan_full, plan_block, mats, step, hparams, ws=None, stream=None):
 def muon_apply(plan, mats, full, inv_norm, hparams, ws, stream=None):
     """NS + weight apply for the plan's matrices given group inverse norms
     (device fp32 [plan.n_groups]); muon_step = update + this."""
-    arr = _matrices(mats)
+    _require(inv_norm, "inv_norm", torch.float32, plan.device, numel=plan.n_groups)
+    arr = _matrices(mats, plan.device)
     _check(_LIB.muon_apply(plan.hptr, arr, len(mats), int(full), _ptr(inv_norm),
                            ctypes.byref(hparams), _ptr(ws), ws.numel(), _stream(stream)))
 
@@ -376,7 +399,16 @@ def grasp_step(state, grad, warm, mu=0.95, ns_steps=5, coeffs=QUINTIC, eps=1e-7,
     """One GRASP step: state updated in place, grad (in: g) overwritten with
     O = NS(M_t), weight (optional) updated.  ns_precision: "f32" (fp32
     MFMAs) or "bf16x3" (fp32 operands, products from a bf16 hi + lo split)."""
+    if grad.dim() != 2:
+        raise ValueError("grad must be a 2-D matrix")
     rows, cols = grad.shape
+    _require(grad, "grad", grad.dtype, grad.device)
+    _dtype(grad)
+    if (state.rows, state.cols) != (rows, cols):
+        raise ValueError(f"state is {state.rows} x {state.cols}, grad {rows} x {cols}")
+    _require(warm, "warm", torch.float32, grad.device, shape=(cols, state.rank))
+    if weight is not None:
+        _require(weight, "weight", torch.float32, grad.device, numel=rows * cols)
     if ws is None:
         ws = torch.empty(_LIB.grasp_workspace_bytes(rows, cols, state.rank), dtype=torch.uint8,
                          device=grad.device)

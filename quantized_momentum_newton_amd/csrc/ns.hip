@@ -1959,10 +1959,30 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
             return fail(QM_E_SHAPE, "matrix %d: blocks do not tile it", i);
         if (std::min(br, bc) > (1 << 16) || std::max(br, bc) > (1 << 22))
             return fail(QM_E_UNSUPPORTED, "matrix %d: too large", i);
-        const int64_t nb = (M.rows / br) * (M.cols / bc);
+        const int64_t nbc = M.cols / bc, nb = (M.rows / br) * nbc;
         if (pt[i].group_lo != g0 || pt[i].group_hi != g0 + nb - 1)
             return fail(QM_E_PLAN, "matrix %d: plan groups %d..%d, expected %lld..%lld", i, pt[i].group_lo,
                         pt[i].group_hi, (long long)g0, (long long)(g0 + nb - 1));
+        if (nb > 1) {
+            // Every NS block must be a union of whole 256-element quantisation
+            // blocks (its norm group is a set of blocks), and the plan must give
+            // quantisation block k the group of the NS block holding it, in
+            // row-major block order: g0 + (r / br) nbc + c / bc.
+            const bool whole = nbc == 1 ? (br * M.cols) % kBlock == 0 : M.cols % kBlock == 0 && bc % kBlock == 0;
+            if (!whole)
+                return fail(QM_E_SHAPE, "matrix %d: a 256-element quantisation block straddles two %lld x %lld blocks",
+                            i, (long long)br, (long long)bc);
+            const int32_t *bg = reinterpret_cast<const int32_t *>(static_cast<const char *>(host_plan) +
+                                                                  h->off_block_group) + pt[i].block_offset;
+            const int64_t nqb = (pt[i].numel + kBlock - 1) / kBlock;
+            for (int64_t k = 0; k < nqb; k++) {
+                const int64_t e = k * kBlock, r = e / M.cols, c = e % M.cols;
+                const int64_t want = g0 + (r / br) * nbc + c / bc;
+                if (bg[k] != want)
+                    return fail(QM_E_PLAN, "matrix %d: quantisation block %lld is in group %d, its %lld x %lld block is %lld",
+                                i, (long long)k, bg[k], (long long)br, (long long)bc, (long long)want);
+            }
+        }
         if (M.weight && !aligned(M.weight, 4)) return fail(QM_E_ALIGN, "matrix %d: weight misaligned", i);
         if (carrier && (M.cols % 32 || bc % 32))
             return fail(QM_E_SHAPE, "matrix %d: the MXFP8 carrier needs cols and block_cols multiples of 32", i);
@@ -1970,6 +1990,26 @@ qm_status check_step_plan(const void *host_plan, const qm_muon_matrix *mats, int
     }
     if (h->n_groups != g0) return fail(QM_E_PLAN, "plan has %d groups, expected %lld", h->n_groups, (long long)g0);
     *out = h;
+    return QM_OK;
+}
+
+// The full-step and block-step plans of muon_step must describe the same
+// tensors: the state of one step is the input of the next whichever plan
+// updates it.
+qm_status check_same_tensors(const void *plan_a, const void *plan_b) {
+    qm_status st;
+    const PlanHeader *ha = plan_header(plan_a, &st);
+    if (!ha) return st;
+    const PlanHeader *hb = plan_header(plan_b, &st);
+    if (!hb) return st;
+    if (ha->n_tensors != hb->n_tensors) return fail(QM_E_PLAN, "full and block plans differ in tensor count");
+    const PlanTensor *a = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(plan_a) + ha->off_tensors);
+    const PlanTensor *b = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(plan_b) + hb->off_tensors);
+    for (int32_t i = 0; i < ha->n_tensors; i++)
+        if (a[i].codes != b[i].codes || a[i].absmax != b[i].absmax || a[i].grad != b[i].grad ||
+            a[i].numel != b[i].numel || a[i].dtype != b[i].dtype || a[i].grad_cols != b[i].grad_cols ||
+            (a[i].grad_cols && a[i].grad_ld != b[i].grad_ld))
+            return fail(QM_E_PLAN, "tensor %d: the full and block plans point at different buffers", i);
     return QM_OK;
 }
 
@@ -1994,6 +2034,7 @@ size_t step_ws_total(const void *host_plan_full, const void *host_plan_block, co
     size_t need = step_ws_bytes(h, host_plan_full, mats, n_mats, true, precision, carrier);
     if (host_plan_block) {
         if (check_step_plan(host_plan_block, mats, n_mats, false, &h, carrier) != QM_OK) return 0;
+        if (check_same_tensors(host_plan_full, host_plan_block) != QM_OK) return 0;
         need = std::max(need, step_ws_bytes(h, host_plan_block, mats, n_mats, false, precision, carrier));
     }
     return need;
@@ -2078,10 +2119,13 @@ extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_
     if (st != QM_OK) return st;
     st = check_step_plan(hplan, mats, n_mats, full, &h, car);
     if (st != QM_OK) return st;
-    if (full && host_plan_block) {
+    if (host_plan_block) {
         const PlanHeader *hb = nullptr;
-        st = check_step_plan(host_plan_block, mats, n_mats, false, &hb, car);
-        if (st != QM_OK) return st;
+        if (full) {
+            st = check_step_plan(host_plan_block, mats, n_mats, false, &hb, car);
+            if (st != QM_OK) return st;
+        }
+        if ((st = check_same_tensors(host_plan_full, host_plan_block)) != QM_OK) return st;
     }
     const size_t need = step_ws_total(host_plan_full, host_plan_block, mats, n_mats, hp->precision, car);
     if (!ws || ws_bytes < need) return fail(QM_E_WORKSPACE, "workspace needs %zu bytes", need);

@@ -290,3 +290,140 @@ def test_ns_precisions_workspace_and_validation():
     for prec in (3, -1):
         assert LIB.ns_orthogonalize(x, L.QM_F32, 64, 256, 256, 1, 0, 5, 3.4445, -4.775, 2.0315, 1e-7, None, prec,
                                     ws, 1 << 40, None) == 1
+
+
+def _cpu_plan(rows, cols):
+    import torch
+    codes = torch.zeros(rows * cols, dtype=torch.int8)
+    absmax = torch.zeros((rows * cols + 255) // 256, dtype=torch.float32)
+    grad = torch.zeros(rows * cols, dtype=torch.bfloat16)
+    return q.Plan([(codes, absmax, grad)], [(0, 0, rows * cols, 0)], 1)
+
+
+@pytest.mark.parametrize("bad,exc", [
+    ("bf16", TypeError),          # a bf16 master weight: the C side writes rows x cols fp32
+    ("strided", ValueError),      # not contiguous
+    ("short", ValueError),        # fewer than rows x cols elements
+    ("device", ValueError),       # another device than the plan's
+])
+def test_muon_wrappers_reject_bad_weights(bad, exc):
+    """muon_step / muon_apply / the workspace query check every weight before
+    its address reaches the library (no call here gets that far)."""
+    import torch
+    rows, cols = 64, 256
+    plan = _cpu_plan(rows, cols)
+    w = {"bf16": torch.zeros((rows, cols), dtype=torch.bfloat16),
+         "strided": torch.zeros((rows, 2 * cols), dtype=torch.float32)[:, ::2],
+         "short": torch.zeros((rows, cols - 8), dtype=torch.float32),
+         "device": torch.zeros((rows, cols), dtype=torch.float32, device="meta")}[bad]
+    mats = [(rows, cols, rows, cols, w)]
+    hp = q.make_hparams(period=1)
+    with pytest.raises(exc):
+        q.muon_step(plan, None, mats, 1, hp, ws=torch.empty(256, dtype=torch.uint8))
+    with pytest.raises(exc):
+        q.muon_step_workspace_bytes(plan, None, mats, hparams=hp)
+    with pytest.raises(exc):
+        q.muon_apply(plan, mats, True, torch.zeros(1, dtype=torch.float32), hp, torch.empty(256, dtype=torch.uint8))
+
+
+def test_muon_apply_rejects_bad_inverse_norms():
+    import torch
+    plan = _cpu_plan(64, 256)
+    mats = [(64, 256, 64, 256, None)]
+    hp = q.make_hparams(period=1)
+    ws = torch.empty(256, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        q.muon_apply(plan, mats, True, torch.zeros(2, dtype=torch.float32), hp, ws)
+    with pytest.raises(TypeError):
+        q.muon_apply(plan, mats, True, torch.zeros(1, dtype=torch.float64), hp, ws)
+
+
+@pytest.mark.parametrize("bad", ["grad_strided", "grad_shape", "warm_shape", "warm_dtype", "weight_dtype",
+                                 "weight_numel"])
+def test_grasp_step_rejects_bad_arguments(bad):
+    import torch
+    rows, cols, rank = 128, 192, 8
+    st = q.GraspState(rows, cols, rank, device="cpu")
+    grad = torch.zeros((rows, cols), dtype=torch.float32)
+    warm = torch.zeros((cols, rank), dtype=torch.float32)
+    weight = None
+    if bad == "grad_strided":
+        grad = torch.zeros((rows, 2 * cols), dtype=torch.float32)[:, :cols]
+    elif bad == "grad_shape":
+        grad = torch.zeros((rows, cols + 64), dtype=torch.float32)
+    elif bad == "warm_shape":
+        warm = torch.zeros((rows, rank), dtype=torch.float32)
+    elif bad == "warm_dtype":
+        warm = torch.zeros((cols, rank), dtype=torch.bfloat16)
+    elif bad == "weight_dtype":
+        weight = torch.zeros((rows, cols), dtype=torch.bfloat16)
+    else:
+        weight = torch.zeros((rows, cols // 2), dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        q.grasp_step(st, grad, warm, weight=weight, ws=torch.empty(256, dtype=torch.uint8))
+
+
+def _step_call(hplan_full, hplan_block, mats_spec, step=1, call=True):
+    """(workspace bytes, muon_step status); call=False skips muon_step (a valid
+    request would go on to launch kernels)."""
+    mats = (L.MuonMatrix * len(mats_spec))()
+    for i, (r, c, br, bc) in enumerate(mats_spec):
+        mats[i] = L.MuonMatrix(r, c, br, bc, None)
+    h = q.make_hparams(period=2)
+    fake = ctypes.c_void_p(BASE)
+    ws = ctypes.c_void_p(BASE + (1 << 34))
+    vp = lambda b: ctypes.cast(b, ctypes.c_void_p) if b is not None else None
+    need = LIB.muon_step_workspace_bytes_ex(vp(hplan_full), vp(hplan_block), mats, len(mats_spec), ctypes.byref(h))
+    if not call:
+        return need, None
+    st = LIB.muon_step(vp(hplan_full), fake, vp(hplan_block), fake if hplan_block is not None else None, mats,
+                       len(mats_spec), step, ctypes.byref(h), ws, 1 << 40, None)
+    return need, st
+
+
+def test_block_plan_numbering_must_be_row_major():
+    """A 64 x 1024 matrix in four 64 x 256 blocks: the block plan must give
+    quantisation block k the group of its NS block in row-major block order.
+    The same groups numbered right to left are refused (each block would get
+    another block's norm)."""
+    rows, cols, bc = 64, 1024, 256
+    tens = _tensors([(rows * cols, L.QM_BF16)])
+    _, full = _encode(tens, _segs([(0, 0, rows * cols, 0)]), 1)
+    ok = [(0, r * cols + j * bc, bc, j) for r in range(rows) for j in range(4)]
+    rev = [(0, r * cols + j * bc, bc, 3 - j) for r in range(rows) for j in range(4)]
+    _, good = _encode(tens, _segs(ok), 4)
+    _, bad = _encode(tens, _segs(rev), 4)
+    need, _ = _step_call(full, good, [(rows, cols, rows, bc)], call=False)
+    assert need > 0, LIB.qm_last_error()
+    need, st = _step_call(full, bad, [(rows, cols, rows, bc)])
+    assert need == 0 and st == 8, LIB.qm_last_error()
+    assert "group" in LIB.qm_last_error().decode()
+
+
+@pytest.mark.parametrize("rows,cols,br,bc,groups", [
+    (4, 384, 4, 128, [0, 1, 2, 0, 1, 2]),     # 128-column blocks: quantisation blocks cross them
+    (8, 96, 4, 96, [0, 1, 1]),                # 4 x 96 = 384 elements per block: not whole blocks
+])
+def test_block_plan_straddling_quantisation_blocks_refused(rows, cols, br, bc, groups):
+    tens = _tensors([(rows * cols, L.QM_BF16)])
+    _, full = _encode(tens, _segs([(0, 0, rows * cols, 0)]), 1)
+    n = rows * cols
+    segs = [(0, 256 * k, min(256, n - 256 * k), g) for k, g in enumerate(groups)]
+    st0, blk = _encode(tens, _segs(segs), max(groups) + 1)
+    assert st0 == 0, LIB.qm_last_error()
+    need, st = _step_call(full, blk, [(rows, cols, br, bc)])
+    assert need == 0 and st == 4, LIB.qm_last_error()
+    assert "straddles" in LIB.qm_last_error().decode()
+
+
+def test_full_and_block_plans_must_share_tensors():
+    rows, cols, bc = 64, 1024, 256
+    tens = _tensors([(rows * cols, L.QM_BF16)])
+    _, full = _encode(tens, _segs([(0, 0, rows * cols, 0)]), 1)
+    other = _tensors([(rows * cols, L.QM_BF16)])
+    other[0].grad = other[0].grad + (1 << 28)       # the block plan points at another grad buffer
+    segs = [(0, r * cols + j * bc, bc, j) for r in range(rows) for j in range(4)]
+    _, blk = _encode(other, _segs(segs), 4)
+    for step in (1, 2):                             # a block step and a full step
+        need, st = _step_call(full, blk, [(rows, cols, rows, bc)], step)
+        assert need == 0 and st == 8, LIB.qm_last_error()
