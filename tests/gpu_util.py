@@ -6,6 +6,7 @@ import torch
 
 import oracle
 from harness import inputs as H
+from oracle import ns
 
 TORCH_TO_ORACLE = {torch.float32: oracle.F32, torch.bfloat16: oracle.BF16, torch.float16: oracle.F16}
 
@@ -95,3 +96,16 @@ def as_f64(t):
 # below 1e-4 on these inputs.
 NS_BF16_REL, NS_BF16_COS = 2e-2, 0.999
 NS_F32_REL, NS_F32_COS = 1e-4, 0.99999
+# fp32-operand NS whose output is stored in bf16 (the GRASP grads): rounding to
+# nearest bf16 moves every element by at most 2^-9 of its magnitude, so
+# ||bf16(O) - O||_F <= 2^-9 ||O||_F on top of the fp32 arithmetic's bound.
+NS_F32_BF16OUT_REL = NS_F32_REL + 2.0 ** -9
+
+
+def ns_whole(M, steps, coeffs, eps, inv_norm=None):
+    """fp64 NS_T(M) for every row: the oracle's spectral route (one Gram
+    product and one symmetric eigensolve; in exact arithmetic the same matrix
+    as the iteration, and pinned to it on the CPU).  Affordable at the full
+    sizes where running the iteration itself on the host would take minutes."""
+    M = np.asarray(M, dtype=np.float64)
+    return ns.spectral_rows(M, np.arange(M.shape[0]), steps, coeffs, eps, inv_norm)

@@ -14,10 +14,9 @@ import pytest
 import torch
 
 import quantized_momentum_newton_amd as q
-from gpu_util import NS_BF16_COS, NS_BF16_REL, as_f64, host, ns_parity, say
+from gpu_util import NS_BF16_COS, NS_BF16_REL, NS_F32_BF16OUT_REL, NS_F32_COS, as_f64, host, ns_parity, ns_whole, say
 from harness import inputs as H
 from oracle import grasp as OG
-from oracle import ns
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -148,7 +147,8 @@ def test_grasp_generic_mgs_path(rows, cols, k):
 @pytest.mark.parametrize("ns_precision", ["f32", "bf16x3"])
 def test_grasp_4096_full_size(ns_precision):
     """4096x4096, rank-8 spike of norm 10x the noise, mu = 0.95, 20 steps:
-    state checked on every step, NS on sampled rows at the last step."""
+    state checked on every step; NS of the last step, whole, within the
+    fp32-operand bound plus the rounding of O into the bf16 grad."""
     cfg = H.grasp_4096_shape()
     rows, cols, k, mu = cfg["rows"], cfg["cols"], cfg["rank"], cfg["mu"]
     spike = H.spike(rows, cols, k, DEV, 1005)
@@ -166,7 +166,7 @@ def test_grasp_4096_full_size(ns_precision):
         torch.cuda.synchronize()
         ref, M, P32, R32, _ = OG.grasp_step(prev, gh, mu, hw, 5, COEF, H.NS_EPS, with_ns=False)
         mism += compare_step(st, ref, M, P32, R32)
-    rows_s = np.sort(np.random.default_rng(7).choice(rows, 24, replace=False))
-    ref_rows = ns.spectral_rows(M.astype(np.float64), rows_s, 5, COEF, H.NS_EPS)
-    _within(as_f64(g)[rows_s], ref_rows, "O (sampled rows)")
+    rel, cos = ns_parity(as_f64(g), ns_whole(M, 5, COEF, H.NS_EPS))
+    say(f"   t20 O (whole, {ns_precision}): relF {rel:.3e} min cos {cos:.7f}")
+    assert rel <= NS_F32_BF16OUT_REL and cos >= NS_F32_COS, (rel, cos)
     say("code mismatches over 20 steps:", mism)

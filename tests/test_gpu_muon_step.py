@@ -12,9 +12,9 @@ import torch
 import oracle
 import quantized_momentum_newton_amd as q
 from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, assert_bits_equal, host, host_grad,
-                      ns_parity, say)
+                      ns_parity, ns_whole, say)
 from harness import inputs as H
-from oracle import muonbp, ns
+from oracle import muonbp
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -81,8 +81,8 @@ def test_reduced_muonbp_run_20_steps():
 
 
 def test_llama8b_layer_full_step():
-    """One full Muon step on the Llama-8B layer: state bit-exact, O and the
-    weight change on sampled rows of every matrix."""
+    """One full Muon step on the Llama-8B layer: state bit-exact; O and the
+    weight change of every matrix, whole, against the fp64 oracle."""
     tensors, segments, ng = H.llama8b_layer_layout()
     trip, mats, hin = [], [], []
     for i, (name, r, c) in enumerate(tensors):
@@ -103,24 +103,22 @@ def test_llama8b_layer_full_step():
     states, outs, S, inv, _ = oracle.update_normalize_groups(
         [(a, b) for a, b, _ in hin], [g for _, _, g in hin], [oracle.BF16] * 7, segments, ng,
         H.BETA, H.NS_EPS, write_normalized=False)
-    rng = np.random.default_rng(5)
     for i, (name, r, c) in enumerate(tensors):
         assert_bits_equal(host(trip[i][0]), states[i][0], f"codes[{name}]")
         assert_bits_equal(host(trip[i][1]), states[i][1], f"absmax[{name}]")
         m = oracle.widen(outs[i], oracle.BF16).astype(np.float64).reshape(r, c)
-        rows = np.sort(rng.choice(r, 24, replace=False))
-        ref = ns.spectral_rows(m, rows, 5, COEF, H.NS_EPS, inv_norm=float(inv[i]))
-        O = as_f64(trip[i][2]).reshape(r, c)[rows]
-        _within(O, ref, f"O[{name}]")
+        ref = ns_whole(m, 5, COEF, H.NS_EPS, inv_norm=float(inv[i]))
+        _within(as_f64(trip[i][2]).reshape(r, c), ref, f"O[{name}]")
         s = 0.2 * math.sqrt(max(r, c))
-        dW = host(mats[i][4])[rows].astype(np.float64) - W0[i][rows]
+        dW = host(mats[i][4]).astype(np.float64) - W0[i]
         _within(dW, -0.02 * s * ref, f"dW[{name}]")
 
 
-def test_muonbp_full_size_state_and_sampled_ns():
+def test_muonbp_full_size_state_and_ns():
     """4096x14336, 8 column blocks, P = 5, 20 steps: the q8 state is
-    bit-exact on all 20 steps (it does not depend on NS or W); NS is checked
-    on sampled rows at a block step (4) and a full step (5)."""
+    bit-exact on all 20 steps (it does not depend on NS or W); O and the
+    weight change are compared whole at a block step (t = 4: all 8 blocks)
+    and at a full step (t = 5)."""
     cfg = H.muonbp_4096x14336_shape()
     r, c, br, bc = cfg["rows"], cfg["cols"], cfg["block_rows"], cfg["block_cols"]
     codes, absmax = H.prior_state(r * c, DEV, 1004, 0)
@@ -130,35 +128,43 @@ def test_muonbp_full_size_state_and_sampled_ns():
     mats = [(r, c, br, bc, w)]
     full, block = _plans(trip, mats)
     params = q.make_hparams(lr_full=cfg["lr_full"], lr_block=cfg["lr_block"],
-                            rms_scale=cfg["rms_scale"], period=cfg["period"])
+                            rms_scale=cfg["rms_scale"], period=cfg["period"], weight_decay=cfg["weight_decay"])
     hc, ha = host(codes), host(absmax)
     bid = muonbp.block_group_ids(r, c, br, bc)
     fid = np.zeros(bid.size, np.int32)
-    rows = np.sort(np.random.default_rng(6).choice(r, 16, replace=False))
     for t in range(1, cfg["steps"] + 1):
         g.copy_(H.grad((r, c), torch.bfloat16, DEV, 1004, 0, t).reshape(-1))
         torch.cuda.synchronize()
         gh = host_grad(g)
+        check_ns = t in (4, 5)
+        if check_ns:
+            W0 = as_f64(w)
         say("muonbp step", t)
         q.muon_step(full, block, mats, t, params)
         torch.cuda.synchronize()
         hc, ha, m, bs = oracle.q8_update(hc, ha, gh, H.BETA, oracle.BF16)
         assert_bits_equal(host(codes), hc, f"t{t} codes")
         assert_bits_equal(host(absmax), ha, f"t{t} absmax")
-        if t in (4, 5):
+        if check_ns:
             is_full = t % 5 == 0
             gid = fid if is_full else bid
             ngr = 1 if is_full else 8
             inv = oracle.group_inv_norm(oracle.group_sums([bs], [gid], ngr), H.NS_EPS)
             mf = oracle.widen(m, oracle.BF16).astype(np.float64).reshape(r, c)
             O = as_f64(g).reshape(r, c)
+            dW = as_f64(w) - W0
             if is_full:
-                _within(O[rows], ns.spectral_rows(mf, rows, 5, COEF, H.NS_EPS, float(inv[0])), "full O")
+                ref = ns_whole(mf, 5, COEF, H.NS_EPS, float(inv[0]))
+                s, lr = muonbp.rms_factor(r, c, cfg["rms_scale"]), cfg["lr_full"]
+                _within(O, ref, "full O")
+                _within(dW, -lr * (s * ref + cfg["weight_decay"] * W0), "full dW")
             else:
+                s, lr = muonbp.rms_factor(br, bc, cfg["rms_scale"]), cfg["lr_block"]
                 for j in range(8):
-                    ref = ns.spectral_rows(mf[:, bc * j:bc * (j + 1)], rows, 5, COEF, H.NS_EPS,
-                                           float(inv[j]))
-                    _within(O[rows, bc * j:bc * (j + 1)], ref, f"block {j} O")
+                    sl = slice(bc * j, bc * (j + 1))
+                    ref = ns_whole(mf[:, sl], 5, COEF, H.NS_EPS, float(inv[j]))
+                    _within(O[:, sl], ref, f"block {j} O")
+                    _within(dW[:, sl], -lr * (s * ref + cfg["weight_decay"] * W0[:, sl]), f"block {j} dW")
 
 
 def test_muon_step_on_strided_grad_views():

@@ -3,14 +3,14 @@
 bf16 mode: relative Frobenius error <= 2e-2 and every row's cosine >= 0.999
 (the workload's stated bound); f32 and bf16x3 modes (fp32 operands; fp32
 MFMAs, or bf16 MFMAs on a hi + lo split): <= 1e-4 and >= 0.99999.  At full
-size the oracle runs through its spectral route on sampled rows.
+size the oracle runs through its spectral route, over every row.
 """
 import numpy as np
 import pytest
 import torch
 
 import quantized_momentum_newton_amd as q
-from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, ns_parity, say)
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, ns_parity, ns_whole, say)
 from harness import inputs as H
 from oracle import ns
 
@@ -103,22 +103,16 @@ def test_blocked_small():
     _check(as_f64(x), ns.ns_blocked(x0, 256, 128, 5, COEF, H.NS_EPS), "bf16")
 
 
-def _sample_rows(n, k, seed):
-    r = np.random.default_rng(seed).choice(n, size=k, replace=False)
-    return np.sort(np.concatenate([[0, n - 1], r]))
-
-
 @pytest.mark.parametrize("name,shape", [("q", (4096, 4096)), ("k", (1024, 4096)),
                                         ("gate", (14336, 4096)), ("down", (4096, 14336))])
-def test_llama8b_shapes_full_size_sampled(name, shape):
+def test_llama8b_shapes_full_size(name, shape):
+    """The Llama-8B layer's shapes, whole output against the fp64 oracle."""
     say("full-size NS", name, shape)
     x = H.grad(shape, torch.bfloat16, DEV, 1003, name == "gate", shape[0])
     x0 = as_f64(x)
     q.ns_orthogonalize(x, 5, COEF, H.NS_EPS)
     torch.cuda.synchronize()
-    rows = _sample_rows(shape[0], 64, 3)
-    ref = ns.spectral_rows(x0, rows, 5, COEF, H.NS_EPS)
-    _check(as_f64(x)[rows], ref, "bf16")
+    _check(as_f64(x), ns_whole(x0, 5, COEF, H.NS_EPS), "bf16")
 
 
 @pytest.mark.parametrize("precision", ["f32", "bf16x3"])
@@ -126,30 +120,28 @@ def test_llama8b_shapes_full_size_sampled(name, shape):
 def test_f32_mid_and_small_tile_runs(shape, precision):
     """fp32-operand runs on the sizes whose products take 128 x 128 or 64 x 64
     tiles (3000 x 3300 is padded to 3072 x 3328; the 4096-square Gram takes
-    64 x 64, its X = aX + BX 128 x 128); sampled rows against the exact
+    64 x 64, its X = aX + BX 128 x 128); whole output against the exact
     iterate."""
     say("fp32-operand NS", shape, precision)
     x = H.grad(shape, torch.float32, DEV, 2101, *shape)
     x0 = as_f64(x)
     q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
     torch.cuda.synchronize()
-    rows = _sample_rows(shape[0], 32, 5)
-    ref = ns.spectral_rows(x0, rows, 5, COEF, H.NS_EPS)
-    _check(as_f64(x)[rows], ref, precision)
+    _check(as_f64(x), ns_whole(x0, 5, COEF, H.NS_EPS), precision)
 
 
-def test_blocked_muonbp_shape_sampled():
-    """4096x14336 cut into 8 column blocks of 4096x1792, one batched NS."""
+def test_blocked_muonbp_shape():
+    """4096x14336 cut into 8 column blocks of 4096x1792, one batched NS; every
+    block whole against its own fp64 NS."""
     x = H.grad((4096, 14336), torch.bfloat16, DEV, 1004)
     x0 = as_f64(x)
     q.ns_orthogonalize_blocked(x, 4096, 1792, 5, COEF, H.NS_EPS)
     torch.cuda.synchronize()
     out = as_f64(x)
-    rows = _sample_rows(4096, 32, 4)
     for j in range(8):
-        blk = x0[:, 1792 * j:1792 * (j + 1)]
-        ref = ns.spectral_rows(blk, rows, 5, COEF, H.NS_EPS)
-        _check(out[rows, 1792 * j:1792 * (j + 1)], ref, "bf16")
+        say("  block", j)
+        ref = ns_whole(x0[:, 1792 * j:1792 * (j + 1)], 5, COEF, H.NS_EPS)
+        _check(out[:, 1792 * j:1792 * (j + 1)], ref, "bf16")
 
 
 @pytest.mark.parametrize("precision,dtype", [("bf16", torch.bfloat16), ("f32", torch.float32),

@@ -126,9 +126,11 @@ def test_interleaved_qkv_segments():
     assert plan.n_blocks == 57344 and len(segs) == 3072
 
 
-def test_layerset28_full_size_sampled():
-    """All 140 tensors of the 28-layer set in the benchmark's launch; layers 0
-    and 27 checked element by element against the oracle."""
+def test_layerset28_full_size():
+    """All 140 tensors of the 28-layer set in the benchmark's launch: every
+    tensor's codes, absmax and normalised grad bit for bit, every one of the
+    196 group sums (rtol 1e-12) and inverse norms (bit for bit) against the
+    oracle."""
     tensors, segments, ng = H.layerset28_layout()
     shapes = [(r, c) for (_, r, c) in tensors]
     qs = Q8Set.__new__(Q8Set)
@@ -140,11 +142,11 @@ def test_layerset28_full_size_sampled():
         qs.codes.append(c)
         qs.absmax.append(a)
         qs.grads.append(g)
-    sample = list(range(5)) + list(range(135, 140))
     torch.cuda.synchronize()
-    qs.snapshot(sample)
-    say("28-layer set, 140 tensors, checking", sample)
-    run_and_compare(qs, segments, ng, H.BETA, H.NS_EPS, check_idx=sample)
+    qs.snapshot()
+    say("28-layer set, 140 tensors,", ng, "groups")
+    assert len(shapes) == 140 and ng == 196
+    run_and_compare(qs, segments, ng, H.BETA, H.NS_EPS)
 
 
 def test_llama8b_layer_update_full():
