@@ -200,6 +200,28 @@ QM_API qm_status qmuon_update_normalize_groups_ex(const void *host_plan,
                                            double *group_sumsq, void *ws,
                                            size_t ws_bytes, qm_stream_t stream);
 
+/* qmuon_update_normalize_groups without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The workspace is a fixed
+ * QM_NOALLOC_SCRATCH_BYTES array in device memory, one per GPU, set up on
+ * the first call on that GPU and held until the process ends; the call
+ * itself allocates nothing.  Every call on one GPU uses the same array:
+ * calls that overlap on one GPU (two streams, or two host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs to start at
+ * zero; a call writes every byte it reads.  Semantics and outputs as
+ * qmuon_update_normalize_groups with nearest rounding.
+ * Errors: as qmuon_update_normalize_groups; QM_E_WORKSPACE when the plan
+ * needs more than QM_NOALLOC_SCRATCH_BYTES (qm_update_workspace_bytes tells:
+ * about 8 bytes per 256-element block, so up to about 2e9 elements). */
+#define QM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+QM_API qm_status qmuon_update_normalize_groups_noalloc(const void *host_plan,
+                                                       const void *dev_plan,
+                                                       float beta, float eps,
+                                                       int32_t write_normalized,
+                                                       float *group_inv_norm,
+                                                       double *group_sumsq,
+                                                       qm_stream_t stream);
+
 /* The update emitting a row-wise MXFP8 carrier of m instead of writing m
  * to the grads ("Quantized Muon Momentum", section "Wave18B MXFP8 Carrier
  * Probe": uint8 E4M3 data, uint8 E8M0 inverse scales per 32 elements of a

@@ -9,6 +9,9 @@ Entry points (same names as the C ABI in include/qmuon.h):
   Plan(...)                        qm_plan_encode + one host-to-device copy
   qmuon_update_multi               q8 momentum update, many tensors, one launch
   qmuon_update_normalize_groups    update + grouped Frobenius normalisation
+  qmuon_update_normalize_groups_noalloc
+                                   the same without a workspace (fixed per-GPU
+                                   scratch; for callers that cannot allocate)
   MXCarrier, qmuon_update_mxfp8_carrier
                                    update emitting the MXFP8 carrier of m
   ns_orthogonalize_mxfp8           Newton-Schulz of a carrier-held matrix
@@ -202,6 +205,19 @@ def qmuon_update_normalize_groups(plan, beta, eps, write_normalized=True, group_
         _check(_LIB.qmuon_update_normalize_groups_ex(
             plan.hptr, plan.dptr, beta, eps, int(write_normalized), _round_opts(rounding, seed, offset),
             _ptr(group_inv_norm), _ptr(group_sumsq), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def qmuon_update_normalize_groups_noalloc(plan, beta, eps, write_normalized=True, group_inv_norm=None,
+                                          group_sumsq=None, stream=None):
+    """qmuon_update_normalize_groups with the library's fixed per-GPU scratch
+    instead of a workspace (the call allocates nothing).  Calls that overlap
+    on one GPU race: order them.  Plans needing more than
+    QM_NOALLOC_SCRATCH_BYTES of workspace are refused."""
+    for t, dt, n in ((group_inv_norm, torch.float32, plan.n_groups), (group_sumsq, torch.float64, plan.n_groups)):
+        if t is not None:
+            _require(t, "group output", dt, plan.device, numel=n)
+    _check(_LIB.qmuon_update_normalize_groups_noalloc(plan.hptr, plan.dptr, beta, eps, int(write_normalized),
+                                                      _ptr(group_inv_norm), _ptr(group_sumsq), _stream(stream)))
 
 
 class MXCarrier:

@@ -15,6 +15,7 @@ STATUS_NAMES = {0: "QM_OK", 1: "QM_E_ARG", 2: "QM_E_ALIGN", 3: "QM_E_DTYPE",
                 7: "QM_E_UNSUPPORTED", 8: "QM_E_PLAN"}
 QM_F32, QM_BF16, QM_F16 = 0, 1, 2
 QM_NS_BF16, QM_NS_F32, QM_NS_BF16X3 = 0, 1, 2
+QM_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 c_void_p = ctypes.c_void_p
 c_i32 = ctypes.c_int32
@@ -69,6 +70,8 @@ SIGNATURES = {
                                               c_void_p, c_void_p, c_void_p, c_size, c_void_p]),
     "qmuon_update_multi_ex": (c_i32, [c_void_p, c_void_p, c_f32, ctypes.POINTER(RoundOpts), c_void_p,
                                       c_void_p]),
+    "qmuon_update_normalize_groups_noalloc": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_i32,
+                                                       c_void_p, c_void_p, c_void_p]),
     "qmuon_update_normalize_groups_ex": (c_i32, [c_void_p, c_void_p, c_f32, c_f32, c_i32,
                                                  ctypes.POINTER(RoundOpts), c_void_p, c_void_p,
                                                  c_void_p, c_size, c_void_p]),

@@ -19,6 +19,8 @@
 // lane and 4 quarters, one block per quarter.  Tasks of all tensors form one
 // grid-stride index space, so one launch covers the whole tensor list.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -758,6 +760,61 @@ qm_status update_carrier(const void *host_plan, const void *dev_plan, float beta
 }
 
 }  // namespace
+
+// ---------------------------------------------------- no-allocation variant
+//
+// qmuon_update_normalize_groups for callers that cannot allocate: its
+// workspace (per-block fp64 sums, chunk partials, group sums, inverse norms;
+// every byte written before it is read in a call, so nothing is cleared) is
+// a fixed array in device memory, one per GPU, held until the process ends.
+// In host code `scratch` only names the array; its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static_assert(QM_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[QM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kScratchBytes = QM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices] = {};
+
+qm_status scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(QM_E_HIP, "no current device");
+    if (dev >= kMaxScratchDevices) return fail(QM_E_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return fail(QM_E_HIP, "scratch address: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return QM_OK;
+}
+
+}  // namespace
+
+extern "C" qm_status qmuon_update_normalize_groups_noalloc(const void *host_plan, const void *dev_plan, float beta,
+                                                           float eps, int32_t write_normalized,
+                                                           float *group_inv_norm, double *group_sumsq,
+                                                           qm_stream_t stream) {
+    clear_error();
+    const PlanHeader *h = nullptr;
+    qm_status st = validate_update(host_plan, dev_plan, beta, &h);
+    if (st != QM_OK) return st;
+    const size_t need = qm_update_workspace_bytes(host_plan);
+    if (need > kScratchBytes)
+        return fail(QM_E_WORKSPACE, "plan needs %zu bytes of workspace, above the %zu-byte static scratch", need,
+                    kScratchBytes);
+    if (!(eps >= 0.0f) || isinf(eps)) return fail(QM_E_ARG, "eps must be finite and >= 0");
+    if (write_normalized != 0 && write_normalized != 1) return fail(QM_E_ARG, "write_normalized must be 0 or 1");
+    if (group_inv_norm && !aligned(group_inv_norm, 4)) return fail(QM_E_ALIGN, "group_inv_norm alignment");
+    if (group_sumsq && !aligned(group_sumsq, 8)) return fail(QM_E_ALIGN, "group_sumsq alignment");
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != QM_OK) return st;
+    return run_update_normalize(h, dev_plan, beta, eps, write_normalized != 0, group_inv_norm, group_sumsq, ws,
+                                nullptr, static_cast<hipStream_t>(stream));
+}
 
 extern "C" qm_status qmuon_update_mxfp8_carrier(const void *host_plan, const void *dev_plan, float beta, float eps,
                                                 uint8_t *rowwise_data, uint8_t *rowwise_scale_inv, float *inv_norm,
