@@ -26,6 +26,18 @@ times the CPU oracle on a bounded sample of the same workload.
 E8M0 scales, 5.0625 B/element, and the NS prologue decodes them); the update
 / NS split then comes from the per-kernel timer.
 
+The default run (llama8b without --carrier, --extras on) also measures the
+other three spec workloads, each in its own timed region after the
+headline's buffers are freed, and adds them to the same JSON line:
+  layerset28: the 28-layer 2048-hidden set, grouped update + normalisation
+              (10.03 B/element), GB/s and fraction of HBM peak;
+  muonbp:     4096x14336 in 8 column blocks, P = 5, steps 1..20: ms per step,
+              NS TFLOP/s (symmetric FLOPs of all 20 steps over the NS-phase
+              event time) and fraction of bf16 peak, the dominant kernel's
+              live roofline;
+  grasp:      GRASP 4096x4096 rank 8: steps/s, state-path GB/s, f32 NS
+              TFLOP/s and fraction of the fp32 MFMA peak.
+
 Other workloads (not the headline): --workload layerset28 (the 28-layer
 2048-hidden set, grouped update + normalisation only), --workload muonbp
 (4096x14336, 8 column blocks, P = 5), --workload grasp (GRASP 4096x4096,
@@ -60,6 +72,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b",
                     choices=["llama8b", "layerset28", "muonbp", "grasp", "fp32_256x512"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default run: skip the layerset28 / muonbp / grasp sub-results")
     ap.add_argument("--rounding", default="nearest", choices=["nearest", "stochastic"],
                     help="requantisation rounding of the update (the headline uses nearest)")
     ap.add_argument("--carrier", action="store_true",
@@ -254,28 +268,166 @@ def bench_small(args, q, H, torch):
                        "ns_precision": args.ns_precision}}
 
 
+def timed_steps(args, torch, q, step, n_events):
+    """Warm-up steps, then args.steps timed steps with n_events HIP events per
+    step (recorded on torch's current stream, which the library launches on)
+    and the library's per-kernel timer on.  step(i, events): i counts from 1
+    over warm-up and timed steps.  Returns (per-step event lists, per-class
+    (ms, launches), total ms)."""
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    for i in range(1, args.warmup + 1):
+        step(i, mk())
+    evs = [mk() for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    q.timing_enable(True)
+    start.record()
+    for k in range(args.steps):
+        step(args.warmup + 1 + k, evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    q.timing_enable(False)
+    return evs, {k: q.timing_read(k) for k in q.KERNEL_CLASSES}, start.elapsed_time(stop)
+
+
+def extra_layerset28(args, q, H, torch):
+    """28-layer set: one grouped update + normalisation per step (write-back of
+    the normalised grads), 10.03 B/element."""
+    tensors, segments, ng = H.layerset28_layout()
+    trip, numel = [], 0
+    for i, (_, r, c) in enumerate(tensors):
+        codes, absmax = H.prior_state(r * c, "cuda", 1002, i)
+        g = H.grad((r, c), torch.bfloat16, "cuda", 1002, i, outlier_frac=0.01).reshape(-1)
+        trip.append((codes, absmax, g))
+        numel += r * c
+    plan = q.Plan(trip, segments, ng)
+    ws = plan.workspace()
+    inv = torch.empty(ng, dtype=torch.float32, device="cuda")
+
+    def step(i, ev):
+        ev[0].record()
+        q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv, ws=ws)
+        ev[1].record()
+
+    evs, pc, total = timed_steps(args, torch, q, step, 2)
+    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    gbs = numel * (BYTES_PER_ELEM_UPDATE + BYTES_PER_ELEM_SCALE) / (ms * 1e-3) / 1e9
+    upd_ms, n = pc["q8_update"]
+    rl = roofline("hbm", numel * BYTES_PER_ELEM_UPDATE, upd_ms / n, None)
+    rl["kernel"] = "q8_update"
+    return {"value": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_per_step": round(ms, 4),
+            "config": {"workload": "layerset28_grouped_update_normalize", "tensors": len(tensors), "groups": ng,
+                       "elements": numel, "grad_dtype": "bf16", "state": "int8"},
+            "roofline": rl,
+            "kernels": {k: round(v[0] / v[1], 4) for k, v in pc.items() if v[1]}}
+
+
+def extra_muonbp(args, q, H, torch):
+    """MuonBP 4096x14336, 8 column blocks of 4096x1792, P = 5: the update with
+    the step's plan, then NS + weight apply (muon_step's two halves, so events
+    time the NS phase).  Timed steps are numbered 1.. after the warm-up, so a
+    20-step region holds 16 block steps and 4 full steps."""
+    cfg = H.muonbp_4096x14336_shape()
+    r, c, br, bc = cfg["rows"], cfg["cols"], cfg["block_rows"], cfg["block_cols"]
+    codes, absmax = H.prior_state(r * c, "cuda", 1004, 0)
+    g = H.grad((r, c), torch.bfloat16, "cuda", 1004, 0).reshape(-1)
+    w = H.weights((r, c), "cuda", 1004, 0)
+    trip, mats = [(codes, absmax, g)], [(r, c, br, bc, w)]
+    full = q.Plan(trip, [(0, 0, r * c, 0)], 1)
+    segs, ngb = H.blocked_segments(r, c, br, bc)
+    blk = q.Plan(trip, segs, ngb)
+    hp = q.make_hparams(beta=H.BETA, eps=H.NS_EPS, coeffs=H.NS_COEFFS, lr_full=cfg["lr_full"],
+                        lr_block=cfg["lr_block"], rms_scale=cfg["rms_scale"], ns_steps=H.NS_STEPS,
+                        period=cfg["period"])
+    ws = torch.empty(q.muon_step_workspace_bytes(full, blk, mats, hparams=hp), dtype=torch.uint8, device="cuda")
+    ws_u = torch.empty(max(full.workspace_bytes(), blk.workspace_bytes()), dtype=torch.uint8, device="cuda")
+    inv = {True: torch.empty(1, dtype=torch.float32, device="cuda"),
+           False: torch.empty(ngb, dtype=torch.float32, device="cuda")}
+    period = cfg["period"]
+    kinds = []
+
+    def step(i, ev):
+        t = i if i <= args.warmup else i - args.warmup      # timed steps restart at t = 1
+        is_full = t % period == 0
+        p = full if is_full else blk
+        ev[0].record()
+        q.qmuon_update_normalize_groups(p, H.BETA, H.NS_EPS, False, group_inv_norm=inv[is_full], ws=ws_u)
+        ev[1].record()
+        q.muon_apply(p, mats, is_full, inv[is_full], hp, ws)
+        ev[2].record()
+        if i > args.warmup:
+            kinds.append(is_full)
+
+    evs, pc, total = timed_steps(args, torch, q, step, 3)
+    ns_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    m_b, n_b = min(br, bc), max(br, bc)
+    m_f, n_f = min(r, c), max(r, c)
+    nblk = (r // br) * (c // bc)
+    fl = sum(ns_sym_flops(r, c, H.NS_STEPS) if f else nblk * ns_sym_flops(br, bc, H.NS_STEPS) for f in kinds)
+    # algorithmic work of every launch of each product class over the region
+    n_full = sum(kinds)
+    n_blk = len(kinds) - n_full
+    T = H.NS_STEPS
+    work = {"ns_gram": T * (n_full * m_f * (m_f + 1) * n_f + n_blk * nblk * m_b * (m_b + 1) * n_b),
+            "ns_poly": T * (n_full * m_f * m_f * (m_f + 1) + n_blk * nblk * m_b * m_b * (m_b + 1)),
+            "ns_xupdate": T * (n_full * 2 * m_f * m_f * n_f + n_blk * nblk * 2 * m_b * m_b * n_b)}
+    dom = max(work, key=lambda k: pc[k][0])
+    rl = roofline("mfma", work[dom], pc[dom][0], None)   # all launches: total work over total time
+    rl["kernel"] = dom
+    tfl = fl / (ns_ms * 1e-3) / 1e12
+    return {"value": round(1000.0 * len(step_ms) / sum(step_ms), 3), "unit": "steps/s",
+            "ms_per_step": round(sum(step_ms) / len(step_ms), 4), "per_step_ms": percentiles(step_ms),
+            "ns_tflops": round(tfl, 2), "ns_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "ns_ms_total": round(ns_ms, 3), "ns_flops_total": fl, "full_steps": n_full, "block_steps": n_blk,
+            "config": {"workload": "muonbp_4096x14336_P5", "blocks": nblk, "block_shape": [br, bc],
+                       "ns_steps": T, "ns_precision": "bf16"},
+            "roofline": rl,
+            "kernels": {k: {"ms": round(v[0], 3), "launches": v[1]} for k, v in pc.items() if v[1]}}
+
+
+def extra_grasp(args, q, H, torch):
+    """GRASP 4096x4096 rank 8 with the fp32-MFMA NS (the bench_grasp line)."""
+    a = argparse.Namespace(**vars(args))
+    a.ns_precision = "f32"
+    r = bench_grasp(a, q, H, torch)
+    cfg = r["config"]
+    return {"value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"],
+            "per_step_ms": r["per_step_ms"], "state_gbs": cfg["state_gbs"], "ns_tflops": cfg["ns_tflops"],
+            "ns_frac_of_f32_peak": cfg["ns_frac_of_peak"], "ns_peak_tflops": cfg["ns_peak_tflops"],
+            "config": {"workload": cfg["workload"], "ns_steps": cfg["ns_steps"], "ns_precision": "f32"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    import torch
+    import quantized_momentum_newton_amd as q
+    from harness import inputs as H
+    torch.cuda.init()
     if args.workload in ("grasp", "fp32_256x512"):
-        import torch
-        import quantized_momentum_newton_amd as q
-        from harness import inputs as H
-        torch.cuda.init()
         fn = bench_grasp if args.workload == "grasp" else bench_small
         out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
         out.update(fn(args, q, H, torch))
         print(json.dumps(out), flush=True)
         return
-    import torch
-    import quantized_momentum_newton_amd as q
-    from harness import inputs as H
+    out = bench_layer(args, q, H, torch)
+    if args.workload == "llama8b" and not args.carrier and not args.no_extras:
+        # the other north-star workloads, each in its own timed region
+        for name, fn in (("layerset28", extra_layerset28), ("muonbp", extra_muonbp), ("grasp", extra_grasp)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            out[name] = fn(args, q, H, torch)
+    print(json.dumps(out), flush=True)
+
+
+def bench_layer(args, q, H, torch):
+    """The llama8b / layerset28 / muonbp workloads as the headline line."""
     dev = "cuda"
-    torch.cuda.init()
 
     if args.workload == "llama8b":
         tensors, segments, ng = H.llama8b_layer_layout()
@@ -396,7 +548,7 @@ def main():
                        "gbs": round(numel * {"q8_update": BYTES_PER_ELEM_UPDATE, "q8_scale": BYTES_PER_ELEM_SCALE}
                                     .get(k, 0.0) / (ms / n * 1e-3) / 1e9, 1)}
                    for k, (ms, n) in per_class.items() if n}
-        out.update({"value": round(gbs, 2), "unit": "GB/s", "dtype": "f32",
+        out.update({"value": round(gbs, 2), "unit": "GB/s", "dtype": "bf16",
                     "config": {"workload": "layerset28_grouped_update_normalize", "tensors": len(tensors),
                                "groups": ng, "elements": numel, "grad_dtype": "bf16", "state": "int8"},
                     "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
@@ -433,7 +585,7 @@ def main():
                                "handoff": "mxfp8_carrier" if args.carrier else "bf16_grad"}})
     if host_q is not None:
         out["cpu_baseline"] = cpu_baseline(host_q, host_ns, H.NS_STEPS)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":
