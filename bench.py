@@ -42,7 +42,9 @@ Other workloads (not the headline): --workload layerset28 (the 28-layer
 2048-hidden set, grouped update + normalisation only), --workload muonbp
 (4096x14336, 8 column blocks, P = 5), --workload grasp (GRASP 4096x4096,
 rank 8: steps/s, state-path GB/s and f32 NS TFLOP/s against the fp32 peak),
---workload fp32_256x512 (one small fp32 matrix, latency in us per step).
+--workload fp32_256x512 (one small fp32 matrix, latency in us per step),
+--workload hbm_stream (the library's stream copy at the update's byte counts:
+the achievable HBM rate of a 50/50 read/write stream).
 per_step_ms gives the 10/50/90th percentiles of the per-step event times.
 """
 import argparse
@@ -70,7 +72,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b",
-                    choices=["llama8b", "layerset28", "muonbp", "grasp", "fp32_256x512"])
+                    choices=["llama8b", "layerset28", "muonbp", "grasp", "fp32_256x512", "hbm_stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="default run: skip the layerset28 / muonbp / grasp sub-results")
@@ -268,6 +270,37 @@ def bench_small(args, q, H, torch):
                        "ns_precision": args.ns_precision}}
 
 
+def bench_hbm_stream(args, q, H, torch):
+    """The achievable HBM rate for a 50/50 read/write stream: the library's
+    stream copy (the q8 update's access pattern) over as many bytes as the
+    q8 update moves on the Llama-8B layer (read + write = 6.03125 B/element x
+    218M elements) and on the 28-layer set (x 1.32G elements)."""
+    out = {}
+    for name, numel in (("llama8b_layer_update_bytes", 218103808), ("layerset28_update_bytes", 1321205760)):
+        n = int(numel * BYTES_PER_ELEM_UPDATE / 2) // 4096 * 4096      # bytes read = bytes written
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        evs = []
+        for t in range(args.warmup + args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            q.hbm_stream_copy(src, dst)
+            e[1].record()
+            if t >= args.warmup:
+                evs.append(e)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in evs]
+        avg = sum(ms) / len(ms)
+        out[name] = {"bytes_per_copy": 2 * n, "ms": round(avg, 4), "gbs": round(2 * n / (avg * 1e-3) / 1e9, 1),
+                     "per_copy_ms": percentiles(ms)}
+        del src, dst
+        torch.cuda.empty_cache()
+    head = out["llama8b_layer_update_bytes"]
+    return {"metric": METRIC, "value": head["gbs"], "unit": "GB/s", "dtype": "u8",
+            "ms_per_step": head["ms"], "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
+            "config": {"workload": "hbm_stream_copy", "sizes": out}}
+
+
 def timed_steps(args, torch, q, step, n_events):
     """Warm-up steps, then args.steps timed steps with n_events HIP events per
     step (recorded on torch's current stream, which the library launches on)
@@ -408,8 +441,8 @@ def main():
     import quantized_momentum_newton_amd as q
     from harness import inputs as H
     torch.cuda.init()
-    if args.workload in ("grasp", "fp32_256x512"):
-        fn = bench_grasp if args.workload == "grasp" else bench_small
+    if args.workload in ("grasp", "fp32_256x512", "hbm_stream"):
+        fn = {"grasp": bench_grasp, "fp32_256x512": bench_small, "hbm_stream": bench_hbm_stream}[args.workload]
         out = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
         out.update(fn(args, q, H, torch))

@@ -484,6 +484,16 @@ QM_API qm_status qm_timing_enable(int32_t on);
 QM_API qm_status qm_timing_read(int32_t kernel_class, double *total_ms,
                                 int64_t *launches);
 
+/* Measurement aid: copy `bytes` from src to dst (device pointers, 16-byte
+ * aligned, bytes a multiple of 16, not overlapping) with the q8 update
+ * kernel's access pattern (16-byte non-temporal loads and stores, each wave
+ * instruction one contiguous 1 KiB span).  It gives the achievable HBM rate
+ * for a 50/50 read/write stream, the ceiling the update kernels are measured
+ * against, and a kernel of exactly known traffic to calibrate HBM byte
+ * counters.  Errors: QM_E_ARG (null, overlap), QM_E_ALIGN, QM_E_HIP. */
+QM_API qm_status qm_hbm_stream_copy(const void *src, void *dst, size_t bytes,
+                                    qm_stream_t stream);
+
 /* ------------------------------------------------------------------------ */
 QM_API const char *qm_status_string(qm_status s);
 QM_API const char *qm_last_error(void);

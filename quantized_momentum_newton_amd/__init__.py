@@ -379,6 +379,18 @@ def muon_apply(plan, mats, full, inv_norm, hparams, ws, stream=None):
                            ctypes.byref(hparams), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def hbm_stream_copy(src, dst, stream=None):
+    """Measurement aid: copy src into dst (same byte size, contiguous, 16-byte
+    aligned) with the update kernels' access pattern."""
+    for t in (src, dst):
+        if not t.is_contiguous():
+            raise ValueError("stream copy operands must be contiguous")
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("stream copy operands differ in size")
+    _check(_LIB.qm_hbm_stream_copy(_ptr(src), _ptr(dst), n, _stream(stream)))
+
+
 GRASP_GRID = 64
 
 

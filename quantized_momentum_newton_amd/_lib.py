@@ -102,6 +102,7 @@ SIGNATURES = {
                            c_void_p, c_size, c_void_p]),
     "qm_timing_enable": (c_i32, [c_i32]),
     "qm_timing_read": (c_i32, [c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
+    "qm_hbm_stream_copy": (c_i32, [c_void_p, c_void_p, c_size, c_void_p]),
     "qm_status_string": (ctypes.c_char_p, [c_i32]),
     "qm_last_error": (ctypes.c_char_p, []),
     "qm_abi_version": (ctypes.c_int, []),

@@ -27,6 +27,7 @@ UNITS = [
     ("q8_update.hip", ["-ffp-contract=off"]),
     ("ns.hip", []),
     ("grasp.hip", ["-ffp-contract=off"]),
+    ("hbm_stream.hip", []),
     ("plan.cpp", []),
     ("timing.cpp", ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]),
 ]

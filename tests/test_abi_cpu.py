@@ -427,3 +427,12 @@ def test_full_and_block_plans_must_share_tensors():
     for step in (1, 2):                             # a block step and a full step
         need, st = _step_call(full, blk, [(rows, cols, rows, bc)], step)
         assert need == 0 and st == 8, LIB.qm_last_error()
+
+
+def test_hbm_stream_copy_validates_before_launch():
+    v = ctypes.c_void_p
+    assert LIB.qm_hbm_stream_copy(None, v(BASE), 1024, None) == 1
+    assert LIB.qm_hbm_stream_copy(v(BASE), v(BASE + 4096), 1000, None) == 2       # size not a multiple of 16
+    assert LIB.qm_hbm_stream_copy(v(BASE + 8), v(BASE + 8192), 1024, None) == 2   # misaligned source
+    assert LIB.qm_hbm_stream_copy(v(BASE), v(BASE + 512), 1024, None) == 1        # overlap
+    assert LIB.qm_hbm_stream_copy(v(BASE), v(BASE + 4096), 0, None) == 0          # nothing to copy
