@@ -49,6 +49,7 @@ def lib():
         L.or_mx_scale_byte.argtypes = [ctypes.c_float]
         L.or_mx_scale_byte.restype = ctypes.c_uint8
         L.or_q8_update_carrier.argtypes = [p, p, p, ctypes.c_int, i64, ctypes.c_float, p, p, p]
+        L.or_q8_update_carrier_t.argtypes = [p, p, p, ctypes.c_int, i64, i64, ctypes.c_float, p, p, p]
         L.or_q8_update.restype = None
         L.or_group_sums.argtypes = [p, p, i64, ctypes.c_int32, p]
         L.or_group_inv_norm.argtypes = [p, ctypes.c_int32, ctypes.c_float, p]
@@ -180,6 +181,34 @@ def q8_update_carrier(codes, absmax, grad, beta, dtype=F32):
     sums = np.empty((numel + BLOCK - 1) // BLOCK, dtype=np.float64)
     lib().or_q8_update_carrier(_ptr(codes), _ptr(absmax), _ptr(g), dtype, numel, ctypes.c_float(beta),
                                _ptr(payload), _ptr(scales), _ptr(sums))
+    return codes, absmax, payload, scales, sums
+
+
+def transposed_carrier_applies(rows, cols):
+    """Reading R29: in carrier mode a tall matrix (rows > cols) whose rows are
+    a multiple of 128 and columns a multiple of 256, orthogonalised whole, is
+    handed over as the row-wise carrier of its transpose."""
+    return rows > cols and rows % 128 == 0 and cols % 256 == 0
+
+
+def q8_update_carrier_t(codes, absmax, grad, beta, rows, cols, dtype=F32):
+    """The q8 update of a rows x cols tensor emitting the MXFP8 carrier of
+    m^T (q8.c or_q8_update_carrier_t): state as q8_update; payload uint8
+    (cols, rows) with byte [c][r] coding m[r][c]; scales uint8 (cols, rows / 32),
+    one per 32 consecutive rows of a column.  rows a multiple of 32."""
+    codes = np.array(codes, dtype=np.int8, copy=True).ravel()
+    absmax = np.array(absmax, dtype=np.float32, copy=True).ravel()
+    g = np.ascontiguousarray(grad, dtype=np.float32 if dtype == F32 else np.uint16).reshape(-1)  # read in place
+    numel = rows * cols
+    if rows % 32:
+        raise ValueError("rows must be a multiple of 32")
+    if codes.size != numel or g.size != numel or absmax.size != (numel + BLOCK - 1) // BLOCK:
+        raise ValueError("shape mismatch between codes, absmax and grad")
+    payload = np.zeros((cols, rows), np.uint8)
+    scales = np.zeros((cols, rows // 32), np.uint8)
+    sums = np.empty((numel + BLOCK - 1) // BLOCK, dtype=np.float64)
+    lib().or_q8_update_carrier_t(_ptr(codes), _ptr(absmax), _ptr(g), dtype, rows, cols, ctypes.c_float(beta),
+                                 _ptr(payload), _ptr(scales), _ptr(sums))
     return codes, absmax, payload, scales, sums
 
 

@@ -61,12 +61,19 @@ def muon_step(W, codes, absmax, grad, dtype, t, rows, cols, block_rows,
     carrier: m reaches Newton-Schulz as the MXFP8 carrier ("Quantized Muon
     Momentum", section "Wave18B MXFP8 Carrier Probe"): the NS input is the
     decoded carrier times the group inverse norm, which still comes from the
-    fp32 m of the update; otherwise it is m as stored in the grad dtype."""
+    fp32 m of the update; otherwise it is m as stored in the grad dtype.  A
+    tall matrix orthogonalised whole (rows > cols, rows % 128 == 0,
+    cols % 256 == 0) travels as the carrier of m^T, one scale per 32 rows of
+    a column (reading R29)."""
     full = is_full_step(t, period)
     br, bc = (rows, cols) if full else (block_rows, block_cols)
     gid = block_group_ids(rows, cols, br, bc)
     ngroups = (rows // br) * (cols // bc)
-    if carrier:
+    if carrier and br == rows and bc == cols and oracle.transposed_carrier_applies(rows, cols):
+        # a tall matrix orthogonalised whole: the carrier of m^T (reading R29)
+        c2, a2, payload, scales, bsum = oracle.q8_update_carrier_t(codes, absmax, grad, beta, rows, cols, dtype)
+        mf = oracle.decode_carrier(payload, scales).reshape(cols, rows).T.ravel()
+    elif carrier:
         c2, a2, payload, scales, bsum = oracle.q8_update_carrier(codes, absmax, grad, beta, dtype)
         mf = oracle.decode_carrier(payload, scales)
     else:

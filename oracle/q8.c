@@ -46,6 +46,7 @@
  *     output word e mod 4; round up iff u < frac(x).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -370,6 +371,78 @@ void or_q8_update_carrier(int8_t *codes, float *absmax, const void *grad, int dt
             block_sumsq[b] = s;
         }
     }
+}
+
+/*
+ * The carrier of a tall matrix handed over transposed (reading R29): the q8
+ * update of a rows x cols row-major tensor (codes/absmax/block sums exactly
+ * as or_q8_update, nearest rounding; the grad only read), with the MXFP8
+ * carrier of m^T in place of m's: payload_t is cols x rows row-major (byte
+ * [c][r] codes m[r][c]) and scales_t is cols x rows/32, one E8M0 byte per 32
+ * consecutive rows of a column, each with the rule of or_q8_update_carrier.
+ * rows a multiple of 32.
+ */
+void or_q8_update_carrier_t(int8_t *codes, float *absmax, const void *grad, int dtype,
+                            int64_t rows, int64_t cols, float beta, uint8_t *payload_t,
+                            uint8_t *scales_t, double *block_sumsq)
+{
+    const int64_t numel = rows * cols;
+    const int64_t nblk = (numel + OR_BLOCK - 1) / OR_BLOCK;
+    const float omb = 1.0f - beta;
+    float *m = malloc((size_t)numel * sizeof(float));
+    if (!m) return;
+    /* the update, block by block (the same operations as or_q8_update) */
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nblk; b++) {
+        const int64_t lo = b * OR_BLOCK;
+        const int64_t hi = (lo + OR_BLOCK < numel) ? lo + OR_BLOCK : numel;
+        const float step = absmax[b] / 127.0f;
+        float amax = 0.0f;
+        for (int64_t i = lo; i < hi; i++) {
+            const float old = (float)codes[i] * step;
+            const float g = load_grad(grad, dtype, i);
+            const float t1 = beta * old;
+            const float t2 = omb * g;
+            m[i] = t1 + t2;
+            const float a = fabsf(m[i]);
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0f) {
+            for (int64_t i = lo; i < hi; i++) codes[i] = 0;
+        } else {
+            const float inv = 127.0f / amax;
+            for (int64_t i = lo; i < hi; i++) {
+                float q = rintf(m[i] * inv);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+                codes[i] = (int8_t)q;
+            }
+        }
+        absmax[b] = amax;
+        if (block_sumsq) {
+            double sum = 0.0;
+            for (int64_t i = lo; i < hi; i++) sum += (double)m[i] * (double)m[i];
+            block_sumsq[b] = sum;
+        }
+    }
+    /* the carrier of m^T: 32 consecutive rows of one column per MX block */
+    const int64_t nrb = rows / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++) {
+        for (int64_t g = 0; g < nrb; g++) {
+            float bm = 0.0f;
+            for (int64_t r = 32 * g; r < 32 * g + 32; r++) {
+                const float a = fabsf(m[r * cols + c]);
+                if (a > bm) bm = a;
+            }
+            const uint8_t sb = or_mx_scale_byte(bm);
+            scales_t[c * nrb + g] = sb;
+            const float inv_scale = ldexpf(1.0f, -((int)sb - 127));
+            for (int64_t r = 32 * g; r < 32 * g + 32; r++)
+                payload_t[c * rows + r] = bm == 0.0f ? 0 : or_e4m3_from_f32(m[r * cols + c] * inv_scale);
+        }
+    }
+    free(m);
 }
 
 /* --------------------------------------------------------- group norms */

@@ -163,3 +163,59 @@ def test_carrier_zero_and_tiny_blocks():
 def test_carrier_rejects_ragged_sizes():
     with pytest.raises(ValueError):
         oracle.q8_update_carrier(np.zeros(40, np.int8), np.zeros(1, np.float32), np.zeros(40, np.float32), 0.9)
+
+
+# ------------------------------------------------------- transposed carrier
+# A tall matrix orthogonalised whole travels as the row-wise carrier of m^T:
+# one E8M0 scale per 32 consecutive rows of a column (reading R29).
+
+@pytest.mark.parametrize("rows,cols,dtype", [(512, 256, oracle.F32), (256, 512, oracle.BF16),
+                                              (96, 64, oracle.F16)])
+def test_transposed_carrier_state_matches_plain_update(rows, cols, dtype):
+    codes, absmax, g = _q8_inputs(rows * cols, rows + cols, dtype)
+    c1, a1, p, s, sums1 = oracle.q8_update_carrier_t(codes, absmax, g, 0.9, rows, cols, dtype)
+    c2, a2, _, sums2 = oracle.q8_update(codes, absmax, g.copy(), 0.9, dtype)
+    assert np.array_equal(c1, c2) and np.array_equal(a1.view(np.uint32), a2.view(np.uint32))
+    assert np.array_equal(sums1, sums2)
+    assert p.shape == (cols, rows) and s.shape == (cols, rows // 32)
+
+
+def test_transposed_carrier_is_the_rowwise_carrier_of_the_transpose():
+    """beta = 0 makes m equal to the fp32 grad exactly, so the transposed
+    carrier of g must equal, byte for byte, the row-wise carrier (pinned above
+    against the format) of g^T."""
+    rows, cols = 256, 96
+    codes, absmax, g = _q8_inputs(rows * cols, 11)
+    g = g.reshape(rows, cols)
+    g[:, 5] = 0.0                                  # a zero column: zero bytes, scale byte 0
+    _, _, p, s, _ = oracle.q8_update_carrier_t(codes, absmax, g.reshape(-1), 0.0, rows, cols)
+    gt = np.ascontiguousarray(g.T).reshape(-1)
+    _, _, p_rw, s_rw, _ = oracle.q8_update_carrier(np.zeros(rows * cols, np.int8),
+                                                    np.zeros(rows * cols // 256, np.float32), gt, 0.0)
+    assert np.array_equal(p.reshape(-1), p_rw) and np.array_equal(s.reshape(-1), s_rw)
+    assert np.all(p[5] == 0) and np.all(s[5] == 0)
+
+
+def test_transposed_carrier_decodes_to_m_within_e4m3_precision():
+    rows, cols = 384, 256
+    codes, absmax, g = _q8_inputs(rows * cols, 13)
+    _, _, p, s, _ = oracle.q8_update_carrier_t(codes, absmax, g, 0.95, rows, cols)
+    _, _, m, _ = oracle.q8_update(codes, absmax, g.copy(), 0.95)
+    mt = m.astype(np.float64).reshape(rows, cols).T            # (cols, rows)
+    dec = oracle.decode_carrier(p, s).reshape(cols, rows)
+    scale = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    bound = np.maximum.reduce([np.abs(mt) * 2.0 ** -4, scale * 2.0 ** -10, np.abs(mt) - 448 * scale])
+    assert np.all(np.abs(dec - mt) <= bound * (1 + 1e-12))
+    bm = np.abs(mt).reshape(cols, rows // 32, 32).max(axis=2)
+    assert np.array_equal(s, np.vectorize(lambda v: oracle.mx_scale_byte(float(np.float32(v))))(bm).astype(np.uint8))
+
+
+def test_transposed_carrier_rule_and_shape_checks():
+    assert oracle.transposed_carrier_applies(14336, 4096)
+    assert not oracle.transposed_carrier_applies(4096, 14336)      # wide: the row-wise carrier
+    assert not oracle.transposed_carrier_applies(4096, 4096)       # square: the row-wise carrier
+    assert not oracle.transposed_carrier_applies(14336 + 64, 4096)  # rows off the 128 grid
+    assert not oracle.transposed_carrier_applies(14336, 4096 + 128)  # cols off the 256 grid
+    with pytest.raises(ValueError):
+        oracle.q8_update_carrier_t(np.zeros(40 * 8, np.int8), np.zeros(2, np.float32), np.zeros(40 * 8, np.float32),
+                                   0.9, 40, 8)
