@@ -1292,6 +1292,7 @@ struct NsRequest {
     const uint8_t *sc = nullptr;   // carrier scales and their row pitch
     int64_t sld = 0;
     int64_t out_ld = 0;            // row pitch of out; 0: ld
+    int32_t src_t = 0;             // the source holds the transpose (cols x rows, pitch ld) of a tall matrix
 };
 
 // Row pitch of the internal operands: the padded width plus one 128-byte
@@ -1474,8 +1475,10 @@ qm_status launch_gram_mx(MxGramArgs args, int tiles, hipStream_t stream) {
 // 128-byte k-tile, and the carrier rows and scale rows aligned for the
 // 16-byte and 4-byte loads.
 bool mx_gram_ok(const NsRequest &r) {
-    return r.dtype == kSrcMx8 && r.inv && r.rows <= r.cols && r.rows % 256 == 0 && r.cols % 128 == 0 &&
-           aligned(r.src, 16) && r.ld % 16 == 0 && aligned(r.sc, 4) && r.sld % 4 == 0;
+    // rows and K of the iterated matrix (the source as stored when it holds a transpose)
+    const int64_t xr = r.src_t ? r.cols : r.rows, xc = r.src_t ? r.rows : r.cols;
+    return r.dtype == kSrcMx8 && r.inv && xr <= xc && xr % 256 == 0 && xc % 128 == 0 && aligned(r.src, 16) &&
+           r.ld % 16 == 0 && aligned(r.sc, 4) && r.sld % 4 == 0;
 }
 
 // bf16: X[0], X[1] ping-pong (X = aX + BX reads X in its K x N layout);
@@ -1524,7 +1527,7 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
                 M.ldc = B.g.ldm;
                 M.tiles_m = tm;
                 M.tile_begin = tx;
-                M.k_tiles = (int32_t)(r.cols / 128);
+                M.k_tiles = (int32_t)((r.src_t ? r.rows : r.cols) / 128);
                 tx += tm * (tm + 1) / 2;
                 continue;
             }
@@ -1684,7 +1687,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         it.sld = r.sld;
         it.dtype = r.dtype;
         it.vec = r.dtype != kSrcMx8 && aligned(r.src, 16) && (r.ld * (r.dtype == QM_F32 ? 4 : 2)) % 16 == 0 ? 1 : 0;
-        it.tall = r.rows > r.cols ? 1 : 0;
+        it.tall = !r.src_t && r.rows > r.cols ? 1 : 0;   // a stored transpose is read as it is
         it.inv = r.inv;
         it.X = bufs[i].X[0];
         it.XT = bufs[i].XT[0];   // null for bf16
@@ -1900,6 +1903,15 @@ struct CarrierIn {
     const uint8_t *data, *scale;
 };
 
+// Whether matrix i travels as the transposed carrier on this step: a tall
+// matrix orthogonalised whole (a full step, or blocks the size of the
+// matrix) with rows a multiple of 128 and cols of 256, so that the carrier
+// of m^T feeds the block-scaled Gram along the matrix's rows.
+bool transposed_carrier(const qm_muon_matrix &M, int32_t i, bool full) {
+    const bool whole = full || (M.block_rows == M.rows && M.block_cols == M.cols);
+    return whole && i < 64 && M.rows > M.cols && M.rows % 128 == 0 && M.cols % 256 == 0;
+}
+
 std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan, const qm_muon_matrix *mats,
                                      int32_t n, bool full, const float *inv, const qm_muon_hparams *hp,
                                      const CarrierIn *carrier = nullptr) {
@@ -1924,7 +1936,18 @@ std::vector<NsRequest> step_requests(const PlanHeader *h, const void *host_plan,
                 req.push_back(NsRequest{grad + goff * esz, grad + goff * esz, br, bc, gld, dt, dt, ip,
                                         M.weight ? M.weight + woff : nullptr, M.cols, lr * s,
                                         lr * hp->weight_decay});
-                if (carrier) {   // dense (rows, cols) bytes and (rows, cols / 32) scales of tensor i
+                if (carrier && transposed_carrier(M, i, full)) {
+                    // the carrier of m^T: dense (cols, rows) bytes and (cols, rows / 32) scales
+                    NsRequest &r = req.back();
+                    const int64_t e0 = pt[i].block_offset * kBlock;
+                    r.src = carrier->data + e0;
+                    r.ld = M.rows;
+                    r.dtype = kSrcMx8;
+                    r.sc = carrier->scale + e0 / 32;
+                    r.sld = M.rows / 32;
+                    r.out_ld = gld;
+                    r.src_t = 1;
+                } else if (carrier) {   // dense (rows, cols) bytes and (rows, cols / 32) scales of tensor i
                     NsRequest &r = req.back();
                     const int64_t e0 = pt[i].block_offset * kBlock, e = (bi * br) * M.cols + bj * bc;
                     r.src = carrier->data + e0 + e;
@@ -2144,7 +2167,11 @@ extern "C" qm_status muon_step(const void *host_plan_full, const void *dev_plan_
     uint8_t *cdata = reinterpret_cast<uint8_t *>(p + upd);
     uint8_t *cscale = cdata + align_up(h->n_blocks * kBlock, 256);
     if ((st = check_carrier(h, hplan, cdata, cscale)) != QM_OK) return st;
-    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s, cdata, cscale);
+    std::vector<TallCarrier> tall;
+    for (int32_t i = 0; i < n_mats; i++)
+        if (transposed_carrier(mats[i], i, full)) tall.push_back(TallCarrier{i, mats[i].rows, mats[i].cols});
+    st = run_update_normalize(h, dplan, hp->beta, hp->eps, false, nullptr, nullptr, ws, &ro, s, cdata, cscale, hplan,
+                              tall.data(), (int)tall.size());
     if (st != QM_OK) return st;
     const CarrierIn cin{cdata, cscale};
     return apply_phase(h, hplan, mats, n_mats, full, uw.inv, hp, p + upd + carrier_ws_bytes(h), s, &cin);

@@ -391,15 +391,174 @@ template <int DT, bool SUMS, bool SR, bool CAR>
 __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_update_kernel(
     const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
     const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
-    double *__restrict__ block_sums, SrParams sr, CarrierOut co) {
+    double *__restrict__ block_sums, SrParams sr, CarrierOut co, uint64_t skip) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
     for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
         const int ti = task_tensor[find_tensor(task_offsets, n_tensors, task)];
+        if (ti < 64 && ((skip >> ti) & 1u)) continue;   // updated by the tall-carrier kernel
         const PlanTensor T = tensors[ti];
         update_task<DT, SUMS, SR, CAR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti, co);
+    }
+}
+
+// ------------------------------------ K1T: tall matrices, carrier of m^T
+// A tall rows x cols tensor (rows % kTallRows == 0, cols % 256 == 0) whose
+// carrier goes to Newton-Schulz transposed: data (cols, rows) with byte
+// [c][r] coding m[r][c], one E8M0 byte per 32 consecutive rows of a column.
+// One workgroup per kTallRows x 256 tile, in passes of 32 rows.  Every row of
+// the tile is one whole 256-element quantisation block, updated exactly as
+// K1 does (codes, absmax, block sums of the same binary32 m) and, as in K1's
+// 16-bit path, by 32 lanes of 8 consecutive elements: in step i of a pass,
+// wave w's lane half h takes row 8 w + 4 h + i, lane l % 32 columns
+// 8 (l % 32) .. + 7, so after four steps a lane holds four consecutive rows of
+// eight columns.  The pass's 256 column-block maxima go through LDS, each lane
+// encodes its 4 x 8 elements (one E4M3 word of four rows per column) and the
+// words collect, transposed, in LDS; at the end every thread stores its
+// column's kTallRows bytes and kTallRows / 32 scale bytes.
+constexpr int kMaxTall = 8;
+constexpr int kTallPasses = 1;
+constexpr int kTallRows = 32 * kTallPasses;
+struct TallItem {
+    int32_t tensor;        // index in the plan's tensor table
+    int32_t tiles_c;       // cols / 256
+    int64_t rows, cols;
+    int64_t tile_begin;    // first workgroup of this tensor
+};
+struct TallArgs {
+    TallItem it[kMaxTall];
+    int32_t n;
+};
+
+template <int DT, bool SUMS>
+__global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTensor *__restrict__ tensors, TallArgs ta,
+                                                                 float beta, double *__restrict__ block_sums,
+                                                                 CarrierOut co) {
+    static_assert(kThreads == 256, "four waves of eight rows per pass");
+    __shared__ float cmax[4][256];
+    __shared__ float cinv[256];
+    __shared__ uint32_t sbyte[256];
+    __shared__ uint32_t tbytes[256][kTallRows / 4 + 1];   // column c's bytes as words (+1 against bank conflicts)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, cl = lane & 31;
+    int k = 0;
+    while (k + 1 < ta.n && ta.it[k + 1].tile_begin <= (int64_t)blockIdx.x) k++;
+    const TallItem &it = ta.it[k];
+    const int64_t t = (int64_t)blockIdx.x - it.tile_begin;
+    const int64_t tr = t / it.tiles_c, tc = t % it.tiles_c;
+    const int64_t r0 = kTallRows * tr, c0 = 256 * tc;
+    const PlanTensor T = tensors[it.tensor];
+    int8_t *codes = reinterpret_cast<int8_t *>(T.codes);
+    float *absmax = reinterpret_cast<float *>(T.absmax);
+    const float omb = 1.0f - beta;
+    sbyte[threadIdx.x] = 0;
+
+    for (int pass = 0; pass < kTallPasses; pass++) {
+        float m[4][8];
+        float cm[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) cm[j] = 0.0f;
+        uint2 qv[4];
+        float g[4][8];
+        int64_t kb[4];
+        float step[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {   // all loads of the pass first
+            const int64_t r = r0 + 32 * pass + 8 * wave + 4 * h + i;
+            const int64_t e = r * it.cols + c0 + 8 * cl;
+            kb[i] = (r * it.cols + c0) / kBlock;   // the row segment's block
+            step[i] = absmax[kb[i]] / 127.0f;
+            qv[i] = *reinterpret_cast<const uint2 *>(codes + e);
+            load_grad_vec<DT>(reinterpret_cast<const void *>(T.grad), gpos(T, e), g[i]);
+            if constexpr (DT == QM_F32) load_grad_vec<DT>(reinterpret_cast<const void *>(T.grad), gpos(T, e) + 4, g[i] + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t r = r0 + 32 * pass + 8 * wave + 4 * h + i;
+            const int64_t e = r * it.cols + c0 + 8 * cl;
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t w = j < 4 ? qv[i].x : qv[i].y;
+                const float old = (float)(int8_t)(w >> (8 * (j & 3))) * step[i];
+                const float t1 = beta * old;
+                const float t2 = omb * g[i][j];
+                m[i][j] = t1 + t2;
+                amax = fmaxf(amax, fabsf(m[i][j]));
+                cm[j] = fmaxf(cm[j], fabsf(m[i][j]));
+            }
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+            const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+            uint2 qo = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                float q = rintf(m[i][j] * inv);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+                const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q << (8 * (j & 3));
+                if (j < 4) qo.x |= b;
+                else qo.y |= b;
+            }
+            *reinterpret_cast<uint2 *>(codes + e) = qo;
+            if constexpr (SUMS) {
+                double sq = 0.0;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const double d = (double)m[i][j];
+                    sq += d * d;
+                }
+#pragma unroll
+                for (int off = 1; off < 32; off <<= 1) sq += __shfl_xor(sq, off);
+                if (cl == 0) block_sums[T.block_offset + kb[i]] = sq;
+            }
+            if (cl == 0) absmax[kb[i]] = amax;
+        }
+        // column maxima over the wave's 8 rows (the two lane halves), then LDS
+#pragma unroll
+        for (int j = 0; j < 8; j++) cm[j] = fmaxf(cm[j], __shfl_xor(cm[j], 32));
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) cmax[wave][8 * cl + j] = cm[j];
+        }
+        __syncthreads();
+        {
+            // column c = thread: its block maximum over the pass's 32 rows, the
+            // E8M0 byte (biased exponent minus 8, 0 for zero or tiny blocks, as
+            // in K1) and 2^(127 - byte) to scale by
+            const int c = threadIdx.x;
+            const float xm = fmaxf(fmaxf(cmax[0][c], cmax[1][c]), fmaxf(cmax[2][c], cmax[3][c]));
+            const uint32_t xe = __float_as_uint(xm) >> 23;
+            const uint32_t sb = xe > 8u ? xe - 8u : 0u;
+            cinv[c] = __uint_as_float((254u - sb) << 23);
+            sbyte[c] |= sb << (8 * pass);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const int c = 8 * cl + j;
+            const float sc = cinv[c];
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) x[i] = m[i][j] * sc;   // exact: a power of two
+            tbytes[c][8 * pass + 2 * wave + h] = e4m3x4_rne_sat(x);   // rows 8 w + 4 h .. + 3 of the pass
+        }
+        __syncthreads();   // cmax and cinv are rewritten by the next pass
+    }
+    {
+        const int c = threadIdx.x;
+        uint8_t *dst = co.data + T.block_offset * kBlock + (c0 + c) * it.rows + r0;
+#pragma unroll
+        for (int q = 0; q < kTallRows / 16; q++)
+            *reinterpret_cast<uint4 *>(dst + 16 * q) =
+                make_uint4(tbytes[c][4 * q], tbytes[c][4 * q + 1], tbytes[c][4 * q + 2], tbytes[c][4 * q + 3]);
+        uint8_t *sdst = co.scale + T.block_offset * (kBlock / 32) + (c0 + c) * (it.rows / 32) + r0 / 32;
+        if constexpr (kTallPasses == 4) *reinterpret_cast<uint32_t *>(sdst) = sbyte[c];
+        else
+#pragma unroll
+            for (int p = 0; p < kTallPasses; p++) sdst[p] = (uint8_t)(sbyte[c] >> (8 * p));
     }
 }
 
@@ -579,7 +738,7 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
 
 template <int DT, bool SR, bool CAR>
 void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, const SrParams &sr,
-                      const CarrierOut &co, hipStream_t stream) {
+                      const CarrierOut &co, uint64_t skip, hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
@@ -588,25 +747,66 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const int grid = stream_grid(hi - lo);
     if (block_sums)
         q8_update_kernel<DT, true, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                          beta, block_sums, sr, co);
+                                                                          beta, block_sums, sr, co, skip);
     else
         q8_update_kernel<DT, false, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                           beta, nullptr, sr, co);
+                                                                           beta, nullptr, sr, co, skip);
 }
 
 template <bool SR, bool CAR>
 void launch_update_all(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                       const SrParams &sr, const CarrierOut &co, hipStream_t stream) {
-    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
-    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
-    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+                       const SrParams &sr, const CarrierOut &co, hipStream_t stream, uint64_t skip = 0) {
+    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
+    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
+    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
 }
 
-// co non-null: the carrier replaces the grad write (nearest rounding only).
+// The tall tensors of one grad dtype, at most kMaxTall per launch.
+template <int DT>
+void launch_tall_dt(const PlanHeader *h, const void *host_plan, const void *dev_plan, float beta,
+                    double *block_sums, const CarrierOut &co, const qm::TallCarrier *tall, int n_tall,
+                    hipStream_t stream) {
+    const PlanTensor *hp = reinterpret_cast<const PlanTensor *>(static_cast<const char *>(host_plan) + h->off_tensors);
+    TallArgs ta{};
+    int64_t tiles = 0;
+    auto flush = [&]() {
+        if (ta.n == 0) return;
+        const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
+        if (block_sums)
+            q8_update_tcar_kernel<DT, true><<<(unsigned)tiles, kThreads, 0, stream>>>(tens, ta, beta, block_sums, co);
+        else
+            q8_update_tcar_kernel<DT, false><<<(unsigned)tiles, kThreads, 0, stream>>>(tens, ta, beta, nullptr, co);
+        ta = TallArgs{};
+        tiles = 0;
+    };
+    for (int k = 0; k < n_tall; k++) {
+        if (hp[tall[k].tensor].dtype != DT) continue;
+        TallItem &it = ta.it[ta.n++];
+        it.tensor = tall[k].tensor;
+        it.rows = tall[k].rows;
+        it.cols = tall[k].cols;
+        it.tiles_c = (int32_t)(it.cols / 256);
+        it.tile_begin = tiles;
+        tiles += (it.rows / kTallRows) * it.tiles_c;
+        if (ta.n == kMaxTall) flush();
+    }
+    flush();
+}
+
+// co non-null: the carrier replaces the grad write (nearest rounding only);
+// tall (with co): tensors whose carrier goes out transposed, by K1T.
 qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                        const qm_round_opts *ro, const CarrierOut *co, hipStream_t stream) {
+                        const qm_round_opts *ro, const CarrierOut *co, hipStream_t stream,
+                        const void *host_plan = nullptr, const qm::TallCarrier *tall = nullptr, int n_tall = 0) {
     Timed tm(stream, QM_K_Q8_UPDATE);
-    if (co)
+    if (co && n_tall > 0) {
+        uint64_t skip = 0;
+        for (int k = 0; k < n_tall; k++) skip |= (uint64_t)1 << tall[k].tensor;
+        launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, *co, stream, skip);
+        launch_tall_dt<QM_F32>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
+        launch_tall_dt<QM_BF16>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
+        launch_tall_dt<QM_F16>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
+    } else if (co)
         launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, *co, stream);
     else if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
         launch_update_all<true, false>(h, dev_plan, beta, block_sums, SrParams{ro->seed, ro->offset},
@@ -658,12 +858,13 @@ UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
 qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float beta, float eps,
                                bool write_normalized, float *inv_out, double *sums_out, void *ws,
                                const qm_round_opts *ro, hipStream_t stream, uint8_t *carrier_data,
-                               uint8_t *carrier_scale) {
+                               uint8_t *carrier_scale, const void *host_plan, const TallCarrier *tall, int n_tall) {
     const UpdateWorkspace w = update_workspace(h, ws);
     float *inv = inv_out ? inv_out : w.inv;
     double *sums = sums_out ? sums_out : w.group_sums;
     const CarrierOut co{carrier_data, carrier_scale};
-    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, carrier_data ? &co : nullptr, stream);
+    qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, carrier_data ? &co : nullptr, stream,
+                                 host_plan, tall, n_tall);
     if (st != QM_OK) return st;
     st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
     if (st != QM_OK) return st;

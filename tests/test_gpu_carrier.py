@@ -298,7 +298,8 @@ def test_muon_step_carrier_mode_muonbp():
 
 def test_muon_step_carrier_mode_llama8b_layer():
     """One full carrier-mode step on the Llama-8B layer: state bit-exact, O
-    and dW of every matrix, whole, against NS of the decoded carrier."""
+    and dW of every matrix, whole, against NS of the decoded carrier (gate
+    and up travel as the carrier of m^T, so every first Gram runs on fp8)."""
     tensors, segments, ng = H.llama8b_layer_layout()
     trip, mats, hin = [], [], []
     for i, (name, r, c) in enumerate(tensors):
@@ -317,11 +318,15 @@ def test_muon_step_carrier_mode_llama8b_layer():
     q.muon_step(full, None, mats, 1, params)
     torch.cuda.synchronize()
     for i, (name, r, c) in enumerate(tensors):
-        c2, a2, p, s, bs = oracle.q8_update_carrier(hin[i][0], hin[i][1], hin[i][2], H.BETA, oracle.BF16)
+        if oracle.transposed_carrier_applies(r, c):    # gate, up: the carrier of m^T (R29)
+            c2, a2, p, s, bs = oracle.q8_update_carrier_t(hin[i][0], hin[i][1], hin[i][2], H.BETA, r, c, oracle.BF16)
+            m = oracle.decode_carrier(p, s).reshape(c, r).T
+        else:
+            c2, a2, p, s, bs = oracle.q8_update_carrier(hin[i][0], hin[i][1], hin[i][2], H.BETA, oracle.BF16)
+            m = oracle.decode_carrier(p, s).reshape(r, c)
         assert_bits_equal(host(trip[i][0]), c2, f"codes[{name}]")
         assert_bits_equal(host(trip[i][1]), a2, f"absmax[{name}]")
         inv = oracle.group_inv_norm(oracle.group_sums([bs], [np.zeros(bs.size, np.int32)], 1), H.NS_EPS)[0]
-        m = oracle.decode_carrier(p, s).reshape(r, c)
         ref = ns_whole(m, 5, COEF, H.NS_EPS, inv_norm=float(np.float32(inv)))
         _within(as_f64(trip[i][2]).reshape(r, c), ref, f"O[{name}]")
         sc = 0.2 * math.sqrt(max(r, c))
@@ -496,3 +501,49 @@ def test_muon_step_carrier_mode_fp32_operand_ns(precision):
         rel, cos = ns_parity(as_f64(trip[i][2]).reshape(r, c), O)
         say(f"   O[{i}]: relF {rel:.3e} min cos {cos:.7f}")
         assert rel <= NS_F32_REL and cos >= NS_F32_COS, (i, rel, cos)
+
+
+def test_muon_step_transposed_carrier_bytes():
+    """Tall matrices orthogonalised whole travel as the carrier of m^T (one
+    E8M0 byte per 32 rows of a column): the bytes and scales the update writes
+    into the step's workspace equal the oracle's, bit for bit, as do the state
+    and the group norms; a wide matrix beside them keeps the row-wise carrier;
+    O and dW within the bf16 bound."""
+    shapes = [(512, 256), (384, 256), (256, 512), (1024, 512)]
+    trip, mats, W_host, states = [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 3601, i)
+        g = H.grad((r, c), torch.bfloat16, DEV, 3601, i).reshape(-1)
+        w = H.weights((r, c), DEV, 3601, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, w))
+        W_host.append(as_f64(w))
+        states.append((host(codes), host(absmax)))
+    torch.cuda.synchronize()
+    gh = [host_grad(t[2]) for t in trip]
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], len(shapes))
+    params = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, weight_decay=0.01, rms_scale=0.2,
+                            ns_steps=5, period=1, carrier=True)
+    ws = torch.empty(q.muon_step_workspace_bytes(plan, None, mats, hparams=params), dtype=torch.uint8, device=DEV)
+    say("transposed-carrier step", shapes)
+    q.muon_step(plan, None, mats, 1, params, ws=ws)
+    torch.cuda.synchronize()
+    upd = -(-plan.workspace_bytes() // 256) * 256
+    nb = plan.n_blocks
+    cdata = host(ws[upd:upd + nb * 256])
+    s0 = upd + -(-nb * 256 // 256) * 256
+    cscale = host(ws[s0:s0 + nb * 8])
+    for i, (r, c) in enumerate(shapes):
+        b0 = plan.block_offsets[i]
+        if oracle.transposed_carrier_applies(r, c):
+            c2, a2, p, s, _ = oracle.q8_update_carrier_t(states[i][0], states[i][1], gh[i], 0.95, r, c, oracle.BF16)
+        else:
+            c2, a2, p, s, _ = oracle.q8_update_carrier(states[i][0], states[i][1], gh[i], 0.95, oracle.BF16)
+        assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
+        assert_bits_equal(cdata[b0 * 256:b0 * 256 + r * c], p.reshape(-1), f"carrier data[{i}]")
+        assert_bits_equal(cscale[b0 * 8:b0 * 8 + r * c // 32], s.reshape(-1), f"carrier scales[{i}]")
+        W2, _, _, O, _ = muonbp.muon_step(W_host[i], states[i][0], states[i][1], gh[i], oracle.BF16, 1, r, c, r, c,
+                                          1, 0.95, 1e-7, COEF, 5, 0.02, 0.02, 0.2, 0.01, carrier=True)
+        _within(as_f64(trip[i][2]).reshape(r, c), O, f"O[{i}]")
+        _within(as_f64(mats[i][4]) - W_host[i], W2 - W_host[i], f"dW[{i}]")
