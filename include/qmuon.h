@@ -342,7 +342,13 @@ typedef struct {
                             MXFP8 carrier of qmuon_update_mxfp8_carrier (in
                             the workspace; grads only read until O is
                             written; nearest rounding; cols and block_cols
-                            multiples of 32); 0: m is written to the grads */
+                            multiples of 32); a tall matrix orthogonalised
+                            whole (rows > cols, rows % 128 == 0, cols % 256
+                            == 0, among the first 64) travels instead as the
+                            row-wise carrier of m^T (one scale per 32 rows of
+                            a column), which the first Gram product reads
+                            along its contraction; 0: m is written to the
+                            grads */
     uint64_t seed;       /* Philox key for stochastic rounding               */
 } qm_muon_hparams;
 
