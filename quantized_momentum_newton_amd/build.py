@@ -33,20 +33,45 @@ UNITS = [
 ]
 
 
+# Per-kernel register use of the last build (the compiler's resource-usage
+# remarks), one line per kernel: name, VGPRs, AGPRs, VGPR spill, SGPR spill,
+# scratch bytes per lane, occupancy.  tests/test_build_cpu.py checks it.
+USAGE = os.path.join(BUILD, "kernel_resources.tsv")
+
+
+def _resource_lines(stderr):
+    import re
+    rows, cur = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"name": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill|ScratchSize \[bytes/lane\]|"
+                      r"Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1)] = int(m.group(2))
+    return ["\t".join(str(r.get(k, "")) for k in ("name", "VGPRs", "AGPRs", "VGPRs Spill", "SGPRs Spill",
+                                                 "ScratchSize [bytes/lane]", "Occupancy [waves/SIMD]"))
+            for r in rows]
+
+
 def _compile(src, extra, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "c++"]
-    cmd = [HIPCC, *HIP_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
+    cmd = [HIPCC, *HIP_FLAGS, *extra, *remarks, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{r.stdout}\n{r.stderr}")
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l and "kernel-resource-usage" not in l)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    return obj
+    return obj, _resource_lines(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
@@ -54,7 +79,12 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     units = [(s, f) for s, f in UNITS if os.path.exists(os.path.join(CSRC, s))]
     with cf.ThreadPoolExecutor(max_workers=min(4, len(units))) as ex:
-        objs = list(ex.map(lambda u: _compile(u[0], u[1], verbose), units))
+        done = list(ex.map(lambda u: _compile(u[0], u[1], verbose), units))
+    objs = [o for o, _ in done]
+    with open(USAGE, "w") as f:
+        f.write("kernel\tvgprs\tagprs\tvgpr_spill\tsgpr_spill\tscratch_per_lane\toccupancy\n")
+        for _, rows in done:
+            f.writelines(r + "\n" for r in rows)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

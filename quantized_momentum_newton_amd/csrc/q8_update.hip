@@ -243,6 +243,7 @@ __device__ __forceinline__ void sr_words(int64_t e, const SrParams &sr, uint32_t
 struct CarrierOut {
     uint8_t *data;
     uint8_t *scale;
+    uint64_t skip;   // tensors (index < 64) whose carrier another kernel writes (K1T): K1 leaves them alone
 };
 
 template <int DT, bool SUMS, bool SR, bool CAR>
@@ -391,14 +392,16 @@ template <int DT, bool SUMS, bool SR, bool CAR>
 __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_update_kernel(
     const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
     const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
-    double *__restrict__ block_sums, SrParams sr, CarrierOut co, uint64_t skip) {
+    double *__restrict__ block_sums, SrParams sr, CarrierOut co) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
     for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
         const int ti = task_tensor[find_tensor(task_offsets, n_tensors, task)];
-        if (ti < 64 && ((skip >> ti) & 1u)) continue;   // updated by the tall-carrier kernel
+        if constexpr (CAR) {
+            if (ti < 64 && ((co.skip >> ti) & 1u)) continue;   // updated by the tall-carrier kernel
+        }
         const PlanTensor T = tensors[ti];
         update_task<DT, SUMS, SR, CAR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti, co);
     }
@@ -738,7 +741,7 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
 
 template <int DT, bool SR, bool CAR>
 void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, const SrParams &sr,
-                      const CarrierOut &co, uint64_t skip, hipStream_t stream) {
+                      const CarrierOut &co, hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
@@ -747,18 +750,18 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const int grid = stream_grid(hi - lo);
     if (block_sums)
         q8_update_kernel<DT, true, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                          beta, block_sums, sr, co, skip);
+                                                                          beta, block_sums, sr, co);
     else
         q8_update_kernel<DT, false, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                           beta, nullptr, sr, co, skip);
+                                                                           beta, nullptr, sr, co);
 }
 
 template <bool SR, bool CAR>
 void launch_update_all(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                       const SrParams &sr, const CarrierOut &co, hipStream_t stream, uint64_t skip = 0) {
-    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
-    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
-    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, skip, stream);
+                       const SrParams &sr, const CarrierOut &co, hipStream_t stream) {
+    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
 }
 
 // The tall tensors of one grad dtype, at most kMaxTall per launch.
@@ -800,9 +803,9 @@ qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, d
                         const void *host_plan = nullptr, const qm::TallCarrier *tall = nullptr, int n_tall = 0) {
     Timed tm(stream, QM_K_Q8_UPDATE);
     if (co && n_tall > 0) {
-        uint64_t skip = 0;
-        for (int k = 0; k < n_tall; k++) skip |= (uint64_t)1 << tall[k].tensor;
-        launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, *co, stream, skip);
+        CarrierOut cs = *co;
+        for (int k = 0; k < n_tall; k++) cs.skip |= (uint64_t)1 << tall[k].tensor;
+        launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, cs, stream);
         launch_tall_dt<QM_F32>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
         launch_tall_dt<QM_BF16>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
         launch_tall_dt<QM_F16>(h, host_plan, dev_plan, beta, block_sums, *co, tall, n_tall, stream);
@@ -810,10 +813,10 @@ qm_status launch_update(const PlanHeader *h, const void *dev_plan, float beta, d
         launch_update_all<false, true>(h, dev_plan, beta, block_sums, SrParams{0, 0}, *co, stream);
     else if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
         launch_update_all<true, false>(h, dev_plan, beta, block_sums, SrParams{ro->seed, ro->offset},
-                                       CarrierOut{nullptr, nullptr}, stream);
+                                       CarrierOut{nullptr, nullptr, 0}, stream);
     else
-        launch_update_all<false, false>(h, dev_plan, beta, block_sums, SrParams{0, 0}, CarrierOut{nullptr, nullptr},
-                                        stream);
+        launch_update_all<false, false>(h, dev_plan, beta, block_sums, SrParams{0, 0},
+                                        CarrierOut{nullptr, nullptr, 0}, stream);
     return check_launch("q8 update");
 }
 
@@ -862,7 +865,7 @@ qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float 
     const UpdateWorkspace w = update_workspace(h, ws);
     float *inv = inv_out ? inv_out : w.inv;
     double *sums = sums_out ? sums_out : w.group_sums;
-    const CarrierOut co{carrier_data, carrier_scale};
+    const CarrierOut co{carrier_data, carrier_scale, 0};
     qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, carrier_data ? &co : nullptr, stream,
                                  host_plan, tall, n_tall);
     if (st != QM_OK) return st;
