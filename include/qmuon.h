@@ -175,7 +175,11 @@ QM_API qm_status qmuon_update_multi_ex(const void *host_plan, const void *dev_pl
  * accumulates per-block sums of m*m; S_g sums them per group (fp64, fixed
  * order, no atomics); inv_g = (float)(1 / (sqrt(S_g) + eps)).
  *   write_normalized = 1: every grad element becomes
- *     round(float(m_stored) * inv_g) (the page's in-place semantics);
+ *     round(float(m_stored) * inv_g) (the page's in-place semantics: the
+ *     value an in-place scale of the stored m gives).  Run as two streaming
+ *     passes: block sums of m first, then the update with the normalised
+ *     value written in place of m (m recomputed bit for bit), so the grad
+ *     buffer never holds the unnormalised m;
  *   write_normalized = 0: grads keep m and only inv_g is produced, for a
  *     Newton-Schulz call to fold in.
  *   group_inv_norm: nullable [n_groups] fp32 out.
@@ -470,14 +474,16 @@ QM_API qm_status grasp_step(const qm_grasp_state *state, int64_t rows,
 typedef enum {
     QM_K_Q8_UPDATE = 0,     /* blockwise q8 momentum update kernel */
     QM_K_GROUP_REDUCE = 1,  /* per-group sum of squares (both stages) */
-    QM_K_Q8_SCALE = 2,      /* in-place normalisation pass */
+    QM_K_Q8_SCALE = 2,      /* in-place normalisation pass: no longer launched (the
+                             * normalising update writes normalised values itself) */
     QM_K_NS_NORM = 3,       /* Frobenius norm of NS inputs (both stages) */
     QM_K_NS_PROLOGUE = 4,   /* orientation, scaling, X and X^T */
     QM_K_NS_GRAM = 5,       /* A = X X^T (symmetric product) */
     QM_K_NS_POLY = 6,       /* B = b A + c A A (symmetric product) */
     QM_K_NS_XUPDATE = 7,    /* X = a X + B X */
     QM_K_NS_WRITEBACK = 8,  /* output and fused weight update */
-    QM_K_CLASSES = 9
+    QM_K_Q8_SUMS = 9,       /* block sums of m only: first pass of the normalising update */
+    QM_K_CLASSES = 10
 } qm_kernel_class;
 
 /* on != 0: clear records and start recording; on == 0: stop.

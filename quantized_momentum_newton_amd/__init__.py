@@ -89,7 +89,7 @@ def abi_version():
 
 # Kernel classes of qm_timing_read (qm_kernel_class in include/qmuon.h).
 KERNEL_CLASSES = {"q8_update": 0, "group_reduce": 1, "q8_scale": 2, "ns_norm": 3, "ns_prologue": 4,
-                  "ns_gram": 5, "ns_poly": 6, "ns_xupdate": 7, "ns_writeback": 8}
+                  "ns_gram": 5, "ns_poly": 6, "ns_xupdate": 7, "ns_writeback": 8, "q8_sums": 9}
 
 
 def timing_enable(on=True):

@@ -97,7 +97,7 @@ template <int DT> __device__ __forceinline__ void narrow(void *p, int64_t i, flo
 // step, so their loads and stores carry the non-temporal hint and do not
 // displace what other work keeps in the caches.  Measured: back-to-back
 // update calls 8-11 % faster (Llama-8B layer, 28-layer set), the 28-layer
-// grouped update with its scale pass 5 %, the update inside a full Muon step
+// grouped update with its normalisation 5 %, the update inside a full Muon step
 // about 1 %.  The hint needs plain vector types.
 typedef unsigned ntv4 __attribute__((ext_vector_type(4)));
 typedef unsigned ntv2 __attribute__((ext_vector_type(2)));
@@ -191,6 +191,15 @@ __device__ __forceinline__ int find_tensor(const int64_t *task_offsets, int n, i
     return lo;
 }
 
+// Position in task order of the tensor holding `task`, for a wave whose
+// tasks only increase: a binary search for its first task (pos < 0), then a
+// forward scan from the previous position, usually zero or one step.
+__device__ __forceinline__ int tensor_pos(const int64_t *task_offsets, int n, int pos, int64_t task) {
+    if (pos < 0) return find_tensor(task_offsets, n, task);
+    while (pos + 1 < n && task_offsets[pos + 1] <= task) pos++;
+    return pos;
+}
+
 // ------------------------------------------------------------ K1: update
 
 // Stochastic rounding: Philox4x32-10 ("Parallel random numbers: as easy as
@@ -246,28 +255,154 @@ struct CarrierOut {
     uint64_t skip;   // tensors (index < 64) whose carrier another kernel writes (K1T): K1 leaves them alone
 };
 
-template <int DT, bool SUMS, bool SR, bool CAR>
+// What one update launch writes.
+//  kOutM:    codes, absmax and m into the grad buffer (the update as defined).
+//  kOutNorm: codes, absmax and m * (its group's inverse norm) into the grad
+//            buffer: the second pass of the normalising update, after a
+//            sums pass (q8_sums_kernel) and the group reduction.  m is
+//            recomputed from the same inputs with the same operations, so it
+//            has the sums pass's bits, and the value written is what an
+//            in-place scale of the stored m makes of it: m rounded to the
+//            grad dtype, times the inverse norm in fp32, rounded again.
+// The two passes move 9.05 bytes per bf16 element (grad, codes and absmax
+// read twice, written once) where the update followed by a scale pass moves
+// 10.03: re-reading the state costs less than re-reading and rewriting m.
+enum { kOutM = 0, kOutNorm = 2 };
+struct NormIn {
+    const int32_t *block_group;   // group of every block of the plan
+    const float *inv;             // inverse norm of every group
+};
+
+// m as the grad buffer stores it, widened back to fp32
+template <int DT> __device__ __forceinline__ float stored(float v) {
+    if constexpr (DT == QM_F32) return v;
+    else if constexpr (DT == QM_BF16) return bf16_val(bf16_rne(v));
+    else return f16_val(f16_rne(v));
+}
+
+// One task's inputs as a lane holds them, still packed as loaded (so a
+// wave can hold several tasks' loads in flight): per part, its kEpl codes
+// (four per word) and grads (16 bytes), zero past the tensor's end, and its
+// block's step absmax / 127.
+template <int DT> struct TaskIn {
+    static constexpr int EPL = Elem<DT>::kEpl;
+    static constexpr int PARTS = kTaskElems / (64 * EPL);
+    uint32_t qw[PARTS][EPL / 4];
+    uint32_t gw[PARTS][4];
+    float step[PARTS];
+    int nvalid;   // elements of the task inside the tensor
+};
+
+// Element j of a lane's 16 grad bytes, widened to fp32.
+template <int DT> __device__ __forceinline__ float grad_elem(const uint32_t *gw, int j) {
+    if constexpr (DT == QM_F32) return __uint_as_float(gw[j]);
+    else {
+        const uint16_t h = (uint16_t)(gw[j / 2] >> (16 * (j % 2)));
+        return DT == QM_BF16 ? bf16_val(h) : f16_val(h);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_task(const PlanTensor &T, int64_t lt, int lane, TaskIn<DT> &in) {
+    constexpr int EPL = TaskIn<DT>::EPL, PARTS = TaskIn<DT>::PARTS, ES = Elem<DT>::kSize;
+    const int64_t e_task = lt * kTaskElems;
+    const int64_t rem = T.numel - e_task;
+    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
+    in.nvalid = nvalid;
+    const int8_t *codes = reinterpret_cast<const int8_t *>(T.codes) + e_task;
+    const float *absmax = reinterpret_cast<const float *>(T.absmax) + lt * kBlocksPerTask;
+    const char *grad = reinterpret_cast<const char *>(T.grad);   // addressed through gpos
+#pragma unroll
+    for (int p = 0; p < PARTS; p++) {
+        const int e0 = p * 64 * EPL + lane * EPL;
+        in.step[p] = e0 < nvalid ? absmax[e0 / kBlock] / 127.0f : 0.0f;
+        if (e0 + EPL <= nvalid) {
+            const ntv4 v = __builtin_nontemporal_load(reinterpret_cast<const ntv4 *>(grad + gpos(T, e_task + e0) * ES));
+            in.gw[p][0] = v.x; in.gw[p][1] = v.y; in.gw[p][2] = v.z; in.gw[p][3] = v.w;
+            if constexpr (EPL == 8) {
+                const ntv2 c = __builtin_nontemporal_load(reinterpret_cast<const ntv2 *>(codes + e0));
+                in.qw[p][0] = c.x; in.qw[p][1] = c.y;
+            } else {
+                in.qw[p][0] = *reinterpret_cast<const uint32_t *>(codes + e0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; k++) in.gw[p][k] = 0u;
+#pragma unroll
+            for (int k = 0; k < EPL / 4; k++) in.qw[p][k] = 0u;
+#pragma unroll
+            for (int j = 0; j < EPL; j++) {
+                if (e0 + j >= nvalid) continue;
+                in.qw[p][j / 4] |= (uint32_t)(uint8_t)codes[e0 + j] << (8 * (j % 4));
+                const char *gp = grad + gpos(T, e_task + e0 + j) * ES;
+                if constexpr (DT == QM_F32) in.gw[p][j] = *reinterpret_cast<const uint32_t *>(gp);
+                else in.gw[p][j / 2] |= (uint32_t)*reinterpret_cast<const uint16_t *>(gp) << (16 * (j % 2));
+            }
+        }
+    }
+}
+
+// m = beta (q step) + (1 - beta) g: two rounded products and a rounded sum
+__device__ __forceinline__ float ema1(int8_t q, float step, float g, float beta, float omb) {
+    const float old = (float)q * step;
+    const float t1 = beta * old;
+    const float t2 = omb * g;
+    return t1 + t2;
+}
+
+// m of part p of a loaded task
+template <int DT>
+__device__ __forceinline__ void ema_part(const TaskIn<DT> &in, int p, float beta, float omb, float *m) {
+#pragma unroll
+    for (int j = 0; j < TaskIn<DT>::EPL; j++)
+        m[j] = ema1((int8_t)(in.qw[p][j / 4] >> (8 * (j % 4))), in.step[p], grad_elem<DT>(in.gw[p], j), beta, omb);
+}
+
+// Sum of m*m over one block: the lane's kEpl squares in fp64 in order, then
+// a butterfly over the block's lanes (every lane of the block gets the sum).
+template <int DT> __device__ __forceinline__ double block_sum(const float *mp) {
+    constexpr int EPL = Elem<DT>::kEpl, LPB = kBlock / EPL;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < EPL; j++) {
+        const double d = (double)mp[j];
+        s += d * d;
+    }
+#pragma unroll
+    for (int off = 1; off < LPB; off <<= 1) s += __shfl_xor(s, off);
+    return s;
+}
+
+template <int DT, bool SUMS, bool SR, bool CAR, int OUT>
 __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, float beta, float omb,
                                             double *block_sums, int lane, const SrParams &sr, uint32_t tensor,
-                                            const CarrierOut &co) {
+                                            const CarrierOut &co, const NormIn &nz) {
+    static_assert(OUT != kOutNorm || (!SUMS && !CAR), "the normalising pass writes no sums and no carrier");
     constexpr int EPL = Elem<DT>::kEpl;
     constexpr int PARTS = kTaskElems / (64 * EPL);
     constexpr int LPB = kBlock / EPL;  // lanes per block
     constexpr int LPX = 32 / EPL;      // lanes per 32-element carrier block
     const int64_t e_task = lt * kTaskElems;
-    const int64_t rem = T.numel - e_task;
-    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
     int8_t *codes = reinterpret_cast<int8_t *>(T.codes) + e_task;
     float *absmax = reinterpret_cast<float *>(T.absmax) + lt * kBlocksPerTask;
     void *grad = reinterpret_cast<void *>(T.grad);   // addressed through gpos
 
+    const int64_t rem = T.numel - e_task;
+    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
     float m[PARTS][EPL];
+    float gscale[PARTS];   // kOutNorm: the inverse norm of each part's block
 #pragma unroll
     for (int p = 0; p < PARTS; p++) {
         const int e0 = p * 64 * EPL + lane * EPL;
         const int kb = e0 / kBlock;
         float step = 0.0f;
-        if (e0 < nvalid) step = absmax[kb] / 127.0f;
+        gscale[p] = 0.0f;
+        if (e0 < nvalid) {
+            step = absmax[kb] / 127.0f;
+            if constexpr (OUT == kOutNorm)   // one group: a wave-uniform load, else the block's group
+                gscale[p] = nz.inv[T.group_lo == T.group_hi ? T.group_lo
+                                                             : nz.block_group[T.block_offset + lt * kBlocksPerTask + kb]];
+        }
         int8_t q[EPL];
         float g[EPL];
         if (e0 + EPL <= nvalid) {
@@ -282,12 +417,7 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
             }
         }
 #pragma unroll
-        for (int j = 0; j < EPL; j++) {
-            const float old = (float)q[j] * step;
-            const float t1 = beta * old;
-            const float t2 = omb * g[j];
-            m[p][j] = t1 + t2;
-        }
+        for (int j = 0; j < EPL; j++) m[p][j] = ema1(q[j], step, g[j], beta, omb);
     }
 
 #pragma unroll
@@ -351,27 +481,34 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                     *reinterpret_cast<uint32_t *>(co.data + ce) = w[0];
                 if ((lane % LPX) == 0) co.scale[ce / 32] = (uint8_t)sb;
             }
-        } else if (e0 + EPL <= nvalid) {
-            store_codes_vec<EPL>(codes, e0, q);
-            store_grad_vec<DT>(grad, gpos(T, e_task + e0), m[p]);
         } else {
-#pragma unroll
-            for (int j = 0; j < EPL; j++)
-                if (e0 + j < nvalid) {
-                    codes[e0 + j] = q[j];
-                    narrow<DT>(grad, gpos(T, e_task + e0 + j), m[p][j]);
-                }
-        }
-        double s = 0.0;
-        if constexpr (SUMS) {
+            // kOutNorm: the product is pinned to an fp32 register (empty asm)
+            // before it is narrowed, or the f16 path fuses it into one
+            // v_fma_mixlo_f16 and skips the product's fp32 rounding
+            float y[EPL];
 #pragma unroll
             for (int j = 0; j < EPL; j++) {
-                const double d = (double)m[p][j];
-                s += d * d;
+                if constexpr (OUT == kOutNorm) {
+                    y[j] = stored<DT>(m[p][j]) * gscale[p];
+                    asm volatile("" : "+v"(y[j]));
+                } else {
+                    y[j] = m[p][j];
+                }
             }
+            if (e0 + EPL <= nvalid) {
+                store_codes_vec<EPL>(codes, e0, q);
+                store_grad_vec<DT>(grad, gpos(T, e_task + e0), y);
+            } else {
 #pragma unroll
-            for (int off = 1; off < LPB; off <<= 1) s += __shfl_xor(s, off);
+                for (int j = 0; j < EPL; j++)
+                    if (e0 + j < nvalid) {
+                        codes[e0 + j] = q[j];
+                        narrow<DT>(grad, gpos(T, e_task + e0 + j), y[j]);
+                    }
+            }
         }
+        double s = 0.0;
+        if constexpr (SUMS) s = block_sum<DT>(m[p]);
         if ((lane % LPB) == 0 && kb * kBlock < nvalid) {
             absmax[kb] = amax;
             if constexpr (SUMS) block_sums[T.block_offset + lt * kBlocksPerTask + kb] = s;
@@ -388,22 +525,64 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
 // With stochastic rounding the Philox state costs registers: 6 waves.
 template <int DT, bool SR> constexpr int update_wgs_per_cu() { return DT == QM_F32 || SR ? 6 : 8; }
 
-template <int DT, bool SUMS, bool SR, bool CAR>
+template <int DT, bool SUMS, bool SR, bool CAR, int OUT>
 __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, SR>())) void q8_update_kernel(
     const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
     const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
-    double *__restrict__ block_sums, SrParams sr, CarrierOut co) {
+    double *__restrict__ block_sums, SrParams sr, CarrierOut co, NormIn nz) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float omb = 1.0f - beta;
     const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
+    int pos = -1;
     for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
-        const int ti = task_tensor[find_tensor(task_offsets, n_tensors, task)];
+        pos = tensor_pos(task_offsets, n_tensors, pos, task);
+        const int ti = task_tensor[pos];
         if constexpr (CAR) {
             if (ti < 64 && ((co.skip >> ti) & 1u)) continue;   // updated by the tall-carrier kernel
         }
         const PlanTensor T = tensors[ti];
-        update_task<DT, SUMS, SR, CAR>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti, co);
+        update_task<DT, SUMS, SR, CAR, OUT>(T, task - T.task_offset, beta, omb, block_sums, lane, sr, (uint32_t)ti, co,
+                                            nz);
+    }
+}
+
+// ------------------------------------------------ sums pass (normalising update)
+// Block sums of m only, nothing else written; m and its sums are computed
+// exactly as the update computes them.  A read-only stream runs fastest with
+// a moderate grid whose waves sweep the data together (grid-stride): about 8
+// workgroups per CU (measured 7.1 TB/s for a plain 16-byte read stream at
+// that size, 5.5 with one task per wave).  Each wave finds its next tensor by
+// a forward scan from the last one.
+constexpr int kSumsGrid = 2048;
+
+template <int DT>
+__global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, false>())) void q8_sums_kernel(
+    const PlanTensor *__restrict__ tensors, const int64_t *__restrict__ task_offsets,
+    const int32_t *__restrict__ task_tensor, int n_tensors, int64_t task_lo, int64_t task_hi, float beta,
+    double *__restrict__ block_sums) {
+    constexpr int EPL = Elem<DT>::kEpl, PARTS = TaskIn<DT>::PARTS, LPB = kBlock / EPL;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float omb = 1.0f - beta;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
+    int pos = -1;
+    for (int64_t task = task_lo + (int64_t)blockIdx.x * kWavesPerWG + wave; task < task_hi; task += stride) {
+        pos = tensor_pos(task_offsets, n_tensors, pos, task);
+        const PlanTensor T = tensors[task_tensor[pos]];
+        const int64_t lt = task - T.task_offset;
+        TaskIn<DT> in;
+        load_task<DT>(T, lt, lane, in);
+        const int64_t boff = T.block_offset + lt * kBlocksPerTask;
+#pragma unroll
+        for (int p = 0; p < PARTS; p++) {
+            const int e0 = p * 64 * EPL + lane * EPL;
+            const int kb = e0 / kBlock;
+            float m[EPL];
+            ema_part<DT>(in, p, beta, omb, m);
+            const double s = block_sum<DT>(m);
+            if ((lane % LPB) == 0 && kb * kBlock < in.nvalid) block_sums[boff + kb] = s;
+        }
     }
 }
 
@@ -643,68 +822,6 @@ __global__ __launch_bounds__(64) void group_final_kernel(const int64_t *__restri
     }
 }
 
-// ------------------------------------------------------------ K3: scale pass
-
-template <int DT>
-__device__ __forceinline__ void scale_task(const PlanTensor &T, int64_t lt, const int32_t *block_group,
-                                           const float *inv, int lane) {
-    constexpr int EPL = Elem<DT>::kEpl;
-    constexpr int PARTS = kTaskElems / (64 * EPL);
-    const int64_t e_task = lt * kTaskElems;
-    const int64_t rem = T.numel - e_task;
-    const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
-    void *grad = reinterpret_cast<void *>(T.grad);   // addressed through gpos
-    const int32_t *bg = block_group + T.block_offset + lt * kBlocksPerTask;
-#pragma unroll
-    for (int p = 0; p < PARTS; p++) {
-        const int e0 = p * 64 * EPL + lane * EPL;
-        if (e0 >= nvalid) continue;
-        const float s = inv[bg[e0 / kBlock]];
-        // The product is pinned to an fp32 register (empty asm) before it is
-        // narrowed: otherwise the f16 path becomes one v_fma_mixlo_f16 (h * s
-        // + 0 rounded once to f16), which turns -0 into +0 and skips the fp32
-        // rounding of the product that the definition has.
-        if (e0 + EPL <= nvalid) {
-            const int64_t ge = gpos(T, e_task + e0);
-            float v[EPL];
-            load_grad_vec<DT>(grad, ge, v);
-#pragma unroll
-            for (int j = 0; j < EPL; j++) {
-                v[j] = v[j] * s;
-                asm volatile("" : "+v"(v[j]));
-            }
-            store_grad_vec<DT>(grad, ge, v);
-        } else {
-            for (int j = 0; j < EPL && e0 + j < nvalid; j++) {
-                const int64_t ge = gpos(T, e_task + e0 + j);
-                float v = widen<DT>(grad, ge) * s;
-                asm volatile("" : "+v"(v));
-                narrow<DT>(grad, ge, v);
-            }
-        }
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void q8_scale_kernel(const PlanTensor *__restrict__ tensors,
-                                                            const int64_t *__restrict__ task_offsets,
-                                                            const int32_t *__restrict__ task_tensor,
-                                                            int n_tensors, int64_t n_tasks,
-                                                            const int32_t *__restrict__ block_group,
-                                                            const float *__restrict__ inv) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t stride = (int64_t)gridDim.x * kWavesPerWG;
-    for (int64_t task = (int64_t)blockIdx.x * kWavesPerWG + wave; task < n_tasks; task += stride) {
-        const PlanTensor T = tensors[task_tensor[find_tensor(task_offsets, n_tensors, task)]];
-        const int64_t lt = task - T.task_offset;
-        switch (T.dtype) {
-            case QM_F32: scale_task<QM_F32>(T, lt, block_group, inv, lane); break;
-            case QM_BF16: scale_task<QM_BF16>(T, lt, block_group, inv, lane); break;
-            default: scale_task<QM_F16>(T, lt, block_group, inv, lane); break;
-        }
-    }
-}
-
 // Workgroups per streaming launch: one task per wave (the kernels keep
 // their grid-stride loop, which then runs once).  Measured on the 8B layer,
 // this beat grids capped at 8, 16 or 32 workgroups per CU by 5-10 %: the
@@ -739,29 +856,32 @@ qm_status validate_update(const void *host_plan, const void *dev_plan, float bet
     return QM_OK;
 }
 
-template <int DT, bool SR, bool CAR>
+template <int DT, bool SR, bool CAR, int OUT>
 void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, const SrParams &sr,
-                      const CarrierOut &co, hipStream_t stream) {
+                      const CarrierOut &co, const NormIn &nz, hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
     const int64_t *toff = section<int64_t>(dev_plan, h->off_task_offsets);
     const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
     const int grid = stream_grid(hi - lo);
-    if (block_sums)
-        q8_update_kernel<DT, true, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                          beta, block_sums, sr, co);
+    if constexpr (OUT == kOutNorm)
+        q8_update_kernel<DT, false, SR, false, OUT><<<grid, kThreads, 0, stream>>>(
+            tens, toff, tt, h->n_tensors, lo, hi, beta, nullptr, sr, co, nz);
+    else if (block_sums)
+        q8_update_kernel<DT, true, SR, CAR, OUT><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+                                                                               beta, block_sums, sr, co, nz);
     else
-        q8_update_kernel<DT, false, SR, CAR><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
-                                                                           beta, nullptr, sr, co);
+        q8_update_kernel<DT, false, SR, CAR, OUT><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+                                                                                beta, nullptr, sr, co, nz);
 }
 
-template <bool SR, bool CAR>
+template <bool SR, bool CAR, int OUT = kOutM>
 void launch_update_all(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums,
-                       const SrParams &sr, const CarrierOut &co, hipStream_t stream) {
-    launch_update_dt<QM_F32, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
-    launch_update_dt<QM_BF16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
-    launch_update_dt<QM_F16, SR, CAR>(h, dev_plan, beta, block_sums, sr, co, stream);
+                       const SrParams &sr, const CarrierOut &co, hipStream_t stream, const NormIn &nz = NormIn{}) {
+    launch_update_dt<QM_F32, SR, CAR, OUT>(h, dev_plan, beta, block_sums, sr, co, nz, stream);
+    launch_update_dt<QM_BF16, SR, CAR, OUT>(h, dev_plan, beta, block_sums, sr, co, nz, stream);
+    launch_update_dt<QM_F16, SR, CAR, OUT>(h, dev_plan, beta, block_sums, sr, co, nz, stream);
 }
 
 // The tall tensors of one grad dtype, at most kMaxTall per launch.
@@ -834,13 +954,38 @@ qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const d
     return check_launch("group reduce");
 }
 
-qm_status launch_scale(const PlanHeader *h, const void *dev_plan, const float *inv, hipStream_t stream) {
-    Timed tm(stream, QM_K_Q8_SCALE);
-    q8_scale_kernel<<<stream_grid(h->n_tasks), kThreads, 0, stream>>>(
+template <int DT>
+void launch_sums_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, hipStream_t stream) {
+    const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
+    if (hi <= lo) return;
+    q8_sums_kernel<DT><<<std::min(stream_grid(hi - lo), kSumsGrid), kThreads, 0, stream>>>(
         section<PlanTensor>(dev_plan, h->off_tensors), section<int64_t>(dev_plan, h->off_task_offsets),
-        section<int32_t>(dev_plan, h->off_task_tensor), h->n_tensors, h->n_tasks,
-        section<int32_t>(dev_plan, h->off_block_group), inv);
-    return check_launch("group scale");
+        section<int32_t>(dev_plan, h->off_task_tensor), h->n_tensors, lo, hi, beta, block_sums);
+}
+
+// The normalising update in two streaming passes (the sums pass, then
+// kOutNorm once the group reduction has the inverse norms).
+qm_status launch_update_normalized(const PlanHeader *h, const void *dev_plan, float beta, const UpdateWorkspace &w,
+                                   float eps, double *sums, float *inv, const qm_round_opts *ro, hipStream_t stream) {
+    {
+        Timed tm(stream, QM_K_Q8_SUMS);
+        launch_sums_dt<QM_F32>(h, dev_plan, beta, w.block_sums, stream);
+        launch_sums_dt<QM_BF16>(h, dev_plan, beta, w.block_sums, stream);
+        launch_sums_dt<QM_F16>(h, dev_plan, beta, w.block_sums, stream);
+        const qm_status st = check_launch("q8 sums pass");
+        if (st != QM_OK) return st;
+    }
+    qm_status st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
+    if (st != QM_OK) return st;
+    Timed tm(stream, QM_K_Q8_UPDATE);
+    const NormIn nz{section<int32_t>(dev_plan, h->off_block_group), inv};
+    if (ro && ro->rounding == QM_ROUND_STOCHASTIC)
+        launch_update_all<true, false, kOutNorm>(h, dev_plan, beta, nullptr, SrParams{ro->seed, ro->offset},
+                                                 CarrierOut{nullptr, nullptr, 0}, stream, nz);
+    else
+        launch_update_all<false, false, kOutNorm>(h, dev_plan, beta, nullptr, SrParams{0, 0},
+                                                  CarrierOut{nullptr, nullptr, 0}, stream, nz);
+    return check_launch("q8 normalising update");
 }
 
 UpdateWorkspace update_workspace(const PlanHeader *h, void *ws) {
@@ -865,14 +1010,13 @@ qm_status run_update_normalize(const PlanHeader *h, const void *dev_plan, float 
     const UpdateWorkspace w = update_workspace(h, ws);
     float *inv = inv_out ? inv_out : w.inv;
     double *sums = sums_out ? sums_out : w.group_sums;
+    if (write_normalized && !carrier_data)
+        return launch_update_normalized(h, dev_plan, beta, w, eps, sums, inv, ro, stream);
     const CarrierOut co{carrier_data, carrier_scale, 0};
     qm_status st = launch_update(h, dev_plan, beta, w.block_sums, ro, carrier_data ? &co : nullptr, stream,
                                  host_plan, tall, n_tall);
     if (st != QM_OK) return st;
-    st = launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
-    if (st != QM_OK) return st;
-    if (write_normalized) st = launch_scale(h, dev_plan, inv, stream);
-    return st;
+    return launch_group_reduce(h, dev_plan, w.block_sums, w.partials, eps, sums, inv, stream);
 }
 
 qm_status check_carrier(const PlanHeader *h, const void *host_plan, const void *data, const void *scale) {

@@ -174,7 +174,7 @@ def test_timing_recorder_host_checks():
     q.timing_enable(False)
     for k in q.KERNEL_CLASSES:
         assert q.timing_read(k) == (0.0, 0)
-    assert sorted(q.KERNEL_CLASSES.values()) == list(range(9))
+    assert sorted(q.KERNEL_CLASSES.values()) == list(range(10))
 
 
 @pytest.mark.parametrize("c1,ld1,off1,c2,ld2,off2,status", [

@@ -4,6 +4,7 @@ bounds ask for.  The figures are the compiler's resource-usage remarks,
 which quantized_momentum_newton_amd/build.py records in
 _build/kernel_resources.tsv; the test is skipped when no build left it."""
 import os
+import re
 
 import pytest
 
@@ -21,7 +22,7 @@ def _rows():
 
 def test_every_kernel_was_recorded():
     names = " ".join(r["kernel"] for r in _rows())
-    for k in ("q8_update_kernel", "q8_update_tcar_kernel", "q8_scale_kernel", "chunk_reduce_kernel",
+    for k in ("q8_update_kernel", "q8_update_tcar_kernel", "q8_sums_kernel", "chunk_reduce_kernel",
               "gemm_nt_kernel", "gram_mx_kernel", "prologue_kernel", "writeback_kernel", "hbm_stream_kernel"):
         assert k in names, k
 
@@ -35,8 +36,10 @@ def test_no_kernel_spills():
 def test_update_kernels_keep_their_occupancy():
     """The 16-bit-grad update kernels (nearest rounding) stream at 8 waves
     per SIMD in 64 VGPRs; one more register halves the waves in flight."""
-    rows = [r for r in _rows() if "q8_update_kernelILi1E" in r["kernel"] or "q8_update_kernelILi2E" in r["kernel"]]
-    rows = [r for r in rows if "ELb0ELb0EE" in r["kernel"] or "ELb0ELb1EE" in r["kernel"]]   # no stochastic rounding
-    assert rows
+    # template <dtype, sums, stochastic rounding, carrier, output mode>: bf16 / f16, nearest
+    # and the read-only sums pass of the normalising update, per dtype
+    pat = re.compile(r"q8_update_kernelILi[12]ELb[01]ELb0ELb[01]ELi[02]EE|q8_sums_kernelILi[12]EE")
+    rows = [r for r in _rows() if pat.search(r["kernel"])]
+    assert len(rows) == 2 * (4 + 1 + 1), [r["kernel"] for r in rows]   # per dtype: plain / carrier x sums, normalising, sums pass
     for r in rows:
         assert int(r["vgprs"]) <= 64 and int(r["occupancy"]) >= 8, (r["kernel"], r["vgprs"], r["occupancy"])

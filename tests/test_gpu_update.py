@@ -241,9 +241,12 @@ def test_launch_timing_records_each_kernel_class():
     q.timing_enable(False)
     q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
     torch.cuda.synchronize()
-    for k in ("q8_update", "group_reduce", "q8_scale"):
+    # the normalising update: a sums pass, the group reduction, the update
+    # writing normalised values (no separate scale pass)
+    for k in ("q8_sums", "group_reduce", "q8_update"):
         ms, n = q.timing_read(k)
         assert n == 2 and ms > 0.0, (k, ms, n)
+    assert q.timing_read("q8_scale") == (0.0, 0)
     assert q.timing_read("ns_gram") == (0.0, 0)
 
 
