@@ -459,12 +459,17 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
             }
         }
         if constexpr (CAR) {
+            // E8M0 byte: biased exponent of xmax minus 8, 0 for zero / tiny blocks
+            const uint32_t xe = __float_as_uint(xmax) >> 23;
+            const uint32_t sb = xe > 8u ? xe - 8u : 0u;
+            // lane l (l % 4 LPX == 0) collects the bytes of the four carrier
+            // blocks from l on, stored as one word (all lanes take part)
+            uint32_t sb4 = sb;
+#pragma unroll
+            for (int k = 1; k < 4; k++) sb4 |= (uint32_t)__shfl_down((int)sb, k * LPX) << (8 * k);
             // numel is a multiple of 32, so a carrier block is all valid or all past the end
             if (e0 < nvalid) {
                 store_codes_vec<EPL>(codes, e0, q);
-                // E8M0 byte: biased exponent of xmax minus 8, 0 for zero / tiny blocks
-                const uint32_t xe = __float_as_uint(xmax) >> 23;
-                const uint32_t sb = xe > 8u ? xe - 8u : 0u;
                 const float inv_s = __uint_as_float((254u - sb) << 23);   // 2^(127 - sb), exact
                 uint32_t w[EPL / 4];
 #pragma unroll
@@ -479,7 +484,13 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                     *reinterpret_cast<uint2 *>(co.data + ce) = make_uint2(w[0], w[1]);
                 else
                     *reinterpret_cast<uint32_t *>(co.data + ce) = w[0];
-                if ((lane % LPX) == 0) co.scale[ce / 32] = (uint8_t)sb;
+                if ((lane % (4 * LPX)) == 0) {
+                    const int nb = (nvalid - e0) / 32;   // carrier blocks of the four inside the tensor
+                    if (nb >= 4)
+                        *reinterpret_cast<uint32_t *>(co.scale + ce / 32) = sb4;   // ce / 32 is a multiple of 4
+                    else
+                        for (int k = 0; k < nb; k++) co.scale[ce / 32 + k] = (uint8_t)(sb4 >> (8 * k));
+                }
             }
         } else {
             // kOutNorm: the product is pinned to an fp32 register (empty asm)
@@ -730,12 +741,18 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
         __syncthreads();   // cmax and cinv are rewritten by the next pass
     }
     {
-        const int c = threadIdx.x;
-        uint8_t *dst = co.data + T.block_offset * kBlock + (c0 + c) * it.rows + r0;
+        // the tile's carrier rows (columns c0 .. c0 + 255 of m) hold kTallRows
+        // bytes each: CPR threads store one row as 16-byte pieces, so a wave
+        // writes 64 / CPR whole row segments at a time
+        constexpr int CPR = kTallRows / 16;
+        uint8_t *dst0 = co.data + T.block_offset * kBlock + c0 * it.rows + r0;
 #pragma unroll
-        for (int q = 0; q < kTallRows / 16; q++)
-            *reinterpret_cast<uint4 *>(dst + 16 * q) =
-                make_uint4(tbytes[c][4 * q], tbytes[c][4 * q + 1], tbytes[c][4 * q + 2], tbytes[c][4 * q + 3]);
+        for (int q = 0; q < CPR; q++) {
+            const int c = (q * 256 + threadIdx.x) / CPR, k = threadIdx.x % CPR;
+            *reinterpret_cast<uint4 *>(dst0 + (int64_t)c * it.rows + 16 * k) =
+                make_uint4(tbytes[c][4 * k], tbytes[c][4 * k + 1], tbytes[c][4 * k + 2], tbytes[c][4 * k + 3]);
+        }
+        const int c = threadIdx.x;
         uint8_t *sdst = co.scale + T.block_offset * (kBlock / 32) + (c0 + c) * (it.rows / 32) + r0 / 32;
         if constexpr (kTallPasses == 4) *reinterpret_cast<uint32_t *>(sdst) = sbyte[c];
         else
