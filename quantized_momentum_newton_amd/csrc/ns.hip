@@ -21,11 +21,13 @@
 //     of any shapes): tiles of all matrices form one index space, the matrix
 //     with the longest K first, so 256 CUs stay busy even when one matrix
 //     alone has few tiles.
-//   * 256x256 output tiles, four waves of 128x128 (accumulators in AGPRs),
-//     K-tiles of 128 bytes per row double-buffered in LDS and filled by
-//     direct global-to-LDS loads (no staging registers); a 16-byte XOR
-//     swizzle keeps the 16-byte fragment reads free of bank conflicts
-//     (64 banks: 16 lanes per cycle).
+//   * 256x256 output tiles, eight waves of 128x64 (two per SIMD, fp32
+//     accumulators in registers), K-tiles of 128 bytes per row in a ring of
+//     five one-operand LDS slots filled by direct global-to-LDS loads (no
+//     staging registers); a 16-byte XOR swizzle keeps the 16-byte fragment
+//     reads free of bank conflicts (64 banks: 16 lanes per cycle).  fp32
+//     runs on matrices too small for a full round of 256x256 tiles take
+//     128x128 or 64x64 tiles.
 //   * Tiles are ordered in bands of 4 tile rows walked column by column, and
 //     each XCD's 32 concurrent workgroups cover a 4x8 block of tiles (12
 //     operand panels shared in that XCD's L2).  A symmetric product of
