@@ -1,0 +1,68 @@
+"""GPU parity of whole-matrix Muon steps on seeded random sets of matrices.
+
+Each case draws 2-7 matrices of random shapes (multiples of 32 from 32 to
+1280 on each side, tall, wide and square mixed), so one step's grouped
+products cover matrices of different K, partial 256-tiles, and symmetric
+launches of several rounds whose tiles are dealt over the XCDs; some cases
+carry no weights, some use fp32-operand NS.  The int8 state must match the
+oracle bit for bit, the NS output and the weight change within the bound of
+the NS precision.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_momentum_newton_amd as q
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_BF16OUT_REL, NS_F32_COS, as_f64, assert_bits_equal, host,
+                      host_grad, ns_parity, say)
+from harness import inputs as H
+from oracle import muonbp
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+COEF = tuple(float(np.float32(c)) for c in H.NS_COEFFS)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_matrix_sets_full_step(case):
+    rng = np.random.default_rng(7700 + case)
+    n = int(rng.integers(2, 8))
+    shapes = [(32 * int(rng.integers(1, 41)), 32 * int(rng.integers(1, 41))) for _ in range(n)]
+    precision = "f32" if case % 4 == 3 else "bf16"
+    with_w = [bool(rng.integers(0, 4)) for _ in range(n)]
+    wd = float(rng.choice([0.0, 0.01]))
+    t = int(rng.integers(1, 30))
+    say("random set", case, shapes, precision, "weights", with_w, "wd", wd, "t", t)
+    trip, mats, W0, states, gh = [], [], [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 7800 + case, i)
+        g = H.grad((r, c), torch.bfloat16, DEV, 7800 + case, i).reshape(-1)
+        w = H.weights((r, c), DEV, 7800 + case, i) if with_w[i] else None
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, w))
+    torch.cuda.synchronize()
+    for i in range(n):
+        states.append((host(trip[i][0]), host(trip[i][1])))
+        gh.append(host_grad(trip[i][2]))
+        W0.append(as_f64(mats[i][4]) if with_w[i] else None)
+    plan = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)], n)
+    hp = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, lr_block=0.01, weight_decay=wd,
+                        rms_scale=0.2, ns_steps=5, period=1, precision=precision)
+    q.muon_step(plan, None, mats, t, hp)
+    torch.cuda.synchronize()
+    lim_rel, lim_cos = (NS_BF16_REL, NS_BF16_COS) if precision == "bf16" else (NS_F32_BF16OUT_REL, NS_F32_COS)
+    for i, (r, c) in enumerate(shapes):
+        Wref = W0[i] if with_w[i] else np.zeros((r, c))
+        W2, c2, a2, O, is_full = muonbp.muon_step(Wref, states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c, r,
+                                                  c, 1, 0.95, 1e-7, COEF, 5, 0.02, 0.01, 0.2, wd)
+        assert is_full
+        assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
+        rel, cos = ns_parity(as_f64(trip[i][2]).reshape(r, c), O)
+        say(f"   O[{i}] {r}x{c}: relF {rel:.3e} min cos {cos:.6f}")
+        assert rel <= lim_rel and cos >= lim_cos, (i, rel, cos)
+        if with_w[i]:
+            rel, cos = ns_parity(as_f64(mats[i][4]) - W0[i], W2 - W0[i])
+            say(f"   dW[{i}]: relF {rel:.3e} min cos {cos:.6f}")
+            assert rel <= lim_rel and cos >= lim_cos, (i, rel, cos)
