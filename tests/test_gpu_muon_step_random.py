@@ -1,12 +1,14 @@
-"""GPU parity of whole-matrix Muon steps on seeded random sets of matrices.
+"""GPU parity of Muon steps on seeded random sets of matrices.
 
-Each case draws 2-7 matrices of random shapes (multiples of 32 from 32 to
+Whole-matrix steps: each case draws 2-7 matrices of random shapes (multiples of 32 from 32 to
 1280 on each side, tall, wide and square mixed), so one step's grouped
 products cover matrices of different K, partial 256-tiles, and symmetric
 launches of several rounds whose tiles are dealt over the XCDs; some cases
 carry no weights, some use fp32-operand NS.  The int8 state must match the
 oracle bit for bit, the NS output and the weight change within the bound of
-the NS precision.
+the NS precision.  Block steps: 1-3 matrices cut into random block grids
+(block columns of 256 or 512, block rows of 32 to 512), every block checked
+against its own NS bound.
 """
 import numpy as np
 import pytest
@@ -66,3 +68,62 @@ def test_random_matrix_sets_full_step(case):
             rel, cos = ns_parity(as_f64(mats[i][4]) - W0[i], W2 - W0[i])
             say(f"   dW[{i}]: relF {rel:.3e} min cos {cos:.6f}")
             assert rel <= lim_rel and cos >= lim_cos, (i, rel, cos)
+
+
+def _blocked_plans(trip, mats):
+    full = q.Plan(trip, [(i, 0, r * c, i) for i, (r, c, _, _, _) in enumerate(mats)], len(mats))
+    segs, g0 = [], 0
+    for i, (r, c, br, bc, _) in enumerate(mats):
+        s, ng = H.blocked_segments(r, c, br, bc, i, g0)
+        segs += s
+        g0 += ng
+    return full, q.Plan(trip, segs, g0)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_block_partitions_block_step(case):
+    """Block steps (t not a multiple of P = 5) on random block partitions:
+    every block its own NS in one grouped launch, blocks of different shapes
+    and orientations across the matrices."""
+    rng = np.random.default_rng(7900 + case)
+    n = int(rng.integers(1, 4))
+    mats_spec = []
+    for _ in range(n):
+        ncb = int(rng.integers(1, 5))                 # column blocks of 256 * k columns
+        bc = 256 * int(rng.integers(1, 3))
+        nrb = int(rng.integers(1, 5))
+        br = 32 * int(rng.integers(1, 17))
+        mats_spec.append((nrb * br, ncb * bc, br, bc))
+    t = int(rng.choice([1, 2, 3, 4, 6, 7]))
+    say("random blocks", case, mats_spec, "t", t)
+    trip, mats, W0, states, gh = [], [], [], [], []
+    for i, (r, c, br, bc) in enumerate(mats_spec):
+        codes, absmax = H.prior_state(r * c, DEV, 7950 + case, i)
+        g = H.grad((r, c), torch.bfloat16, DEV, 7950 + case, i).reshape(-1)
+        w = H.weights((r, c), DEV, 7950 + case, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, br, bc, w))
+    torch.cuda.synchronize()
+    for i in range(n):
+        states.append((host(trip[i][0]), host(trip[i][1])))
+        gh.append(host_grad(trip[i][2]))
+        W0.append(as_f64(mats[i][4]))
+    full, block = _blocked_plans(trip, mats)
+    hp = q.make_hparams(beta=0.95, eps=1e-7, coeffs=COEF, lr_full=0.02, lr_block=0.01, weight_decay=0.01,
+                        rms_scale=0.2, ns_steps=5, period=5)
+    q.muon_step(full, block, mats, t, hp)
+    torch.cuda.synchronize()
+    for i, (r, c, br, bc) in enumerate(mats_spec):
+        W2, c2, a2, O, is_full = muonbp.muon_step(W0[i], states[i][0], states[i][1], gh[i], oracle.BF16, t, r, c, br,
+                                                  bc, 5, 0.95, 1e-7, COEF, 5, 0.02, 0.01, 0.2, 0.01)
+        assert not is_full
+        assert_bits_equal(host(trip[i][0]), c2, f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), a2, f"absmax[{i}]")
+        got = as_f64(trip[i][2]).reshape(r, c)
+        for bi in range(r // br):          # every block against its own bound
+            for bj in range(c // bc):
+                sl = (slice(bi * br, (bi + 1) * br), slice(bj * bc, (bj + 1) * bc))
+                rel, cos = ns_parity(got[sl], O[sl])
+                assert rel <= NS_BF16_REL and cos >= NS_BF16_COS, (i, bi, bj, rel, cos)
+        rel, cos = ns_parity(as_f64(mats[i][4]) - W0[i], W2 - W0[i])
+        assert rel <= NS_BF16_REL and cos >= NS_BF16_COS, (i, rel, cos)
