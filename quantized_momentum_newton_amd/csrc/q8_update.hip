@@ -267,7 +267,7 @@ struct CarrierOut {
 // The two passes move 9.05 bytes per bf16 element (grad, codes and absmax
 // read twice, written once) where the update followed by a scale pass moves
 // 10.03: re-reading the state costs less than re-reading and rewriting m.
-enum { kOutM = 0, kOutNorm = 2 };
+enum { kOutM = 0, kOutNorm = 1 };
 struct NormIn {
     const int32_t *block_group;   // group of every block of the plan
     const float *inv;             // inverse norm of every group
@@ -280,8 +280,8 @@ template <int DT> __device__ __forceinline__ float stored(float v) {
     else return f16_val(f16_rne(v));
 }
 
-// One task's inputs as a lane holds them, still packed as loaded (so a
-// wave can hold several tasks' loads in flight): per part, its kEpl codes
+// One task's inputs as a lane holds them, still packed as loaded (all of a
+// task's loads are issued before any arithmetic): per part, its kEpl codes
 // (four per word) and grads (16 bytes), zero past the tensor's end, and its
 // block's step absmax / 127.
 template <int DT> struct TaskIn {

@@ -38,7 +38,7 @@ def test_update_kernels_keep_their_occupancy():
     per SIMD in 64 VGPRs; one more register halves the waves in flight."""
     # template <dtype, sums, stochastic rounding, carrier, output mode>: bf16 / f16, nearest
     # and the read-only sums pass of the normalising update, per dtype
-    pat = re.compile(r"q8_update_kernelILi[12]ELb[01]ELb0ELb[01]ELi[02]EE|q8_sums_kernelILi[12]EE")
+    pat = re.compile(r"q8_update_kernelILi[12]ELb[01]ELb0ELb[01]ELi[01]EE|q8_sums_kernelILi[12]EE")
     rows = [r for r in _rows() if pat.search(r["kernel"])]
     assert len(rows) == 2 * (4 + 1 + 1), [r["kernel"] for r in rows]   # per dtype: plain / carrier x sums, normalising, sums pass
     for r in rows:
