@@ -17,7 +17,11 @@ two symmetric products at lower-triangle cost).  `roofline` is for the
 dominant kernel (the one with the largest share of device time, measured live
 per launch with the library's event timer over the timed steps: the
 X <- aX + BX product, MFMA bound); `roofline_update` for the HBM-bound q8
-update kernel.  `traffic` is filled from the committed counter summary only
+update kernel.  The event timer runs on the even-numbered timed steps only:
+its events cost the stream about 14 us per update call and 0.1 ms per step,
+so value, ns_tflops and per_step_ms come from the odd-numbered steps, the
+per-kernel figures from the even ones; ms_per_step is the whole timed region
+over all steps.  `traffic` is filled from the committed counter summary only
 while the kernel source still has the hash recorded there.  `cpu_baseline`
 times the CPU oracle on a bounded sample of the same workload.
 
@@ -45,7 +49,7 @@ rank 8: steps/s, state-path GB/s and f32 NS TFLOP/s against the fp32 peak),
 --workload fp32_256x512 (one small fp32 matrix, latency in us per step),
 --workload hbm_stream (the library's stream copy at the update's byte counts:
 the achievable HBM rate of a 50/50 read/write stream).
-per_step_ms gives the 10/50/90th percentiles of the per-step event times.
+per_step_ms gives the 10/50/90th percentiles of the per-step event times (odd-numbered steps).
 """
 import argparse
 import hashlib
@@ -207,25 +211,18 @@ def bench_grasp(args, q, H, torch):
     st = q.GraspState(rows, cols, k)
     ws = torch.empty(q.grasp_workspace_bytes(rows, cols, k), dtype=torch.uint8, device=dev)
     g = torch.empty_like(grads[0])
-    evs = []
-    for t in range(args.warmup + args.steps):
-        g.copy_(grads[t % 4])
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        if t == args.warmup:
-            torch.cuda.synchronize()
-            q.timing_enable(True)
+    def step(i, e):
+        g.copy_(grads[(i - 1) % 4])
         e[0].record()
         q.grasp_step(st, g, warm, mu=cfg["mu"], ns_steps=H.NS_STEPS, coeffs=H.NS_COEFFS, eps=H.NS_EPS, ws=ws,
                      ns_precision=args.ns_precision)
         e[1].record()
-        if t >= args.warmup:
-            evs.append(e)
-    torch.cuda.synchronize()
-    q.timing_enable(False)
-    ms = [a.elapsed_time(b) for a, b in evs]
+
+    evs, pc, _ = timed_steps(args, torch, q, step, 2)
+    ms = [evs[k][0].elapsed_time(evs[k][1]) for k in call_steps(args.steps)]
     step_ms = sum(ms) / len(ms)
-    ns_ms = sum(q.timing_read(c)[0] for c in ("ns_norm", "ns_prologue", "ns_gram", "ns_poly", "ns_xupdate",
-                                                "ns_writeback")) / args.steps
+    ns_ms = sum(pc[c][0] for c in ("ns_norm", "ns_prologue", "ns_gram", "ns_poly", "ns_xupdate",
+                                   "ns_writeback")) / len(timer_steps(args.steps))
     state_ms = step_ms - ns_ms
     numel = rows * cols
     state_bytes = numel * 15.25             # three passes over the fp32 momentum plus the codes
@@ -307,25 +304,42 @@ def bench_hbm_stream(args, q, H, torch):
             "config": {"workload": "hbm_stream_copy", "sizes": out}}
 
 
+def timer_steps(n):
+    """Timed steps that run the library's per-kernel timer: the even-numbered
+    ones.  Its events ride on the dispatches but still cost the stream a few
+    microseconds per launch group (about 14 us on the headline update call),
+    so whole-call figures come from the other steps (all of them when fewer
+    than two are timed)."""
+    return [k for k in range(n) if k % 2 == 0]
+
+
+def call_steps(n):
+    return [k for k in range(n) if k % 2 == 1] if n >= 2 else list(range(n))
+
+
 def timed_steps(args, torch, q, step, n_events):
     """Warm-up steps, then args.steps timed steps with n_events HIP events per
-    step (recorded on torch's current stream, which the library launches on)
-    and the library's per-kernel timer on.  step(i, events): i counts from 1
-    over warm-up and timed steps.  Returns (per-step event lists, per-class
-    (ms, launches), total ms)."""
+    step (recorded on torch's current stream, which the library launches on),
+    the library's per-kernel timer on the steps timer_steps names.
+    step(i, events): i counts from 1 over warm-up and timed steps.  Returns
+    (per-step event lists, per-class (ms, launches) over the timer steps,
+    total ms)."""
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
     for i in range(1, args.warmup + 1):
         step(i, mk())
     evs = [mk() for _ in range(args.steps)]
+    timed = set(timer_steps(args.steps))
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    q.timing_enable(True)
     start.record()
     for k in range(args.steps):
+        if k in timed:
+            q.timing_enable(True, resume=k > 0)
         step(args.warmup + 1 + k, evs[k])
+        if k in timed:
+            q.timing_enable(False)
     stop.record()
     torch.cuda.synchronize()
-    q.timing_enable(False)
     return evs, {k: q.timing_read(k) for k in q.KERNEL_CLASSES}, start.elapsed_time(stop)
 
 
@@ -349,7 +363,8 @@ def extra_layerset28(args, q, H, torch):
         ev[1].record()
 
     evs, pc, total = timed_steps(args, torch, q, step, 2)
-    ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    cs = call_steps(args.steps)
+    ms = sum(evs[k][0].elapsed_time(evs[k][1]) for k in cs) / len(cs)
     gbs = numel * (BYTES_PER_ELEM_UPDATE + BYTES_PER_ELEM_SCALE) / (ms * 1e-3) / 1e9
     moved = numel * (BYTES_PER_ELEM_UPDATE + BYTES_PER_ELEM_SUMS) / (ms * 1e-3) / 1e9
     upd_ms, n = pc["q8_update"]
@@ -400,15 +415,17 @@ def extra_muonbp(args, q, H, torch):
             kinds.append(is_full)
 
     evs, pc, total = timed_steps(args, torch, q, step, 3)
-    ns_ms = sum(e[1].elapsed_time(e[2]) for e in evs)
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    cs = call_steps(args.steps)
+    ns_ms = sum(evs[k][1].elapsed_time(evs[k][2]) for k in cs)
+    step_ms = [evs[k][0].elapsed_time(evs[k][2]) for k in cs]
     m_b, n_b = min(br, bc), max(br, bc)
     m_f, n_f = min(r, c), max(r, c)
     nblk = (r // br) * (c // bc)
-    fl = sum(ns_sym_flops(r, c, H.NS_STEPS) if f else nblk * ns_sym_flops(br, bc, H.NS_STEPS) for f in kinds)
-    # algorithmic work of every launch of each product class over the region
-    n_full = sum(kinds)
-    n_blk = len(kinds) - n_full
+    fl = sum(ns_sym_flops(r, c, H.NS_STEPS) if kinds[k] else nblk * ns_sym_flops(br, bc, H.NS_STEPS) for k in cs)
+    # algorithmic work of every launch of each product class over the timer steps
+    tk = [kinds[k] for k in timer_steps(args.steps)]
+    n_full = sum(tk)
+    n_blk = len(tk) - n_full
     T = H.NS_STEPS
     work = {"ns_gram": T * (n_full * m_f * (m_f + 1) * n_f + n_blk * nblk * m_b * (m_b + 1) * n_b),
             "ns_poly": T * (n_full * m_f * m_f * (m_f + 1) + n_blk * nblk * m_b * m_b * (m_b + 1)),
@@ -420,7 +437,8 @@ def extra_muonbp(args, q, H, torch):
     return {"value": round(1000.0 * len(step_ms) / sum(step_ms), 3), "unit": "steps/s",
             "ms_per_step": round(sum(step_ms) / len(step_ms), 4), "per_step_ms": percentiles(step_ms),
             "ns_tflops": round(tfl, 2), "ns_frac": round(tfl / BF16_PEAK_TFLOPS, 4),
-            "ns_ms_total": round(ns_ms, 3), "ns_flops_total": fl, "full_steps": n_full, "block_steps": n_blk,
+            "ns_ms_total": round(ns_ms, 3), "ns_flops_total": fl,
+            "full_steps": sum(kinds[k] for k in cs), "block_steps": sum(not kinds[k] for k in cs),
             "config": {"workload": "muonbp_4096x14336_P5", "blocks": nblk, "block_shape": [br, bc],
                        "ns_steps": T, "ns_precision": "bf16"},
             "roofline": rl,
@@ -548,36 +566,23 @@ def bench_layer(args, q, H, torch):
             ev[1].record()
             ev[2].record()
 
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    for t in range(1, args.warmup + 1):
-        step(t, mk())
-    torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    q.timing_enable(True)
-    start.record()
-    for t in range(args.steps):
-        step(args.warmup + 1 + t, evs[t])
-    stop.record()
-    torch.cuda.synchronize()
-    q.timing_enable(False)
-    total_ms = start.elapsed_time(stop)
-    per_class = {k: q.timing_read(k) for k in q.KERNEL_CLASSES}
+    evs, per_class, total_ms = timed_steps(args, torch, q, step, 3)
+    cs = call_steps(args.steps)
+    n_timer = len(timer_steps(args.steps))
     if args.ref_copy_mib > 0:
         src = torch.empty(args.ref_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    upd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    ns_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    upd_ms = sum(evs[k][0].elapsed_time(evs[k][1]) for k in cs) / len(cs)
+    ns_ms = sum(evs[k][1].elapsed_time(evs[k][2]) for k in cs) / len(cs)
     if args.carrier and args.workload == "llama8b":
         call_ms = upd_ms
-        upd_ms = (per_class["q8_update"][0] + per_class["group_reduce"][0]) / args.steps
+        upd_ms = (per_class["q8_update"][0] + per_class["group_reduce"][0]) / n_timer
         ns_ms = call_ms - upd_ms
     ms_per_step = total_ms / args.steps
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    step_ms = [evs[k][0].elapsed_time(evs[k][2]) for k in cs]
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 4), "per_step_ms": percentiles(step_ms), "higher_is_better": True,

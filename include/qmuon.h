@@ -464,12 +464,16 @@ QM_API qm_status grasp_step(const qm_grasp_state *state, int64_t rows,
 /* ------------------------------------------------------------------------
  * Launch timing (measurement aid, off by default).
  *
- * While enabled, every launch of the classes below is bracketed by two HIP
- * events recorded on the launch stream, so a reader gets the same per-launch
- * device time a kernel-trace profiler reports.  Enabling clears earlier
- * records; disabling keeps them for qm_timing_read.  Not for use inside HIP
- * graph capture.  The recorder is process-wide and locked; launches from
- * several threads are recorded but interleave in one list.
+ * While enabled, the launches of each class below carry two HIP events on
+ * their dispatches (hipExtLaunchKernel: the start event on the first kernel
+ * of the class's launch group, the stop event on its last), so a reader gets
+ * the same per-launch device time a kernel-trace profiler reports.  The events
+ * still cost the stream a few microseconds per launch group, so a caller
+ * timing whole calls may record on some steps only (mode 2 below).  Enabling
+ * clears earlier records unless resumed with mode 2; disabling keeps them for
+ * qm_timing_read.  Not for use inside HIP graph capture.  The recorder is
+ * process-wide and locked; launches from several threads are recorded but
+ * interleave in one list.
  */
 typedef enum {
     QM_K_Q8_UPDATE = 0,     /* blockwise q8 momentum update kernel */
@@ -486,8 +490,9 @@ typedef enum {
     QM_K_CLASSES = 10
 } qm_kernel_class;
 
-/* on != 0: clear records and start recording; on == 0: stop.
- * Errors: QM_E_HIP (event creation failed). */
+/* on == 1: clear records and start recording; on == 2: resume recording,
+ * keeping the records so far; on == 0: stop.
+ * Errors: QM_E_ARG (another value), QM_E_HIP (event creation failed). */
 QM_API qm_status qm_timing_enable(int32_t on);
 
 /* Sum of the recorded launch durations of one class (milliseconds) and the

@@ -92,9 +92,10 @@ KERNEL_CLASSES = {"q8_update": 0, "group_reduce": 1, "q8_scale": 2, "ns_norm": 3
                   "ns_gram": 5, "ns_poly": 6, "ns_xupdate": 7, "ns_writeback": 8, "q8_sums": 9}
 
 
-def timing_enable(on=True):
-    """Start (clearing earlier records) or stop recording launch times."""
-    _check(_LIB.qm_timing_enable(1 if on else 0))
+def timing_enable(on=True, resume=False):
+    """Start (clearing earlier records), resume (keeping them) or stop
+    recording launch times."""
+    _check(_LIB.qm_timing_enable((2 if resume else 1) if on else 0))
 
 
 def timing_read(kernel_class):

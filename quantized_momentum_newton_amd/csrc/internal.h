@@ -17,17 +17,36 @@ struct PlanHeader;
 const PlanHeader *plan_header(const void *host_blob, qm_status *st);
 
 // Launch timing: while qm_timing_enable(1) is in effect, a Timed object
-// records a HIP event on `stream` when built and another when destroyed,
-// bracketing the launches of its scope under kernel class `cls`.
+// opens a record of kernel class `cls`: a pair of HIP events.  The launches
+// of its scope made through launch() (launch.h) carry the events on their
+// dispatches (the start event on the first, the stop event on every one, so
+// it ends up on the last), which puts no separate event packets between the
+// kernels on the stream.  A scope that launched nothing leaves no record.
+// The innermost open scope of the calling thread takes the launches.
+struct TimedScope {
+    void *start = nullptr, *stop = nullptr;   // hipEvent_t
+    int token = -1;
+    bool started = false;
+    TimedScope *outer = nullptr;
+};
+TimedScope *&timed_current();
 bool timing_on();
-int timing_begin(void *stream, int cls);
-void timing_end(void *stream, int token);
+int timing_begin(int cls, void **start, void **stop);
+void timing_end(int token, bool launched);
 struct Timed {
-    void *stream;
-    int token;
-    Timed(void *s, int cls) : stream(s), token(timing_on() ? timing_begin(s, cls) : -1) {}
+    TimedScope sc;
+    Timed(void * /*stream*/, int cls) {
+        if (timing_on()) sc.token = timing_begin(cls, &sc.start, &sc.stop);
+        if (sc.token >= 0) {
+            sc.outer = timed_current();
+            timed_current() = &sc;
+        }
+    }
     ~Timed() {
-        if (token >= 0) timing_end(stream, token);
+        if (sc.token >= 0) {
+            timed_current() = sc.outer;
+            timing_end(sc.token, sc.started);
+        }
     }
     Timed(const Timed &) = delete;
     Timed &operator=(const Timed &) = delete;

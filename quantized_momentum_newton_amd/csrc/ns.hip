@@ -48,6 +48,7 @@
 
 #include "grasp_internal.h"
 #include "internal.h"
+#include "launch.h"
 #include "plan_layout.h"
 #include "q8_internal.h"
 #include "qmuon.h"
@@ -1451,7 +1452,7 @@ qm_status launch_gemm(GemmArgs<T> args, int tiles, hipStream_t stream) {
     args.xcd = SYM && use_xcd(args, tiles, C::MINB) ? 1 : 0;
     const int grid = args.xcd ? xcd_grid(args, tiles) : tiles;
     Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, stream, args);
+    launch(kern, dim3(grid), dim3(NT), lds, stream, args);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "gemm launch: %s", hipGetErrorString(e));
     return QM_OK;
@@ -1465,7 +1466,7 @@ qm_status launch_gram_mx(MxGramArgs args, int tiles, hipStream_t stream) {
     args.xcd = use_xcd(args, tiles, 1) ? 1 : 0;
     const int grid = args.xcd ? xcd_grid(args, tiles) : tiles;
     Timed tm(stream, QM_K_NS_GRAM);
-    hipLaunchKernelGGL(gram_mx_kernel, dim3(grid), dim3(512), kMxGramLds, stream, args);
+    launch(gram_mx_kernel, dim3(grid), dim3(512), kMxGramLds, stream, args);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "mx gram launch: %s", hipGetErrorString(e));
     return QM_OK;
@@ -1706,12 +1707,12 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     }
     if (need_norm) {
         Timed tm(stream, QM_K_NS_NORM);
-        norm_partial_kernel<<<dim3(kNormChunks, nit), 256, 0, stream>>>(pa, partials);
-        norm_final_kernel<<<nit, 64, 0, stream>>>(partials, eps, inv_ws);
+        launch(norm_partial_kernel, dim3(kNormChunks, nit), 256, 0, stream, pa, partials);
+        launch(norm_final_kernel, nit, 64, 0, stream, partials, eps, inv_ws);
     }
     {
         Timed tm(stream, QM_K_NS_PROLOGUE);
-        prologue_kernel<T><<<tiles, 256, 0, stream>>>(pa);
+        launch(prologue_kernel<T>, tiles, 256, 0, stream, pa);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "prologue: %s", hipGetErrorString(e));
@@ -1759,7 +1760,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         for (int i = 0; i < nit; i++) pa.it[i].X = bufs[i].X[cur[i]];
     {
         Timed tm(stream, QM_K_NS_WRITEBACK);
-        writeback_kernel<T><<<tiles, 256, 0, stream>>>(pa, wb);
+        launch(writeback_kernel<T>, tiles, 256, 0, stream, pa, wb);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return fail(QM_E_HIP, "writeback: %s", hipGetErrorString(e));

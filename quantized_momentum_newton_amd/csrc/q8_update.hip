@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "launch.h"
 #include "plan_layout.h"
 #include "q8_internal.h"
 #include "qmuon.h"
@@ -883,13 +884,13 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
     const int grid = stream_grid(hi - lo);
     if constexpr (OUT == kOutNorm)
-        q8_update_kernel<DT, false, SR, false, OUT><<<grid, kThreads, 0, stream>>>(
+        launch(q8_update_kernel<DT, false, SR, false, OUT>, grid, kThreads, 0, stream,
             tens, toff, tt, h->n_tensors, lo, hi, beta, nullptr, sr, co, nz);
     else if (block_sums)
-        q8_update_kernel<DT, true, SR, CAR, OUT><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+        launch(q8_update_kernel<DT, true, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors, lo, hi,
                                                                                beta, block_sums, sr, co, nz);
     else
-        q8_update_kernel<DT, false, SR, CAR, OUT><<<grid, kThreads, 0, stream>>>(tens, toff, tt, h->n_tensors, lo, hi,
+        launch(q8_update_kernel<DT, false, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors, lo, hi,
                                                                                 beta, nullptr, sr, co, nz);
 }
 
@@ -913,9 +914,9 @@ void launch_tall_dt(const PlanHeader *h, const void *host_plan, const void *dev_
         if (ta.n == 0) return;
         const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
         if (block_sums)
-            q8_update_tcar_kernel<DT, true><<<(unsigned)tiles, kThreads, 0, stream>>>(tens, ta, beta, block_sums, co);
+            launch(q8_update_tcar_kernel<DT, true>, (unsigned)tiles, kThreads, 0, stream, tens, ta, beta, block_sums, co);
         else
-            q8_update_tcar_kernel<DT, false><<<(unsigned)tiles, kThreads, 0, stream>>>(tens, ta, beta, nullptr, co);
+            launch(q8_update_tcar_kernel<DT, false>, (unsigned)tiles, kThreads, 0, stream, tens, ta, beta, nullptr, co);
         ta = TallArgs{};
         tiles = 0;
     };
@@ -962,12 +963,12 @@ qm_status launch_group_reduce(const PlanHeader *h, const void *dev_plan, const d
     const int64_t *ro = section<int64_t>(dev_plan, h->off_run_offsets);
     const int64_t *co = section<int64_t>(dev_plan, h->off_chunk_offsets);
     Timed tm(stream, QM_K_GROUP_REDUCE);
-    chunk_reduce_kernel<<<(unsigned)h->n_chunks, kThreads, 0, stream>>>(
+    launch(chunk_reduce_kernel, (unsigned)h->n_chunks, kThreads, 0, stream,
         ro, section<PlanRun>(dev_plan, h->off_runs), co, section<int32_t>(dev_plan, h->off_chunk_group),
         block_sums, partials);
     qm_status st = check_launch("chunk reduce");
     if (st != QM_OK) return st;
-    group_final_kernel<<<(unsigned)h->n_groups, 64, 0, stream>>>(co, partials, eps, group_sums, inv);
+    launch(group_final_kernel, (unsigned)h->n_groups, 64, 0, stream, co, partials, eps, group_sums, inv);
     return check_launch("group reduce");
 }
 
@@ -975,7 +976,7 @@ template <int DT>
 void launch_sums_dt(const PlanHeader *h, const void *dev_plan, float beta, double *block_sums, hipStream_t stream) {
     const int64_t lo = h->dt_task_lo[DT], hi = h->dt_task_hi[DT];
     if (hi <= lo) return;
-    q8_sums_kernel<DT><<<std::min(stream_grid(hi - lo), kSumsGrid), kThreads, 0, stream>>>(
+    launch(q8_sums_kernel<DT>, std::min(stream_grid(hi - lo), kSumsGrid), kThreads, 0, stream,
         section<PlanTensor>(dev_plan, h->off_tensors), section<int64_t>(dev_plan, h->off_task_offsets),
         section<int32_t>(dev_plan, h->off_task_tensor), h->n_tensors, lo, hi, beta, block_sums);
 }

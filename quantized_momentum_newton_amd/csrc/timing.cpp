@@ -1,9 +1,9 @@
 // Launch timing recorder behind qm_timing_enable / qm_timing_read.
 //
 // A pool of HIP event pairs is reused across enable cycles; each Timed scope
-// takes the next pair, records its start event on the launch stream, and
-// records the end event when the scope closes.  Reading waits on the end
-// events and sums hipEventElapsedTime per kernel class.
+// takes the next pair, and the scope's launches carry it on their dispatches
+// (launch.h).  Reading waits on the stop events and sums
+// hipEventElapsedTime per kernel class.
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
@@ -29,7 +29,12 @@ std::atomic<bool> g_on{false};
 
 bool timing_on() { return g_on.load(std::memory_order_relaxed); }
 
-int timing_begin(void *stream, int cls) {
+TimedScope *&timed_current() {
+    static thread_local TimedScope *cur = nullptr;
+    return cur;
+}
+
+int timing_begin(int cls, void **start, void **stop) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_on) return -1;
     if (g_used == g_pool.size()) {
@@ -43,14 +48,15 @@ int timing_begin(void *stream, int cls) {
     }
     Rec &r = g_pool[g_used];
     r.cls = cls;
-    if (hipEventRecord(r.start, static_cast<hipStream_t>(stream)) != hipSuccess) return -1;
+    *start = r.start;
+    *stop = r.stop;
     return (int)g_used++;
 }
 
-void timing_end(void *stream, int token) {
+void timing_end(int token, bool launched) {
     std::lock_guard<std::mutex> lk(g_mu);
     if (token < 0 || (size_t)token >= g_used) return;
-    (void)hipEventRecord(g_pool[(size_t)token].stop, static_cast<hipStream_t>(stream));
+    if (!launched) g_pool[(size_t)token].cls = -1;   // no kernel carried the events
 }
 
 }  // namespace qm
@@ -59,8 +65,9 @@ using namespace qm;
 
 extern "C" qm_status qm_timing_enable(int32_t on) {
     clear_error();
+    if (on < 0 || on > 2) return fail(QM_E_ARG, "timing mode %d (0 stop, 1 start, 2 resume)", (int)on);
     std::lock_guard<std::mutex> lk(g_mu);
-    if (on) g_used = 0;
+    if (on == 1) g_used = 0;
     g_on = on != 0;
     return QM_OK;
 }

@@ -170,7 +170,10 @@ def test_timing_recorder_host_checks():
     assert LIB.qm_timing_read(99, ctypes.byref(ms), ctypes.byref(n)) == 1  # QM_E_ARG
     assert LIB.qm_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == 1  # QM_E_ARG
     assert LIB.qm_timing_read(0, None, ctypes.byref(n)) == 1  # QM_E_ARG
+    assert LIB.qm_timing_enable(3) == 1 and LIB.qm_timing_enable(-1) == 1   # QM_E_ARG: modes 0, 1, 2 only
     q.timing_enable(True)
+    q.timing_enable(False)
+    q.timing_enable(True, resume=True)
     q.timing_enable(False)
     for k in q.KERNEL_CLASSES:
         assert q.timing_read(k) == (0.0, 0)

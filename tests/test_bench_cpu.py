@@ -20,3 +20,21 @@ def test_bench_help_lists_the_workloads():
     assert r.returncode == 0
     for w in ("llama8b", "layerset28", "muonbp", "grasp", "fp32_256x512"):
         assert w in r.stdout
+
+
+def test_timer_and_call_steps_split_the_timed_steps():
+    """The per-kernel timer runs on the even-numbered timed steps, whole-call
+    figures come from the odd ones; together they are every step once, and a
+    20-step MuonBP region (P = 5) keeps its 4 : 1 block/full mix in both."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for n in range(1, 41):
+        t, c = bench.timer_steps(n), bench.call_steps(n)
+        assert t and c
+        if n >= 2:
+            assert sorted(t + c) == list(range(n)) and not set(t) & set(c)
+        else:
+            assert t == c == [0]
+    full = [(k + 1) % 5 == 0 for k in range(20)]
+    for idx in (bench.timer_steps(20), bench.call_steps(20)):
+        assert sum(full[k] for k in idx) == 2 and len(idx) == 10

@@ -229,17 +229,21 @@ def test_determinism_and_canaries():
 
 
 def test_launch_timing_records_each_kernel_class():
-    """The event timer sees one launch per kernel class per call, with a
-    positive duration, and nothing while it is off."""
+    """The event timer sees one launch group per kernel class per call, with
+    a positive duration, nothing while it is off, and keeps its records
+    across a resume.  The q8 update here is two launches (a bf16 and an fp32
+    tensor): the class's one record spans both."""
     qs = Q8Set([(4096, 512), (1000,)], [torch.bfloat16, torch.float32], seed=1011)
     plan = q.Plan(qs.triples(), [(0, 0, 4096 * 512, 0), (1, 0, 1000, 1)], 2)
     inv = torch.empty(2, dtype=torch.float32, device=DEV)
-    say("launch timing: update+normalize twice")
+    say("launch timing: update+normalize timed, untimed, resumed")
     q.timing_enable(True)
-    for _ in range(2):
-        q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
     q.timing_enable(False)
     q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    q.timing_enable(True, resume=True)
+    q.qmuon_update_normalize_groups(plan, H.BETA, H.NS_EPS, True, group_inv_norm=inv)
+    q.timing_enable(False)
     torch.cuda.synchronize()
     # the normalising update: a sums pass, the group reduction, the update
     # writing normalised values (no separate scale pass)
@@ -248,6 +252,17 @@ def test_launch_timing_records_each_kernel_class():
         assert n == 2 and ms > 0.0, (k, ms, n)
     assert q.timing_read("q8_scale") == (0.0, 0)
     assert q.timing_read("ns_gram") == (0.0, 0)
+    say("launch timing: NS of one 512 x 768 matrix, T = 5")
+    x = H.grad((512, 768), torch.bfloat16, DEV, 1012, 0)
+    q.timing_enable(True)
+    q.ns_orthogonalize(x, steps=5)
+    q.timing_enable(False)
+    torch.cuda.synchronize()
+    for k, want in (("ns_norm", 1), ("ns_prologue", 1), ("ns_gram", 5), ("ns_poly", 5), ("ns_xupdate", 5),
+                    ("ns_writeback", 1)):
+        ms, n = q.timing_read(k)
+        assert n == want and ms > 0.0, (k, ms, n)
+    assert q.timing_read("q8_update") == (0.0, 0)
 
 
 def _fused_views(rows, widths, pad, dtype, seed):
