@@ -36,14 +36,55 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerWG = kThreads / 64;
 
+// ------------------------------------------------------------ global pointers
+
+// A device address as a pointer the compiler knows points to global memory.
+// The tensor addresses the plan holds, and the pointers inside argument
+// structs, are otherwise generic, and their accesses compile to flat
+// instructions: a 64-bit address per lane, and both the vector-memory and
+// the LDS counters, so each wait for a lane shuffle's result also waits for
+// the outstanding loads and stores.
+template <typename T> __device__ __forceinline__ T *gmem(uint64_t a) {
+    return (T *)(__attribute__((address_space(1))) T *)a;
+}
+template <typename T> __device__ __forceinline__ T *gmem(T *p) { return gmem<T>((uint64_t)p); }
+
+// ------------------------------------------------------------ lane exchange
+
+// Lane l's value from lane l ^ k.  For k < 32 (inside l's 32-lane half) a
+// ds_swizzle in bit-mask mode, which needs no lane-address register, unlike
+// the generic shuffle used for k = 32.  Every lane must be active.
+__device__ __forceinline__ int xor_lanes(int v, int k) {
+    switch (k) {
+        case 1: return __builtin_amdgcn_ds_swizzle(v, 0x041f);
+        case 2: return __builtin_amdgcn_ds_swizzle(v, 0x081f);
+        case 4: return __builtin_amdgcn_ds_swizzle(v, 0x101f);
+        case 8: return __builtin_amdgcn_ds_swizzle(v, 0x201f);
+        case 16: return __builtin_amdgcn_ds_swizzle(v, 0x401f);
+        default: return __shfl_xor(v, k);
+    }
+}
+__device__ __forceinline__ float xor_lanes(float v, int k) { return __int_as_float(xor_lanes(__float_as_int(v), k)); }
+__device__ __forceinline__ double xor_lanes(double v, int k) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)xor_lanes((int)(uint32_t)u, k), hi = (uint32_t)xor_lanes((int)(uint32_t)(u >> 32), k);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // ------------------------------------------------------------ conversions
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// Two fp32 values to packed bf16 (a in the low half), round to nearest even,
+// a NaN kept quiet with its sign and top payload bits: gfx950's
+// v_cvt_pk_bf16_f32, one instruction for the pair.  It gives the same bits as
+// the integer form (add 0x7fff plus the kept lsb, shift; NaN: top half | 0x40)
+// for every fp32 input, subnormals and NaNs included (checked exhaustively
+// on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)bf16x2_rne(f, 0.0f); }
 __device__ __forceinline__ float bf16_val(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 __device__ __forceinline__ uint16_t f16_rne(float f) {
@@ -130,9 +171,8 @@ template <int DT> __device__ __forceinline__ void store_grad_vec(void *g, int64_
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            const uint32_t lo = DT == QM_BF16 ? bf16_rne(in[2 * k]) : f16_rne(in[2 * k]);
-            const uint32_t hi = DT == QM_BF16 ? bf16_rne(in[2 * k + 1]) : f16_rne(in[2 * k + 1]);
-            w[k] = lo | (hi << 16);
+            if constexpr (DT == QM_BF16) w[k] = bf16x2_rne(in[2 * k], in[2 * k + 1]);
+            else w[k] = (uint32_t)f16_rne(in[2 * k]) | ((uint32_t)f16_rne(in[2 * k + 1]) << 16);
         }
         v.x = w[0]; v.y = w[1]; v.z = w[2]; v.w = w[3];
     }
@@ -152,21 +192,20 @@ template <int N> __device__ __forceinline__ void load_codes_vec(const int8_t *c,
         for (int k = 0; k < 4; k++) q[k] = (int8_t)(v >> (8 * k));
     }
 }
-template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int64_t e, const int8_t *q) {
+// Four codes from the low bytes of a, b, c, d (a in the lowest byte): three
+// byte permutes.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);   // a.0, b.0, 0, 0
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);   // c.0, d.0, 0, 0
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // a.0, b.0, c.0, d.0
+}
+// N codes, each the low byte of q[j], stored at element offset e.
+template <int N> __device__ __forceinline__ void store_codes_vec(int8_t *c, int64_t e, const uint32_t *q) {
     if constexpr (N == 8) {
-        uint2 v = {0u, 0u};
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            v.x |= (uint32_t)(uint8_t)q[k] << (8 * k);
-            v.y |= (uint32_t)(uint8_t)q[4 + k] << (8 * k);
-        }
-        ntv2 nv = {v.x, v.y};
+        ntv2 nv = {pack_low_bytes(q[0], q[1], q[2], q[3]), pack_low_bytes(q[4], q[5], q[6], q[7])};
         __builtin_nontemporal_store(nv, reinterpret_cast<ntv2 *>(c + e));
     } else {
-        uint32_t v = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) v |= (uint32_t)(uint8_t)q[k] << (8 * k);
-        *reinterpret_cast<uint32_t *>(c + e) = v;
+        *reinterpret_cast<uint32_t *>(c + e) = pack_low_bytes(q[0], q[1], q[2], q[3]);
     }
 }
 
@@ -303,20 +342,33 @@ template <int DT> __device__ __forceinline__ float grad_elem(const uint32_t *gw,
     }
 }
 
-template <int DT>
+// DEFER: the block maxima are loaded with the codes and grads and divided
+// only once all of the task's loads are in flight (a lane past the tensor's
+// end reads its task's last valid block and keeps step 0); otherwise each
+// part's step is formed before its codes and grads are loaded.  Measured:
+// deferring makes the grid-stride sums pass about 2 % faster and the
+// one-task-per-wave update kernels up to 6 % slower.
+template <int DT, bool DEFER>
 __device__ __forceinline__ void load_task(const PlanTensor &T, int64_t lt, int lane, TaskIn<DT> &in) {
     constexpr int EPL = TaskIn<DT>::EPL, PARTS = TaskIn<DT>::PARTS, ES = Elem<DT>::kSize;
     const int64_t e_task = lt * kTaskElems;
     const int64_t rem = T.numel - e_task;
     const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
     in.nvalid = nvalid;
-    const int8_t *codes = reinterpret_cast<const int8_t *>(T.codes) + e_task;
-    const float *absmax = reinterpret_cast<const float *>(T.absmax) + lt * kBlocksPerTask;
-    const char *grad = reinterpret_cast<const char *>(T.grad);   // addressed through gpos
+    const int8_t *codes = gmem<const int8_t>(T.codes) + e_task;
+    const float *absmax = gmem<const float>(T.absmax) + lt * kBlocksPerTask;
+    const char *grad = gmem<const char>(T.grad);   // addressed through gpos
+    float am[PARTS];
+    if constexpr (DEFER)
+#pragma unroll
+        for (int p = 0; p < PARTS; p++) {
+            const int e0 = p * 64 * EPL + lane * EPL;
+            am[p] = absmax[(e0 < nvalid ? e0 : nvalid - 1) / kBlock];
+        }
 #pragma unroll
     for (int p = 0; p < PARTS; p++) {
         const int e0 = p * 64 * EPL + lane * EPL;
-        in.step[p] = e0 < nvalid ? absmax[e0 / kBlock] / 127.0f : 0.0f;
+        if constexpr (!DEFER) in.step[p] = e0 < nvalid ? absmax[e0 / kBlock] / 127.0f : 0.0f;
         if (e0 + EPL <= nvalid) {
             const ntv4 v = __builtin_nontemporal_load(reinterpret_cast<const ntv4 *>(grad + gpos(T, e_task + e0) * ES));
             in.gw[p][0] = v.x; in.gw[p][1] = v.y; in.gw[p][2] = v.z; in.gw[p][3] = v.w;
@@ -341,6 +393,9 @@ __device__ __forceinline__ void load_task(const PlanTensor &T, int64_t lt, int l
             }
         }
     }
+    if constexpr (DEFER)
+#pragma unroll
+        for (int p = 0; p < PARTS; p++) in.step[p] = p * 64 * EPL + lane * EPL < nvalid ? am[p] / 127.0f : 0.0f;
 }
 
 // m = beta (q step) + (1 - beta) g: two rounded products and a rounded sum
@@ -370,7 +425,7 @@ template <int DT> __device__ __forceinline__ double block_sum(const float *mp) {
         s += d * d;
     }
 #pragma unroll
-    for (int off = 1; off < LPB; off <<= 1) s += __shfl_xor(s, off);
+    for (int off = 1; off < LPB; off <<= 1) s += xor_lanes(s, off);
     return s;
 }
 
@@ -384,41 +439,39 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
     constexpr int LPB = kBlock / EPL;  // lanes per block
     constexpr int LPX = 32 / EPL;      // lanes per 32-element carrier block
     const int64_t e_task = lt * kTaskElems;
-    int8_t *codes = reinterpret_cast<int8_t *>(T.codes) + e_task;
-    float *absmax = reinterpret_cast<float *>(T.absmax) + lt * kBlocksPerTask;
-    void *grad = reinterpret_cast<void *>(T.grad);   // addressed through gpos
+    int8_t *codes = gmem<int8_t>(T.codes) + e_task;
+    float *absmax = gmem<float>(T.absmax) + lt * kBlocksPerTask;
+    void *grad = gmem<void>(T.grad);   // addressed through gpos
 
     const int64_t rem = T.numel - e_task;
     const int nvalid = rem < kTaskElems ? (int)rem : kTaskElems;
     float m[PARTS][EPL];
     float gscale[PARTS];   // kOutNorm: the inverse norm of each part's block
+    {
+        // kOutNorm: each part's group (one group: wave-uniform, else the
+        // block's entry) is looked up first, so that its inverse norm, which
+        // depends on it, can be loaded while the task's loads are in flight
+        int grp[PARTS];
 #pragma unroll
-    for (int p = 0; p < PARTS; p++) {
-        const int e0 = p * 64 * EPL + lane * EPL;
-        const int kb = e0 / kBlock;
-        float step = 0.0f;
-        gscale[p] = 0.0f;
-        if (e0 < nvalid) {
-            step = absmax[kb] / 127.0f;
-            if constexpr (OUT == kOutNorm)   // one group: a wave-uniform load, else the block's group
-                gscale[p] = nz.inv[T.group_lo == T.group_hi ? T.group_lo
-                                                             : nz.block_group[T.block_offset + lt * kBlocksPerTask + kb]];
+        for (int p = 0; p < PARTS; p++) {
+            const int e0 = p * 64 * EPL + lane * EPL;
+            grp[p] = -1;
+            if constexpr (OUT == kOutNorm)
+                if (e0 < nvalid)
+                    grp[p] = T.group_lo == T.group_hi
+                                 ? T.group_lo
+                                 : gmem(nz.block_group)[T.block_offset + lt * kBlocksPerTask + e0 / kBlock];
         }
-        int8_t q[EPL];
-        float g[EPL];
-        if (e0 + EPL <= nvalid) {
-            load_codes_vec<EPL>(codes, e0, q);
-            load_grad_vec<DT>(grad, gpos(T, e_task + e0), g);
-        } else {
+        TaskIn<DT> in;
+        load_task<DT, false>(T, lt, lane, in);   // every load of the task before any arithmetic
 #pragma unroll
-            for (int j = 0; j < EPL; j++) {
-                const bool ok = e0 + j < nvalid;
-                q[j] = ok ? codes[e0 + j] : (int8_t)0;
-                g[j] = ok ? widen<DT>(grad, gpos(T, e_task + e0 + j)) : 0.0f;
-            }
+        for (int p = 0; p < PARTS; p++) {
+            gscale[p] = 0.0f;
+            if constexpr (OUT == kOutNorm)
+                if (grp[p] >= 0) gscale[p] = gmem(nz.inv)[grp[p]];
         }
 #pragma unroll
-        for (int j = 0; j < EPL; j++) m[p][j] = ema1(q[j], step, g[j], beta, omb);
+        for (int p = 0; p < PARTS; p++) ema_part<DT>(in, p, beta, omb, m[p]);
     }
 
 #pragma unroll
@@ -431,12 +484,12 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         // the first butterfly stages reduce over the lanes of one 32-element
         // carrier block, the rest over the 256-element block
 #pragma unroll
-        for (int off = 1; off < LPX; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        for (int off = 1; off < LPX; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
         const float xmax = amax;
 #pragma unroll
-        for (int off = LPX; off < LPB; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        for (int off = LPX; off < LPB; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
         const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
-        int8_t q[EPL];
+        uint32_t q[EPL];   // codes in the low bytes
         if constexpr (SR) {
             // floor(x) + 1 with probability frac(x); u = top 24 bits * 2^-24
             uint32_t w[EPL];
@@ -449,15 +502,16 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                 const float u = (float)(w[j] >> 8) * 0x1p-24f;
                 float r = u < x - fl ? fl + 1.0f : fl;
                 r = fminf(fmaxf(r, -127.0f), 127.0f);
-                q[j] = (int8_t)(int)r;
+                q[j] = (uint32_t)(int)r;
             }
         } else {
+            // clamped, then rounded to nearest even by adding 1.5 * 2^23, whose
+            // ulp is 1: the sum's low byte is the code in two's complement.
+            // The same codes as rounding first and clamping after (|x| <= 127
+            // but for rounding; a NaN clamps to -127 either way).
 #pragma unroll
-            for (int j = 0; j < EPL; j++) {
-                float r = rintf(m[p][j] * inv);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                q[j] = (int8_t)(int)r;
-            }
+            for (int j = 0; j < EPL; j++)
+                q[j] = __float_as_uint(fminf(fmaxf(m[p][j] * inv, -127.0f), 127.0f) + 0x1.8p23f);
         }
         if constexpr (CAR) {
             // E8M0 byte: biased exponent of xmax minus 8, 0 for zero / tiny blocks
@@ -482,15 +536,15 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
                 }
                 const int64_t ce = T.block_offset * kBlock + e_task + e0;
                 if constexpr (EPL == 8)
-                    *reinterpret_cast<uint2 *>(co.data + ce) = make_uint2(w[0], w[1]);
+                    *reinterpret_cast<uint2 *>(gmem(co.data) + ce) = make_uint2(w[0], w[1]);
                 else
-                    *reinterpret_cast<uint32_t *>(co.data + ce) = w[0];
+                    *reinterpret_cast<uint32_t *>(gmem(co.data) + ce) = w[0];
                 if ((lane % (4 * LPX)) == 0) {
                     const int nb = (nvalid - e0) / 32;   // carrier blocks of the four inside the tensor
                     if (nb >= 4)
-                        *reinterpret_cast<uint32_t *>(co.scale + ce / 32) = sb4;   // ce / 32 is a multiple of 4
+                        *reinterpret_cast<uint32_t *>(gmem(co.scale) + ce / 32) = sb4;   // ce / 32 is a multiple of 4
                     else
-                        for (int k = 0; k < nb; k++) co.scale[ce / 32 + k] = (uint8_t)(sb4 >> (8 * k));
+                        for (int k = 0; k < nb; k++) gmem(co.scale)[ce / 32 + k] = (uint8_t)(sb4 >> (8 * k));
                 }
             }
         } else {
@@ -514,7 +568,7 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
 #pragma unroll
                 for (int j = 0; j < EPL; j++)
                     if (e0 + j < nvalid) {
-                        codes[e0 + j] = q[j];
+                        codes[e0 + j] = (int8_t)q[j];
                         narrow<DT>(grad, gpos(T, e_task + e0 + j), y[j]);
                     }
             }
@@ -530,11 +584,15 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
 
 // One launch per grad dtype present, over that dtype's task range (the plan
 // orders the task space by dtype), so each kernel carries one element path.
-// The update is bound by how many bytes are in flight per CU: specialised,
-// the 16-bit paths fit 8 waves per SIMD in 64 VGPRs and the fp32 path 6
-// waves in 80, without spills (the kernel with all three element paths took
-// 112 VGPRs, i.e. 4 waves).
-// With stochastic rounding the Philox state costs registers: 6 waves.
+// Specialised, the kernels fit 7-8 waves per SIMD (60-72 VGPRs) without
+// spills; the launch bound asks for at least 8 on the 16-bit paths and 6 on
+// the fp32 and stochastic-rounding ones (the kernel with all three element
+// paths took 112 VGPRs, i.e. 4 waves).  Counters put the bf16 update near
+// the VALU's limit as well as the memory's (about 415 VALU instructions per
+// 1024-element task, 72 % of the VALU's cycles, before the last cuts), so
+// per-element instructions matter: the hardware bf16 conversion, rounding by
+// an added constant, byte permutes for the code words, swizzles for the
+// butterflies, global rather than flat accesses.
 template <int DT, bool SR> constexpr int update_wgs_per_cu() { return DT == QM_F32 || SR ? 6 : 8; }
 
 template <int DT, bool SUMS, bool SR, bool CAR, int OUT>
@@ -584,7 +642,7 @@ __global__ __launch_bounds__(kThreads, (update_wgs_per_cu<DT, false>())) void q8
         const PlanTensor T = tensors[task_tensor[pos]];
         const int64_t lt = task - T.task_offset;
         TaskIn<DT> in;
-        load_task<DT>(T, lt, lane, in);
+        load_task<DT, true>(T, lt, lane, in);
         const int64_t boff = T.block_offset + lt * kBlocksPerTask;
 #pragma unroll
         for (int p = 0; p < PARTS; p++) {
@@ -645,8 +703,8 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
     const int64_t tr = t / it.tiles_c, tc = t % it.tiles_c;
     const int64_t r0 = kTallRows * tr, c0 = 256 * tc;
     const PlanTensor T = tensors[it.tensor];
-    int8_t *codes = reinterpret_cast<int8_t *>(T.codes);
-    float *absmax = reinterpret_cast<float *>(T.absmax);
+    int8_t *codes = gmem<int8_t>(T.codes);
+    float *absmax = gmem<float>(T.absmax);
     const float omb = 1.0f - beta;
     sbyte[threadIdx.x] = 0;
 
@@ -666,8 +724,8 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
             kb[i] = (r * it.cols + c0) / kBlock;   // the row segment's block
             step[i] = absmax[kb[i]] / 127.0f;
             qv[i] = *reinterpret_cast<const uint2 *>(codes + e);
-            load_grad_vec<DT>(reinterpret_cast<const void *>(T.grad), gpos(T, e), g[i]);
-            if constexpr (DT == QM_F32) load_grad_vec<DT>(reinterpret_cast<const void *>(T.grad), gpos(T, e) + 4, g[i] + 4);
+            load_grad_vec<DT>(gmem<const void>(T.grad), gpos(T, e), g[i]);
+            if constexpr (DT == QM_F32) load_grad_vec<DT>(gmem<const void>(T.grad), gpos(T, e) + 4, g[i] + 4);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -685,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
                 cm[j] = fmaxf(cm[j], fabsf(m[i][j]));
             }
 #pragma unroll
-            for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+            for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
             const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
             uint2 qo = {0u, 0u};
 #pragma unroll
@@ -705,7 +763,7 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
                     sq += d * d;
                 }
 #pragma unroll
-                for (int off = 1; off < 32; off <<= 1) sq += __shfl_xor(sq, off);
+                for (int off = 1; off < 32; off <<= 1) sq += xor_lanes(sq, off);
                 if (cl == 0) block_sums[T.block_offset + kb[i]] = sq;
             }
             if (cl == 0) absmax[kb[i]] = amax;
@@ -746,7 +804,7 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
         // bytes each: CPR threads store one row as 16-byte pieces, so a wave
         // writes 64 / CPR whole row segments at a time
         constexpr int CPR = kTallRows / 16;
-        uint8_t *dst0 = co.data + T.block_offset * kBlock + c0 * it.rows + r0;
+        uint8_t *dst0 = gmem(co.data) + T.block_offset * kBlock + c0 * it.rows + r0;
 #pragma unroll
         for (int q = 0; q < CPR; q++) {
             const int c = (q * 256 + threadIdx.x) / CPR, k = threadIdx.x % CPR;
@@ -754,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
                 make_uint4(tbytes[c][4 * k], tbytes[c][4 * k + 1], tbytes[c][4 * k + 2], tbytes[c][4 * k + 3]);
         }
         const int c = threadIdx.x;
-        uint8_t *sdst = co.scale + T.block_offset * (kBlock / 32) + (c0 + c) * (it.rows / 32) + r0 / 32;
+        uint8_t *sdst = gmem(co.scale) + T.block_offset * (kBlock / 32) + (c0 + c) * (it.rows / 32) + r0 / 32;
         if constexpr (kTallPasses == 4) *reinterpret_cast<uint32_t *>(sdst) = sbyte[c];
         else
 #pragma unroll
