@@ -25,6 +25,12 @@
  *   - the EMA is two separately rounded products and one rounded sum (no FMA);
  *   - "nearest" rounding is round-half-to-even (rintf in the default mode);
  *   - an all-zero block stores codes 0 and absmax 0;
+ *   - requantisation: x = m * (127 / amax), rounded, clamped to [-127, 127]
+ *     with fmaxf / fminf (which return the number when the other operand is
+ *     NaN, so a NaN m codes as -127); for a block so small (amax < 2^-64)
+ *     that 127 / amax could overflow, m and amax are both scaled by 2^64
+ *     first, which is exact and leaves x unchanged wherever 127 / amax is
+ *     finite (a zero element then stays 0 instead of 0 * inf);
  *   - the new absmax is taken over the fp32 m (before rounding m to the grad
  *     dtype), and so is the block sum of squares;
  *   - block sums of squares are accumulated in fp64 (squares of fp32 values
@@ -55,6 +61,18 @@
 #define OR_BLOCK 256
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F16 = 2 };
+
+/* ----------------------------------------------------------- requantise */
+
+/* x = (m * s) * inv with s and inv from here: s = 2^64 for amax < 2^-64
+ * (amax * s is exact), else 1; inv = 127 / (amax * s). */
+static inline void requant_scale(float amax, float *s, float *inv) {
+    *s = amax < 0x1p-64f ? 0x1p64f : 1.0f;
+    *inv = 127.0f / (amax * *s);
+}
+
+/* A rounded value clamped to [-127, 127] (NaN -> -127). */
+static inline int8_t code_of(float q) { return (int8_t)fminf(fmaxf(q, -127.0f), 127.0f); }
 
 /* ---------------------------------------------------------------- dtypes */
 
@@ -219,9 +237,10 @@ void or_q8_update_ex(int8_t *codes, float *absmax, void *grad, int dtype,
         if (amax == 0.0f) {
             for (int64_t i = lo; i < hi; i++) codes[i] = 0;
         } else {
-            const float inv = 127.0f / amax;
+            float sc, inv;
+            requant_scale(amax, &sc, &inv);
             for (int64_t i = lo; i < hi; i++) {
-                const float x = m[i - lo] * inv;
+                const float x = (m[i - lo] * sc) * inv;
                 float q;
                 if (rounding == OR_ROUND_STOCHASTIC) {
                     const float fl = floorf(x);
@@ -229,9 +248,7 @@ void or_q8_update_ex(int8_t *codes, float *absmax, void *grad, int dtype,
                 } else {
                     q = rintf(x);
                 }
-                if (q > 127.0f) q = 127.0f;
-                if (q < -127.0f) q = -127.0f;
-                codes[i] = (int8_t)q;
+                codes[i] = code_of(q);
             }
         }
         absmax[b] = amax;
@@ -353,13 +370,9 @@ void or_q8_update_carrier(int8_t *codes, float *absmax, const void *grad, int dt
         if (amax == 0.0f) {
             for (int64_t i = lo; i < hi; i++) codes[i] = 0;
         } else {
-            const float inv = 127.0f / amax;
-            for (int64_t i = lo; i < hi; i++) {
-                float q = rintf(m[i - lo] * inv);
-                if (q > 127.0f) q = 127.0f;
-                if (q < -127.0f) q = -127.0f;
-                codes[i] = (int8_t)q;
-            }
+            float sc, inv;
+            requant_scale(amax, &sc, &inv);
+            for (int64_t i = lo; i < hi; i++) codes[i] = code_of(rintf((m[i - lo] * sc) * inv));
         }
         absmax[b] = amax;
         if (block_sumsq) {
@@ -410,13 +423,9 @@ void or_q8_update_carrier_t(int8_t *codes, float *absmax, const void *grad, int 
         if (amax == 0.0f) {
             for (int64_t i = lo; i < hi; i++) codes[i] = 0;
         } else {
-            const float inv = 127.0f / amax;
-            for (int64_t i = lo; i < hi; i++) {
-                float q = rintf(m[i] * inv);
-                if (q > 127.0f) q = 127.0f;
-                if (q < -127.0f) q = -127.0f;
-                codes[i] = (int8_t)q;
-            }
+            float sc, inv;
+            requant_scale(amax, &sc, &inv);
+            for (int64_t i = lo; i < hi; i++) codes[i] = code_of(rintf((m[i] * sc) * inv));
         }
         absmax[b] = amax;
         if (block_sumsq) {

@@ -71,6 +71,19 @@ __device__ __forceinline__ double xor_lanes(double v, int k) {
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// ------------------------------------------------------------ requantisation scale
+
+// x = (m * s) * inv: s = 2^64 for a block so small (0 < amax < 2^-64) that
+// 127 / amax could overflow, else 1; inv = 127 / (amax * s), 0 for an
+// all-zero block.  Scaling by a power of two is exact, so x is
+// m * (127 / amax) wherever that quotient is finite; in the tiny range the
+// codes stay those of nearest rounding (a zero element stays 0 instead of
+// 0 * inf).
+__device__ __forceinline__ float requant_inv(float amax, float &s) {
+    s = amax > 0.0f && amax < 0x1p-64f ? 0x1p64f : 1.0f;
+    return amax == 0.0f ? 0.0f : 127.0f / (amax * s);
+}
+
 // ------------------------------------------------------------ conversions
 
 // Two fp32 values to packed bf16 (a in the low half), round to nearest even,
@@ -488,7 +501,14 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
         const float xmax = amax;
 #pragma unroll
         for (int off = LPX; off < LPB; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
-        const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+        float sc;
+        const float inv = requant_inv(amax, sc);
+        float mx[EPL];   // m, scaled by sc only when some lane of the wave has a tiny block
+#pragma unroll
+        for (int j = 0; j < EPL; j++) mx[j] = m[p][j];
+        if (__any(sc != 1.0f))
+#pragma unroll
+            for (int j = 0; j < EPL; j++) mx[j] = m[p][j] * sc;
         uint32_t q[EPL];   // codes in the low bytes
         if constexpr (SR) {
             // floor(x) + 1 with probability frac(x); u = top 24 bits * 2^-24
@@ -497,7 +517,7 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
             for (int k = 0; k < EPL; k += 4) sr_words(e_task + e0 + k, sr, tensor, w + k);
 #pragma unroll
             for (int j = 0; j < EPL; j++) {
-                const float x = m[p][j] * inv;
+                const float x = mx[j] * inv;
                 const float fl = floorf(x);
                 const float u = (float)(w[j] >> 8) * 0x1p-24f;
                 float r = u < x - fl ? fl + 1.0f : fl;
@@ -511,7 +531,7 @@ __device__ __forceinline__ void update_task(const PlanTensor &T, int64_t lt, flo
             // but for rounding; a NaN clamps to -127 either way).
 #pragma unroll
             for (int j = 0; j < EPL; j++)
-                q[j] = __float_as_uint(fminf(fmaxf(m[p][j] * inv, -127.0f), 127.0f) + 0x1.8p23f);
+                q[j] = __float_as_uint(fminf(fmaxf(mx[j] * inv, -127.0f), 127.0f) + 0x1.8p23f);
         }
         if constexpr (CAR) {
             // E8M0 byte: biased exponent of xmax minus 8, 0 for zero / tiny blocks
@@ -744,11 +764,12 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
             }
 #pragma unroll
             for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
-            const float inv = amax == 0.0f ? 0.0f : 127.0f / amax;
+            float sc;
+            const float inv = requant_inv(amax, sc);
             uint2 qo = {0u, 0u};
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                float q = rintf(m[i][j] * inv);
+                float q = rintf((m[i][j] * sc) * inv);
                 q = fminf(fmaxf(q, -127.0f), 127.0f);
                 const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q << (8 * (j & 3));
                 if (j < 4) qo.x |= b;

@@ -416,3 +416,73 @@ def test_nonfinite_grad_stays_in_its_block():
     assert_bits_equal(codes.reshape(16, 256)[keep].ravel(), c_ref.reshape(16, 256)[keep].ravel(), "codes, finite blocks")
     assert_bits_equal(absmax[keep], a_ref[keep], "absmax, finite blocks")
     assert codes.min() >= -127 and codes.max() <= 127
+    # the oracle's reading for non-finite m (NaN codes -127, an infinite
+    # block maximum makes 127 / amax zero) holds on the GPU as well
+    assert_bits_equal(codes, c_ref, "codes, all blocks")
+    assert_bits_equal(absmax, a_ref, "absmax, all blocks")
+
+
+def _absmax_giving(target_bits, qv):
+    """A block absmax a with fl(qv * fl(a / 127)) equal to the fp32 value of
+    target_bits (searched among a's neighbours in fp32), or None."""
+    t = np.array([target_bits], dtype=np.uint32).view(np.float32)[0]
+    g64 = np.float64(t) * 127.0 / qv
+    if not (0 < g64 < np.finfo(np.float32).max):
+        return None
+    guess = np.float32(g64)
+    gi = np.array([guess], dtype=np.float32).view(np.int32)[0]
+    for d in sorted(range(-400, 401), key=abs):
+        a = np.array([gi + d], dtype=np.int32).view(np.float32)[0]
+        if not np.isfinite(a) or a <= 0:
+            continue
+        step = np.float32(a) / np.float32(127.0)
+        with np.errstate(over="ignore"):
+            m = np.float32(qv) * step
+        if m.view(np.uint32) == np.uint32(target_bits):
+            return a
+    return None
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_grad_rounding_edge_values_match_oracle(dtype):
+    """With beta = 1, m is the dequantised state q * (absmax / 127) exactly, so
+    chosen block maxima put m on the narrowing's edge cases: bf16 and f16
+    rounding ties with an even and an odd kept bit, one ulp either side of a
+    tie, fp32 subnormals (ties among them), values that round to the largest
+    finite value or to infinity, and the smallest normals.  The grad's bits,
+    codes and absmax must match the oracle, whose rounding is integer
+    arithmetic on the bit patterns."""
+    targets = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x40C38000, 0x41818000,
+               0x00808000, 0x00818000, 0x00008000, 0x00018000, 0x00000001, 0x007FFFFF, 0x00400000,
+               0x7F7F8000, 0x7F7F7FFF, 0x7F7FFFFF, 0x7E808000, 0x00800000,
+               # f16: ties at 13 dropped bits, the f16 subnormal range, the largest finite f16
+               0x3F801000, 0x3F803000, 0x3F800FFF, 0x33801000, 0x33803000, 0x477FE000, 0x477FF000, 0x38801000]
+    blocks, absmax, codes = [], [], []
+    rng = np.random.default_rng(2025)
+    for tb in targets:
+        for qv in (1, 127, 3):
+            a = _absmax_giving(tb, qv)
+            if a is None:
+                continue
+            c = rng.integers(-127, 128, size=256).astype(np.int8)
+            c[:64] = qv
+            c[64:128] = -qv
+            blocks.append(tb)
+            absmax.append(a)
+            codes.append(c)
+    say("grad rounding edge values:", len(blocks), "blocks", dtype)
+    assert len(blocks) >= 40
+    n = 256 * len(blocks)
+    h_codes = np.concatenate(codes)
+    h_absmax = np.array(absmax, dtype=np.float32)
+    g = torch.zeros(n, dtype=dtype, device=DEV)             # (1 - beta) g = 0
+    codes_d = torch.from_numpy(h_codes.copy()).to(DEV)
+    absmax_d = torch.from_numpy(h_absmax.copy()).to(DEV)
+    plan = q.Plan([(codes_d, absmax_d, g)], [(0, 0, n, 0)], 1)
+    q.qmuon_update_multi(plan, 1.0)
+    torch.cuda.synchronize()
+    odt = TORCH_TO_ORACLE[dtype]
+    c2, a2, m2, _ = oracle.q8_update(h_codes, h_absmax, np.zeros(n, dtype=np.uint16), 1.0, odt)
+    assert_bits_equal(host(codes_d), c2, "codes")
+    assert_bits_equal(host(absmax_d), a2, "absmax")
+    assert_bits_equal(host_grad(g), m2, "stored m")

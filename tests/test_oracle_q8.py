@@ -143,6 +143,45 @@ def test_beta_one_is_idempotent():
     assert np.array_equal(q, codes)
 
 
+@pytest.mark.parametrize("scale", [1e30, 1e-20, 1e-37, 2.0 ** -64, 2.0 ** -64 * (1 - 2.0 ** -24), 5e-39, 2e-41])
+def test_beta_one_is_idempotent_at_every_block_scale(scale):
+    """The idempotence above at block maxima from 1e30 down to subnormals:
+    the codes stay the nearest levels even where 127 / amax overflows
+    binary32 (block maxima below about 3.7e-37), and zero codes stay 0."""
+    n = 256 * 4
+    rng = np.random.default_rng(777)
+    codes = rng.integers(-127, 128, n).astype(np.int8)
+    codes[::7] = 0
+    codes[5::256] = 127
+    codes[6::256] = -127
+    absmax = np.full(4, scale, np.float32)
+    q, a, m, _ = oracle.q8_update(codes, absmax, np.zeros(n, np.float32), 1.0, F32)
+    assert np.all(a > 0) and np.all(np.isfinite(a))
+    assert np.array_equal(q, codes)
+
+
+def test_non_finite_momentum_codes():
+    """Reading for non-finite m (outside the method's contract, defined so
+    both implementations agree): a NaN m codes as -127 (the clamp returns
+    the number when its other operand is NaN) and is ignored by the block
+    maximum; an infinite m makes its block's absmax infinite, so 127 / amax
+    is 0: the block's finite elements code 0 and the infinite one
+    (inf * 0 = NaN) -127."""
+    n = 512
+    codes = np.zeros(n, np.int8)
+    absmax = np.zeros(2, np.float32)
+    g = _grad(n)
+    g[10] = np.nan
+    g[300] = np.inf
+    q, a, m, _ = oracle.q8_update(codes, absmax, g, 0.0, F32)
+    assert np.isnan(m[10]) and q[10] == -127
+    finite0 = np.delete(np.arange(256), 10)
+    assert a[0] == np.max(np.abs(g[finite0]))
+    assert np.max(np.abs(q[finite0].astype(np.int32))) == 127
+    assert np.isinf(a[1]) and q[300] == -127
+    assert np.all(q[256:300] == 0) and np.all(q[301:512] == 0)
+
+
 def test_zero_block_and_partial_tail():
     """A block of zeros stores codes 0 / absmax 0; numel = 1000 has 4 blocks,
     the last one covering elements 768..999 only."""
