@@ -443,21 +443,19 @@ def _absmax_giving(target_bits, qv):
     return None
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_grad_rounding_edge_values_match_oracle(dtype):
-    """With beta = 1, m is the dequantised state q * (absmax / 127) exactly, so
-    chosen block maxima put m on the narrowing's edge cases: bf16 and f16
-    rounding ties with an even and an odd kept bit, one ulp either side of a
-    tie, fp32 subnormals (ties among them), values that round to the largest
-    finite value or to infinity, and the smallest normals.  The grad's bits,
-    codes and absmax must match the oracle, whose rounding is integer
-    arithmetic on the bit patterns."""
+def _edge_state():
+    """Codes and block maxima whose dequantised values (beta = 1) are the
+    narrowing's edge cases: bf16 and f16 rounding ties with an even and an
+    odd kept bit, one ulp either side of a tie, fp32 subnormals (ties among
+    them), values that round to the largest finite value or to infinity, the
+    smallest normals; block maxima from 1e38 down to 1e-43, so 127 / amax
+    overflows binary32 in the smallest blocks."""
     targets = [0x3F808000, 0x3F818000, 0x3F807FFF, 0x3F808001, 0x40C38000, 0x41818000,
                0x00808000, 0x00818000, 0x00008000, 0x00018000, 0x00000001, 0x007FFFFF, 0x00400000,
                0x7F7F8000, 0x7F7F7FFF, 0x7F7FFFFF, 0x7E808000, 0x00800000,
                # f16: ties at 13 dropped bits, the f16 subnormal range, the largest finite f16
                0x3F801000, 0x3F803000, 0x3F800FFF, 0x33801000, 0x33803000, 0x477FE000, 0x477FF000, 0x38801000]
-    blocks, absmax, codes = [], [], []
+    absmax, codes = [], []
     rng = np.random.default_rng(2025)
     for tb in targets:
         for qv in (1, 127, 3):
@@ -467,22 +465,42 @@ def test_grad_rounding_edge_values_match_oracle(dtype):
             c = rng.integers(-127, 128, size=256).astype(np.int8)
             c[:64] = qv
             c[64:128] = -qv
-            blocks.append(tb)
+            c[200:208] = 0
             absmax.append(a)
             codes.append(c)
-    say("grad rounding edge values:", len(blocks), "blocks", dtype)
-    assert len(blocks) >= 40
-    n = 256 * len(blocks)
-    h_codes = np.concatenate(codes)
-    h_absmax = np.array(absmax, dtype=np.float32)
+    return np.concatenate(codes), np.array(absmax, dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype,mode", [(torch.bfloat16, "nearest"), (torch.float16, "nearest"),
+                                        (torch.bfloat16, "stochastic"), (torch.bfloat16, "carrier")])
+def test_grad_rounding_edge_values_match_oracle(dtype, mode):
+    """With beta = 1, m is the dequantised state q * (absmax / 127) exactly,
+    so the edge state above puts m on the narrowing's edge cases and the
+    requantisation on the smallest block scales.  The grad's bits (or the
+    carrier's bytes and scales), codes and absmax must match the oracle,
+    whose rounding is integer arithmetic on the bit patterns."""
+    h_codes, h_absmax = _edge_state()
+    n = h_codes.size
+    say("edge values:", n // 256, "blocks", dtype, mode)
+    assert n // 256 >= 40
     g = torch.zeros(n, dtype=dtype, device=DEV)             # (1 - beta) g = 0
     codes_d = torch.from_numpy(h_codes.copy()).to(DEV)
     absmax_d = torch.from_numpy(h_absmax.copy()).to(DEV)
     plan = q.Plan([(codes_d, absmax_d, g)], [(0, 0, n, 0)], 1)
-    q.qmuon_update_multi(plan, 1.0)
-    torch.cuda.synchronize()
     odt = TORCH_TO_ORACLE[dtype]
-    c2, a2, m2, _ = oracle.q8_update(h_codes, h_absmax, np.zeros(n, dtype=np.uint16), 1.0, odt)
+    zeros = np.zeros(n, dtype=np.uint16)
+    if mode == "carrier":
+        car = q.qmuon_update_mxfp8_carrier(plan, 1.0, 1e-7)
+        torch.cuda.synchronize()
+        c2, a2, pay, sc, _ = oracle.q8_update_carrier(h_codes, h_absmax, zeros, 1.0, odt)
+        assert_bits_equal(host(car.data(0)), pay, "carrier bytes")
+        assert_bits_equal(host(car.scale_inv(0)), sc, "carrier scales")
+    else:
+        sr = mode == "stochastic"
+        q.qmuon_update_multi(plan, 1.0, rounding=mode, seed=99, offset=5)
+        torch.cuda.synchronize()
+        c2, a2, m2, _ = oracle.q8_update(h_codes, h_absmax, zeros, 1.0, odt,
+                                         oracle.ROUND_STOCHASTIC if sr else oracle.ROUND_NEAREST, 99, 5)
+        assert_bits_equal(host_grad(g), m2, "stored m")
     assert_bits_equal(host(codes_d), c2, "codes")
     assert_bits_equal(host(absmax_d), a2, "absmax")
-    assert_bits_equal(host_grad(g), m2, "stored m")
