@@ -1155,14 +1155,12 @@ __device__ __forceinline__ int seg_len(int64_t row, int64_t col, int64_t rows, i
 
 // Eight carrier elements (r, c .. c+7) of one 32-element block, as fp32:
 // E4M3 byte (sign, 4 exponent bits biased by 7, 3 mantissa bits,
-// subnormals k 2^-9, S.1111.111 NaN) times 2^(scale byte - 127).
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    const uint32_t mag = c & 0x7fu;
-    float v = mag >= 8u ? __uint_as_float((mag + (120u << 3)) << 20)   // rebias the exponent 7 -> 127
-                        : (float)mag * 0x1p-9f;
-    if (mag == 0x7fu) v = __builtin_nanf("");
-    return (c & 0x80u) ? -v : v;
-}
+// subnormals k 2^-9, S.1111.111 NaN) times 2^(scale byte - 127).  gfx950's
+// v_cvt_scalef32_pk_f32_fp8 decodes two bytes and applies the scale, given
+// as an fp32, in one instruction; for every byte and every scale byte
+// 0..254 its result has the bits of the field-by-field decode scaled with
+// ldexp (an exhaustive comparison on gfx950; the carrier parity tests check
+// the decode through the NS output).
 __device__ __forceinline__ void load_mx8(const uint8_t *data, const uint8_t *sc, int64_t r, int64_t c, int64_t ld,
                                          int64_t sld, int n, float *v) {
     if (n == 0) {
@@ -1171,12 +1169,13 @@ __device__ __forceinline__ void load_mx8(const uint8_t *data, const uint8_t *sc,
         return;
     }
     const uint2 w = *reinterpret_cast<const uint2 *>(data + r * ld + c);
-    const int e = (int)sc[r * sld + c / 32] - 127;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        v[k] = ldexpf(e4m3_value((w.x >> (8 * k)) & 0xffu), e);
-        v[4 + k] = ldexpf(e4m3_value((w.y >> (8 * k)) & 0xffu), e);
-    }
+    const float scale = ldexpf(1.0f, (int)sc[r * sld + c / 32] - 127);
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, scale, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.x, scale, true);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, scale, false);
+    const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w.y, scale, true);
+    v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+    v[4] = d[0]; v[5] = d[1]; v[6] = e[0]; v[7] = e[1];
 }
 
 // X0 = orient(src) * inv, written as X (m_p x n_p) and, for fp32 runs, X^T
