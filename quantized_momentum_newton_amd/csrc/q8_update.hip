@@ -743,7 +743,8 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
             const int64_t e = r * it.cols + c0 + 8 * cl;
             kb[i] = (r * it.cols + c0) / kBlock;   // the row segment's block
             step[i] = absmax[kb[i]] / 127.0f;
-            qv[i] = *reinterpret_cast<const uint2 *>(codes + e);
+            const ntv2 qn = __builtin_nontemporal_load(reinterpret_cast<const ntv2 *>(codes + e));
+            qv[i] = make_uint2(qn.x, qn.y);
             load_grad_vec<DT>(gmem<const void>(T.grad), gpos(T, e), g[i]);
             if constexpr (DT == QM_F32) load_grad_vec<DT>(gmem<const void>(T.grad), gpos(T, e) + 4, g[i] + 4);
         }
@@ -766,16 +767,17 @@ __global__ __launch_bounds__(kThreads) void q8_update_tcar_kernel(const PlanTens
             for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, xor_lanes(amax, off));
             float sc;
             const float inv = requant_inv(amax, sc);
-            uint2 qo = {0u, 0u};
+            float mx[8];   // m, scaled by sc only when some lane of the wave has a tiny block
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                float q = rintf((m[i][j] * sc) * inv);
-                q = fminf(fmaxf(q, -127.0f), 127.0f);
-                const uint32_t b = (uint32_t)(uint8_t)(int8_t)(int)q << (8 * (j & 3));
-                if (j < 4) qo.x |= b;
-                else qo.y |= b;
-            }
-            *reinterpret_cast<uint2 *>(codes + e) = qo;
+            for (int j = 0; j < 8; j++) mx[j] = m[i][j];
+            if (__any(sc != 1.0f))
+#pragma unroll
+                for (int j = 0; j < 8; j++) mx[j] = m[i][j] * sc;
+            // nearest rounding by the added 1.5 * 2^23, as in K1
+            uint32_t q[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) q[j] = __float_as_uint(fminf(fmaxf(mx[j] * inv, -127.0f), 127.0f) + 0x1.8p23f);
+            store_codes_vec<8>(codes, e, q);
             if constexpr (SUMS) {
                 double sq = 0.0;
 #pragma unroll
@@ -961,16 +963,40 @@ void launch_update_dt(const PlanHeader *h, const void *dev_plan, float beta, dou
     const PlanTensor *tens = section<PlanTensor>(dev_plan, h->off_tensors);
     const int64_t *toff = section<int64_t>(dev_plan, h->off_task_offsets);
     const int32_t *tt = section<int32_t>(dev_plan, h->off_task_tensor);
-    const int grid = stream_grid(hi - lo);
-    if constexpr (OUT == kOutNorm)
-        launch(q8_update_kernel<DT, false, SR, false, OUT>, grid, kThreads, 0, stream,
-            tens, toff, tt, h->n_tensors, lo, hi, beta, nullptr, sr, co, nz);
-    else if (block_sums)
-        launch(q8_update_kernel<DT, true, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors, lo, hi,
-                                                                               beta, block_sums, sr, co, nz);
-    else
-        launch(q8_update_kernel<DT, false, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors, lo, hi,
-                                                                                beta, nullptr, sr, co, nz);
+    auto go = [&](int64_t a, int64_t b) {
+        const int grid = stream_grid(b - a);
+        if constexpr (OUT == kOutNorm)
+            launch(q8_update_kernel<DT, false, SR, false, OUT>, grid, kThreads, 0, stream, tens, toff, tt,
+                   h->n_tensors, a, b, beta, nullptr, sr, co, nz);
+        else if (block_sums)
+            launch(q8_update_kernel<DT, true, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors,
+                   a, b, beta, block_sums, sr, co, nz);
+        else
+            launch(q8_update_kernel<DT, false, SR, CAR, OUT>, grid, kThreads, 0, stream, tens, toff, tt, h->n_tensors,
+                   a, b, beta, nullptr, sr, co, nz);
+    };
+    if (!(CAR && co.skip)) {
+        go(lo, hi);
+        return;
+    }
+    // Tensors whose carrier another kernel writes (K1T) get no waves at all:
+    // one launch per run of consecutive other tensors in task order (the
+    // host blob holds the same tables as the device copy).
+    const int64_t *htoff = section<int64_t>(h, h->off_task_offsets);
+    const int32_t *htt = section<int32_t>(h, h->off_task_tensor);
+    int64_t run = -1;
+    for (int k = 0; k < h->n_tensors; k++) {
+        const int64_t a = htoff[k];
+        if (htoff[k + 1] <= lo || a >= hi) continue;   // another dtype's range
+        const int ti = htt[k];
+        const bool skipped = ti < 64 && ((co.skip >> ti) & 1u);
+        if (!skipped && run < 0) run = a;
+        if (skipped && run >= 0) {
+            go(run, a);
+            run = -1;
+        }
+    }
+    if (run >= 0) go(run, hi);
 }
 
 template <bool SR, bool CAR, int OUT = kOutM>
