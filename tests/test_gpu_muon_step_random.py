@@ -32,12 +32,15 @@ DEV = "cuda"
 COEF = tuple(float(np.float32(c)) for c in H.NS_COEFFS)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", list(range(12)) + [100, 101, 102, 103])
 def test_random_matrix_sets_full_step(case):
+    """Cases 0-11: bf16 NS, every fourth fp32-operand NS on fp32 MFMAs;
+    cases 100-103: fp32-operand NS on bf16 MFMAs from a hi + lo split
+    (bf16x3), held to the same fp32 bound."""
     rng = np.random.default_rng(7700 + case)
     n = int(rng.integers(2, 8))
     shapes = [(32 * int(rng.integers(4, 41)), 32 * int(rng.integers(4, 41))) for _ in range(n)]
-    precision = "f32" if case % 4 == 3 else "bf16"
+    precision = "bf16x3" if case >= 100 else "f32" if case % 4 == 3 else "bf16"
     with_w = [bool(rng.integers(0, 4)) for _ in range(n)]
     wd = float(rng.choice([0.0, 0.01]))
     t = int(rng.integers(1, 30))
