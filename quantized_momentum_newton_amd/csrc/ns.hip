@@ -1069,6 +1069,23 @@ __device__ __forceinline__ int find_item(const PrologueArgs &a, int L) {
     return item;
 }
 
+// Origin (i0, j0) of 64 x 64 tile t of an item.  When the caller-side
+// matrix (the one read in the prologue, written in the write-back) is the
+// transpose of X, consecutive tiles walk down X's rows (i fastest), which
+// is along the caller's contiguous rows: neighbouring workgroups then touch
+// neighbouring 256-byte pieces of one row instead of pieces one row pitch
+// apart, all at the same offset within the row.
+__device__ __forceinline__ void tile_origin(const NsItem &it, int t, bool caller_tall, int64_t &i0, int64_t &j0) {
+    if (caller_tall) {
+        const int tm = (int)(it.mp / 64);
+        i0 = (int64_t)(t % tm) * 64;
+        j0 = (int64_t)(t / tm) * 64;
+    } else {
+        i0 = (int64_t)(t / it.tiles_n) * 64;
+        j0 = (int64_t)(t % it.tiles_n) * 64;
+    }
+}
+
 // Partial sums of squares: grid (kNormChunks, items); each workgroup covers
 // a fixed slice of the item's rows; fixed combine order.
 __global__ __launch_bounds__(256) void norm_partial_kernel(PrologueArgs a, double *partials) {
@@ -1188,8 +1205,8 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueArgs a) {
     __shared__ float tile[64][65];
     const int item = find_item(a, blockIdx.x);
     const NsItem &it = a.it[item];
-    const int t = blockIdx.x - it.tile_begin;
-    const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
+    int64_t i0, j0;
+    tile_origin(it, blockIdx.x - it.tile_begin, it.tall, i0, j0);
     const float s = it.inv ? it.inv[0] : a.inv_ws[item];
     const int r = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;   // 32 rows x 8 segments per pass
     // source rows are rows of X, or of X^T when the source is tall
@@ -1242,11 +1259,26 @@ __global__ __launch_bounds__(256) void writeback_kernel(PrologueArgs a, Writebac
     __shared__ float tile[64][65];
     const int item = find_item(a, blockIdx.x);
     const NsItem &it = a.it[item];
-    const int t = blockIdx.x - it.tile_begin;
-    const int64_t i0 = (int64_t)(t / it.tiles_n) * 64, j0 = (int64_t)(t % it.tiles_n) * 64;
     const FinalOut &fo = wb.fo[item];
+    int64_t i0, j0;
+    tile_origin(it, blockIdx.x - it.tile_begin, fo.tall, i0, j0);
     const T *X = static_cast<const T *>(it.X);
     const int r = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
+    // caller rows are rows of X, or of X^T when the caller's matrix is tall
+    const int64_t orows = fo.tall ? fo.n : fo.m, ocols = fo.tall ? fo.m : fo.n;
+    const int64_t or0 = fo.tall ? j0 : i0, oc0 = fo.tall ? i0 : j0;
+    // The weight segments do not depend on X: their loads are issued first,
+    // so their latency overlaps that of X and the LDS transpose.  (Plain
+    // accesses: non-temporal loads and stores made this kernel 5-10 %
+    // slower on the 8B layer.)
+    int n[2];
+    float w[2][8];
+#pragma unroll
+    for (int pass = 0; pass < 2; pass++) {
+        const int64_t orow = or0 + r + 32 * pass, oc = oc0 + c8;
+        n[pass] = seg_len(orow, oc, orows, ocols);
+        if (fo.w) load_seg(fo.w, orow * fo.ldw + oc, QM_F32, n[pass], fo.vec_w, w[pass]);
+    }
 #pragma unroll
     for (int pass = 0; pass < 2; pass++) {
         const int rr = r + 32 * pass;
@@ -1256,25 +1288,20 @@ __global__ __launch_bounds__(256) void writeback_kernel(PrologueArgs a, Writebac
         for (int k = 0; k < 8; k++) tile[rr][c8 + k] = v[k];
     }
     __syncthreads();
-    // caller rows are rows of X, or of X^T when the caller's matrix is tall
-    const int64_t orows = fo.tall ? fo.n : fo.m, ocols = fo.tall ? fo.m : fo.n;
-    const int64_t or0 = fo.tall ? j0 : i0, oc0 = fo.tall ? i0 : j0;
 #pragma unroll
     for (int pass = 0; pass < 2; pass++) {
         const int rr = r + 32 * pass;
         const int64_t orow = or0 + rr, oc = oc0 + c8;
-        const int n = seg_len(orow, oc, orows, ocols);
-        if (n == 0) continue;
+        if (n[pass] == 0) continue;
         float v[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) v[k] = fo.tall ? tile[c8 + k][rr] : tile[rr][c8 + k];
-        store_seg(fo.out, orow * fo.ld + oc, fo.dtype, n, fo.vec_out, v);
+        store_seg(fo.out, orow * fo.ld + oc, fo.dtype, n[pass], fo.vec_out, v);
         if (fo.w) {
-            float w[8];
-            load_seg(fo.w, orow * fo.ldw + oc, QM_F32, n, fo.vec_w, w);
+            float *wp = w[pass];
 #pragma unroll
-            for (int k = 0; k < 8; k++) w[k] = w[k] - (fo.lr_s * v[k] + fo.lr_wd * w[k]);
-            store_seg(fo.w, orow * fo.ldw + oc, QM_F32, n, fo.vec_w, w);
+            for (int k = 0; k < 8; k++) wp[k] = wp[k] - (fo.lr_s * v[k] + fo.lr_wd * wp[k]);
+            store_seg(fo.w, orow * fo.ldw + oc, QM_F32, n[pass], fo.vec_w, wp);
         }
     }
 }
