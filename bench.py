@@ -230,7 +230,7 @@ def bench_grasp(args, q, H, torch):
     # the arithmetic's own ceiling: the fp32 MFMA peak, or a third of the
     # bf16 MFMA peak for bf16x3 (three bf16 products per fp32 product)
     peak = F32_PEAK_TFLOPS if args.ns_precision == "f32" else BF16_PEAK_TFLOPS / 3
-    return {"metric": METRIC, "value": round(1000.0 / step_ms, 3), "unit": "steps/s", "dtype": "f32",
+    return {"metric": METRIC, "value": round(1000.0 / step_ms, 3), "unit": "steps/s", "dtype": args.ns_precision,
             "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
             "config": {"workload": "grasp_4096x4096_rank8", "ns_steps": H.NS_STEPS, "ns_precision": args.ns_precision,
                        "state_ms": round(state_ms, 4), "ns_ms": round(ns_ms, 4),
@@ -267,7 +267,7 @@ def bench_small(args, q, H, torch):
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in evs]
     step_ms = sum(ms) / len(ms)
-    return {"metric": METRIC, "value": round(step_ms * 1e3, 2), "unit": "us/step", "dtype": "f32",
+    return {"metric": METRIC, "value": round(step_ms * 1e3, 2), "unit": "us/step", "dtype": args.ns_precision,
             "higher_is_better": False, "ms_per_step": round(step_ms, 4), "per_step_ms": percentiles(ms),
             "config": {"workload": "fp32_256x512_muon_step", "ns_steps": H.NS_STEPS,
                        "ns_precision": args.ns_precision}}
