@@ -32,10 +32,10 @@ DEV = "cuda"
 COEF = tuple(float(np.float32(c)) for c in H.NS_COEFFS)
 
 
-@pytest.mark.parametrize("case", list(range(12)) + [100, 101, 102, 103])
+@pytest.mark.parametrize("case", list(range(24)) + list(range(100, 108)))
 def test_random_matrix_sets_full_step(case):
-    """Cases 0-11: bf16 NS, every fourth fp32-operand NS on fp32 MFMAs;
-    cases 100-103: fp32-operand NS on bf16 MFMAs from a hi + lo split
+    """Cases 0-23: bf16 NS, every fourth fp32-operand NS on fp32 MFMAs;
+    cases 100-107: fp32-operand NS on bf16 MFMAs from a hi + lo split
     (bf16x3), held to the same fp32 bound."""
     rng = np.random.default_rng(7700 + case)
     n = int(rng.integers(2, 8))
@@ -89,7 +89,7 @@ def _blocked_plans(trip, mats):
     return full, q.Plan(trip, segs, g0)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(16))
 def test_random_block_partitions_block_step(case):
     """Block steps (t not a multiple of P = 5) on random block partitions:
     every block its own NS in one grouped launch, blocks of different shapes
@@ -138,7 +138,7 @@ def test_random_block_partitions_block_step(case):
         assert rel <= NS_BF16_REL and cos >= NS_BF16_COS, (i, rel, cos)
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(16))
 def test_random_sets_carrier_mode(case):
     """Whole-matrix steps in MXFP8-carrier mode on random sets: tall matrices
     (rows a multiple of 128, cols of 256) take the carrier of m^T, the others

@@ -51,7 +51,7 @@ def random_case(rng):
     return numels, dts, segments, n_groups, beta, write_normalized, stochastic
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(96))
 def test_random_plans_match_oracle(case):
     rng = np.random.default_rng(9000 + case)
     numels, dts, segments, ng, beta, wn, sr = random_case(rng)
