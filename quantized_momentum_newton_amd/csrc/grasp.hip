@@ -137,30 +137,57 @@ __global__ __launch_bounds__(kThreads) void colnorm_kernel(const float *Rd, cons
 }
 
 // ------------------------------------------------- momentum and Y = M Q
-// Four rows per workgroup, lane t walks columns t, t+256, ...:
+// kMomRows rows per workgroup, lane t walks columns t, t+256, ...:
 //   M_prev = (float)(res + sum_c Pd[i][c] Rd[j][c])  (fp64, c in order)
 //   M = fl(fl(mu * M_prev) + g);   Y[i][c] = sum_j M[i][j] Q[j][c] (fp64)
+// Column j's factor rows Rd[j] and Q[j] are loaded once for the rows, and
+// the rows' elements are computed as independent straight-line
+// code, so their loads are in flight together (rows past the matrix's end
+// recompute row i0 and are dropped).  Each row's sums still run over j in
+// the same order.
+constexpr int kMomRows = 2;
+
 template <int K>
 __global__ __launch_bounds__(kThreads) void momentum_kernel(const uint8_t *res_codes, const float *res_rmax,
                                                             const float *res_cmax, const float *Pd, const float *Rd,
                                                             const double *Q, const void *g, int gdt, float mu, Dims d,
                                                             float *M, double *Y) {
-    __shared__ double part[4][4 * K];
-    const int64_t i0 = (int64_t)blockIdx.x * 4;
+    __shared__ double part[4][kMomRows * K];
+    const int64_t i0 = (int64_t)blockIdx.x * kMomRows;
+    const int nr = (int)min((int64_t)kMomRows, d.rows - i0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    double y[4][K];
+    double y[kMomRows][K];
 #pragma unroll
-    for (int r = 0; r < 4; r++)
+    for (int r = 0; r < kMomRows; r++)
 #pragma unroll
         for (int c = 0; c < K; c++) y[r][c] = 0.0;
+    float p[kMomRows][K];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const int64_t i = i0 + r;
-        if (i >= d.rows) break;
-        float p[K];
+    for (int r = 0; r < kMomRows; r++)
 #pragma unroll
-        for (int c = 0; c < K; c++) p[c] = Pd[i * K + c];
-        for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
+        for (int c = 0; c < K; c++) p[r][c] = Pd[(i0 + (r < nr ? r : 0)) * K + c];
+    for (int64_t j = threadIdx.x; j < d.cols; j += kThreads) {
+        // 16-byte loads of the factor rows (lanes hold consecutive rows)
+        float rd[K];
+        double qj[K];
+        if constexpr (K % 4 == 0) {
+#pragma unroll
+            for (int c = 0; c < K; c += 4) *reinterpret_cast<float4 *>(rd + c) = *reinterpret_cast<const float4 *>(Rd + j * K + c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < K; c++) rd[c] = Rd[j * K + c];
+        }
+        if constexpr (K % 2 == 0) {
+#pragma unroll
+            for (int c = 0; c < K; c += 2) *reinterpret_cast<double2 *>(qj + c) = *reinterpret_cast<const double2 *>(Q + j * K + c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < K; c++) qj[c] = Q[j * K + c];
+        }
+        float m[kMomRows];
+#pragma unroll
+        for (int r = 0; r < kMomRows; r++) {
+            const int64_t i = i0 + (r < nr ? r : 0);
             const uint8_t byte = res_codes[i * d.packed_cols + (j >> 1)];
             const int nib = (j & 1) ? (byte >> 4) : (byte & 0xF);
             const int code = nib >= 8 ? nib - 16 : nib;
@@ -169,18 +196,23 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const uint8_t *res_c
             const float resd = (float)code * step;
             double acc = (double)resd;
 #pragma unroll
-            for (int c = 0; c < K; c++) acc = acc + (double)p[c] * (double)Rd[j * K + c];
+            for (int c = 0; c < K; c++) acc = acc + (double)p[r][c] * (double)rd[c];
             const float mprev = (float)acc;
             const float t1 = mu * mprev;
-            const float m = t1 + load_grad(g, i * d.cols + j, gdt);
-            M[i * d.cols + j] = m;
+            m[r] = t1 + load_grad(g, i * d.cols + j, gdt);
+        }
 #pragma unroll
-            for (int c = 0; c < K; c++) y[r][c] += (double)m * Q[j * K + c];
+        for (int r = 0; r < kMomRows; r++) {
+            if (r < nr) {
+                M[(i0 + r) * d.cols + j] = m[r];
+#pragma unroll
+                for (int c = 0; c < K; c++) y[r][c] += (double)m[r] * qj[c];
+            }
         }
     }
     // fixed-order reduction: butterfly inside each wave, then waves 0..3
 #pragma unroll
-    for (int r = 0; r < 4; r++)
+    for (int r = 0; r < kMomRows; r++)
 #pragma unroll
         for (int c = 0; c < K; c++) {
             double v = y[r][c];
@@ -189,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const uint8_t *res_c
             if (lane == 0) part[wave][r * K + c] = v;
         }
     __syncthreads();
-    if (threadIdx.x < 4 * K) {
+    if (threadIdx.x < kMomRows * K) {
         const int r = threadIdx.x / K, c = threadIdx.x % K;
         if (i0 + r < d.rows)
             Y[(i0 + r) * K + c] = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
@@ -501,7 +533,7 @@ qm_status launched(const char *what) {
 template <int K>
 void launch_rank_kernels(const qm_grasp_state *s, const Dims &d, const Ws &w, const void *grad, int gdt, float mu,
                          hipStream_t st) {
-    momentum_kernel<K><<<(unsigned)((d.rows + 3) / 4), kThreads, 0, st>>>(
+    momentum_kernel<K><<<(unsigned)((d.rows + kMomRows - 1) / kMomRows), kThreads, 0, st>>>(
         s->res_codes, s->res_rmax, s->res_cmax, w.Pd, w.Rd, w.Q, grad, gdt, mu, d, w.M, w.Y);
 }
 

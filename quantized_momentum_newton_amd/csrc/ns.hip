@@ -1086,37 +1086,6 @@ __device__ __forceinline__ void tile_origin(const NsItem &it, int t, bool caller
     }
 }
 
-// Partial sums of squares: grid (kNormChunks, items); each workgroup covers
-// a fixed slice of the item's rows; fixed combine order.
-__global__ __launch_bounds__(256) void norm_partial_kernel(PrologueArgs a, double *partials) {
-    const int item = blockIdx.y;
-    const NsItem &it = a.it[item];
-    if (it.inv) return;   // scale given (always so for a carrier source): nothing to sum
-    const int64_t rows = it.tall ? it.n : it.m, cols = it.tall ? it.m : it.n;
-    const int64_t per = (rows + kNormChunks - 1) / kNormChunks;
-    const int64_t r0 = blockIdx.x * per, r1 = min(rows, r0 + per);
-    double acc = 0.0;
-    for (int64_t r = r0; r < r1; r++)
-        for (int64_t c = threadIdx.x; c < cols; c += 256) {
-            const double v = (double)load_any(it.src, r * it.ld + c, it.dtype);
-            acc += v * v;
-        }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    __shared__ double part[4];
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) partials[item * kNormChunks + blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
-}
-
-__global__ void norm_final_kernel(const double *partials, float eps, float *inv_out) {
-    const int item = blockIdx.x;
-    if (threadIdx.x != 0) return;
-    double s = 0.0;
-    for (int k = 0; k < kNormChunks; k++) s += partials[item * kNormChunks + k];
-    inv_out[item] = (float)(1.0 / (sqrt(s) + (double)eps));
-}
-
 // Eight consecutive elements of a caller matrix at element index e, as
 // fp32: n of them valid (0..8), zero beyond.  vec: the segment starts
 // 16-byte aligned, so a full one moves with 16-byte accesses.
@@ -1168,6 +1137,50 @@ __device__ __forceinline__ void store_seg(void *p, int64_t e, int dtype, int n, 
 __device__ __forceinline__ int seg_len(int64_t row, int64_t col, int64_t rows, int64_t cols) {
     if (row >= rows || col >= cols) return 0;
     return cols - col < 8 ? (int)(cols - col) : 8;
+}
+
+// Partial sums of squares: grid (kNormChunks, items); each workgroup covers
+// a fixed slice of the item's rows, seen as a row-major list of 8-element
+// segments; thread t adds segments t, t + 256, ... in order (four loads in
+// flight), then a fixed combine order.
+__global__ __launch_bounds__(256) void norm_partial_kernel(PrologueArgs a, double *partials) {
+    const int item = blockIdx.y;
+    const NsItem &it = a.it[item];
+    if (it.inv) return;   // scale given (always so for a carrier source): nothing to sum
+    const int64_t rows = it.tall ? it.n : it.m, cols = it.tall ? it.m : it.n;
+    const int64_t per = (rows + kNormChunks - 1) / kNormChunks;
+    const int64_t r0 = blockIdx.x * per, r1 = min(rows, r0 + per);
+    const int64_t spr = (cols + 7) / 8;   // segments per row
+    const int64_t nseg = r1 > r0 ? (r1 - r0) * spr : 0;
+    double acc = 0.0;
+    for (int64_t s0 = threadIdx.x; s0 < nseg; s0 += 4 * 256) {
+        float v[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t sg = s0 + u * 256;
+            const int64_t r = r0 + sg / spr, c = (sg % spr) * 8;
+            const int n = sg < nseg ? (int)min((int64_t)8, cols - c) : 0;
+            load_seg(it.src, r * it.ld + c, it.dtype, n, it.vec, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+#pragma unroll
+            for (int k = 0; k < 8; k++) acc += (double)v[u][k] * (double)v[u][k];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    __shared__ double part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) partials[item * kNormChunks + blockIdx.x] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+__global__ void norm_final_kernel(const double *partials, float eps, float *inv_out) {
+    const int item = blockIdx.x;
+    if (threadIdx.x != 0) return;
+    double s = 0.0;
+    for (int k = 0; k < kNormChunks; k++) s += partials[item * kNormChunks + k];
+    inv_out[item] = (float)(1.0 / (sqrt(s) + (double)eps));
 }
 
 // Eight carrier elements (r, c .. c+7) of one 32-element block, as fp32:
