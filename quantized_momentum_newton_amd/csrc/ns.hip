@@ -452,6 +452,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         if constexpr (RING) return smem + __builtin_amdgcn_readfirstlane((2 * kt + 1) % SLOTS * HS);
         else return smem + (kt % NSTAGE) * STAGE + BM * ROWB;
     };
+    // In the k-loop, ring slot j places after P of tile kt, slot
+    // (2 kt + j) mod SLOTS, from a running base instead of a division per use
+    // (the scalar division cost the Gram 1.5 %).
+    int rbase = 0;
+    auto ring = [&](int j) -> char * {
+        const int r = rbase + j;
+        return smem + __builtin_amdgcn_readfirstlane((r >= SLOTS ? r - SLOTS : r) * HS);
+    };
 
     // Direct loads: one instruction moves RPI tile rows (1 KiB) into LDS;
     // lane l lands at row r0 + l / CPR, position l % CPR, so it fetches global
@@ -554,9 +562,9 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         for (int d = part * DPS; d < (part + 1) * DPS && d < DPT; d++) {
             if constexpr (RING) {
                 if (d < QI) {
-                    if (kt + 1 < KT) dma_q(kt + 1, qbuf(kt + 1), d);
+                    if (kt + 1 < KT) dma_q(kt + 1, ring(3), d);
                 } else {
-                    if (kt + 2 < KT) dma_p(kt + 2, pbuf(kt + 2), d - QI);
+                    if (kt + 2 < KT) dma_p(kt + 2, ring(4), d - QI);
                 }
             } else {
                 const int nk = kt + NSTAGE - 1;
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     };
     const int dkt0 = (int)(((int64_t)bi * BM + wm * WM) / KK);   // first k-tile of this wave's D rows
     for (int kt = 0; kt < KT; kt++) {
-        const char *cp = pbuf(kt), *cq = qbuf(kt);
+        const char *cp = RING ? ring(0) : pbuf(kt), *cq = RING ? ring(1) : qbuf(kt);
         if constexpr (!DMF) {
             if (dloop) gather_d(cq, kt);
         }
@@ -688,7 +696,14 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         else
             wait_vmcnt_tiles<DPT>(min(KT - 1, kt + NSTAGE - 1) - (kt + 1));
         kloop_barrier();
-        if (kt + 1 < KT) read_frags(pbuf(kt + 1), qbuf(kt + 1), 0, fa[STEPS & 1], fb[STEPS & 1]);
+        if (kt + 1 < KT) {
+            if constexpr (RING) read_frags(ring(2), ring(3), 0, fa[STEPS & 1], fb[STEPS & 1]);
+            else read_frags(pbuf(kt + 1), qbuf(kt + 1), 0, fa[STEPS & 1], fb[STEPS & 1]);
+        }
+        if constexpr (RING) {
+            rbase += 2;
+            if (rbase >= SLOTS) rbase -= SLOTS;
+        }
     }
 
     // ---------------------------------------------------------- epilogue
