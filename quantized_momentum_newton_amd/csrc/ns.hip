@@ -182,6 +182,7 @@ template <typename T> struct GItem {
     int32_t tiles_n;       // tile columns (== tiles_m for the symmetric products)
     int32_t tile_begin;    // first logical tile of this matrix
     int32_t k_tiles;       // K / (128 / sizeof(T))
+    int64_t unit_begin;    // stream-K: first k-tile unit of this matrix (tiles x k_tiles before it)
 };
 
 template <typename T> struct GemmArgs {
@@ -195,6 +196,11 @@ template <typename T> struct GemmArgs {
     // tile is a block of the Q operand (see gemm_nt_kernel).
     int32_t dloop;
     float dgain;
+    // stream-K launches: sk_units k-tile units (all tiles' k-tiles, items in
+    // launch order), workgroup w takes [w sk_len, (w + 1) sk_len); parts of
+    // split tiles go to sk_part, two 4 BM BN-byte slots per workgroup
+    int64_t sk_units, sk_len;
+    float *sk_part;
 };
 
 // Workgroup -> (item, tile position in the item's band order).  Workgroups
@@ -364,9 +370,16 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int tiles) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
+// One output tile, or one k-range of it.  The k-tiles [ka, kb) of tile t of
+// item `item` are multiplied; the tile whole (ka = 0, kb = k_tiles) leaves
+// through the epilogue, a part of it (stream-K) stores its raw fp32
+// accumulators to `part`.  fix_unit >= 0 (stream-K fix-up, ka = kb = 0):
+// the accumulators are the sum of the tile's stored parts, in k order, and
+// leave through the epilogue.
 template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
           bool SYM, bool QT, bool X3>
-__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs<T> &args, int item, int t, int ka, int kb, float *part,
+                                          int64_t fix_unit) {
     constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     constexpr int FM = WM / 32, FN = WN / 32;
@@ -403,22 +416,16 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-    int item = 0, t = 0;
-    if (SYM && args.xcd) {
-        if (!xcd_tile(blockIdx.x, args, item, t)) return;   // uniform: the whole workgroup
-    } else {
-        const int L = wg_position(blockIdx.x, gridDim.x);
-        while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
-        t = L - args.it[item].tile_begin;
-    }
     const GItem<T> &I = args.it[item];
     int bi, bj;
     if constexpr (SYM) band_coords_tri(t, I.tiles_n, bi, bj);
     else band_coords(t, I.tiles_m, I.tiles_n, bi, bj);
 
-    const char *Pg = reinterpret_cast<const char *>(I.P + (int64_t)bi * BM * I.ldp);
-    const char *Qg = reinterpret_cast<const char *>(QT ? I.Q + (int64_t)bj * BN : I.Q + (int64_t)bj * BN * I.ldq);
     const int64_t ldpb = I.ldp * (int64_t)sizeof(T), ldqb = I.ldq * (int64_t)sizeof(T);
+    // operand panels from k-tile ka on
+    const char *Pg = reinterpret_cast<const char *>(I.P + (int64_t)bi * BM * I.ldp) + (int64_t)ka * ROWB;
+    const char *Qg = QT ? reinterpret_cast<const char *>(I.Q + (int64_t)bj * BN) + (int64_t)ka * (ROWB / (int)sizeof(T)) * ldqb
+                        : reinterpret_cast<const char *>(I.Q + (int64_t)bj * BN * I.ldq) + (int64_t)ka * ROWB;
     const int lrw = lane / CPR, lch = lane % CPR;
 
     // One DMA instruction of the Q operand's k-tile kt (i < QI) into the Q
@@ -484,7 +491,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.0f;
 
-    const int KT = I.k_tiles;
+    const int KT = kb - ka;   // k-tiles of this call, counted from ka
     const int lrow = lane & 31, lhalf = lane >> 5;
     // QT reads.  ds_read_b64_tr_b16 works on groups of 16 lanes: if lane s
     // of a group points at 4 consecutive elements, lane t receives element
@@ -575,22 +582,24 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
             }
         }
     };
-    if constexpr (RING) {
-        issue_p(0);
-        issue_q(0);
-        if (KT > 1) issue_p(1);
-        wait_vmcnt_tiles<PI>(KT > 1 ? 1 : 0);
-    } else {
+    if (KT > 0) {
+        if constexpr (RING) {
+            issue_p(0);
+            issue_q(0);
+            if (KT > 1) issue_p(1);
+            wait_vmcnt_tiles<PI>(KT > 1 ? 1 : 0);
+        } else {
 #pragma unroll
-        for (int k = 0; k < NSTAGE - 1; k++)
-            if (k < KT) {
-                issue_p(k);
-                issue_q(k);
-            }
-        wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
+            for (int k = 0; k < NSTAGE - 1; k++)
+                if (k < KT) {
+                    issue_p(k);
+                    issue_q(k);
+                }
+            wait_vmcnt_tiles<DPT>(min(NSTAGE - 2, KT - 1));
+        }
+        kloop_barrier();
+        read_frags(pbuf(0), qbuf(0), 0, fa[0], fb[0]);
     }
-    kloop_barrier();
-    read_frags(pbuf(0), qbuf(0), 0, fa[0], fb[0]);
     // The D term in the k-loop.  For X = aX + BX (Q = X, or X^T in fp32
     // runs) and for B = bA + cA^2 (Q = A, symmetric), D's tile (bi, bj)
     // equals the Q panel bj at k in [bi BM, bi BM + BM): element (row R,
@@ -607,7 +616,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
 #pragma unroll
         for (int i = 0; i < FM; i++) {
             const int64_t rb = (int64_t)bi * BM + wm * WM + i * 32;  // first k of sub-tile i
-            if (rb / KK != kt) continue;
+            if (rb / KK != kt + ka) continue;
             const int kk0 = (int)(rb % KK) + 4 * lhalf;
 #pragma unroll
             for (int j = 0; j < FN; j++) {
@@ -644,7 +653,7 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         const int q = e >> 1;
         return u32x4{q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
     };
-    const int dkt0 = (int)(((int64_t)bi * BM + wm * WM) / KK);   // first k-tile of this wave's D rows
+    const int dkt0 = (int)(((int64_t)bi * BM + wm * WM) / KK) - ka;   // first k-tile of this wave's D rows
     for (int kt = 0; kt < KT; kt++) {
         const char *cp = RING ? ring(0) : pbuf(kt), *cq = RING ? ring(1) : qbuf(kt);
         if constexpr (!DMF) {
@@ -703,6 +712,46 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         if constexpr (RING) {
             rbase += 2;
             if (rbase >= SLOTS) rbase -= SLOTS;
+        }
+    }
+
+    // ------------------------------------------------ stream-K parts
+    // A part's accumulators are stored and loaded in register order: per
+    // (wave, i, j, four-row group) one 16-byte unit per lane, 1 KiB per wave
+    // instruction.  The parts of a tile come from consecutive workgroups w
+    // of the stream-K launch (each takes units [w len, (w + 1) len)); the
+    // part that begins a workgroup's range sits in slot 2 w, a later one
+    // (its last, begun at a tile start) in slot 2 w + 1.
+    auto part_at = [&](float *base, int i, int j, int r4) -> float4 * {
+        return reinterpret_cast<float4 *>(base) + (((wave * FM + i) * FN + j) * 4 + r4) * 64 + lane;
+    };
+    if (part) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; r4++)
+                    *part_at(part, i, j, r4) =
+                        float4{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+        return;
+    }
+    if (fix_unit >= 0) {
+        const int64_t len = args.sk_len, u1 = fix_unit + I.k_tiles;
+        for (int64_t w = fix_unit / len; w * len < u1; w++) {   // k order
+            float *src = args.sk_part + (size_t)(2 * w + (fix_unit > w * len ? 1 : 0)) * BM * BN;
+#pragma unroll
+            for (int i = 0; i < FM; i++)
+#pragma unroll
+                for (int j = 0; j < FN; j++)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; r4++) {
+                        const float4 v = *part_at(src, i, j, r4);
+                        acc[i][j][4 * r4] += v.x;
+                        acc[i][j][4 * r4 + 1] += v.y;
+                        acc[i][j][4 * r4 + 2] += v.z;
+                        acc[i][j][4 * r4 + 3] += v.w;
+                    }
         }
     }
 
@@ -817,6 +866,65 @@ __global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(Ge
         }
         kloop_barrier();
     }
+}
+
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
+          bool SYM, bool QT, bool X3>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_nt_kernel(GemmArgs<T> args) {
+    int item = 0, t = 0;
+    if (SYM && args.xcd) {
+        if (!xcd_tile(blockIdx.x, args, item, t)) return;   // uniform: the whole workgroup
+    } else {
+        const int L = wg_position(blockIdx.x, gridDim.x);
+        while (item + 1 < args.n_items && args.it[item + 1].tile_begin <= L) item++;
+        t = L - args.it[item].tile_begin;
+    }
+    gemm_tile<T, BM, BN, WAVES_M, WAVES_N, ROWB, NSTAGE, SLOTS, MINB, EPI, SYM, QT, X3>(args, item, t, 0, args.it[item].k_tiles, nullptr, -1);
+}
+
+// Stream-K: a launch whose tiles would leave the last round of workgroups
+// partly filled splits their k-tiles evenly over the workgroups instead.
+// Workgroup w multiplies units [w len, (w + 1) len) of the units of all
+// tiles (item by item, tile by tile, k-tile by k-tile): whole tiles leave
+// through the epilogue, the pieces of a tile cut by a range boundary store
+// their raw accumulators; gemm_sk_fixup_kernel then adds each cut tile's
+// pieces in k order and runs the epilogue.  The sum order is fixed, so
+// outputs are the same from run to run.
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
+          bool SYM, bool QT, bool X3>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_sk_kernel(GemmArgs<T> args) {
+    const int64_t len = args.sk_len, w = blockIdx.x;
+    int64_t u = w * len;
+    const int64_t u1 = u + len < args.sk_units ? u + len : args.sk_units;
+    while (u < u1) {   // uniform
+        int item = 0;
+        while (item + 1 < args.n_items && args.it[item + 1].unit_begin <= u) item++;
+        const GItem<T> &I = args.it[item];
+        const int64_t rel = u - I.unit_begin;
+        const int t = (int)(rel / I.k_tiles), ka = (int)(rel % I.k_tiles);
+        const int kb = (int)(ka + (u1 - u) < I.k_tiles ? ka + (u1 - u) : I.k_tiles);
+        float *part = ka == 0 && kb == I.k_tiles
+                          ? nullptr
+                          : args.sk_part + (size_t)(2 * w + (u > w * len ? 1 : 0)) * BM * BN;
+        gemm_tile<T, BM, BN, WAVES_M, WAVES_N, ROWB, NSTAGE, SLOTS, MINB, EPI, SYM, QT, X3>(args, item, t, ka, kb, part, -1);
+        u += kb - ka;
+    }
+}
+
+// One workgroup per range boundary b = (w + 1) len: the tile that b cuts is
+// finished by the workgroup of the first boundary inside it.
+template <typename T, int BM, int BN, int WAVES_M, int WAVES_N, int ROWB, int NSTAGE, int SLOTS, int MINB, int EPI,
+          bool SYM, bool QT, bool X3>
+__global__ __launch_bounds__(WAVES_M *WAVES_N * 64, MINB) void gemm_sk_fixup_kernel(GemmArgs<T> args) {
+    const int64_t len = args.sk_len, b = (int64_t)(blockIdx.x + 1) * len;
+    if (b >= args.sk_units) return;
+    int item = 0;
+    while (item + 1 < args.n_items && args.it[item + 1].unit_begin <= b) item++;
+    const GItem<T> &I = args.it[item];
+    const int64_t rel = b - I.unit_begin;
+    const int64_t ut = b - rel % I.k_tiles;   // first unit of the cut tile
+    if (ut == b || b - len > ut) return;      // b starts a tile, or an earlier boundary owns it
+    gemm_tile<T, BM, BN, WAVES_M, WAVES_N, ROWB, NSTAGE, SLOTS, MINB, EPI, SYM, QT, X3>(args, item, (int)(rel / I.k_tiles), 0, 0, nullptr, ut);
 }
 
 // ------------------------------------------------------------ MX Gram
@@ -1400,12 +1508,14 @@ std::vector<std::vector<size_t>> make_chunks(const std::vector<NsRequest> &req) 
 
 constexpr int64_t kNormBytes = align_up_const(kMaxItems * kNormChunks * 8, 256) + align_up_const(kMaxItems * 4, 256);
 
+int64_t sk_part_bytes(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int precision);
+
 size_t ns_ws_bytes_req(const std::vector<NsRequest> &req, int precision) {
     int64_t best = 0;
     for (const auto &ch : make_chunks(req)) {
         int64_t s = 0;
         for (size_t i : ch) s += geometry(req[i].rows, req[i].cols, elem_size(precision)).item_bytes;
-        best = std::max(best, s);
+        best = std::max(best, s + sk_part_bytes(req, ch, precision));
     }
     return (size_t)(best + kNormBytes);
 }
@@ -1512,6 +1622,47 @@ qm_status launch_gemm(GemmArgs<T> args, int tiles, hipStream_t stream) {
     return QM_OK;
 }
 
+// Whether a launch of `tiles` tiles at per_cu workgroups per CU runs
+// stream-K: it fills more than one round and leaves more than a tenth of
+// its last round idle.  Used for fp32 symmetric products only, whose fp32
+// MFMA work per tile is large against the 4 BM BN bytes a part moves.
+bool sk_wanted(int64_t tiles, int per_cu) {
+    const double r = (double)tiles / (double)(cu_count() * per_cu);
+    return r > 1.0 && std::ceil(r) - r > 0.1;
+}
+
+template <typename T, typename C, int EPI, bool SYM, bool QT = false, bool X3 = false>
+qm_status launch_gemm_sk(GemmArgs<T> args, int tiles, float *part, hipStream_t stream) {
+    constexpr int NT = C::WM * C::WN * 64;
+    constexpr size_t lds = C::SLOTS ? (size_t)C::SLOTS * C::BM * C::ROWB : (size_t)C::NST * (C::BM + C::BN) * C::ROWB;
+    auto kern = gemm_sk_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT, X3>;
+    auto fix = gemm_sk_fixup_kernel<T, C::BM, C::BN, C::WM, C::WN, C::ROWB, C::NST, C::SLOTS, C::MINB, EPI, SYM, QT, X3>;
+    static std::atomic<bool> attr_set[kMaxDevices] = {}, attr_fix[kMaxDevices] = {};
+    qm_status st = reserve_lds(reinterpret_cast<const void *>(kern), lds, attr_set);
+    if (st == QM_OK) st = reserve_lds(reinterpret_cast<const void *>(fix), lds, attr_fix);
+    if (st != QM_OK) return st;
+    int64_t units = 0;
+    for (int i = 0; i < args.n_items; i++) {
+        GItem<T> &I = args.it[i];
+        const int cnt = (i + 1 < args.n_items ? args.it[i + 1].tile_begin : tiles) - I.tile_begin;
+        I.unit_begin = units;
+        units += (int64_t)cnt * I.k_tiles;
+    }
+    const int64_t slots = cu_count() * C::MINB;
+    args.total_tiles = tiles;
+    args.xcd = 0;
+    args.sk_units = units;
+    args.sk_len = (units + slots - 1) / slots;
+    args.sk_part = part;
+    const int grid = (int)((units + args.sk_len - 1) / args.sk_len);   // <= slots: two part slots each
+    Timed tm(stream, EPI == EPI_GRAM ? QM_K_NS_GRAM : EPI == EPI_POLY ? QM_K_NS_POLY : QM_K_NS_XUPDATE);
+    launch(kern, dim3(grid), dim3(NT), lds, stream, args);
+    if (grid > 1) launch(fix, dim3(grid - 1), dim3(NT), lds, stream, args);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QM_E_HIP, "stream-K gemm launch: %s", hipGetErrorString(e));
+    return QM_OK;
+}
+
 qm_status launch_gram_mx(MxGramArgs args, int tiles, hipStream_t stream) {
     static std::atomic<bool> attr_set[kMaxDevices] = {};
     const qm_status st = reserve_lds(reinterpret_cast<const void *>(gram_mx_kernel), kMxGramLds, attr_set);
@@ -1552,11 +1703,14 @@ struct ItemBufs {
 template <typename T, typename CS, typename CR, bool X3>
 qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk,
                        const std::vector<ItemBufs> &bufs, const std::vector<int> &by_n, const std::vector<int> &by_m,
-                       std::vector<int> &cur, int steps, float a, float b, float c, hipStream_t stream) {
+                       std::vector<int> &cur, int steps, float a, float b, float c, hipStream_t stream,
+                       float *sk_part = nullptr) {
     const int nit = (int)chunk.size();
     constexpr bool kQT = sizeof(T) == 2;   // bf16: transposing reads, no X^T copy
     constexpr int64_t kSymK = CS::ROWB / (int64_t)sizeof(T);    // K elements per k-tile
     constexpr int64_t kRectK = CR::ROWB / (int64_t)sizeof(T);
+    // stream-K symmetric products: fp32 runs on the 128 x 128 and 64 x 64 tiles
+    constexpr bool kSk = sizeof(T) == 4 && !X3 && CS::BM < 256;
     for (int s = 0; s < steps; s++) {
         // A = X X^T.  On the first iteration of a bf16 run whose requests
         // are all carriers that qualify, the block-scaled fp8 product runs
@@ -1600,7 +1754,14 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
             tl += tm * (tm + 1) / 2;
         }
         qm_status st = QM_OK;
-        if (g1.n_items) st = launch_gemm<T, CS, EPI_GRAM, true, false, X3>(g1, tl, stream);
+        if (g1.n_items) {
+            if constexpr (kSk) {
+                if (sk_part && sk_wanted(tl, CS::MINB)) st = launch_gemm_sk<T, CS, EPI_GRAM, true, false, X3>(g1, tl, sk_part, stream);
+                else st = launch_gemm<T, CS, EPI_GRAM, true, false, X3>(g1, tl, stream);
+            } else {
+                st = launch_gemm<T, CS, EPI_GRAM, true, false, X3>(g1, tl, stream);
+            }
+        }
         if (st != QM_OK) return st;
         if (gx.n_items) st = launch_gram_mx(gx, tx, stream);
         if (st != QM_OK) return st;
@@ -1626,7 +1787,12 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
             I.k_tiles = (int32_t)(B.g.mp / kSymK);
             tl += tm * (tm + 1) / 2;
         }
-        st = launch_gemm<T, CS, EPI_POLY, true, false, X3>(g2, tl, stream);
+        if constexpr (kSk) {
+            if (sk_part && sk_wanted(tl, CS::MINB)) st = launch_gemm_sk<T, CS, EPI_POLY, true, false, X3>(g2, tl, sk_part, stream);
+            else st = launch_gemm<T, CS, EPI_POLY, true, false, X3>(g2, tl, stream);
+        } else {
+            st = launch_gemm<T, CS, EPI_POLY, true, false, X3>(g2, tl, stream);
+        }
         if (st != QM_OK) return st;
         // X = a X + B X: bf16 reads Q = X (K x N) and writes the other X
         // buffer; fp32 reads Q = X^T and updates X in place, writing X^T.
@@ -1685,22 +1851,43 @@ int64_t tile_count(const std::vector<ItemBufs> &bufs, bool sym, int64_t s) {
     }
     return tiles;
 }
+// fp32 symmetric launches of the 128 x 128 and 64 x 64 configurations run
+// stream-K where sk_wanted says so; the model then counts their tiles as
+// spread evenly over the CUs, plus 5 % for the parts and the fix-up.
+constexpr int kF32Tile[3] = {256, 128, 64};
+constexpr int kF32PerCu[3] = {1, 2, 4};
+bool f32_sym_sk(const std::vector<ItemBufs> &bufs, int k) {
+    return k > 0 && sk_wanted(tile_count(bufs, true, kF32Tile[k]), kF32PerCu[k]);
+}
 int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym, bool x3) {
-    static constexpr int kS[3] = {256, 128, 64};
     static constexpr double kEff[3] = {0.76, 1.0, 0.94};
+    const auto &kS = kF32Tile;
     const int64_t n_cu = cu_count();
     if (x3) return tile_count(bufs, sym, 128) >= n_cu ? 1 : 2;
     int best = 0;
     double best_t = 0;
     for (int k = 0; k < 3; k++) {
         const int64_t tiles = tile_count(bufs, sym, kS[k]);
-        const double t = (double)((tiles + n_cu - 1) / n_cu) * kS[k] * kS[k] / kEff[k];
+        const double rounds = sym && f32_sym_sk(bufs, k) ? 1.05 * (double)tiles / (double)n_cu
+                                                         : (double)((tiles + n_cu - 1) / n_cu);
+        const double t = rounds * kS[k] * kS[k] / kEff[k];
         if (k == 0 || t < best_t) {
             best = k;
             best_t = t;
         }
     }
     return best;
+}
+
+// Bytes of stream-K parts a chunk needs: fp32 runs whose symmetric products
+// run stream-K, two slots of 4 BM BN bytes per workgroup slot of the GPU.
+int64_t sk_part_bytes(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int precision) {
+    if (precision != QM_NS_F32) return 0;
+    std::vector<ItemBufs> bufs(chunk.size());
+    for (size_t i = 0; i < chunk.size(); i++) bufs[i].g = geometry(req[chunk[i]].rows, req[chunk[i]].cols, 4);
+    const int k = pick_f32_tile(bufs, true, false);
+    if (!f32_sym_sk(bufs, k)) return 0;
+    return align_up(2 * cu_count() * kF32PerCu[k] * (int64_t)kF32Tile[k] * kF32Tile[k] * 4, 256);
 }
 
 // X3: fp32 runs on bf16x3 products (precision QM_NS_BF16X3).
@@ -1727,6 +1914,10 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     }
     double *partials = reinterpret_cast<double *>(p);
     float *inv_ws = reinterpret_cast<float *>(p + align_up(kMaxItems * kNormChunks * 8, 256));
+    // stream-K parts (fp32 runs whose symmetric products run stream-K)
+    float *sk_part = !X3 && sizeof(T) == 4 && sk_part_bytes(req, chunk, QM_NS_F32) > 0
+                         ? reinterpret_cast<float *>(p + kNormBytes)
+                         : nullptr;
 
     // ---- prologue: norms (if needed), orientation, padding, X and X^T
     PrologueArgs pa{};
@@ -1799,10 +1990,12 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
         auto run = [&](auto cs) -> qm_status {
             using CS = decltype(cs);
             if constexpr (!X3) {
-                if (tr == 0) return run_products<T, CS, CfgRect, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+                if (tr == 0)
+                    return run_products<T, CS, CfgRect, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream, sk_part);
             }
-            if (tr <= 1) return run_products<T, CS, CfgF32Mid, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
-            return run_products<T, CS, CfgF32Small, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream);
+            if (tr <= 1)
+                return run_products<T, CS, CfgF32Mid, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream, sk_part);
+            return run_products<T, CS, CfgF32Small, X3>(req, chunk, bufs, by_n, by_m, cur, steps, a, b, c, stream, sk_part);
         };
         if constexpr (X3) st = ts <= 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
         else st = ts == 0 ? run(CfgSym{}) : ts == 1 ? run(CfgF32Mid{}) : run(CfgF32Small{});
