@@ -1709,8 +1709,9 @@ qm_status run_products(const std::vector<NsRequest> &req, const std::vector<size
     constexpr bool kQT = sizeof(T) == 2;   // bf16: transposing reads, no X^T copy
     constexpr int64_t kSymK = CS::ROWB / (int64_t)sizeof(T);    // K elements per k-tile
     constexpr int64_t kRectK = CR::ROWB / (int64_t)sizeof(T);
-    // stream-K symmetric products: fp32 runs on the 128 x 128 and 64 x 64 tiles
-    constexpr bool kSk = sizeof(T) == 4 && !X3 && CS::BM < 256;
+    // stream-K symmetric products: fp32-operand runs (f32 and bf16x3) on the
+    // 128 x 128 and 64 x 64 tiles
+    constexpr bool kSk = sizeof(T) == 4 && CS::BM < 256;
     for (int s = 0; s < steps; s++) {
         // A = X X^T.  On the first iteration of a bf16 run whose requests
         // are all carriers that qualify, the block-scaled fp8 product runs
@@ -1879,13 +1880,14 @@ int pick_f32_tile(const std::vector<ItemBufs> &bufs, bool sym, bool x3) {
     return best;
 }
 
-// Bytes of stream-K parts a chunk needs: fp32 runs whose symmetric products
-// run stream-K, two slots of 4 BM BN bytes per workgroup slot of the GPU.
+// Bytes of stream-K parts a chunk needs: fp32-operand runs (f32, bf16x3)
+// whose symmetric products run stream-K, two slots of 4 BM BN bytes per
+// workgroup slot of the GPU.
 int64_t sk_part_bytes(const std::vector<NsRequest> &req, const std::vector<size_t> &chunk, int precision) {
-    if (precision != QM_NS_F32) return 0;
+    if (precision != QM_NS_F32 && precision != QM_NS_BF16X3) return 0;
     std::vector<ItemBufs> bufs(chunk.size());
     for (size_t i = 0; i < chunk.size(); i++) bufs[i].g = geometry(req[chunk[i]].rows, req[chunk[i]].cols, 4);
-    const int k = pick_f32_tile(bufs, true, false);
+    const int k = pick_f32_tile(bufs, true, precision == QM_NS_BF16X3);
     if (!f32_sym_sk(bufs, k)) return 0;
     return align_up(2 * cu_count() * kF32PerCu[k] * (int64_t)kF32Tile[k] * kF32Tile[k] * 4, 256);
 }
@@ -1915,7 +1917,7 @@ qm_status run_chunk(const std::vector<NsRequest> &req, const std::vector<size_t>
     double *partials = reinterpret_cast<double *>(p);
     float *inv_ws = reinterpret_cast<float *>(p + align_up(kMaxItems * kNormChunks * 8, 256));
     // stream-K parts (fp32 runs whose symmetric products run stream-K)
-    float *sk_part = !X3 && sizeof(T) == 4 && sk_part_bytes(req, chunk, QM_NS_F32) > 0
+    float *sk_part = sizeof(T) == 4 && sk_part_bytes(req, chunk, X3 ? QM_NS_BF16X3 : QM_NS_F32) > 0
                          ? reinterpret_cast<float *>(p + kNormBytes)
                          : nullptr;
 

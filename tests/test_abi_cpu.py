@@ -282,20 +282,18 @@ def test_carrier_hparams_and_workspace():
 
 
 def test_ns_precisions_workspace_and_validation():
-    """bf16x3 holds X, A, B in fp32 like the f32 mode; the f32 mode adds the
-    stream-K part slots when its symmetric products run stream-K (two
-    4 x 128 x 128-byte slots per workgroup slot for 2 x 4096^2); an unknown
-    precision is refused before any launch."""
+    """bf16x3 holds X, A, B in fp32 like the f32 mode (same workspace, the
+    stream-K part slots included where the symmetric products take that
+    path: two 4 x 128 x 128-byte slots per workgroup slot for 4096^2, 256 CUs
+    assumed without a GPU); an unknown precision is refused before any
+    launch."""
     for rows, cols in ((64, 256), (300, 200), (4096, 14336), (4096, 4096)):
         f32 = LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_F32)
-        x3 = LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16X3)
-        assert x3 <= f32
-        assert x3 > LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16)
-        if (rows, cols) in ((64, 256), (300, 200)):
-            assert x3 == f32   # no stream-K at these sizes
-    # without a GPU the library assumes 256 CUs: 2 x 256 x 2 slots of 64 KiB
-    assert LIB.ns_workspace_bytes(4096, 4096, 1, L.QM_NS_F32) - \
-        LIB.ns_workspace_bytes(4096, 4096, 1, L.QM_NS_BF16X3) == 2 * 256 * 2 * 128 * 128 * 4
+        assert LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16X3) == f32
+        assert f32 > LIB.ns_workspace_bytes(rows, cols, 2, L.QM_NS_BF16)
+    # X, two X^T, A, B in fp32 (rows padded), plus the part slots
+    assert LIB.ns_workspace_bytes(4096, 4096, 1, L.QM_NS_F32) >= 5 * 4096 * 4096 * 4 + 2 * 256 * 2 * 128 * 128 * 4
+    assert LIB.ns_workspace_bytes(256, 512, 1, L.QM_NS_F32) < 2 * 256 * 2 * 128 * 128 * 4
     x = ctypes.c_void_p(BASE)
     ws = ctypes.c_void_p(BASE + (1 << 34))
     for prec in (3, -1):

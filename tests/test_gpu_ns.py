@@ -119,8 +119,9 @@ def test_llama8b_shapes_full_size(name, shape):
 @pytest.mark.parametrize("shape", [(3000, 3300), (3300, 3000), (2048, 2048), (4096, 4096)])
 def test_f32_mid_and_small_tile_runs(shape, precision):
     """fp32-operand runs on the sizes whose products take 128 x 128 or 64 x 64
-    tiles (3000 x 3300 is padded to 3072 x 3328; the 4096-square Gram takes
-    64 x 64, its X = aX + BX 128 x 128); whole output against the exact
+    tiles (3000 x 3300 is padded to 3072 x 3328; the 4096-square Gram and A^2
+    take 128 x 128 by stream-K, 528 tiles over 512 workgroup slots, its
+    X = aX + BX 128 x 128 tiles whole); whole output against the exact
     iterate."""
     say("fp32-operand NS", shape, precision)
     x = H.grad(shape, torch.float32, DEV, 2101, *shape)
@@ -128,6 +129,24 @@ def test_f32_mid_and_small_tile_runs(shape, precision):
     q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision=precision)
     torch.cuda.synchronize()
     _check(as_f64(x), ns_whole(x0, 5, COEF, H.NS_EPS), precision)
+
+
+def test_stream_k_batch_whole_and_repeatable():
+    """Three 2048-square fp32 matrices in one grouped launch: the symmetric
+    products run stream-K on 64 x 64 tiles (1584 tiles over 1024 workgroup
+    slots, items at different unit offsets, tiles cut between workgroups).
+    Every matrix whole within the f32 bound; a second run gives the same
+    bits (the pieces of a cut tile are added in a fixed order)."""
+    x = H.grad((3, 2048, 2048), torch.float32, DEV, 2103, 2048, 2048)
+    x0 = as_f64(x)
+    y = x.clone()
+    q.ns_orthogonalize(x, 5, COEF, H.NS_EPS, precision="f32")
+    q.ns_orthogonalize(y, 5, COEF, H.NS_EPS, precision="f32")
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    for b in range(3):
+        say("  stream-K batch item", b)
+        _check(as_f64(x[b]), ns_whole(x0[b], 5, COEF, H.NS_EPS), "f32")
 
 
 def test_blocked_muonbp_shape():
