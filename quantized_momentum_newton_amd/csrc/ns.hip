@@ -2047,7 +2047,10 @@ qm_status check_ns_common(void *x, int32_t dtype, int64_t rows, int64_t cols, in
 
 }  // namespace
 
-size_t ns_f32_workspace_bytes(int64_t rows, int64_t cols) { return ns_ws_bytes_uniform(rows, cols, 1, QM_NS_F32); }
+// Either fp32-operand mode (f32 or bf16x3); they may differ in stream-K part slots.
+size_t ns_f32_workspace_bytes(int64_t rows, int64_t cols) {
+    return std::max(ns_ws_bytes_uniform(rows, cols, 1, QM_NS_F32), ns_ws_bytes_uniform(rows, cols, 1, QM_NS_BF16X3));
+}
 
 qm_status run_ns_f32_into(const float *M, int64_t rows, int64_t cols, void *out, int32_t out_dtype, float *w,
                           float lr_s, float lr_wd, int steps, float a, float b, float c, float eps, int32_t precision,
