@@ -11,8 +11,8 @@ import torch
 
 import oracle
 import quantized_momentum_newton_amd as q
-from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_COS, NS_F32_REL, as_f64, assert_bits_equal, host, host_grad,
-                      ns_parity, ns_whole, say)
+from gpu_util import (NS_BF16_COS, NS_BF16_REL, NS_F32_BF16OUT_REL, NS_F32_COS, NS_F32_REL, as_f64,
+                      assert_bits_equal, host, host_grad, ns_parity, ns_whole, say)
 from harness import inputs as H
 from oracle import muonbp
 
@@ -112,6 +112,48 @@ def test_llama8b_layer_full_step():
         s = 0.2 * math.sqrt(max(r, c))
         dW = host(mats[i][4]).astype(np.float64) - W0[i]
         _within(dW, -0.02 * s * ref, f"dW[{name}]")
+
+
+def test_f32_grouped_step_stream_k_mixed_k():
+    """One full step over 2048 x 4096, 3072 x 3072 and 4096 x 2048 in fp32
+    operands: the grouped symmetric products run stream-K over items of
+    different K (4096, 3072, 4096), with tiles cut between workgroups and
+    between matrices.  State bit-exact; O and the weight change (weight
+    decay on) of every matrix, whole, within the fp32-operand bound."""
+    shapes = [(2048, 4096), (3072, 3072), (4096, 2048)]
+    trip, mats, hin = [], [], []
+    for i, (r, c) in enumerate(shapes):
+        codes, absmax = H.prior_state(r * c, DEV, 1011, i)
+        g = H.grad((r, c), torch.bfloat16, DEV, 1011, i).reshape(-1)
+        w = H.weights((r, c), DEV, 1011, i)
+        trip.append((codes, absmax, g))
+        mats.append((r, c, r, c, w))
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        hin.append((host(trip[i][0]), host(trip[i][1]), host_grad(trip[i][2])))
+    W0 = [host(m[4]).astype(np.float64) for m in mats]
+    segments = [(i, 0, r * c, i) for i, (r, c) in enumerate(shapes)]
+    plan = q.Plan(trip, segments, len(shapes))
+    params = q.make_hparams(lr_full=0.02, rms_scale=0.2, weight_decay=0.01, period=1, precision="f32")
+    say("fp32 grouped muon_step, stream-K symmetric products", shapes)
+    q.muon_step(plan, None, mats, 1, params)
+    torch.cuda.synchronize()
+    states, outs, S, inv, _ = oracle.update_normalize_groups(
+        [(a, b) for a, b, _ in hin], [g for _, _, g in hin], [oracle.BF16] * len(shapes), segments, len(shapes),
+        H.BETA, H.NS_EPS, write_normalized=False)
+    for i, (r, c) in enumerate(shapes):
+        assert_bits_equal(host(trip[i][0]), states[i][0], f"codes[{i}]")
+        assert_bits_equal(host(trip[i][1]), states[i][1], f"absmax[{i}]")
+        m = oracle.widen(outs[i], oracle.BF16).astype(np.float64).reshape(r, c)
+        ref = ns_whole(m, 5, COEF, H.NS_EPS, inv_norm=float(inv[i]))
+        rel, cos = ns_parity(as_f64(trip[i][2]).reshape(r, c), ref)
+        say(f"   O[{i}] {r}x{c}: relF {rel:.3e} min cos {cos:.7f}")
+        assert rel <= NS_F32_BF16OUT_REL and cos >= NS_F32_COS, (i, rel, cos)
+        s = 0.2 * math.sqrt(max(r, c))
+        dW = host(mats[i][4]).astype(np.float64) - W0[i]
+        rel, cos = ns_parity(dW, -0.02 * (s * ref + 0.01 * W0[i]))
+        say(f"   dW[{i}]: relF {rel:.3e} min cos {cos:.7f}")
+        assert rel <= NS_F32_BF16OUT_REL and cos >= NS_F32_COS, (i, rel, cos)
 
 
 def test_muonbp_full_size_state_and_ns():
