@@ -31,7 +31,7 @@ E8M0 scales, 5.0625 B/element, and the NS prologue decodes them); the update
 / NS split then comes from the per-kernel timer.
 
 The default run (llama8b without --carrier, --extras on) also measures the
-other three spec workloads, each in its own timed region after the
+three other full-size workloads, each in its own timed region after the
 headline's buffers are freed, and adds them to the same JSON line:
   layerset28: the 28-layer 2048-hidden set, grouped update + normalisation
               (10.03 B/element), GB/s and fraction of HBM peak;
@@ -476,7 +476,7 @@ def main():
         return
     out = bench_layer(args, q, H, torch)
     if args.workload == "llama8b" and not args.carrier and not args.no_extras:
-        # the other spec workloads, each in its own timed region
+        # the three other full-size workloads, each in its own timed region
         for name, fn in (("layerset28", extra_layerset28), ("muonbp", extra_muonbp), ("grasp", extra_grasp)):
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
