@@ -273,7 +273,13 @@ QM_API qm_status qmuon_update_mxfp8_carrier(const void *host_plan,
  * only ("SYRK y reducción fusionada").  The result overwrites x in its dtype.
  * ---------------------------------------------------------------------- */
 
-/* Workspace bytes for ns_orthogonalize on `batch` matrices of this shape. */
+/* Workspace bytes for ns_orthogonalize on `batch` matrices of this shape.
+ * For the fp32-operand precisions (QM_NS_F32, QM_NS_BF16X3) the figure
+ * includes, where the symmetric products take the stream-K path, two part
+ * slots per workgroup slot of the GPU, so it depends on the compute-unit
+ * count of the current device: query it with the device that will run the
+ * call current (the same holds for the muon_step, muon_apply and GRASP
+ * workspace queries). */
 QM_API size_t ns_workspace_bytes(int64_t rows, int64_t cols, int32_t batch,
                           int32_t precision);
 
